@@ -1,0 +1,212 @@
+"""Throughput of the speculative-sampling verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu-baseline]
+
+Workload: the serving batch, B=64 rows, gamma=5 drafts, V=128256 bfloat16
+logits (target [64, 6, 128256], draft [64, 5, 128256]), T=0.7, synthetic
+logits (N(0, 3^2) with 20 boosted tokens per position, draft = target +
+N(0, 1.5^2)), draft tokens drawn from the draft distribution.  A step is one
+call of the whole verify path over one batch.  Inputs are resident in HBM;
+``--sets`` distinct copies of them are rotated so that the 256 MB
+memory-side cache cannot serve a call from the previous one.
+
+Prints one JSON line: verified rows/s (``value``), the achieved HBM bandwidth
+of the dominant kernel (the streaming statistics kernel) on its algorithmic
+bytes against MI355X's 8 TB/s, and the CPU oracle timed on this host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "verified rows/sec + achieved HBM GB/s (% peak), V=128256 γ=5 B=64 bf16"
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_sampling_amd", "csrc",
+                          "specv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_stream_serving_batch.json")
+
+
+def algorithmic_bytes(B, gamma, V, es, caps, eos_cut, greedy):
+    """Logits bytes the round may consult: per row, target rows
+    min(cap, gamma+1) and (stochastic rows) draft rows min(cap, gamma)."""
+    total = 0
+    for b in range(B):
+        cap = caps[b] if caps[b] >= 1 else 1 << 30
+        cap = min(cap, eos_cut[b])
+        nt = min(cap, gamma + 1)
+        nd = 0 if greedy[b] else min(cap, gamma)
+        total += (nt + nd) * V * es
+    return total
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
+        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch of the statistics kernel from committed rocprofv3
+    counter runs, or None when absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle as it stands, on this host, over whole batches of the same
+    workload at successive steps until about ``budget_s`` seconds."""
+    import oracle
+    tf, df = w.target_f32(), w.draft_f32()
+    rows = 0
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify_sample(tf, df, w.tokens, w.temperature, w.top_k, w.top_p,
+                             w.max_new_tokens, w.seed, steps)
+        rows += w.B
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": rows / el, "unit": "verified rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full batches (B={w.B}, steps 0..{steps - 1}) of the same workload, "
+                      f"{el:.1f} s, numpy float64, one process, one thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verify step shards by batch row with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, ROOT)
+    import synth
+    import speculative_decoding_verification_sampling_amd as sv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sv.load_library()
+    dev = torch.device("cuda:0")
+
+    w = synth.serving_batch()
+    B, gamma, V = w.B, w.gamma, w.V
+    sets = []
+    for _ in range(max(1, args.sets)):
+        sets.append((w.target.to(dev), w.draft.to(dev)))
+    tokens = torch.from_numpy(w.tokens).to(dev)
+    params = sv.make_row_params(B, w.temperature, w.top_k, w.top_p, w.max_new_tokens, dev)
+    out = None
+    v = sv.Verifier(B, gamma, V)
+
+    def call(k, step):
+        t, d = sets[k % len(sets)]
+        return v.verify_sample(t, d, tokens, params, w.seed, step, -1, out=out)
+
+    out = call(0, 0)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        call(i, i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    emitted = torch.zeros((), dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i, 1000 + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # emitted tokens per call, averaged over a few steps (outside the timed region)
+    em = []
+    for i in range(8):
+        o = call(i, 1000 + i)
+        torch.cuda.synchronize()
+        em.append(int(o["num_emitted"].sum()))
+    tokens_per_call = float(np.mean(em))
+
+    # per-kernel durations from HIP events recorded by the library on the
+    # stream the kernels run on
+    v.set_profiling(True)
+    v.profile(reset=True)
+    for i in range(args.steps):
+        call(i, 1000 + i)
+    torch.cuda.synchronize()
+    n, ms_stats, ms_decide = v.profile(reset=True)
+    v.set_profiling(False)
+    avg_stats = ms_stats / n
+    avg_decide = ms_decide / n
+
+    es = w.bytes_per_element()
+    eos_cut = [1 << 30] * B
+    greedy = [bool(t == 0) for t in w.temperature]
+    abytes = algorithmic_bytes(B, gamma, V, es, w.max_new_tokens, eos_cut, greedy)
+    achieved = abytes / (avg_stats * 1e-3) / 1e9
+    traffic = stored_traffic()
+
+    rows_per_s = B / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "verified rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"serving batch B={B} gamma={gamma} V={V} bf16 T=0.7, "
+                               "20 boosted tokens, draft noise 1.5",
+                   "B": B, "gamma": gamma, "V": V, "rotated_input_sets": len(sets)},
+        "emitted_tokens_per_s": tokens_per_call / (ms_step * 1e-3),
+        "step_hbm_gbps_algorithmic": abytes / (ms_step * 1e-3) / 1e9,
+        "kernels_us": {"k_stream": avg_stats * 1e3, "k_sample": avg_decide * 1e3},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_stream",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": abytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    v.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

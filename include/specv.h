@@ -1,0 +1,184 @@
+/*
+ * libspecv: the speculative-sampling verify step on AMD Instinct MI355X
+ * (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * The operation (one verification round per batch row) is the one defined in
+ * "11.1 核心原理: Draft + Verify 与 Rejection Sampling", section 11.1.2 and
+ * pseudo-code 10-1, and in "Fast Inference from Transformers via Speculative
+ * Decoding" (speculative sampling):
+ *
+ *   for i = 0 .. gamma-1:   accept d_i with probability min(1, p_i(d_i) / q_i(d_i))
+ *                            (uniform u: accept iff u * q_i(d_i) < p_i(d_i))
+ *   at the first rejection:  emit t ~ norm(max(p_i - q_i, 0)) and stop
+ *   if all were accepted:    emit the bonus t ~ p_gamma
+ *   greedy rows:             accept while d_i == argmax p_i, emit the argmax
+ *                            at the first mismatch (or as the bonus)
+ *
+ * p_i / q_i are the target / draft distributions after temperature, top-k and
+ * top-p (11.1.2: both processed, q kept as the truncated distribution actually
+ * sampled).  Emission stops after the first emitted EOS and after
+ * max_new_tokens tokens; a correction or bonus token past the cap is not drawn
+ * (remark after pseudo-code 10-1).
+ *
+ * Layouts (all device memory unless stated):
+ *   target logits  [B, gamma+1, V]: row (b, i) starts at
+ *                  target + b*t_stride_b + i*t_stride_pos (strides in
+ *                  ELEMENTS); vocabulary contiguous.  Row i checks draft d_i;
+ *                  row gamma is the bonus distribution (11.1.1 alignment).
+ *   draft logits   [B, gamma, V] likewise; row (b, i) is q_i for d_i.
+ *   draft tokens   int32 [B, gamma], contiguous.
+ *   outputs        int32 num_accepted [B], out_tokens [B, gamma+1] (emitted
+ *                  tokens then -1 padding), num_emitted [B], row_flags [B].
+ *
+ * Random numbers: Philox4x32-10 (Salmon et al., SC'11), key = seed (low word
+ * first), counter = (b, i, purpose, step), u = (word0 >> 8) * 2^-24.
+ * Purposes: 1 accept test, 2 correction sample, 3 bonus sample (0 is left to
+ * the caller's draft sampler).  b is the row index within the call.
+ *
+ * Ownership: the caller owns every input and output buffer.  A handle owns a
+ * device workspace allocated once by specv_create and freed by
+ * specv_destroy; verify calls allocate nothing.  One handle serves one stream
+ * at a time (calls on a handle must not overlap).
+ *
+ * Errors: every argument error is reported synchronously, before anything is
+ * enqueued, as a non-zero specv_status.  Calls are otherwise asynchronous on
+ * the given stream; outputs are valid once the stream reaches them.  Data
+ * faults found on the device never abort: they set row_flags bits and the row
+ * takes the documented fallback.
+ */
+#ifndef SPECV_H
+#define SPECV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef SPECV_API
+#define SPECV_API __attribute__((visibility("default")))
+#endif
+
+typedef struct specv_ctx* specv_handle;
+
+typedef enum {
+    SPECV_OK = 0,
+    SPECV_E_NULL = 1,      /* a required pointer is NULL                          */
+    SPECV_E_SHAPE = 2,     /* B, gamma or V out of range, bad strides             */
+    SPECV_E_DTYPE = 3,     /* dtype not one of specv_dtype                        */
+    SPECV_E_ALIGN = 4,     /* output or token pointer not 4-byte aligned          */
+    SPECV_E_CAPACITY = 5,  /* B, gamma or V above the handle's configured maximum */
+    SPECV_E_PARAM = 6,     /* bad handle configuration                            */
+    SPECV_E_NOMEM = 7,     /* workspace allocation failed (specv_create)          */
+    SPECV_E_HIP = 8        /* a HIP runtime call failed                           */
+} specv_status;
+
+typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype;
+
+/* Row flag bits (row_flags[b]). */
+#define SPECV_FLAG_TOKEN_OOR          (1 << 0) /* a draft token outside [0, V): row emits nothing   */
+#define SPECV_FLAG_NONFINITE_ROW      (1 << 1) /* a consulted row has NaN/+inf or no finite value:
+                                                  row emits nothing                                 */
+#define SPECV_FLAG_Q_ZERO             (1 << 2) /* an accept test met d_i outside q_i's support
+                                                  (accepted iff p_i(d_i) > 0)                       */
+#define SPECV_FLAG_RESIDUAL_FALLBACK  (1 << 3) /* residual mass 0 / not finite: sampled from p_i    */
+#define SPECV_FLAG_CAND_OVERFLOW      (1 << 4) /* truncation candidates exceeded the workspace:
+                                                  the row emits nothing                             */
+#define SPECV_FLAG_TOPP_NEAR          (1 << 5) /* a top-p cumulative mass was within 1e-5 of top_p  */
+#define SPECV_FLAG_UNSUPPORTED        (1 << 6) /* truncation the handle cannot run: top_p < 1
+                                                  without 0 < top_k < V, or top_k above the
+                                                  handle's max_top_k: the row emits nothing         */
+
+#define SPECV_MAX_GAMMA 32
+#define SPECV_MAX_TOP_K 1024
+#define SPECV_MAX_VOCAB 524288
+
+typedef struct {
+    int device;      /* HIP device ordinal the handle runs on                     */
+    int max_batch;   /* largest B of any call                                     */
+    int max_gamma;   /* largest gamma (0 .. SPECV_MAX_GAMMA)                      */
+    int max_vocab;   /* largest V (at most SPECV_MAX_VOCAB)                       */
+    int max_top_k;   /* largest top_k of truncated rows (0 .. SPECV_MAX_TOP_K);
+                        0 reserves no candidate workspace: truncated rows are then
+                        flagged SPECV_FLAG_UNSUPPORTED                            */
+} specv_config;
+
+/* Per-row sampling parameters, device array [B] (16 bytes each). */
+typedef struct {
+    float temperature;      /* > 0: stochastic verify of z / T; == 0: greedy row        */
+    int32_t top_k;          /* 0 < k < V keeps tokens >= the k-th largest logit (ties
+                               kept); <= 0 or >= V: off                                  */
+    float top_p;            /* < 1: keep the smallest value-ordered set with mass >=
+                               top_p (ties kept); >= 1: off                              */
+    int32_t max_new_tokens; /* >= 1: at most this many tokens emitted; <= 0: no cap      */
+} specv_row_params;
+
+/* Optional diagnostic outputs (device pointers, each may be NULL). */
+typedef struct {
+    float* p_at_draft;    /* [B, gamma]: p_i(d_i) for every accept test run, NaN otherwise */
+    float* q_at_draft;    /* [B, gamma]: q_i(d_i) likewise                                */
+    float* residual_sum;  /* [B]: sum_v max(p_n - q_n, 0) at the rejected position, else 0 */
+} specv_diag;
+
+/* Create a handle: selects cfg->device and allocates the workspace sized for
+ * (max_batch, max_gamma, max_vocab).  *out is set on success only. */
+SPECV_API specv_status specv_create(const specv_config* cfg, specv_handle* out);
+
+/* Stochastic verification of B rows (rows whose temperature is 0 are verified
+ * greedily).
+ *   stream          hipStream_t (NULL = the null stream), as an opaque pointer
+ *   target_logits   [B, gamma+1, V] of dtype, row strides t_stride_b / t_stride_pos
+ *   draft_logits    [B, gamma, V] of dtype, row strides d_stride_b / d_stride_pos
+ *                   (may be NULL when gamma == 0)
+ *   draft_tokens    int32 [B, gamma] (may be NULL when gamma == 0)
+ *   row_params      specv_row_params [B]
+ *   seed, step      Philox key and the counter's step word
+ *   eos_id          token that ends emission, or -1 for none
+ *   out_*           see the layout above; out_row_flags may be NULL
+ *   diag            host struct of optional device pointers, or NULL
+ * B == 0 is a no-op.  1 <= V, 0 <= gamma <= SPECV_MAX_GAMMA. */
+SPECV_API specv_status specv_verify_sample(specv_handle h, void* stream,
+                                 const void* target_logits, int64_t t_stride_b, int64_t t_stride_pos,
+                                 const void* draft_logits, int64_t d_stride_b, int64_t d_stride_pos,
+                                 specv_dtype dtype, int B, int gamma, int V,
+                                 const int32_t* draft_tokens, const specv_row_params* row_params,
+                                 uint64_t seed, uint32_t step, int32_t eos_id,
+                                 int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags,
+                                 const specv_diag* diag);
+
+/* Greedy verification (11.1.2): accept while d_i == argmax of the raw target
+ * logits (lowest index on ties), emit the argmax at the first mismatch or as
+ * the bonus.  Draft logits are not read.
+ *   max_new_tokens  int32 [B] caps (<= 0: no cap), or NULL for none. */
+SPECV_API specv_status specv_verify_greedy(specv_handle h, void* stream,
+                                 const void* target_logits, int64_t t_stride_b, int64_t t_stride_pos,
+                                 specv_dtype dtype, int B, int gamma, int V,
+                                 const int32_t* draft_tokens, const int32_t* max_new_tokens,
+                                 int32_t eos_id,
+                                 int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags);
+
+/* Per-kernel timing for measurement.  With enable != 0 every later verify
+ * call records HIP events on its stream around each of its kernels; the
+ * events are created here (not in the verify calls).  specv_get_profile waits
+ * for the recorded events, returns the number of profiled calls and the summed
+ * milliseconds of the streaming statistics kernel (ms_stats) and of the
+ * decision / sampling kernel (ms_decide) since the last reset, and resets the
+ * sums when reset != 0.  Errors: SPECV_E_NULL, SPECV_E_HIP. */
+SPECV_API specv_status specv_set_profiling(specv_handle h, int enable);
+SPECV_API specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms_stats,
+                                         double* ms_decide);
+
+/* Free the workspace and the handle.  Waits for the device first.  NULL is
+ * accepted. */
+SPECV_API specv_status specv_destroy(specv_handle h);
+
+/* Static description of a status code. */
+SPECV_API const char* specv_status_string(specv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECV_H */

@@ -1,0 +1,282 @@
+"""Python binding of libspecv, the speculative-sampling verify step for MI355X.
+
+Argument marshalling only: every step of the verify path runs in the HIP
+kernels of ``libspecv.so``.  PyTorch supplies device memory (tensors) and
+the stream (``torch.cuda.current_stream()``); no torch computation happens
+on the path.  Build the library first with
+``python -m speculative_decoding_verification_sampling_amd.build``; if it is
+missing, importing works but every call raises.
+
+    v = Verifier(max_batch=64, max_gamma=5, max_vocab=128256)
+    params = make_row_params(64, temperature=0.7, device="cuda")
+    out = v.verify_sample(target, draft, tokens, params, seed=1234)
+    out["out_tokens"], out["num_emitted"], out["num_accepted"], out["row_flags"]
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Verifier",
+    "make_row_params",
+    "load_library",
+    "library_path",
+    "SpecvError",
+    "FLAG_TOKEN_OOR",
+    "FLAG_NONFINITE_ROW",
+    "FLAG_Q_ZERO",
+    "FLAG_RESIDUAL_FALLBACK",
+    "FLAG_CAND_OVERFLOW",
+    "FLAG_TOPP_NEAR",
+    "FLAG_UNSUPPORTED",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+FLAG_TOKEN_OOR = 1 << 0
+FLAG_NONFINITE_ROW = 1 << 1
+FLAG_Q_ZERO = 1 << 2
+FLAG_RESIDUAL_FALLBACK = 1 << 3
+FLAG_CAND_OVERFLOW = 1 << 4
+FLAG_TOPP_NEAR = 1 << 5
+FLAG_UNSUPPORTED = 1 << 6
+
+SPECV_F32 = 0
+SPECV_BF16 = 1
+
+EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_greedy",
+                    "specv_destroy", "specv_status_string", "specv_set_profiling",
+                    "specv_get_profile")
+
+
+class SpecvError(RuntimeError):
+    pass
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_int), ("max_batch", ctypes.c_int),
+                ("max_gamma", ctypes.c_int), ("max_vocab", ctypes.c_int),
+                ("max_top_k", ctypes.c_int)]
+
+
+class _Diag(ctypes.Structure):
+    _fields_ = [("p_at_draft", ctypes.c_void_p), ("q_at_draft", ctypes.c_void_p),
+                ("residual_sum", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path():
+    return os.environ.get("SPECV_LIBRARY", os.path.join(_HERE, "libspecv.so"))
+
+
+def load_library():
+    """Load libspecv.so (once).  Raises SpecvError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise SpecvError(f"libspecv.so not found at {path}; build it with "
+                         "`python -m speculative_decoding_verification_sampling_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, u32, u64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                              ctypes.c_uint32, ctypes.c_uint64)
+    lib.specv_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(vp)]
+    lib.specv_create.restype = ctypes.c_int
+    lib.specv_destroy.argtypes = [vp]
+    lib.specv_destroy.restype = ctypes.c_int
+    lib.specv_status_string.argtypes = [ctypes.c_int]
+    lib.specv_status_string.restype = ctypes.c_char_p
+    lib.specv_verify_sample.argtypes = [
+        vp, vp,
+        vp, i64, i64,
+        vp, i64, i64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, vp,
+        u64, u32, i32,
+        vp, vp, vp, vp,
+        ctypes.POINTER(_Diag)]
+    lib.specv_verify_sample.restype = ctypes.c_int
+    lib.specv_verify_greedy.argtypes = [
+        vp, vp,
+        vp, i64, i64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, vp, i32,
+        vp, vp, vp, vp]
+    lib.specv_verify_greedy.restype = ctypes.c_int
+    lib.specv_set_profiling.argtypes = [vp, ctypes.c_int]
+    lib.specv_set_profiling.restype = ctypes.c_int
+    lib.specv_get_profile.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                      ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_double)]
+    lib.specv_get_profile.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = load_library().specv_status_string(status).decode()
+        raise SpecvError(f"{what} failed: status {status} ({msg})")
+
+
+def make_row_params(B, temperature=1.0, top_k=0, top_p=1.0, max_new_tokens=0, device="cuda"):
+    """specv_row_params[B] as an int32 tensor [B, 4] on ``device``.
+
+    Columns: temperature (float32 bits), top_k, top_p (float32 bits),
+    max_new_tokens.  Each argument is a scalar or a length-B sequence.
+    """
+    rec = np.zeros(B, dtype=[("t", "<f4"), ("k", "<i4"), ("p", "<f4"), ("cap", "<i4")])
+    rec["t"] = temperature
+    rec["k"] = top_k
+    rec["p"] = top_p
+    rec["cap"] = max_new_tokens
+    host = torch.from_numpy(rec.view(np.int32).reshape(B, 4).copy())
+    return host.to(device)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SPECV_BF16
+    if t.dtype == torch.float32:
+        return SPECV_F32
+    raise SpecvError(f"unsupported logits dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _rows(t, name, lead):
+    if not t.is_cuda:
+        raise SpecvError(f"{name} must be a device tensor")
+    if t.dim() != 3 or (lead is not None and t.shape[0] != lead):
+        raise SpecvError(f"{name} must be [B, positions, V], got {tuple(t.shape)}")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise SpecvError(f"{name} must be contiguous along the vocabulary")
+    return t.stride(0), t.stride(1)
+
+
+class Verifier:
+    """A libspecv handle: owns the device workspace for calls up to the given
+    maxima.  Calls run on the current torch stream of the handle's device."""
+
+    def __init__(self, max_batch, max_gamma, max_vocab, max_top_k=0, device=0):
+        lib = load_library()
+        self.device = int(device)
+        cfg = _Config(self.device, int(max_batch), int(max_gamma), int(max_vocab), int(max_top_k))
+        h = ctypes.c_void_p()
+        _check(lib.specv_create(ctypes.byref(cfg), ctypes.byref(h)), "specv_create")
+        self._h = h
+        self.max_batch, self.max_gamma, self.max_vocab = max_batch, max_gamma, max_vocab
+        self.max_top_k = max_top_k
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            load_library().specv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def set_profiling(self, enable=True):
+        """Record HIP events around each kernel of later calls."""
+        _check(load_library().specv_set_profiling(self._h, int(bool(enable))), "specv_set_profiling")
+
+    def profile(self, reset=True):
+        """(calls, ms of the statistics kernel, ms of the decision kernel),
+        summed over profiled calls; waits for the recorded events."""
+        n = ctypes.c_int()
+        a = ctypes.c_double()
+        b = ctypes.c_double()
+        _check(load_library().specv_get_profile(self._h, int(bool(reset)), ctypes.byref(n),
+                                                ctypes.byref(a), ctypes.byref(b)),
+               "specv_get_profile")
+        return n.value, a.value, b.value
+
+    def _stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    def _outputs(self, B, gamma, device, out):
+        if out is not None:
+            return out
+        z = dict(dtype=torch.int32, device=device)
+        return {"num_accepted": torch.empty(B, **z), "out_tokens": torch.empty(B, gamma + 1, **z),
+                "num_emitted": torch.empty(B, **z), "row_flags": torch.empty(B, **z)}
+
+    def verify_sample(self, target, draft, tokens, row_params, seed, step=0, eos_id=-1,
+                      out=None, diag=False):
+        """Stochastic verification.  target [B, gamma+1, V], draft [B, gamma, V]
+        (same dtype), tokens int32 [B, gamma], row_params from make_row_params.
+        Returns a dict of device tensors (plus p_at_draft, q_at_draft,
+        residual_sum when ``diag``).  Asynchronous on the current stream."""
+        B, g1, V = target.shape
+        gamma = g1 - 1
+        tsb, tsp = _rows(target, "target", None)
+        dsb = dsp = 0
+        if gamma > 0:
+            dsb, dsp = _rows(draft, "draft", B)
+            if draft.shape[1] != gamma or draft.shape[2] != V or draft.dtype != target.dtype:
+                raise SpecvError("draft must be [B, gamma, V] with the target's dtype")
+        for t, n in ((tokens, "tokens"), (row_params, "row_params")):
+            if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+                raise SpecvError(f"{n} must be a contiguous int32 device tensor")
+        if tokens.shape != (B, gamma) or row_params.shape != (B, 4):
+            raise SpecvError("tokens must be [B, gamma] and row_params [B, 4]")
+        o = self._outputs(B, gamma, target.device, out)
+        d = None
+        if diag:
+            o["p_at_draft"] = torch.empty(B, gamma, dtype=torch.float32, device=target.device)
+            o["q_at_draft"] = torch.empty(B, gamma, dtype=torch.float32, device=target.device)
+            o["residual_sum"] = torch.empty(B, dtype=torch.float32, device=target.device)
+            d = _Diag(o["p_at_draft"].data_ptr(), o["q_at_draft"].data_ptr(),
+                      o["residual_sum"].data_ptr())
+        st = load_library().specv_verify_sample(
+            self._h, self._stream(),
+            _ptr(target), tsb, tsp,
+            _ptr(draft if gamma > 0 else None), dsb, dsp,
+            _dtype_code(target), B, gamma, V,
+            _ptr(tokens), _ptr(row_params),
+            int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF, int(eos_id),
+            _ptr(o["num_accepted"]), _ptr(o["out_tokens"]), _ptr(o["num_emitted"]),
+            _ptr(o.get("row_flags")),
+            ctypes.byref(d) if d is not None else None)
+        _check(st, "specv_verify_sample")
+        return o
+
+    def verify_greedy(self, target, tokens, max_new_tokens=None, eos_id=-1, out=None):
+        """Greedy verification.  target [B, gamma+1, V], tokens int32 [B, gamma],
+        max_new_tokens int32 [B] device tensor or None."""
+        B, g1, V = target.shape
+        gamma = g1 - 1
+        tsb, tsp = _rows(target, "target", None)
+        if tokens.dtype != torch.int32 or not tokens.is_contiguous() or tokens.shape != (B, gamma):
+            raise SpecvError("tokens must be a contiguous int32 [B, gamma] device tensor")
+        if max_new_tokens is not None and (max_new_tokens.dtype != torch.int32 or
+                                           max_new_tokens.shape != (B,)):
+            raise SpecvError("max_new_tokens must be an int32 [B] device tensor")
+        o = self._outputs(B, gamma, target.device, out)
+        st = load_library().specv_verify_greedy(
+            self._h, self._stream(),
+            _ptr(target), tsb, tsp,
+            _dtype_code(target), B, gamma, V,
+            _ptr(tokens), _ptr(max_new_tokens), int(eos_id),
+            _ptr(o["num_accepted"]), _ptr(o["out_tokens"]), _ptr(o["num_emitted"]),
+            _ptr(o.get("row_flags")))
+        _check(st, "specv_verify_greedy")
+        return o

@@ -1,0 +1,314 @@
+// libspecv C ABI: argument validation, workspace ownership, launches.
+//
+// Every argument error is returned before anything is enqueued.  Calls are
+// asynchronous on the caller's stream and allocate nothing: the workspace is
+// allocated once in specv_create, sized from the handle's maxima.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <new>
+#include <vector>
+
+#include "specv.h"
+#include "specv_internal.hpp"
+
+struct specv_ctx {
+    specv_config cfg;
+    int max_rows;
+    int max_chunks;
+    int cand_cap;      // candidates per (row, chunk); 0 without truncation support
+    specv::Workspace ws;
+    // profiling: a ring of event triples, drained by specv_get_profile or
+    // when the ring wraps
+    bool prof = false;
+    std::vector<hipEvent_t> ev;     // 3 * kProfRing
+    std::vector<char> ev_live;      // kProfRing
+    size_t ev_next = 0;
+    int prof_calls = 0;
+    double ms_stats = 0.0, ms_decide = 0.0;
+};
+
+namespace {
+constexpr size_t kProfRing = 512;
+
+hipError_t drain_slot(specv_ctx* h, size_t slot) {
+    if (!h->ev_live[slot]) return hipSuccess;
+    hipEvent_t* e = &h->ev[3 * slot];
+    hipError_t err = hipEventSynchronize(e[2]);
+    if (err != hipSuccess) return err;
+    float a = 0.f, b = 0.f;
+    err = hipEventElapsedTime(&a, e[0], e[1]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&b, e[1], e[2]);
+    if (err != hipSuccess) return err;
+    h->ms_stats += a;
+    h->ms_decide += b;
+    h->prof_calls += 1;
+    h->ev_live[slot] = 0;
+    return hipSuccess;
+}
+
+// Event triple for the next call, or nullptr when profiling is off.
+hipEvent_t* next_events(specv_ctx* h) {
+    if (!h->prof) return nullptr;
+    const size_t slot = h->ev_next % kProfRing;
+    if (drain_slot(h, slot) != hipSuccess) return nullptr;
+    h->ev_next++;
+    h->ev_live[slot] = 1;
+    return &h->ev[3 * slot];
+}
+}  // namespace
+
+namespace {
+
+template <typename T>
+hipError_t alloc(T** p, size_t count) {
+    *p = nullptr;
+    return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T) + 256);
+}
+
+void free_ws(specv::Workspace& ws) {
+    if (ws.part) (void)hipFree(ws.part);
+    if (ws.wsum) (void)hipFree(ws.wsum);
+    if (ws.counter) (void)hipFree(ws.counter);
+    if (ws.counter2) (void)hipFree(ws.counter2);
+    if (ws.dec) (void)hipFree(ws.dec);
+    if (ws.cand) (void)hipFree(ws.cand);
+    if (ws.cand_cnt) (void)hipFree(ws.cand_cnt);
+    if (ws.trow) (void)hipFree(ws.trow);
+    if (ws.kept) (void)hipFree(ws.kept);
+    ws = specv::Workspace{};
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validation shared by both entry points.
+specv_status check_common(specv_handle h, const void* target, int64_t t_sb, int64_t t_sp,
+                          specv_dtype dtype, int B, int gamma, int V, const int32_t* tokens,
+                          int32_t* out_acc, int32_t* out_tok, int32_t* out_emit,
+                          int32_t* out_flags) {
+    if (!h) return SPECV_E_NULL;
+    if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
+    if (B < 0 || gamma < 0 || gamma > SPECV_MAX_GAMMA || V < 1) return SPECV_E_SHAPE;
+    if (t_sb < 0 || t_sp < 0) return SPECV_E_SHAPE;
+    if (B > h->cfg.max_batch || gamma > h->cfg.max_gamma || V > h->cfg.max_vocab)
+        return SPECV_E_CAPACITY;
+    if (B == 0) return SPECV_OK;
+    if (!target || !out_acc || !out_tok || !out_emit) return SPECV_E_NULL;
+    if (gamma > 0 && !tokens) return SPECV_E_NULL;
+    const size_t es = dtype == SPECV_BF16 ? 2 : 4;
+    if (!aligned(target, es)) return SPECV_E_ALIGN;
+    if (!aligned(out_acc, 4) || !aligned(out_tok, 4) || !aligned(out_emit, 4) ||
+        (out_flags && !aligned(out_flags, 4)) || (tokens && !aligned(tokens, 4)))
+        return SPECV_E_ALIGN;
+    return SPECV_OK;
+}
+
+bool rows_vec_aligned(const void* base, int64_t sb, int64_t sp, size_t es) {
+    return aligned(base, 16) && ((sb * (int64_t)es) % 16) == 0 && ((sp * (int64_t)es) % 16) == 0;
+}
+
+specv::Args base_args(specv_handle h, int B, int gamma, int V) {
+    specv::Args a{};
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.C = (V + specv::kChunk - 1) / specv::kChunk;
+    a.R = 2 * gamma + 1;
+    a.ws = h->ws;
+    a.cand_cap = h->cand_cap;
+    a.max_top_k = h->cfg.max_top_k;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* specv_status_string(specv_status s) {
+    switch (s) {
+        case SPECV_OK: return "ok";
+        case SPECV_E_NULL: return "null pointer argument";
+        case SPECV_E_SHAPE: return "invalid shape or stride";
+        case SPECV_E_DTYPE: return "unsupported dtype";
+        case SPECV_E_ALIGN: return "misaligned pointer";
+        case SPECV_E_CAPACITY: return "size above the handle's configured maximum";
+        case SPECV_E_PARAM: return "invalid configuration";
+        case SPECV_E_NOMEM: return "device allocation failed";
+        case SPECV_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+specv_status specv_create(const specv_config* cfg, specv_handle* out) {
+    if (!cfg || !out) return SPECV_E_NULL;
+    if (cfg->max_batch < 1 || cfg->max_gamma < 0 || cfg->max_gamma > SPECV_MAX_GAMMA ||
+        cfg->max_vocab < 1 || cfg->max_vocab > SPECV_MAX_VOCAB || cfg->max_top_k < 0 ||
+        cfg->max_top_k > SPECV_MAX_TOP_K)
+        return SPECV_E_PARAM;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
+        return SPECV_E_PARAM;
+    if (hipSetDevice(cfg->device) != hipSuccess) return SPECV_E_HIP;
+
+    specv_ctx* h = new (std::nothrow) specv_ctx{};
+    if (!h) return SPECV_E_NOMEM;
+    h->cfg = *cfg;
+    h->max_rows = 2 * cfg->max_gamma + 1;
+    h->max_chunks = (cfg->max_vocab + specv::kChunk - 1) / specv::kChunk;
+    h->cand_cap = cfg->max_top_k > 0 ? cfg->max_top_k + specv::kTieSlack : 0;
+    if (h->cand_cap > specv::kChunk) h->cand_cap = specv::kChunk;
+    const size_t rows = (size_t)cfg->max_batch * h->max_rows;
+    const size_t rc = rows * h->max_chunks;
+    specv::Workspace& ws = h->ws;
+    bool ok = alloc(&ws.part, rc) == hipSuccess &&
+              alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks) == hipSuccess &&
+              alloc(&ws.counter, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
+              alloc(&ws.counter2, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
+              alloc(&ws.dec, (size_t)cfg->max_batch) == hipSuccess;
+    // candidate storage for truncated rows, reserved only when asked for
+    if (ok && h->cand_cap > 0)
+        ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
+             alloc(&ws.cand_cnt, rc) == hipSuccess && alloc(&ws.trow, rows) == hipSuccess &&
+             alloc(&ws.kept, rows * specv::kKeptCap) == hipSuccess;
+    const size_t counter_bytes = (size_t)cfg->max_batch * specv::kCounterStride * sizeof(unsigned);
+    if (ok) ok = hipMemset(ws.counter, 0, counter_bytes) == hipSuccess;
+    if (ok) ok = hipMemset(ws.counter2, 0, counter_bytes) == hipSuccess;
+    if (ok) ok = hipDeviceSynchronize() == hipSuccess;
+    if (!ok) {
+        free_ws(ws);
+        delete h;
+        (void)hipGetLastError();
+        return SPECV_E_NOMEM;
+    }
+    *out = h;
+    return SPECV_OK;
+}
+
+specv_status specv_set_profiling(specv_handle h, int enable) {
+    if (!h) return SPECV_E_NULL;
+    if (enable && h->ev.empty()) {
+        if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
+        h->ev.assign(3 * kProfRing, nullptr);
+        h->ev_live.assign(kProfRing, 0);
+        for (auto& e : h->ev)
+            if (hipEventCreate(&e) != hipSuccess) return SPECV_E_HIP;
+    }
+    h->prof = enable != 0;
+    return SPECV_OK;
+}
+
+specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms_stats,
+                               double* ms_decide) {
+    if (!h) return SPECV_E_NULL;
+    for (size_t s = 0; s < h->ev_live.size(); ++s)
+        if (drain_slot(h, s) != hipSuccess) return SPECV_E_HIP;
+    if (calls) *calls = h->prof_calls;
+    if (ms_stats) *ms_stats = h->ms_stats;
+    if (ms_decide) *ms_decide = h->ms_decide;
+    if (reset) {
+        h->prof_calls = 0;
+        h->ms_stats = h->ms_decide = 0.0;
+    }
+    return SPECV_OK;
+}
+
+specv_status specv_destroy(specv_handle h) {
+    if (!h) return SPECV_OK;
+    (void)hipSetDevice(h->cfg.device);
+    (void)hipDeviceSynchronize();
+    for (auto& e : h->ev)
+        if (e) (void)hipEventDestroy(e);
+    free_ws(h->ws);
+    delete h;
+    return SPECV_OK;
+}
+
+specv_status specv_verify_sample(specv_handle h, void* stream, const void* target_logits,
+                                 int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
+                                 int64_t d_stride_b, int64_t d_stride_pos, specv_dtype dtype, int B,
+                                 int gamma, int V, const int32_t* draft_tokens,
+                                 const specv_row_params* row_params, uint64_t seed, uint32_t step,
+                                 int32_t eos_id, int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags,
+                                 const specv_diag* diag) {
+    specv_status st = check_common(h, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
+                                   draft_tokens, out_num_accepted, out_tokens, out_num_emitted,
+                                   out_row_flags);
+    if (st != SPECV_OK || B == 0) return st;
+    if (!row_params) return SPECV_E_NULL;
+    if (gamma > 0 && !draft_logits) return SPECV_E_NULL;
+    if (d_stride_b < 0 || d_stride_pos < 0) return SPECV_E_SHAPE;
+    const size_t es = dtype == SPECV_BF16 ? 2 : 4;
+    if (gamma > 0 && !aligned(draft_logits, es)) return SPECV_E_ALIGN;
+    if (!aligned(row_params, 16)) return SPECV_E_ALIGN;
+    if (diag && ((diag->p_at_draft && !aligned(diag->p_at_draft, 4)) ||
+                 (diag->q_at_draft && !aligned(diag->q_at_draft, 4)) ||
+                 (diag->residual_sum && !aligned(diag->residual_sum, 4))))
+        return SPECV_E_ALIGN;
+
+    specv::Args a = base_args(h, B, gamma, V);
+    a.tgt = target_logits;
+    a.t_sb = t_stride_b;
+    a.t_sp = t_stride_pos;
+    a.drf = draft_logits;
+    a.d_sb = d_stride_b;
+    a.d_sp = d_stride_pos;
+    a.greedy_all = 0;
+    a.tokens = draft_tokens;
+    a.params = row_params;
+    a.caps = nullptr;
+    a.seed = seed;
+    a.step = step;
+    a.eos = eos_id;
+    a.out_acc = out_num_accepted;
+    a.out_tok = out_tokens;
+    a.out_emit = out_num_emitted;
+    a.out_flags = out_row_flags;
+    a.p_at = diag ? diag->p_at_draft : nullptr;
+    a.q_at = diag ? diag->q_at_draft : nullptr;
+    a.wres = diag ? diag->residual_sum : nullptr;
+    const bool vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es) &&
+                     (gamma == 0 || rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es));
+    if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
+    if (specv::launch_verify(a, dtype == SPECV_BF16, vec, static_cast<hipStream_t>(stream),
+                             next_events(h)) != hipSuccess)
+        return SPECV_E_HIP;
+    return SPECV_OK;
+}
+
+specv_status specv_verify_greedy(specv_handle h, void* stream, const void* target_logits,
+                                 int64_t t_stride_b, int64_t t_stride_pos, specv_dtype dtype, int B,
+                                 int gamma, int V, const int32_t* draft_tokens,
+                                 const int32_t* max_new_tokens, int32_t eos_id,
+                                 int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags) {
+    specv_status st = check_common(h, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
+                                   draft_tokens, out_num_accepted, out_tokens, out_num_emitted,
+                                   out_row_flags);
+    if (st != SPECV_OK || B == 0) return st;
+    if (max_new_tokens && !aligned(max_new_tokens, 4)) return SPECV_E_ALIGN;
+    const size_t es = dtype == SPECV_BF16 ? 2 : 4;
+    specv::Args a = base_args(h, B, gamma, V);
+    a.tgt = target_logits;
+    a.t_sb = t_stride_b;
+    a.t_sp = t_stride_pos;
+    a.drf = nullptr;
+    a.greedy_all = 1;
+    a.tokens = draft_tokens;
+    a.params = nullptr;
+    a.caps = max_new_tokens;
+    a.eos = eos_id;
+    a.out_acc = out_num_accepted;
+    a.out_tok = out_tokens;
+    a.out_emit = out_num_emitted;
+    a.out_flags = out_row_flags;
+    const bool vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es);
+    if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
+    if (specv::launch_verify(a, dtype == SPECV_BF16, vec, static_cast<hipStream_t>(stream),
+                             next_events(h)) != hipSuccess)
+        return SPECV_E_HIP;
+    return SPECV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the libspecv host code and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specv.h"
+
+namespace specv {
+
+constexpr int kBlock = 256;             // threads per workgroup (4 wave64)
+constexpr int kWave = 64;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kChunk = 8192;            // vocabulary entries per chunk (32 per thread)
+constexpr int kPerThread = kChunk / kBlock;
+constexpr int kMaxChunks = 64;          // V <= 64 * 8192 = 524288
+constexpr int kMaxRows = 2 * SPECV_MAX_GAMMA + 1;
+constexpr int kCounterStride = 64;     // one arrival counter per 256-byte slot: atomics
+                                        // on one cache line serialize across the device
+constexpr int kTieSlack = 256;          // candidates per chunk beyond top_k (ties)
+constexpr int kKeptCap = 2048;          // kept set per row after the row-level top-k
+
+// Per (row, chunk) statistics from the streaming pass.
+//  sampling rows: m = max raw logit, s = sum exp2((z - m) * scale)
+//  greedy rows:   m = max raw logit, arg = its lowest index
+struct Part {
+    float m;
+    float s;
+    int arg;
+    unsigned bad;   // 1: NaN / +inf seen
+};
+
+struct Cand {
+    float v;        // raw logit
+    int idx;        // token index
+};
+
+// Result of the row-level truncation (top-k then top-p) for one logits row.
+struct TruncRow {
+    float zmax;     // largest raw logit
+    float tk;       // raw value of the top-k threshold
+    float tstar;    // raw value of the top-p threshold (>= tk)
+    float S;        // sum over the kept set of exp2((z - zmax) * scale)
+    int n_kept;     // kept entries (sorted by value desc, index asc) in Workspace::kept
+    unsigned flags; // SPECV_FLAG_* bits found while truncating
+    int pad0, pad1;
+};
+
+// Outcome of one batch row's accept tests, handed from the streaming
+// kernel to the sampling kernel.
+struct Dec {
+    int kind;             // 0: nothing to sample (outputs written); 1: correction; 2: bonus
+    int pos;              // rejected position, or gamma for the bonus
+    float u;              // uniform of the correction / bonus draw
+    float mt, invt;       // target row max and 1 / sum (exp2 units)
+    float mq, invq;       // draft row max and 1 / sum (correction only)
+    float scale;          // log2(e) / T
+    int nemit;            // tokens emitted before the sampled one
+    int nacc;
+    unsigned flags;
+    int emit[SPECV_MAX_GAMMA + 1];
+};
+
+struct Workspace {
+    Part* part;           // [max_batch * max_rows * max_chunks]
+    float* wsum;          // [max_batch * max_chunks]
+    unsigned* counter;    // [max_batch * kCounterStride] arrivals in the streaming kernel
+    unsigned* counter2;   // [max_batch * kCounterStride] arrivals in the sampling kernel;
+                          // both zero between calls
+    Dec* dec;             // [max_batch]
+    Cand* cand;           // [max_batch * rows * max_chunks * cand_cap]
+    int* cand_cnt;        // [max_batch * rows * max_chunks]
+    TruncRow* trow;       // [max_batch * rows]
+    Cand* kept;           // [max_batch * rows * kKeptCap]
+};
+
+struct Args {
+    const void* tgt;
+    long long t_sb, t_sp;         // element strides of target rows
+    const void* drf;
+    long long d_sb, d_sp;
+    int B, gamma, V;
+    int C;                        // chunks per row
+    int R;                        // logits rows per batch row: 2 * gamma + 1
+    int greedy_all;               // specv_verify_greedy
+    int cand_cap;                 // candidates per (row, chunk); 0: no truncation
+    int max_top_k;
+    const int* tokens;            // [B, gamma]
+    const specv_row_params* params;
+    const int* caps;              // greedy entry point caps or nullptr
+    unsigned long long seed;
+    unsigned step;
+    int eos;
+    int* out_acc;
+    int* out_tok;
+    int* out_emit;
+    int* out_flags;
+    float* p_at;
+    float* q_at;
+    float* wres;
+    Workspace ws;
+};
+
+// Launch the whole verify step on ``stream``.  ``bf16`` selects the element
+// type, ``vec`` the 16-byte vector-load kernels (row starts 16-byte aligned).
+// ``ev`` (nullable) receives three event records: before the statistics
+// kernel, between the two kernels, after the decision kernel.
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream,
+                         hipEvent_t* ev);
+
+}  // namespace specv

@@ -1,0 +1,913 @@
+// libspecv kernels for gfx950 (CDNA4, wave64).
+//
+// The verify step is bandwidth-bound: every logits row that the round may
+// consult is streamed from HBM once with 16-byte loads, reduced to per-chunk
+// statistics, and the sequential part of the round (accept tests, stopping
+// at the first rejection) runs on those statistics.  Only the one row pair
+// that is actually sampled from is read a second time.
+//
+//   k_rowstats  grid (chunks, B * (2*gamma+1)): one workgroup per 8192-entry
+//               chunk of one logits row.  Sampling rows: chunk max and
+//               sum of exp2((z - max) * log2(e) / T).  Greedy rows: chunk max
+//               and its lowest index.  Rows a round cannot consult (past the
+//               cap / first EOS, draft rows of greedy rows) are skipped.
+//   k_decide    grid (chunks, B): every workgroup of a batch row combines
+//               the statistics, draws the accept uniforms and finds the first
+//               rejection (cheap, done redundantly); each then sums the
+//               correction weights max(p - q, 0) of its chunk (or takes the
+//               bonus row's chunk mass from the statistics).  The last
+//               workgroup of the row to finish (atomic counter) picks the
+//               chunk that holds u * W, rescans it with a block prefix sum and
+//               writes the outputs.
+//
+// Sources: "11.1 核心原理: Draft + Verify 与 Rejection Sampling" (11.1.1
+// alignment, 11.1.2 acceptance / residual / greedy, pseudo-code 10-1) and
+// "Fast Inference from Transformers via Speculative Decoding" (speculative
+// sampling, bonus token).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "specv_internal.hpp"
+
+namespace specv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInf = __builtin_huge_valf();
+
+enum Mode { MODE_SAMPLE = 0, MODE_GREEDY = 1, MODE_TRUNC = 2, MODE_SKIP = 3 };
+enum Kind { KIND_NONE = 0, KIND_RESIDUAL = 1, KIND_BONUS = 2 };
+enum Purpose { PURPOSE_ACCEPT = 1, PURPOSE_RESIDUAL = 2, PURPOSE_BONUS = 3 };
+
+// ---------------------------------------------------------------- Philox
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies, key bumped by the Weyl constants between rounds.
+__device__ inline uint4 philox4x32_10(uint4 c, unsigned k0, unsigned k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const unsigned lo0 = 0xD2511F53u * c.x;
+        const unsigned hi0 = __umulhi(0xD2511F53u, c.x);
+        const unsigned lo1 = 0xCD9E8D57u * c.z;
+        const unsigned hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+// u = (word0 >> 8) * 2^-24 for counter (b, i, purpose, step).
+__device__ inline float uniform24(unsigned long long seed, unsigned b, unsigned i,
+                                  unsigned purpose, unsigned step) {
+    const uint4 r = philox4x32_10(make_uint4(b, i, purpose, step), (unsigned)seed,
+                                  (unsigned)(seed >> 32));
+    return (float)(r.x >> 8) * 5.9604644775390625e-08f;
+}
+
+// ---------------------------------------------------------------- helpers
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Hand-off between workgroups of one launch.  Published values are written
+// and read with agent-scope atomic accesses, which are coherent across the
+// XCDs' L2 caches by themselves, so no L2 write-back / invalidate is needed
+// (a __threadfence() would flush the whole L2 of the XCD).  ``wait_stores``
+// makes this wave's outstanding stores complete before the arrival counter is
+// bumped, and keeps the compiler from moving memory accesses across it.
+__device__ inline void publish(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void publish(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void publish(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float published(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int published(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline unsigned published(const unsigned* p) {
+    return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Bump the arrival counter after this thread's published stores completed;
+// returns the previous count.
+__device__ inline unsigned arrive(unsigned* counter) {
+    wait_stores();
+    const unsigned old =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_stores();
+    return old;
+}
+
+__device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <bool BF16>
+__device__ inline float load_elem(const void* row, long long v) {
+    if constexpr (BF16) {
+        const unsigned short h = static_cast<const unsigned short*>(row)[v];
+        return __uint_as_float((unsigned)h << 16);
+    } else {
+        return static_cast<const float*>(row)[v];
+    }
+}
+
+template <bool BF16>
+__device__ inline const void* row_ptr(const void* base, long long stride_b, long long stride_p,
+                                      int b, int i) {
+    const long long off = (long long)b * stride_b + (long long)i * stride_p;
+    if constexpr (BF16) {
+        return static_cast<const unsigned short*>(base) + off;
+    } else {
+        return static_cast<const float*>(base) + off;
+    }
+}
+
+template <bool BF16>
+__device__ inline void unpack16(const uint4& q, float* x) {
+    if constexpr (BF16) {
+        x[0] = bf16_lo(q.x);
+        x[1] = bf16_hi(q.x);
+        x[2] = bf16_lo(q.y);
+        x[3] = bf16_hi(q.y);
+        x[4] = bf16_lo(q.z);
+        x[5] = bf16_hi(q.z);
+        x[6] = bf16_lo(q.w);
+        x[7] = bf16_hi(q.w);
+    } else {
+        x[0] = __uint_as_float(q.x);
+        x[1] = __uint_as_float(q.y);
+        x[2] = __uint_as_float(q.z);
+        x[3] = __uint_as_float(q.w);
+    }
+}
+
+// Load this thread's 32 entries of a chunk into x[]; entries past ``len``
+// read as -inf.  Layout: 16-byte groups, group g = j * kBlock + tid, so each
+// load instruction of the workgroup covers one contiguous 4 KB span.  Every
+// load is issued before any value is used: out-of-range groups load a clamped
+// in-range address and are masked afterwards (no branch around a load).
+template <bool BF16, bool VEC>
+__device__ inline void load_chunk(const void* row, int v0, int len, float (&x)[kPerThread]) {
+    const int tid = threadIdx.x;
+    constexpr int G = BF16 ? 8 : 4;                 // entries per 16-byte group
+    constexpr int NG = kPerThread / G;              // groups per thread
+    if constexpr (VEC) {
+        const uint4* p = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(row) + (size_t)v0 * (BF16 ? 2 : 4));
+        if (len == kChunk) {
+            uint4 q[NG];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) q[j] = p[j * kBlock + tid];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) unpack16<BF16>(q[j], &x[j * G]);
+            return;
+        }
+        if (len >= G) {
+            const int full = len / G;               // groups entirely inside the chunk
+            uint4 q[NG];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                const int g = j * kBlock + tid;
+                q[j] = p[g < full ? g : 0];
+            }
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                unpack16<BF16>(q[j], &x[j * G]);
+                if (j * kBlock + tid >= full) {
+#pragma unroll
+                    for (int e = 0; e < G; ++e) x[j * G + e] = -kInf;
+                }
+            }
+            // entries of the one partial group at the end, if any
+            const int rem = len - full * G;
+            if (rem && tid == full % kBlock) {
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    if (j == full / kBlock) {
+#pragma unroll
+                        for (int e = 0; e < G; ++e)
+                            if (e < rem) x[j * G + e] = load_elem<BF16>(row, (long long)v0 + full * G + e);
+                    }
+                }
+            }
+            return;
+        }
+    }
+    float t[kPerThread];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const int v = (j * kBlock + tid) * G + e;
+            t[j * G + e] = load_elem<BF16>(row, (long long)v0 + (v < len ? v : len - 1));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const int v = (j * kBlock + tid) * G + e;
+            x[j * G + e] = v < len ? t[j * G + e] : -kInf;
+        }
+    }
+}
+
+// Load entries [tid * 32, tid * 32 + 32) of a chunk (contiguous per thread,
+// for the in-order prefix sum); entries past ``len`` read as -inf.
+template <bool BF16, bool VEC>
+__device__ inline void load_contig(const void* row, int v0, int len, float (&x)[kPerThread]) {
+    const int tid = threadIdx.x;
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int NG = kPerThread / G;
+    const int base = tid * kPerThread;
+    if constexpr (VEC) {
+        if (len >= G) {
+            const uint4* p = reinterpret_cast<const uint4*>(
+                static_cast<const char*>(row) + (size_t)v0 * (BF16 ? 2 : 4));
+            const int full = len / G;
+            uint4 q[NG];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                const int g = base / G + j;
+                q[j] = p[g < full ? g : 0];
+            }
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                unpack16<BF16>(q[j], &x[j * G]);
+                if (base / G + j >= full) {
+#pragma unroll
+                    for (int e = 0; e < G; ++e) x[j * G + e] = -kInf;
+                }
+            }
+            const int rem = len - full * G;
+            if (rem && full * G >= base && full * G < base + kPerThread) {
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    if (base / G + j == full) {
+#pragma unroll
+                        for (int e = 0; e < G; ++e)
+                            if (e < rem) x[j * G + e] = load_elem<BF16>(row, (long long)v0 + full * G + e);
+                    }
+                }
+            }
+            return;
+        }
+    }
+    float t[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int v = base + k;
+        t[k] = load_elem<BF16>(row, (long long)v0 + (v < len ? v : len - 1));
+    }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) x[k] = base + k < len ? t[k] : -kInf;
+}
+
+// Index (within the chunk) of entry k of this thread's x[] in load_chunk's layout.
+template <bool BF16>
+__device__ inline int chunk_index(int k) {
+    constexpr int G = BF16 ? 8 : 4;
+    return ((k / G) * kBlock + (int)threadIdx.x) * G + (k % G);
+}
+
+// Merge (m, s) statistics: s is relative to m in units of exp2(. * scale).
+__device__ inline void merge_ms(float& m, float& s, float m2, float s2, float scale) {
+    const float M = fmaxf(m, m2);
+    if (M == -kInf) {            // both empty; keep NaN visible
+        s = s + s2;
+        m = M;
+        return;
+    }
+    s = s * fast_exp2((m - M) * scale) + s2 * fast_exp2((m2 - M) * scale);
+    m = M;
+}
+
+__device__ inline void wave_merge_ms(float& m, float& s, float scale) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, kWave);
+        const float s2 = __shfl_xor(s, off, kWave);
+        merge_ms(m, s, m2, s2, scale);
+    }
+}
+
+// (value, index) argmax merge: larger value wins, lower index on ties.
+__device__ inline void merge_arg(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+__device__ inline void wave_merge_arg(float& v, int& i) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float v2 = __shfl_xor(v, off, kWave);
+        const int i2 = __shfl_xor(i, off, kWave);
+        merge_arg(v, i, v2, i2);
+    }
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+__device__ inline unsigned wave_or(unsigned x) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x |= __shfl_xor(x, off, kWave);
+    return x;
+}
+
+
+// ---------------------------------------------------------------- row plan
+// What one batch row needs, from its parameters and draft tokens alone.
+struct Plan {
+    int mode;
+    int cap;        // tokens the round may emit: max_new_tokens and the first EOS
+    int nt;         // target rows the round may consult
+    int nd;         // draft rows the round may consult
+    float scale;    // log2(e) / T
+    int top_k;
+    float top_p;
+    unsigned flags;
+};
+
+__device__ inline Plan make_plan(const Args& a, int b) {
+    Plan p;
+    float T = 0.f;
+    int k = 0;
+    float tp = 1.f;
+    int cap = 0;
+    if (a.params) {
+        const specv_row_params rp = a.params[b];
+        T = rp.temperature;
+        k = rp.top_k;
+        tp = rp.top_p;
+        cap = rp.max_new_tokens;
+    } else if (a.caps) {
+        cap = a.caps[b];
+    }
+    // emission ends after max_new_tokens tokens and after an emitted EOS; an
+    // EOS among the drafts therefore caps the round at its position + 1
+    int ce = cap >= 1 ? cap : 0x7fffffff;
+    p.flags = 0;
+    for (int i = 0; i < a.gamma; ++i) {
+        const int d = a.tokens[(long long)b * a.gamma + i];
+        if (d < 0 || d >= a.V) p.flags |= SPECV_FLAG_TOKEN_OOR;
+        else if (d == a.eos && i + 1 < ce) ce = i + 1;
+    }
+    p.cap = ce;
+    p.top_k = k;
+    p.top_p = tp;
+    const bool greedy = a.greedy_all || !(T > 0.f);
+    const bool topk_on = k > 0 && k < a.V;
+    const bool topp_on = tp < 1.f;
+    if (p.flags & SPECV_FLAG_TOKEN_OOR) {
+        p.mode = MODE_SKIP;
+    } else if (greedy) {
+        p.mode = MODE_GREEDY;
+    } else if (topk_on || topp_on) {
+        p.mode = MODE_SKIP;                   // truncated rows: candidate path
+        p.flags |= SPECV_FLAG_UNSUPPORTED;
+    } else {
+        p.mode = MODE_SAMPLE;
+    }
+    p.scale = greedy ? 0.f : kLog2e / T;
+    p.nt = min(ce, a.gamma + 1);
+    p.nd = p.mode == MODE_GREEDY ? 0 : min(ce, a.gamma);
+    return p;
+}
+
+__device__ inline long long part_index(const Args& a, int b, int r, int c) {
+    return ((long long)b * a.R + r) * a.C + c;
+}
+
+__device__ inline void publish_part(Part* p, const Part& v) {
+    publish(&p->m, v.m);
+    publish(&p->s, v.s);
+    publish(&p->arg, v.arg);
+    publish(&p->bad, v.bad);
+}
+
+__device__ inline Part published_part(const Part* p) {
+    Part v;
+    v.m = published(&p->m);
+    v.s = published(&p->s);
+    v.arg = published(&p->arg);
+    v.bad = published(&p->bad);
+    return v;
+}
+
+__device__ inline void write_diag_nan(const Args& a, int b, int from) {
+    for (int i = from; i < a.gamma; ++i) {
+        if (a.p_at) a.p_at[(long long)b * a.gamma + i] = __builtin_nanf("");
+        if (a.q_at) a.q_at[(long long)b * a.gamma + i] = __builtin_nanf("");
+    }
+}
+
+// Final outputs of one row: emit[0..nemit) then ``sampled`` (if >= 0), -1 padding.
+__device__ inline void write_outputs(const Args& a, int b, const int* emit, int nemit, int nacc,
+                                     unsigned flags, bool dead, int sampled, float wres) {
+    const int g1 = a.gamma + 1;
+    if (dead) {
+        nemit = 0;
+        nacc = 0;
+        sampled = -1;
+    }
+    for (int j = 0; j < g1; ++j) {
+        int t = -1;
+        if (j < nemit) t = emit[j];
+        else if (j == nemit && sampled >= 0) t = sampled;
+        a.out_tok[(long long)b * g1 + j] = t;
+    }
+    a.out_emit[b] = nemit + (sampled >= 0 ? 1 : 0);
+    a.out_acc[b] = nacc;
+    if (a.out_flags) a.out_flags[b] = (int)flags;
+    if (a.wres) a.wres[b] = wres;
+}
+
+// ---------------------------------------------------------------- decision
+// Run by the last streaming workgroup of batch row b, once every consulted
+// row's chunk statistics are published: combine them, take the accept tests
+// in order and stop at the first rejection (pseudo-code 10-1), or follow the
+// greedy rule.  Rows that need no sampled token get their outputs here; the
+// others leave a Dec record for k_sample.
+template <bool BF16>
+__device__ void decide_row(const Args& a, int b, const Plan& pl) {
+    __shared__ float sM[kMaxRows], sS[kMaxRows];
+    __shared__ int sI[kMaxRows];
+    __shared__ unsigned sBad[kMaxRows];
+    __shared__ float sP[SPECV_MAX_GAMMA], sQ[SPECV_MAX_GAMMA];
+    __shared__ int sQz[SPECV_MAX_GAMMA];
+    __shared__ Dec sd;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const bool greedy = pl.mode == MODE_GREEDY;
+    const float scale = pl.scale;
+    const int nrows = pl.nt + pl.nd;
+    for (int k = wave; k < nrows; k += kWaves) {
+        const int r = k < pl.nt ? k : a.gamma + 1 + (k - pl.nt);
+        float m = -kInf, s = 0.f;
+        int arg = 0x7fffffff;
+        unsigned bad = 0;
+        for (int cc = lane; cc < a.C; cc += kWave) {
+            const Part p = published_part(&a.ws.part[part_index(a, b, r, cc)]);
+            if (greedy) merge_arg(m, arg, p.m, p.arg);
+            else merge_ms(m, s, p.m, p.s, scale);
+            bad |= p.bad;
+        }
+        if (greedy) wave_merge_arg(m, arg);
+        else wave_merge_ms(m, s, scale);
+        bad = wave_or(bad);
+        if (lane == 0) {
+            sM[r] = m;
+            sS[r] = s;
+            sI[r] = arg;
+            sBad[r] = bad || m == -kInf || (!greedy && !(s > 0.f));
+        }
+    }
+    __syncthreads();
+    if (!greedy && tid < pl.nd) {
+        // p_i(d_i) and q_i(d_i), from the raw logits at d_i
+        const int i = tid;
+        const int d = a.tokens[(long long)b * a.gamma + i];
+        const float zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, i), d);
+        const float zq = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i), d);
+        const int rq = a.gamma + 1 + i;
+        sP[i] = fast_exp2((zt - sM[i]) * scale) / sS[i];
+        sQ[i] = fast_exp2((zq - sM[rq]) * scale) / sS[rq];
+        sQz[i] = zq == -kInf;
+    }
+    __syncthreads();
+    if (tid != 0) return;
+
+    sd.kind = KIND_NONE;
+    sd.pos = -1;
+    sd.u = 0.f;
+    sd.nemit = 0;
+    sd.nacc = 0;
+    sd.flags = pl.flags;
+    bool dead = false;
+    int sampled = -1;
+    int tested = 0;
+    const int* toks = a.tokens + (long long)b * a.gamma;
+    if (greedy) {
+        for (int i = 0; i <= a.gamma; ++i) {
+            if (sd.nemit >= pl.cap) break;
+            if (sBad[i]) {
+                dead = true;
+                break;
+            }
+            const int am = sI[i];
+            if (i < a.gamma && toks[i] == am) {
+                sd.emit[sd.nemit++] = am;
+                sd.nacc++;
+                continue;
+            }
+            sampled = am;        // first mismatch, or the bonus position
+            break;
+        }
+    } else {
+        int i = 0;
+        for (; i < a.gamma; ++i) {
+            if (sd.nemit >= pl.cap) break;
+            if (sBad[i] || sBad[a.gamma + 1 + i]) {
+                dead = true;
+                break;
+            }
+            if (sQz[i]) sd.flags |= SPECV_FLAG_Q_ZERO;
+            const float u = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
+            tested = i + 1;
+            if (u * sQ[i] < sP[i]) {             // accept with probability min(1, p/q)
+                sd.emit[sd.nemit++] = toks[i];
+                sd.nacc++;
+                continue;
+            }
+            sd.kind = KIND_RESIDUAL;
+            sd.pos = i;
+            sd.u = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
+            break;
+        }
+        if (!dead && sd.kind == KIND_NONE && i == a.gamma && sd.nemit < pl.cap) {
+            if (sBad[a.gamma]) {
+                dead = true;
+            } else {
+                sd.kind = KIND_BONUS;
+                sd.pos = a.gamma;
+                sd.u = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
+            }
+        }
+        for (int j = 0; j < tested; ++j) {
+            if (a.p_at) a.p_at[(long long)b * a.gamma + j] = sP[j];
+            if (a.q_at) a.q_at[(long long)b * a.gamma + j] = sQ[j];
+        }
+    }
+    write_diag_nan(a, b, tested);
+    if (dead) {
+        sd.flags |= SPECV_FLAG_NONFINITE_ROW;
+        sd.kind = KIND_NONE;
+    }
+    Dec* gd = &a.ws.dec[b];
+    if (sd.kind == KIND_NONE) {
+        write_outputs(a, b, sd.emit, sd.nemit, sd.nacc, sd.flags, dead, sampled, 0.f);
+        gd->kind = KIND_NONE;
+        return;
+    }
+    const int pos = sd.pos;
+    gd->kind = sd.kind;
+    gd->pos = pos;
+    gd->u = sd.u;
+    gd->mt = sM[pos];
+    gd->invt = 1.f / sS[pos];
+    gd->mq = sd.kind == KIND_RESIDUAL ? sM[a.gamma + 1 + pos] : 0.f;
+    gd->invq = sd.kind == KIND_RESIDUAL ? 1.f / sS[a.gamma + 1 + pos] : 0.f;
+    gd->scale = scale;
+    gd->nemit = sd.nemit;
+    gd->nacc = sd.nacc;
+    gd->flags = sd.flags;
+    for (int j = 0; j < sd.nemit; ++j) gd->emit[j] = sd.emit[j];
+}
+
+// ---------------------------------------------------------------- k_stream
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_stream(Args a) {
+    const int c = blockIdx.x;
+    const int row = blockIdx.y;
+    const int b = row / a.R;
+    const int r = row - b * a.R;
+    const int tid = threadIdx.x;
+    const Plan pl = make_plan(a, b);
+    if (pl.mode == MODE_SKIP) {
+        if (r == 0 && c == 0 && tid == 0) {
+            write_outputs(a, b, nullptr, 0, 0, pl.flags, true, -1, 0.f);
+            write_diag_nan(a, b, 0);
+            a.ws.dec[b].kind = KIND_NONE;
+        }
+        return;
+    }
+    const bool is_target = r <= a.gamma;
+    const int pos = is_target ? r : r - a.gamma - 1;
+    if (pos >= (is_target ? pl.nt : pl.nd)) return;   // a row this round cannot consult
+
+    const void* rp = is_target ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos)
+                               : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos);
+    const int v0 = c * kChunk;
+    const int len = min(kChunk, a.V - v0);
+    float x[kPerThread];
+    load_chunk<BF16, VEC>(rp, v0, len, x);
+
+    __shared__ float sm[kWaves], ss[kWaves];
+    __shared__ int si[kWaves];
+    __shared__ unsigned sb[kWaves];
+    __shared__ int sLast;
+    const int lane = tid % kWave, wave = tid / kWave;
+    Part out;
+    if (pl.mode == MODE_GREEDY) {
+        float best = -kInf;
+        int bi = 0x7fffffff;
+        unsigned bad = 0;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            bad |= !(x[k] <= 3.402823466e38f);            // NaN or +inf
+            if (x[k] > best) {                            // strict: keeps the lowest index
+                best = x[k];
+                bi = v0 + chunk_index<BF16>(k);
+            }
+        }
+        wave_merge_arg(best, bi);
+        bad = wave_or(bad);
+        if (lane == 0) {
+            sm[wave] = best;
+            si[wave] = bi;
+            sb[wave] = bad;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 1; w < kWaves; ++w) {
+                merge_arg(best, bi, sm[w], si[w]);
+                bad |= sb[w];
+            }
+            out.m = best;
+            out.s = 0.f;
+            out.arg = bi;
+            out.bad = bad;
+        }
+    } else {
+        // chunk max and sum of exp2((z - max) * scale)
+        const float scale = pl.scale;
+        float m = -kInf;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[k]);
+        const float nms = m == -kInf ? 0.f : -m * scale;
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) s += fast_exp2(fmaf(x[k], scale, nms));
+        wave_merge_ms(m, s, scale);
+        if (lane == 0) {
+            sm[wave] = m;
+            ss[wave] = s;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[w], ss[w], scale);
+            out.m = m;
+            out.s = s;
+            out.arg = -1;
+            out.bad = __builtin_isnan(s) ? 1u : 0u;      // NaN or +inf in the chunk
+        }
+    }
+    if (tid == 0) {
+        publish_part(&a.ws.part[part_index(a, b, r, c)], out);
+        const unsigned expected = (unsigned)((pl.nt + pl.nd) * a.C);
+        sLast = arrive(&a.ws.counter[(long long)b * kCounterStride]) == expected - 1;
+    }
+    __syncthreads();
+    if (!sLast) return;
+    if (tid == 0) publish(&a.ws.counter[(long long)b * kCounterStride], 0u);       // ready for the next call
+    decide_row<BF16>(a, b, pl);
+}
+
+// ---------------------------------------------------------------- k_sample
+// Correction / bonus weight of entry z (target) and zq (draft) of the row
+// pair being sampled.
+struct Weights {
+    int residual;        // 1: max(p - q, 0); 0: p
+    float mt, st, invt;  // target row max, scale, 1 / sum
+    float mq, invq;      // draft row max, 1 / sum
+    // Products are rounded separately (no fused multiply-add) so that equal
+    // p and q rows give exactly zero correction weight.
+    __device__ inline float w(float z, float zq) const {
+        const float p = __fmul_rn(fast_exp2(__fmul_rn(z - mt, st)), invt);
+        if (!residual) return p;
+        const float q = __fmul_rn(fast_exp2(__fmul_rn(zq - mq, st)), invq);
+        return fmaxf(__fsub_rn(p, q), 0.f);
+    }
+};
+
+// grid (chunks, B): each workgroup of a row that needs a sampled token sums
+// its chunk's weight (correction: max(p - q, 0) re-read from the two rows;
+// bonus: from the chunk statistics).  The last workgroup of the row picks the
+// chunk holding u * W, rescans it with a block prefix sum (tokens in
+// ascending order, first running sum > u * W) and writes the outputs.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_sample(Args a) {
+    const int c = blockIdx.x;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const Dec* gd = &a.ws.dec[b];
+    const int kind = gd->kind;
+    if (kind == KIND_NONE) return;
+    const int pos = gd->pos;
+    Weights wt;
+    wt.residual = kind == KIND_RESIDUAL;
+    wt.mt = gd->mt;
+    wt.st = gd->scale;
+    wt.invt = gd->invt;
+    wt.mq = gd->mq;
+    wt.invq = gd->invq;
+    const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos);
+    const void* qrow = wt.residual ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+
+    __shared__ float red[kWaves];
+    __shared__ int sLast;
+    float wc;
+    if (wt.residual) {
+        const int v0 = c * kChunk;
+        const int len = min(kChunk, a.V - v0);
+        float x[kPerThread], y[kPerThread];
+        load_chunk<BF16, VEC>(trow, v0, len, x);
+        load_chunk<BF16, VEC>(qrow, v0, len, y);
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) s += wt.w(x[k], y[k]);
+        s = wave_sum(s);
+        if (lane == 0) red[wave] = s;
+        __syncthreads();
+        wc = red[0];
+        for (int w = 1; w < kWaves; ++w) wc += red[w];
+    } else {
+        const Part p = a.ws.part[part_index(a, b, pos, c)];
+        wc = __fmul_rn(__fmul_rn(p.s, fast_exp2(__fmul_rn(p.m - wt.mt, wt.st))), wt.invt);
+    }
+    if (tid == 0) {
+        publish(&a.ws.wsum[(long long)b * a.C + c], wc);
+        sLast = arrive(&a.ws.counter2[(long long)b * kCounterStride]) == (unsigned)(a.C - 1);
+    }
+    __syncthreads();
+    if (!sLast) return;
+
+    // last workgroup of the row
+    __shared__ float sW[kMaxChunks];
+    __shared__ float sWres, sBase, sTarget;
+    __shared__ int sChunk, sRes, sTok;
+    __shared__ unsigned sFlags;
+    if (tid == 0) {
+        publish(&a.ws.counter2[(long long)b * kCounterStride], 0u);                  // ready for the next call
+        unsigned flags = gd->flags;
+        float W = 0.f;
+        for (int cc = 0; cc < a.C; ++cc) {
+            sW[cc] = published(&a.ws.wsum[(long long)b * a.C + cc]);
+            W += sW[cc];
+        }
+        float wres = 0.f;
+        if (wt.residual) {
+            wres = W;
+            if (!(W > 0.f) || !__builtin_isfinite(W)) {
+                // the correction mass vanished (p == q where the draft was
+                // rejected, or rounding): sample from p at that position
+                flags |= SPECV_FLAG_RESIDUAL_FALLBACK;
+                wt.residual = 0;
+                W = 0.f;
+                for (int cc = 0; cc < a.C; ++cc) {
+                    const Part p = a.ws.part[part_index(a, b, pos, cc)];
+                    sW[cc] = __fmul_rn(__fmul_rn(p.s, fast_exp2(__fmul_rn(p.m - wt.mt, wt.st))),
+                                       wt.invt);
+                    W += sW[cc];
+                }
+            }
+        }
+        const float target = gd->u * W;
+        float acc = 0.f, base = 0.f, lastbase = 0.f;
+        int chosen = -1, lastc = -1;
+        for (int cc = 0; cc < a.C; ++cc) {
+            const float v = sW[cc];
+            if (v > 0.f) {
+                lastc = cc;
+                lastbase = acc;
+            }
+            if (chosen < 0 && acc + v > target) {
+                chosen = cc;
+                base = acc;
+            }
+            acc += v;
+        }
+        if (chosen < 0) {        // rounding: clamp to the last chunk with weight
+            chosen = lastc;
+            base = lastbase;
+        }
+        sChunk = chosen;
+        sBase = base;
+        sTarget = target;
+        sRes = wt.residual;
+        sWres = wres;
+        sFlags = flags;
+        sTok = 0x7fffffff;
+    }
+    __syncthreads();
+    wt.residual = sRes;
+    const int cs = sChunk;
+    int sampled = -1;
+    if (cs >= 0) {
+        const int v0 = cs * kChunk;
+        const int len = min(kChunk, a.V - v0);
+        float w[kPerThread];
+        float tot = 0.f;
+        int lastpos = -1;
+        {
+            float zt[kPerThread], zq[kPerThread];
+            load_contig<BF16, VEC>(trow, v0, len, zt);
+            if (wt.residual) load_contig<BF16, VEC>(qrow, v0, len, zq);
+#pragma unroll
+            for (int k = 0; k < kPerThread; ++k) {
+                const int v = tid * kPerThread + k;
+                const float wk = v < len ? wt.w(zt[k], wt.residual ? zq[k] : 0.f) : 0.f;
+                w[k] = wk;
+                tot += wk;
+                if (wk > 0.f) lastpos = v;
+            }
+        }
+        // inclusive scan of the per-thread totals (thread order = token order)
+        float incl = tot;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float o = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += o;
+        }
+        __shared__ float wtot[kWaves];
+        __shared__ int wlast[kWaves];
+        if (lane == kWave - 1) wtot[wave] = incl;
+        __syncthreads();
+        float wbase = 0.f;
+        for (int w2 = 0; w2 < wave; ++w2) wbase += wtot[w2];
+        const float excl = sBase + wbase + (incl - tot);
+        const float inc = sBase + wbase + incl;
+        const float target = sTarget;
+        // the first thread whose range crosses the target finds the token
+        const unsigned long long hit = __ballot(inc > target && tot > 0.f);
+        if (hit) {
+            const int first = __ffsll((unsigned long long)hit) - 1;
+            if (lane == first) {
+                float run = 0.f;
+                int t = lastpos;
+                bool found = false;
+#pragma unroll
+                for (int k = 0; k < kPerThread; ++k) {
+                    run += w[k];
+                    if (!found && w[k] > 0.f && excl + run > target) {
+                        t = tid * kPerThread + k;
+                        found = true;
+                    }
+                }
+                atomicMin(&sTok, t);
+            }
+        }
+        int lp = lastpos;
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) lp = max(lp, __shfl_xor(lp, off, kWave));
+        if (lane == 0) wlast[wave] = lp;
+        __syncthreads();
+        if (tid == 0) {
+            int t = sTok;
+            if (t == 0x7fffffff) {                 // rounding: the last token with weight
+                t = -1;
+                for (int w2 = 0; w2 < kWaves; ++w2) t = max(t, wlast[w2]);
+            }
+            sTok = t < 0 ? -1 : v0 + t;
+        }
+        __syncthreads();
+        sampled = sTok;
+    }
+    if (tid == 0) {
+        unsigned flags = sFlags;
+        const bool dead = sampled < 0;        // no weight anywhere: cannot happen for finite rows
+        if (dead) flags |= SPECV_FLAG_NONFINITE_ROW;
+        write_outputs(a, b, gd->emit, gd->nemit, gd->nacc, flags, dead, sampled, sWres);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream,
+                         hipEvent_t* ev) {
+    const dim3 block(kBlock);
+    const dim3 g1(a.C, a.B * a.R);
+    const dim3 g2(a.C, a.B);
+    void (*stream_k)(Args);
+    void (*sample_k)(Args);
+    if (bf16) {
+        stream_k = vec ? k_stream<true, true> : k_stream<true, false>;
+        sample_k = vec ? k_sample<true, true> : k_sample<true, false>;
+    } else {
+        stream_k = vec ? k_stream<false, true> : k_stream<false, false>;
+        sample_k = vec ? k_sample<false, true> : k_sample<false, false>;
+    }
+    if (ev) (void)hipEventRecord(ev[0], stream);
+    hipLaunchKernelGGL(stream_k, g1, block, 0, stream, a);
+    if (ev) (void)hipEventRecord(ev[1], stream);
+    hipLaunchKernelGGL(sample_k, g2, block, 0, stream, a);
+    if (ev) (void)hipEventRecord(ev[2], stream);
+    return hipGetLastError();
+}
+
+}  // namespace specv

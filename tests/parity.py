@@ -1,0 +1,168 @@
+"""Compare a GPU verify result with the oracle's, row by row.
+
+Bar (numbers written here, used by every parity test):
+
+* greedy rows, accepted counts and flags: bit-exact;
+* sampled tokens identical, except where floating point legitimately
+  decides differently, which is counted and reported, not failed:
+  - ACCEPT_WINDOW: the uniform lies within 1e-5 of the acceptance threshold
+    min(1, p/q) (oracle values) at the first position that differs;
+  - CDF_WINDOW: at a correction / bonus draw, the GPU's token t has the
+    oracle interval [C(t-1), C(t)] / W within 1e-5 of the uniform;
+  - the oracle marked the row as having a top-p decision within 1e-5 of
+    top_p (its kept set may legitimately differ);
+  once a row has diverged legitimately, its later outputs are not compared;
+* p_i(d_i), q_i(d_i): relative error <= 1e-5 (absolute floor 1e-30);
+* residual sum W: |dW| <= 1e-5 * W + 1e-6 (W is a difference of two
+  normalised fp32 distributions; its absolute error does not scale with W).
+"""
+
+import numpy as np
+
+import oracle
+
+ACCEPT_WINDOW = 1e-5
+CDF_WINDOW = 1e-5
+REL_TOL = 1e-5
+ABS_FLOOR = 1e-30
+W_REL = 1e-5
+W_ABS = 1e-6
+FLAGS_EXACT = (oracle.FLAG_TOKEN_OOR | oracle.FLAG_NONFINITE_ROW | oracle.FLAG_Q_ZERO
+               | oracle.FLAG_RESIDUAL_FALLBACK)
+
+
+class Report:
+    def __init__(self):
+        self.rows = 0
+        self.exact = 0
+        self.tolerated = {"accept_window": 0, "cdf_window": 0, "topp_near": 0}
+        self.failures = []
+        self.value_checks = 0
+        self.w_floor_only = 0
+
+    def fail(self, b, msg):
+        self.failures.append(f"row {b}: {msg}")
+
+    def summary(self):
+        return (f"rows={self.rows} exact={self.exact} tolerated={self.tolerated} "
+                f"value_checks={self.value_checks} w_floor_only={self.w_floor_only} "
+                f"failures={len(self.failures)}")
+
+    def assert_ok(self, max_tolerated_frac=0.02):
+        assert not self.failures, self.summary() + "\n" + "\n".join(self.failures[:20])
+        tol = sum(self.tolerated.values())
+        assert tol <= max(2, max_tolerated_frac * self.rows), self.summary()
+
+
+def _np(x):
+    if hasattr(x, "detach"):
+        return x.detach().cpu().numpy()
+    return np.asarray(x)
+
+
+def _weights(o_ev, target_f32, draft_f32, b, T, k, p):
+    """Oracle weights of the sampled draw of row b (recomputed on demand)."""
+    s = o_ev["sample"]
+    if s.get("weights") is not None:
+        return s["weights"]
+    P = oracle.process_row(target_f32[b, s["pos"]], T, k, p)
+    if s["kind"] == "bonus":
+        return P.probs
+    Q = oracle.process_row(draft_f32[b, s["pos"]], T, k, p)
+    w = np.maximum(P.probs - Q.probs, 0.0)
+    if not (np.isfinite(w.sum()) and w.sum() > 0):
+        w = P.probs
+    return w
+
+
+def compare(gpu, orc, tokens, target_f32=None, draft_f32=None, params=None, greedy=False,
+            report=None):
+    """Classify every row; returns the Report (call .assert_ok())."""
+    rep = report or Report()
+    g_tok = _np(gpu["out_tokens"])
+    g_emit = _np(gpu["num_emitted"])
+    g_acc = _np(gpu["num_accepted"])
+    g_flags = _np(gpu["row_flags"])
+    tokens = _np(tokens)
+    B = g_tok.shape[0]
+    for b in range(B):
+        rep.rows += 1
+        eo = orc["out_tokens"][b, :orc["num_emitted"][b]].tolist()
+        eg = g_tok[b, :g_emit[b]].tolist()
+        fo = int(orc["row_flags"][b])
+        fg = int(g_flags[b])
+        if (g_tok[b, g_emit[b]:] != -1).any():
+            rep.fail(b, "padding is not -1")
+            continue
+        if eo == eg and g_acc[b] == orc["num_accepted"][b] and (fo & FLAGS_EXACT) == (fg & FLAGS_EXACT):
+            rep.exact += 1
+            _check_values(rep, b, gpu, orc, eo, greedy)
+            continue
+        if greedy or (params is not None and params["temperature"][b] == 0):
+            rep.fail(b, f"greedy mismatch gpu={eg} oracle={eo} flags {fg}/{fo}")
+            continue
+        # first differing emitted position
+        j = 0
+        while j < min(len(eo), len(eg)) and eo[j] == eg[j]:
+            j += 1
+        ev = orc["events"][b]
+        tests = {i: (u, pp, qq) for (i, u, pp, qq) in ev["accept_tests"]}
+        o_accepted_j = orc["num_accepted"][b] > j
+        g_accepted_j = g_acc[b] > j
+        if fo & oracle.FLAG_TOPP_NEAR:
+            rep.tolerated["topp_near"] += 1
+            continue
+        if j in tests and o_accepted_j != g_accepted_j:
+            u, pp, qq = tests[j]
+            thr = min(1.0, pp / qq) if qq > 0 else (1.0 if pp > 0 else 0.0)
+            if abs(u - thr) < ACCEPT_WINDOW:
+                rep.tolerated["accept_window"] += 1
+            else:
+                rep.fail(b, f"accept decision differs at {j}: u={u} thr={thr} gpu={eg} oracle={eo}")
+            continue
+        s = ev["sample"]
+        if s is not None and s["pos"] == j and j < len(eg) and not g_accepted_j:
+            T, k, p = (params["temperature"][b], params["top_k"][b], params["top_p"][b])
+            w = _weights(ev, target_f32, draft_f32, b, T, k, p)
+            t = eg[j]
+            if not (0 <= t < len(w)) or w[t] <= 0:
+                rep.fail(b, f"GPU sampled token {t} has zero oracle weight at {j}")
+                continue
+            lo, hi = oracle.cdf_interval(w, t)
+            u = s["u"]
+            dist = 0.0 if lo <= u <= hi else min(abs(u - lo), abs(u - hi))
+            if dist < CDF_WINDOW:
+                rep.tolerated["cdf_window"] += 1
+            else:
+                rep.fail(b, f"sampled token differs at {j}: gpu {t} [{lo},{hi}] oracle {eo[j]} u={u}")
+            continue
+        rep.fail(b, f"mismatch gpu={eg} (acc {g_acc[b]}, flags {fg}) oracle={eo} "
+                    f"(acc {orc['num_accepted'][b]}, flags {fo})")
+    return rep
+
+
+def _check_values(rep, b, gpu, orc, eo, greedy):
+    if greedy or "p_at_draft" not in gpu:
+        return
+    gp = _np(gpu["p_at_draft"])[b]
+    gq = _np(gpu["q_at_draft"])[b]
+    op = orc["p_at_draft"][b]
+    oq = orc["q_at_draft"][b]
+    for i in range(len(op)):
+        if np.isnan(op[i]):
+            if not np.isnan(gp[i]):
+                rep.fail(b, f"p_at_draft[{i}] written for an untested position")
+            continue
+        for g, o, name in ((gp[i], op[i], "p"), (gq[i], oq[i], "q")):
+            rep.value_checks += 1
+            if not abs(g - o) <= REL_TOL * abs(o) + ABS_FLOOR:
+                rep.fail(b, f"{name}_at_draft[{i}] gpu={g!r} oracle={o!r} rel={abs(g-o)/max(abs(o),1e-300):.2e}")
+    if "residual_sum" in gpu:
+        gw = float(_np(gpu["residual_sum"])[b])
+        ow = float(orc["residual_sum"][b])
+        rep.value_checks += 1
+        err = abs(gw - ow)
+        if err > W_REL * ow + W_ABS:
+            rep.fail(b, f"residual sum gpu={gw} oracle={ow}")
+        elif err > W_REL * ow:
+            rep.w_floor_only += 1
