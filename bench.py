@@ -29,7 +29,7 @@ METRIC = "verified rows/sec + achieved HBM GB/s (% peak), V=128256 γ=5 B=64 bf1
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_sampling_amd", "csrc",
                           "specv_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_stream_serving_batch.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_verify_serving_batch.json")
 
 
 def algorithmic_bytes(B, gamma, V, es, caps, eos_cut, greedy):
@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run --steps device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -109,8 +111,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    sv.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_reference:
+        # a plain copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE of these
+        # launches calibrate the counters against bytes actually moved
+        n = args.copy_reference * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes_each_way": n * 4, "launches": args.steps}))
+        return
+    sv.load_library()
 
     w = synth.serving_batch()
     B, gamma, V = w.B, w.gamma, w.V
@@ -159,16 +172,15 @@ def main():
     for i in range(args.steps):
         call(i, 1000 + i)
     torch.cuda.synchronize()
-    n, ms_stats, ms_decide = v.profile(reset=True)
+    n, ms_kernel = v.profile(reset=True)
     v.set_profiling(False)
-    avg_stats = ms_stats / n
-    avg_decide = ms_decide / n
+    avg_kernel = ms_kernel / n
 
     es = w.bytes_per_element()
     eos_cut = [1 << 30] * B
     greedy = [bool(t == 0) for t in w.temperature]
     abytes = algorithmic_bytes(B, gamma, V, es, w.max_new_tokens, eos_cut, greedy)
-    achieved = abytes / (avg_stats * 1e-3) / 1e9
+    achieved = abytes / (avg_kernel * 1e-3) / 1e9
     traffic = stored_traffic()
 
     rows_per_s = B / (ms_step * 1e-3)
@@ -190,10 +202,10 @@ def main():
                    "B": B, "gamma": gamma, "V": V, "rotated_input_sets": len(sets)},
         "emitted_tokens_per_s": tokens_per_call / (ms_step * 1e-3),
         "step_hbm_gbps_algorithmic": abytes / (ms_step * 1e-3) / 1e9,
-        "kernels_us": {"k_stream": avg_stats * 1e3, "k_sample": avg_decide * 1e3},
+        "kernel_us": {"k_verify": avg_kernel * 1e3},
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_stream",
+            "kernel": "k_verify",
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

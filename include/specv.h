@@ -89,6 +89,10 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype;
                                                   without 0 < top_k < V, or top_k above the
                                                   handle's max_top_k: the row emits nothing         */
 
+#define SPECV_FLAG_INTERNAL           (1 << 7) /* the sampling phase timed out waiting for the row's
+                                                  decision (a launch without co-residency): the
+                                                  row's outputs are not valid                      */
+
 #define SPECV_MAX_GAMMA 32
 #define SPECV_MAX_TOP_K 1024
 #define SPECV_MAX_VOCAB 524288
@@ -159,16 +163,14 @@ SPECV_API specv_status specv_verify_greedy(specv_handle h, void* stream,
                                  int32_t* out_num_accepted, int32_t* out_tokens,
                                  int32_t* out_num_emitted, int32_t* out_row_flags);
 
-/* Per-kernel timing for measurement.  With enable != 0 every later verify
- * call records HIP events on its stream around each of its kernels; the
- * events are created here (not in the verify calls).  specv_get_profile waits
- * for the recorded events, returns the number of profiled calls and the summed
- * milliseconds of the streaming statistics kernel (ms_stats) and of the
- * decision / sampling kernel (ms_decide) since the last reset, and resets the
- * sums when reset != 0.  Errors: SPECV_E_NULL, SPECV_E_HIP. */
+/* Kernel timing for measurement.  With enable != 0 every later verify call
+ * records HIP events on its stream around its kernel (each call is one
+ * kernel launch); the events are created here, not in the verify calls.
+ * specv_get_profile waits for the recorded events and returns the number of
+ * profiled calls and their summed kernel milliseconds since the last reset,
+ * and resets the sums when reset != 0.  Errors: SPECV_E_NULL, SPECV_E_HIP. */
 SPECV_API specv_status specv_set_profiling(specv_handle h, int enable);
-SPECV_API specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms_stats,
-                                         double* ms_decide);
+SPECV_API specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms_kernel);
 
 /* Free the workspace and the handle.  Waits for the device first.  NULL is
  * accepted. */

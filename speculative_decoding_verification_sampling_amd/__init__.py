@@ -32,6 +32,7 @@ __all__ = [
     "FLAG_CAND_OVERFLOW",
     "FLAG_TOPP_NEAR",
     "FLAG_UNSUPPORTED",
+    "FLAG_INTERNAL",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -44,6 +45,7 @@ FLAG_RESIDUAL_FALLBACK = 1 << 3
 FLAG_CAND_OVERFLOW = 1 << 4
 FLAG_TOPP_NEAR = 1 << 5
 FLAG_UNSUPPORTED = 1 << 6
+FLAG_INTERNAL = 1 << 7
 
 SPECV_F32 = 0
 SPECV_BF16 = 1
@@ -113,7 +115,6 @@ def load_library():
     lib.specv_set_profiling.argtypes = [vp, ctypes.c_int]
     lib.specv_set_profiling.restype = ctypes.c_int
     lib.specv_get_profile.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
-                                      ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_double)]
     lib.specv_get_profile.restype = ctypes.c_int
     _lib = lib
@@ -199,15 +200,14 @@ class Verifier:
         _check(load_library().specv_set_profiling(self._h, int(bool(enable))), "specv_set_profiling")
 
     def profile(self, reset=True):
-        """(calls, ms of the statistics kernel, ms of the decision kernel),
-        summed over profiled calls; waits for the recorded events."""
+        """(calls, summed kernel milliseconds) over profiled calls; waits for
+        the recorded events."""
         n = ctypes.c_int()
-        a = ctypes.c_double()
-        b = ctypes.c_double()
+        ms = ctypes.c_double()
         _check(load_library().specv_get_profile(self._h, int(bool(reset)), ctypes.byref(n),
-                                                ctypes.byref(a), ctypes.byref(b)),
+                                                ctypes.byref(ms)),
                "specv_get_profile")
-        return n.value, a.value, b.value
+        return n.value, ms.value
 
     def _stream(self):
         return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)

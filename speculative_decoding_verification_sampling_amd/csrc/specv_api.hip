@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -22,11 +23,13 @@ struct specv_ctx {
     // profiling: a ring of event triples, drained by specv_get_profile or
     // when the ring wraps
     bool prof = false;
-    std::vector<hipEvent_t> ev;     // 3 * kProfRing
+    std::vector<hipEvent_t> ev;     // 2 * kProfRing
     std::vector<char> ev_live;      // kProfRing
     size_t ev_next = 0;
     int prof_calls = 0;
-    double ms_stats = 0.0, ms_decide = 0.0;
+    double ms_kernel = 0.0;
+    unsigned epoch = 0;             // call number; the kernel tags published decisions with it
+    int max_grid[4] = {0, 0, 0, 0}; // co-resident grid per (bf16, vec) variant
 };
 
 namespace {
@@ -34,15 +37,13 @@ constexpr size_t kProfRing = 512;
 
 hipError_t drain_slot(specv_ctx* h, size_t slot) {
     if (!h->ev_live[slot]) return hipSuccess;
-    hipEvent_t* e = &h->ev[3 * slot];
-    hipError_t err = hipEventSynchronize(e[2]);
+    hipEvent_t* e = &h->ev[2 * slot];
+    hipError_t err = hipEventSynchronize(e[1]);
     if (err != hipSuccess) return err;
-    float a = 0.f, b = 0.f;
-    err = hipEventElapsedTime(&a, e[0], e[1]);
-    if (err == hipSuccess) err = hipEventElapsedTime(&b, e[1], e[2]);
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, e[0], e[1]);
     if (err != hipSuccess) return err;
-    h->ms_stats += a;
-    h->ms_decide += b;
+    h->ms_kernel += ms;
     h->prof_calls += 1;
     h->ev_live[slot] = 0;
     return hipSuccess;
@@ -55,7 +56,7 @@ hipEvent_t* next_events(specv_ctx* h) {
     if (drain_slot(h, slot) != hipSuccess) return nullptr;
     h->ev_next++;
     h->ev_live[slot] = 1;
-    return &h->ev[3 * slot];
+    return &h->ev[2 * slot];
 }
 }  // namespace
 
@@ -73,6 +74,7 @@ void free_ws(specv::Workspace& ws) {
     if (ws.counter) (void)hipFree(ws.counter);
     if (ws.counter2) (void)hipFree(ws.counter2);
     if (ws.dec) (void)hipFree(ws.dec);
+    if (ws.ready) (void)hipFree(ws.ready);
     if (ws.cand) (void)hipFree(ws.cand);
     if (ws.cand_cnt) (void)hipFree(ws.cand_cnt);
     if (ws.trow) (void)hipFree(ws.trow);
@@ -114,11 +116,26 @@ specv::Args base_args(specv_handle h, int B, int gamma, int V) {
     a.gamma = gamma;
     a.V = V;
     a.C = (V + specv::kChunk - 1) / specv::kChunk;
+    a.U = (a.C + specv::kUnitChunks - 1) / specv::kUnitChunks;
     a.R = 2 * gamma + 1;
     a.ws = h->ws;
     a.cand_cap = h->cand_cap;
     a.max_top_k = h->cfg.max_top_k;
     return a;
+}
+
+// One cooperative launch of the verify kernel, grid sized to what can be
+// co-resident and to the work available.
+specv_status launch(specv_handle h, specv::Args& a, bool bf16, bool vec, void* stream) {
+    if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
+    h->epoch = h->epoch + 1 == 0 ? 1 : h->epoch + 1;
+    a.epoch = h->epoch;
+    const long long work = std::max((long long)a.B * a.R * a.U, (long long)a.B * a.C);
+    const int grid = (int)std::min<long long>(h->max_grid[(bf16 ? 1 : 0) | (vec ? 2 : 0)], work);
+    if (specv::launch_verify(a, bf16, vec, grid, static_cast<hipStream_t>(stream),
+                             next_events(h)) != hipSuccess)
+        return SPECV_E_HIP;
+    return SPECV_OK;
 }
 
 }  // namespace
@@ -162,10 +179,11 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     const size_t rc = rows * h->max_chunks;
     specv::Workspace& ws = h->ws;
     bool ok = alloc(&ws.part, rc) == hipSuccess &&
-              alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks) == hipSuccess &&
+              alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks * 2) == hipSuccess &&
               alloc(&ws.counter, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
               alloc(&ws.counter2, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
-              alloc(&ws.dec, (size_t)cfg->max_batch) == hipSuccess;
+              alloc(&ws.dec, (size_t)cfg->max_batch) == hipSuccess &&
+              alloc(&ws.ready, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess;
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
@@ -174,6 +192,10 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     const size_t counter_bytes = (size_t)cfg->max_batch * specv::kCounterStride * sizeof(unsigned);
     if (ok) ok = hipMemset(ws.counter, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipMemset(ws.counter2, 0, counter_bytes) == hipSuccess;
+    if (ok) ok = hipMemset(ws.ready, 0, counter_bytes) == hipSuccess;
+    for (int v = 0; ok && v < 4; ++v)
+        ok = specv::verify_max_grid(v & 1, (v >> 1) & 1, &h->max_grid[v]) == hipSuccess &&
+             h->max_grid[v] > 0;
     if (ok) ok = hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
         free_ws(ws);
@@ -189,7 +211,7 @@ specv_status specv_set_profiling(specv_handle h, int enable) {
     if (!h) return SPECV_E_NULL;
     if (enable && h->ev.empty()) {
         if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
-        h->ev.assign(3 * kProfRing, nullptr);
+        h->ev.assign(2 * kProfRing, nullptr);
         h->ev_live.assign(kProfRing, 0);
         for (auto& e : h->ev)
             if (hipEventCreate(&e) != hipSuccess) return SPECV_E_HIP;
@@ -198,17 +220,15 @@ specv_status specv_set_profiling(specv_handle h, int enable) {
     return SPECV_OK;
 }
 
-specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms_stats,
-                               double* ms_decide) {
+specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms_kernel) {
     if (!h) return SPECV_E_NULL;
     for (size_t s = 0; s < h->ev_live.size(); ++s)
         if (drain_slot(h, s) != hipSuccess) return SPECV_E_HIP;
     if (calls) *calls = h->prof_calls;
-    if (ms_stats) *ms_stats = h->ms_stats;
-    if (ms_decide) *ms_decide = h->ms_decide;
+    if (ms_kernel) *ms_kernel = h->ms_kernel;
     if (reset) {
         h->prof_calls = 0;
-        h->ms_stats = h->ms_decide = 0.0;
+        h->ms_kernel = 0.0;
     }
     return SPECV_OK;
 }
@@ -270,10 +290,7 @@ specv_status specv_verify_sample(specv_handle h, void* stream, const void* targe
     a.wres = diag ? diag->residual_sum : nullptr;
     const bool vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es) &&
                      (gamma == 0 || rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es));
-    if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
-    if (specv::launch_verify(a, dtype == SPECV_BF16, vec, static_cast<hipStream_t>(stream),
-                             next_events(h)) != hipSuccess)
-        return SPECV_E_HIP;
+    return launch(h, a, dtype == SPECV_BF16, vec, stream);
     return SPECV_OK;
 }
 
@@ -304,10 +321,7 @@ specv_status specv_verify_greedy(specv_handle h, void* stream, const void* targe
     a.out_emit = out_num_emitted;
     a.out_flags = out_row_flags;
     const bool vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es);
-    if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
-    if (specv::launch_verify(a, dtype == SPECV_BF16, vec, static_cast<hipStream_t>(stream),
-                             next_events(h)) != hipSuccess)
-        return SPECV_E_HIP;
+    return launch(h, a, dtype == SPECV_BF16, vec, stream);
     return SPECV_OK;
 }
 

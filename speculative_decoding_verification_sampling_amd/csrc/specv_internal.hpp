@@ -13,6 +13,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = kBlock / kWave;
 constexpr int kChunk = 8192;            // vocabulary entries per chunk (32 per thread)
 constexpr int kPerThread = kChunk / kBlock;
+constexpr int kUnitChunks = 4;          // chunks streamed by one workgroup (one "unit")
 constexpr int kMaxChunks = 64;          // V <= 64 * 8192 = 524288
 constexpr int kMaxRows = 2 * SPECV_MAX_GAMMA + 1;
 constexpr int kCounterStride = 64;     // one arrival counter per 256-byte slot: atomics
@@ -20,7 +21,7 @@ constexpr int kCounterStride = 64;     // one arrival counter per 256-byte slot:
 constexpr int kTieSlack = 256;          // candidates per chunk beyond top_k (ties)
 constexpr int kKeptCap = 2048;          // kept set per row after the row-level top-k
 
-// Per (row, chunk) statistics from the streaming pass.
+// Per (row, unit) statistics from the streaming pass.
 //  sampling rows: m = max raw logit, s = sum exp2((z - m) * scale)
 //  greedy rows:   m = max raw logit, arg = its lowest index
 struct Part {
@@ -63,11 +64,13 @@ struct Dec {
 
 struct Workspace {
     Part* part;           // [max_batch * max_rows * max_chunks]
-    float* wsum;          // [max_batch * max_chunks]
+    float* wsum;          // [max_batch * max_chunks * 2]: per chunk (sampling weight, p mass)
     unsigned* counter;    // [max_batch * kCounterStride] arrivals in the streaming kernel
     unsigned* counter2;   // [max_batch * kCounterStride] arrivals in the sampling kernel;
                           // both zero between calls
     Dec* dec;             // [max_batch]
+    unsigned* ready;      // [max_batch * kCounterStride]: epoch of the call whose decision
+                          // for the row is published
     Cand* cand;           // [max_batch * rows * max_chunks * cand_cap]
     int* cand_cnt;        // [max_batch * rows * max_chunks]
     TruncRow* trow;       // [max_batch * rows]
@@ -81,6 +84,7 @@ struct Args {
     long long d_sb, d_sp;
     int B, gamma, V;
     int C;                        // chunks per row
+    int U;                        // streaming units per row: ceil(C / kUnitChunks)
     int R;                        // logits rows per batch row: 2 * gamma + 1
     int greedy_all;               // specv_verify_greedy
     int cand_cap;                 // candidates per (row, chunk); 0: no truncation
@@ -91,6 +95,7 @@ struct Args {
     unsigned long long seed;
     unsigned step;
     int eos;
+    unsigned epoch;               // per-handle call number (never 0)
     int* out_acc;
     int* out_tok;
     int* out_emit;
@@ -101,11 +106,15 @@ struct Args {
     Workspace ws;
 };
 
-// Launch the whole verify step on ``stream``.  ``bf16`` selects the element
-// type, ``vec`` the 16-byte vector-load kernels (row starts 16-byte aligned).
-// ``ev`` (nullable) receives three event records: before the statistics
-// kernel, between the two kernels, after the decision kernel.
-hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream,
+// Launch the whole verify step on ``stream`` as one kernel (one workgroup per
+// streaming unit and per sampling item; ``grid`` is unused).  ``bf16``
+// selects the element type, ``vec`` the 16-byte vector-load variant (row
+// starts 16-byte aligned).  ``ev`` (nullable) receives two event records
+// around the launch.
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, int grid, hipStream_t stream,
                          hipEvent_t* ev);
+
+// Largest co-resident grid of the verify kernel variant on the current device.
+hipError_t verify_max_grid(bool bf16, bool vec, int* grid);
 
 }  // namespace specv

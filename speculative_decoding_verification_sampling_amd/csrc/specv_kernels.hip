@@ -389,23 +389,30 @@ __device__ inline Plan make_plan(const Args& a, int b) {
     return p;
 }
 
-__device__ inline long long part_index(const Args& a, int b, int r, int c) {
-    return ((long long)b * a.R + r) * a.C + c;
+__device__ inline long long part_index(const Args& a, int b, int r, int unit) {
+    return ((long long)b * a.R + r) * a.U + unit;
 }
 
+// A Part moves as two 64-bit agent-scope accesses.
 __device__ inline void publish_part(Part* p, const Part& v) {
-    publish(&p->m, v.m);
-    publish(&p->s, v.s);
-    publish(&p->arg, v.arg);
-    publish(&p->bad, v.bad);
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+    const unsigned long long lo =
+        (unsigned long long)__float_as_uint(v.m) | ((unsigned long long)__float_as_uint(v.s) << 32);
+    const unsigned long long hi =
+        (unsigned long long)(unsigned)v.arg | ((unsigned long long)v.bad << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline Part published_part(const Part* p) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<Part*>(p));
+    const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Part v;
-    v.m = published(&p->m);
-    v.s = published(&p->s);
-    v.arg = published(&p->arg);
-    v.bad = published(&p->bad);
+    v.m = __uint_as_float((unsigned)lo);
+    v.s = __uint_as_float((unsigned)(lo >> 32));
+    v.arg = (int)(unsigned)hi;
+    v.bad = (unsigned)(hi >> 32);
     return v;
 }
 
@@ -438,11 +445,24 @@ __device__ inline void write_outputs(const Args& a, int b, const int* emit, int 
 }
 
 // ---------------------------------------------------------------- decision
+// Wait (bounded) until ``flag`` holds ``epoch``; false on time-out.  The
+// workgroup that publishes the flag was dispatched before the waiting one
+// and never waits itself, so the wait ends; the bound only guards against a
+// dispatch order other than the hardware's in-order one.
+__device__ inline bool wait_flag(const unsigned* flag, unsigned epoch) {
+    for (int spin = 0; spin < (1 << 20); ++spin) {
+        if (published(flag) == epoch) return true;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+
 // Run by the last streaming workgroup of batch row b, once every consulted
-// row's chunk statistics are published: combine them, take the accept tests
+// row's unit statistics are published: combine them, take the accept tests
 // in order and stop at the first rejection (pseudo-code 10-1), or follow the
 // greedy rule.  Rows that need no sampled token get their outputs here; the
-// others leave a Dec record for k_sample.
+// others publish a Dec record for the sampling phase.  Either way the row's
+// ready flag is set to this call's epoch.
 template <bool BF16>
 __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     __shared__ float sM[kMaxRows], sS[kMaxRows];
@@ -450,6 +470,7 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     __shared__ unsigned sBad[kMaxRows];
     __shared__ float sP[SPECV_MAX_GAMMA], sQ[SPECV_MAX_GAMMA];
     __shared__ int sQz[SPECV_MAX_GAMMA];
+    __shared__ float sUacc[SPECV_MAX_GAMMA], sUres[SPECV_MAX_GAMMA + 1];
     __shared__ Dec sd;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const bool greedy = pl.mode == MODE_GREEDY;
@@ -460,7 +481,7 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
         float m = -kInf, s = 0.f;
         int arg = 0x7fffffff;
         unsigned bad = 0;
-        for (int cc = lane; cc < a.C; cc += kWave) {
+        for (int cc = lane; cc < a.U; cc += kWave) {
             const Part p = published_part(&a.ws.part[part_index(a, b, r, cc)]);
             if (greedy) merge_arg(m, arg, p.m, p.arg);
             else merge_ms(m, s, p.m, p.s, scale);
@@ -478,7 +499,9 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     }
     __syncthreads();
     if (!greedy && tid < pl.nd) {
-        // p_i(d_i) and q_i(d_i), from the raw logits at d_i
+        // p_i(d_i) and q_i(d_i) from the raw logits at d_i, and the uniforms
+        // this position may need (drawn in parallel; only the ones the
+        // sequential rule reaches are used)
         const int i = tid;
         const int d = a.tokens[(long long)b * a.gamma + i];
         const float zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, i), d);
@@ -487,7 +510,11 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
         sP[i] = fast_exp2((zt - sM[i]) * scale) / sS[i];
         sQ[i] = fast_exp2((zq - sM[rq]) * scale) / sS[rq];
         sQz[i] = zq == -kInf;
+        sUacc[i] = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
+        sUres[i] = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
     }
+    if (!greedy && tid == kBlock - 1)
+        sUres[a.gamma] = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
     __syncthreads();
     if (tid != 0) return;
 
@@ -526,16 +553,15 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
                 break;
             }
             if (sQz[i]) sd.flags |= SPECV_FLAG_Q_ZERO;
-            const float u = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
             tested = i + 1;
-            if (u * sQ[i] < sP[i]) {             // accept with probability min(1, p/q)
+            if (sUacc[i] * sQ[i] < sP[i]) {       // accept with probability min(1, p/q)
                 sd.emit[sd.nemit++] = toks[i];
                 sd.nacc++;
                 continue;
             }
             sd.kind = KIND_RESIDUAL;
             sd.pos = i;
-            sd.u = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
+            sd.u = sUres[i];
             break;
         }
         if (!dead && sd.kind == KIND_NONE && i == a.gamma && sd.nemit < pl.cap) {
@@ -544,7 +570,7 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
             } else {
                 sd.kind = KIND_BONUS;
                 sd.pos = a.gamma;
-                sd.u = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
+                sd.u = sUres[a.gamma];
             }
         }
         for (int j = 0; j < tested; ++j) {
@@ -560,38 +586,62 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     Dec* gd = &a.ws.dec[b];
     if (sd.kind == KIND_NONE) {
         write_outputs(a, b, sd.emit, sd.nemit, sd.nacc, sd.flags, dead, sampled, 0.f);
-        gd->kind = KIND_NONE;
-        return;
+        publish(&gd->kind, (int)KIND_NONE);
+    } else {
+        const int pos = sd.pos;
+        const bool res = sd.kind == KIND_RESIDUAL;
+        publish(&gd->kind, sd.kind);
+        publish(&gd->pos, pos);
+        publish(&gd->u, sd.u);
+        publish(&gd->mt, sM[pos]);
+        publish(&gd->invt, 1.f / sS[pos]);
+        publish(&gd->mq, res ? sM[a.gamma + 1 + pos] : 0.f);
+        publish(&gd->invq, res ? 1.f / sS[a.gamma + 1 + pos] : 0.f);
+        publish(&gd->scale, scale);
+        publish(&gd->nemit, sd.nemit);
+        publish(&gd->nacc, sd.nacc);
+        publish(&gd->flags, sd.flags);
+        for (int j = 0; j < sd.nemit; ++j) publish(&gd->emit[j], sd.emit[j]);
     }
-    const int pos = sd.pos;
-    gd->kind = sd.kind;
-    gd->pos = pos;
-    gd->u = sd.u;
-    gd->mt = sM[pos];
-    gd->invt = 1.f / sS[pos];
-    gd->mq = sd.kind == KIND_RESIDUAL ? sM[a.gamma + 1 + pos] : 0.f;
-    gd->invq = sd.kind == KIND_RESIDUAL ? 1.f / sS[a.gamma + 1 + pos] : 0.f;
-    gd->scale = scale;
-    gd->nemit = sd.nemit;
-    gd->nacc = sd.nacc;
-    gd->flags = sd.flags;
-    for (int j = 0; j < sd.nemit; ++j) gd->emit[j] = sd.emit[j];
+    wait_stores();
+    publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
 }
 
-// ---------------------------------------------------------------- k_stream
+// ---------------------------------------------------------------- streaming
+// Issue the 16-byte loads of one full chunk (this thread's four / eight groups).
+template <bool BF16>
+__device__ inline void issue_chunk(const void* row, int v0, uint4 (&q)[kPerThread / (BF16 ? 8 : 4)]) {
+    constexpr int NG = kPerThread / (BF16 ? 8 : 4);
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
+                                                    (size_t)v0 * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int j = 0; j < NG; ++j) q[j] = p[j * kBlock + threadIdx.x];
+}
+
+// One streaming unit t = (b, r, unit): up to kUnitChunks chunks of one logits
+// row, the next chunk's loads issued before the current one is reduced, with
+// per-thread running statistics:
+//   sampling rows: running max m and sum s of exp2((z - m) * scale), the sum
+//                  rescaled when the max grows (one extra exp2 per chunk);
+//   greedy rows:   running max and its lowest index.
+// The unit's statistics are published; the last unit of a batch row to
+// arrive runs the decision.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_stream(Args a) {
-    const int c = blockIdx.x;
-    const int row = blockIdx.y;
+__device__ void stream_unit(const Args& a, int t) {
+    constexpr int NG = kPerThread / (BF16 ? 8 : 4);
+    const int unit = t % a.U;
+    const int row = t / a.U;
     const int b = row / a.R;
     const int r = row - b * a.R;
     const int tid = threadIdx.x;
     const Plan pl = make_plan(a, b);
     if (pl.mode == MODE_SKIP) {
-        if (r == 0 && c == 0 && tid == 0) {
+        if (r == 0 && unit == 0 && tid == 0) {
             write_outputs(a, b, nullptr, 0, 0, pl.flags, true, -1, 0.f);
             write_diag_nan(a, b, 0);
-            a.ws.dec[b].kind = KIND_NONE;
+            publish(&a.ws.dec[b].kind, (int)KIND_NONE);
+            wait_stores();
+            publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
         }
         return;
     }
@@ -601,10 +651,55 @@ __global__ __launch_bounds__(kBlock) void k_stream(Args a) {
 
     const void* rp = is_target ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos)
                                : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos);
-    const int v0 = c * kChunk;
-    const int len = min(kChunk, a.V - v0);
-    float x[kPerThread];
-    load_chunk<BF16, VEC>(rp, v0, len, x);
+    const int c0 = unit * kUnitChunks;
+    const int nfull = a.V / kChunk;                    // chunks without a tail
+    const bool greedy = pl.mode == MODE_GREEDY;
+    const float scale = pl.scale;
+    float m = -kInf, s = 0.f;                          // sampling rows
+    float best = -kInf;                                // greedy rows
+    int bi = 0x7fffffff;
+    unsigned bad = 0;
+
+    uint4 q[NG];
+    if (VEC && c0 < nfull) issue_chunk<BF16>(rp, c0 * kChunk, q);
+#pragma unroll
+    for (int u = 0; u < kUnitChunks; ++u) {
+        const int c = c0 + u;
+        if (c >= a.C) break;
+        float x[kPerThread];
+        if (VEC && c < nfull) {
+            uint4 cur[NG];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) cur[j] = q[j];
+            if (u + 1 < kUnitChunks && c + 1 < nfull) issue_chunk<BF16>(rp, (c + 1) * kChunk, q);
+#pragma unroll
+            for (int j = 0; j < NG; ++j) unpack16<BF16>(cur[j], &x[j * (BF16 ? 8 : 4)]);
+        } else {
+            load_chunk<BF16, VEC>(rp, c * kChunk, min(kChunk, a.V - c * kChunk), x);
+        }
+        if (greedy) {
+            const int v0 = c * kChunk;
+#pragma unroll
+            for (int k = 0; k < kPerThread; ++k) {
+                bad |= !(x[k] <= 3.402823466e38f);        // NaN or +inf
+                if (x[k] > best) {                        // strict: keeps the lowest index
+                    best = x[k];
+                    bi = v0 + chunk_index<BF16>(k);
+                }
+            }
+        } else {
+            float cm = -kInf;
+#pragma unroll
+            for (int k = 0; k < kPerThread; ++k) cm = fmaxf(cm, x[k]);
+            const float nm = fmaxf(m, cm);
+            const float nms = nm == -kInf ? 0.f : -nm * scale;
+            float cs = s * fast_exp2(fmaf(m, scale, nms));
+#pragma unroll
+            for (int k = 0; k < kPerThread; ++k) cs += fast_exp2(fmaf(x[k], scale, nms));
+            s = cs;
+            m = nm;
+        }
+    }
 
     __shared__ float sm[kWaves], ss[kWaves];
     __shared__ int si[kWaves];
@@ -612,18 +707,7 @@ __global__ __launch_bounds__(kBlock) void k_stream(Args a) {
     __shared__ int sLast;
     const int lane = tid % kWave, wave = tid / kWave;
     Part out;
-    if (pl.mode == MODE_GREEDY) {
-        float best = -kInf;
-        int bi = 0x7fffffff;
-        unsigned bad = 0;
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-            bad |= !(x[k] <= 3.402823466e38f);            // NaN or +inf
-            if (x[k] > best) {                            // strict: keeps the lowest index
-                best = x[k];
-                bi = v0 + chunk_index<BF16>(k);
-            }
-        }
+    if (greedy) {
         wave_merge_arg(best, bi);
         bad = wave_or(bad);
         if (lane == 0) {
@@ -643,15 +727,6 @@ __global__ __launch_bounds__(kBlock) void k_stream(Args a) {
             out.bad = bad;
         }
     } else {
-        // chunk max and sum of exp2((z - max) * scale)
-        const float scale = pl.scale;
-        float m = -kInf;
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[k]);
-        const float nms = m == -kInf ? 0.f : -m * scale;
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) s += fast_exp2(fmaf(x[k], scale, nms));
         wave_merge_ms(m, s, scale);
         if (lane == 0) {
             sm[wave] = m;
@@ -663,21 +738,21 @@ __global__ __launch_bounds__(kBlock) void k_stream(Args a) {
             out.m = m;
             out.s = s;
             out.arg = -1;
-            out.bad = __builtin_isnan(s) ? 1u : 0u;      // NaN or +inf in the chunk
+            out.bad = __builtin_isnan(s) ? 1u : 0u;      // NaN or +inf in the unit
         }
     }
     if (tid == 0) {
-        publish_part(&a.ws.part[part_index(a, b, r, c)], out);
-        const unsigned expected = (unsigned)((pl.nt + pl.nd) * a.C);
+        publish_part(&a.ws.part[part_index(a, b, r, unit)], out);
+        const unsigned expected = (unsigned)((pl.nt + pl.nd) * a.U);
         sLast = arrive(&a.ws.counter[(long long)b * kCounterStride]) == expected - 1;
     }
     __syncthreads();
     if (!sLast) return;
-    if (tid == 0) publish(&a.ws.counter[(long long)b * kCounterStride], 0u);       // ready for the next call
+    if (tid == 0) publish(&a.ws.counter[(long long)b * kCounterStride], 0u);   // ready for the next call
     decide_row<BF16>(a, b, pl);
 }
 
-// ---------------------------------------------------------------- k_sample
+// ---------------------------------------------------------------- sampling
 // Correction / bonus weight of entry z (target) and zq (draft) of the row
 // pair being sampled.
 struct Weights {
@@ -694,72 +769,100 @@ struct Weights {
     }
 };
 
-// grid (chunks, B): each workgroup of a row that needs a sampled token sums
-// its chunk's weight (correction: max(p - q, 0) re-read from the two rows;
-// bonus: from the chunk statistics).  The last workgroup of the row picks the
-// chunk holding u * W, rescans it with a block prefix sum (tokens in
-// ascending order, first running sum > u * W) and writes the outputs.
+// Sampling item (b, c), after b's decision is published: sum chunk c's
+// sampling weight (correction max(p - q, 0) from the two rows, or bonus p)
+// and its p mass.  The last item of the row to arrive picks the chunk
+// holding u * W, rescans it with a block prefix sum (tokens in ascending
+// order, first running sum > u * W) and writes the outputs.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_sample(Args a) {
-    const int c = blockIdx.x;
-    const int b = blockIdx.y;
+__device__ void sample_item(const Args& a, int b, int c) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
-    const Dec* gd = &a.ws.dec[b];
-    const int kind = gd->kind;
+    Dec* gd = &a.ws.dec[b];
+    __shared__ int sKind, sPos;
+    __shared__ float sU, sMt, sInvt, sMq, sInvq, sScale;
+    if (tid == 0) {
+        const bool ok = wait_flag(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
+        sKind = ok ? published(&gd->kind) : (int)KIND_NONE;
+        if (ok && sKind != KIND_NONE) {
+            sPos = published(&gd->pos);
+            sU = published(&gd->u);
+            sMt = published(&gd->mt);
+            sInvt = published(&gd->invt);
+            sMq = published(&gd->mq);
+            sInvq = published(&gd->invq);
+            sScale = published(&gd->scale);
+        }
+        if (!ok && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
+    }
+    __syncthreads();
+    const int kind = sKind;
     if (kind == KIND_NONE) return;
-    const int pos = gd->pos;
+    const int pos = sPos;
     Weights wt;
     wt.residual = kind == KIND_RESIDUAL;
-    wt.mt = gd->mt;
-    wt.st = gd->scale;
-    wt.invt = gd->invt;
-    wt.mq = gd->mq;
-    wt.invq = gd->invq;
+    wt.mt = sMt;
+    wt.st = sScale;
+    wt.invt = sInvt;
+    wt.mq = sMq;
+    wt.invq = sInvq;
+    const float u = sU;
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos);
     const void* qrow = wt.residual ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
 
-    __shared__ float red[kWaves];
+    __shared__ float red[2][kWaves];
     __shared__ int sLast;
-    float wc;
-    if (wt.residual) {
+    {
         const int v0 = c * kChunk;
         const int len = min(kChunk, a.V - v0);
         float x[kPerThread], y[kPerThread];
         load_chunk<BF16, VEC>(trow, v0, len, x);
-        load_chunk<BF16, VEC>(qrow, v0, len, y);
-        float s = 0.f;
+        if (wt.residual) load_chunk<BF16, VEC>(qrow, v0, len, y);
+        float sw = 0.f, sp = 0.f;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) s += wt.w(x[k], y[k]);
-        s = wave_sum(s);
-        if (lane == 0) red[wave] = s;
+        for (int k = 0; k < kPerThread; ++k) {
+            const float p = __fmul_rn(fast_exp2(__fmul_rn(x[k] - wt.mt, wt.st)), wt.invt);
+            sp += p;
+            sw += wt.residual ? wt.w(x[k], y[k]) : p;
+        }
+        sw = wave_sum(sw);
+        sp = wave_sum(sp);
+        if (lane == 0) {
+            red[0][wave] = sw;
+            red[1][wave] = sp;
+        }
         __syncthreads();
-        wc = red[0];
-        for (int w = 1; w < kWaves; ++w) wc += red[w];
-    } else {
-        const Part p = a.ws.part[part_index(a, b, pos, c)];
-        wc = __fmul_rn(__fmul_rn(p.s, fast_exp2(__fmul_rn(p.m - wt.mt, wt.st))), wt.invt);
-    }
-    if (tid == 0) {
-        publish(&a.ws.wsum[(long long)b * a.C + c], wc);
-        sLast = arrive(&a.ws.counter2[(long long)b * kCounterStride]) == (unsigned)(a.C - 1);
+        if (tid == 0) {
+            float wc = red[0][0], pc = red[1][0];
+            for (int w = 1; w < kWaves; ++w) {
+                wc += red[0][w];
+                pc += red[1][w];
+            }
+            float* slot = a.ws.wsum + ((long long)b * a.C + c) * 2;
+            publish(slot, wc);
+            publish(slot + 1, pc);
+            sLast = arrive(&a.ws.counter2[(long long)b * kCounterStride]) == (unsigned)(a.C - 1);
+        }
     }
     __syncthreads();
     if (!sLast) return;
 
-    // last workgroup of the row
-    __shared__ float sW[kMaxChunks];
+    // last item of the row
+    __shared__ float sW[kMaxChunks], sPm[kMaxChunks];
     __shared__ float sWres, sBase, sTarget;
     __shared__ int sChunk, sRes, sTok;
     __shared__ unsigned sFlags;
+    for (int cc = tid; cc < a.C; cc += kBlock) {
+        const float* slot = a.ws.wsum + ((long long)b * a.C + cc) * 2;
+        sW[cc] = published(slot);
+        sPm[cc] = published(slot + 1);
+    }
+    __syncthreads();
     if (tid == 0) {
-        publish(&a.ws.counter2[(long long)b * kCounterStride], 0u);                  // ready for the next call
-        unsigned flags = gd->flags;
+        publish(&a.ws.counter2[(long long)b * kCounterStride], 0u);   // ready for the next call
+        unsigned flags = published(&gd->flags);
         float W = 0.f;
-        for (int cc = 0; cc < a.C; ++cc) {
-            sW[cc] = published(&a.ws.wsum[(long long)b * a.C + cc]);
-            W += sW[cc];
-        }
+        for (int cc = 0; cc < a.C; ++cc) W += sW[cc];
         float wres = 0.f;
         if (wt.residual) {
             wres = W;
@@ -770,14 +873,12 @@ __global__ __launch_bounds__(kBlock) void k_sample(Args a) {
                 wt.residual = 0;
                 W = 0.f;
                 for (int cc = 0; cc < a.C; ++cc) {
-                    const Part p = a.ws.part[part_index(a, b, pos, cc)];
-                    sW[cc] = __fmul_rn(__fmul_rn(p.s, fast_exp2(__fmul_rn(p.m - wt.mt, wt.st))),
-                                       wt.invt);
+                    sW[cc] = sPm[cc];
                     W += sW[cc];
                 }
             }
         }
-        const float target = gd->u * W;
+        const float target = u * W;
         float acc = 0.f, base = 0.f, lastbase = 0.f;
         int chosen = -1, lastc = -1;
         for (int cc = 0; cc < a.C; ++cc) {
@@ -849,17 +950,17 @@ __global__ __launch_bounds__(kBlock) void k_sample(Args a) {
             const int first = __ffsll((unsigned long long)hit) - 1;
             if (lane == first) {
                 float run = 0.f;
-                int t = lastpos;
+                int tk = lastpos;
                 bool found = false;
 #pragma unroll
                 for (int k = 0; k < kPerThread; ++k) {
                     run += w[k];
                     if (!found && w[k] > 0.f && excl + run > target) {
-                        t = tid * kPerThread + k;
+                        tk = tid * kPerThread + k;
                         found = true;
                     }
                 }
-                atomicMin(&sTok, t);
+                atomicMin(&sTok, tk);
             }
         }
         int lp = lastpos;
@@ -868,45 +969,76 @@ __global__ __launch_bounds__(kBlock) void k_sample(Args a) {
         if (lane == 0) wlast[wave] = lp;
         __syncthreads();
         if (tid == 0) {
-            int t = sTok;
-            if (t == 0x7fffffff) {                 // rounding: the last token with weight
-                t = -1;
-                for (int w2 = 0; w2 < kWaves; ++w2) t = max(t, wlast[w2]);
+            int tk = sTok;
+            if (tk == 0x7fffffff) {                 // rounding: the last token with weight
+                tk = -1;
+                for (int w2 = 0; w2 < kWaves; ++w2) tk = max(tk, wlast[w2]);
             }
-            sTok = t < 0 ? -1 : v0 + t;
+            sTok = tk < 0 ? -1 : v0 + tk;
         }
         __syncthreads();
         sampled = sTok;
     }
     if (tid == 0) {
+        int emit[SPECV_MAX_GAMMA + 1];
+        const int nemit = published(&gd->nemit);
+        for (int j = 0; j < nemit; ++j) emit[j] = published(&gd->emit[j]);
         unsigned flags = sFlags;
         const bool dead = sampled < 0;        // no weight anywhere: cannot happen for finite rows
         if (dead) flags |= SPECV_FLAG_NONFINITE_ROW;
-        write_outputs(a, b, gd->emit, gd->nemit, gd->nacc, flags, dead, sampled, sWres);
+        write_outputs(a, b, emit, nemit, published(&gd->nacc), flags, dead, sampled, sWres);
     }
+    __syncthreads();      // shared state is reused by the next item
+}
+
+// ---------------------------------------------------------------- k_verify
+// One launch per call, one workgroup per piece of work:
+//   blocks [0, units):            streaming unit t = (b, r, unit), in batch-row
+//                                 order; the last unit of a row decides it;
+//   blocks [units, units + items): sampling item (b, c), waiting for its row's
+//                                 decision.
+// Workgroups are dispatched in increasing order within each XCD, so every
+// streaming workgroup has been dispatched (and never waits) before any
+// sampling workgroup that could wait for it: the waits always end.  Sampling
+// of early rows overlaps the streaming of later ones.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_verify(Args a) {
+    const int units = a.B * a.R * a.U;
+    const int t = blockIdx.x;
+    if (t < units) stream_unit<BF16, VEC>(a, t);
+    else sample_item<BF16, VEC>(a, (t - units) / a.C, (t - units) % a.C);
+}
+
+using KernelFn = void (*)(Args);
+
+KernelFn pick(bool bf16, bool vec) {
+    if (bf16) return vec ? k_verify<true, true> : k_verify<true, false>;
+    return vec ? k_verify<false, true> : k_verify<false, false>;
 }
 
 }  // namespace
 
-hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream,
+hipError_t verify_max_grid(bool bf16, bool vec, int* grid) {
+    int dev = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(pick(bf16, vec)),
+                                                     kBlock, 0);
+    if (e != hipSuccess) return e;
+    *grid = per_cu * prop.multiProcessorCount;
+    return hipSuccess;
+}
+
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, int grid, hipStream_t stream,
                          hipEvent_t* ev) {
-    const dim3 block(kBlock);
-    const dim3 g1(a.C, a.B * a.R);
-    const dim3 g2(a.C, a.B);
-    void (*stream_k)(Args);
-    void (*sample_k)(Args);
-    if (bf16) {
-        stream_k = vec ? k_stream<true, true> : k_stream<true, false>;
-        sample_k = vec ? k_sample<true, true> : k_sample<true, false>;
-    } else {
-        stream_k = vec ? k_stream<false, true> : k_stream<false, false>;
-        sample_k = vec ? k_sample<false, true> : k_sample<false, false>;
-    }
+    (void)grid;
+    const int blocks = a.B * a.R * a.U + a.B * a.C;
     if (ev) (void)hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL(stream_k, g1, block, 0, stream, a);
+    hipLaunchKernelGGL(pick(bf16, vec), dim3(blocks), dim3(kBlock), 0, stream, a);
     if (ev) (void)hipEventRecord(ev[1], stream);
-    hipLaunchKernelGGL(sample_k, g2, block, 0, stream, a);
-    if (ev) (void)hipEventRecord(ev[2], stream);
     return hipGetLastError();
 }
 
