@@ -19,6 +19,7 @@ struct specv_ctx {
     int max_rows;
     int max_chunks;
     int cand_cap;      // candidates per (row, chunk); 0 without truncation support
+    int kept_cap;      // kept-set entries per row
     specv::Workspace ws;
     // profiling: a ring of event triples, drained by specv_get_profile or
     // when the ring wraps
@@ -29,7 +30,6 @@ struct specv_ctx {
     int prof_calls = 0;
     double ms_kernel = 0.0;
     unsigned epoch = 0;             // call number; the kernel tags published decisions with it
-    int max_grid[4] = {0, 0, 0, 0}; // co-resident grid per (bf16, vec) variant
 };
 
 namespace {
@@ -76,7 +76,8 @@ void free_ws(specv::Workspace& ws) {
     if (ws.dec) (void)hipFree(ws.dec);
     if (ws.ready) (void)hipFree(ws.ready);
     if (ws.cand) (void)hipFree(ws.cand);
-    if (ws.cand_cnt) (void)hipFree(ws.cand_cnt);
+    if (ws.cand_meta) (void)hipFree(ws.cand_meta);
+    if (ws.counter_row) (void)hipFree(ws.counter_row);
     if (ws.trow) (void)hipFree(ws.trow);
     if (ws.kept) (void)hipFree(ws.kept);
     ws = specv::Workspace{};
@@ -120,20 +121,18 @@ specv::Args base_args(specv_handle h, int B, int gamma, int V) {
     a.R = 2 * gamma + 1;
     a.ws = h->ws;
     a.cand_cap = h->cand_cap;
+    a.kept_cap = h->kept_cap;
     a.max_top_k = h->cfg.max_top_k;
     return a;
 }
 
-// One cooperative launch of the verify kernel, grid sized to what can be
-// co-resident and to the work available.
+// One launch of the verify kernel; each call gets a new epoch tag.
 specv_status launch(specv_handle h, specv::Args& a, bool bf16, bool vec, void* stream) {
     if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
     h->epoch = h->epoch + 1 == 0 ? 1 : h->epoch + 1;
     a.epoch = h->epoch;
-    const long long work = std::max((long long)a.B * a.R * a.U, (long long)a.B * a.C);
-    const int grid = (int)std::min<long long>(h->max_grid[(bf16 ? 1 : 0) | (vec ? 2 : 0)], work);
-    if (specv::launch_verify(a, bf16, vec, grid, static_cast<hipStream_t>(stream),
-                             next_events(h)) != hipSuccess)
+    if (specv::launch_verify(a, bf16, vec, static_cast<hipStream_t>(stream), next_events(h)) !=
+        hipSuccess)
         return SPECV_E_HIP;
     return SPECV_OK;
 }
@@ -173,8 +172,9 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     h->cfg = *cfg;
     h->max_rows = 2 * cfg->max_gamma + 1;
     h->max_chunks = (cfg->max_vocab + specv::kChunk - 1) / specv::kChunk;
-    h->cand_cap = cfg->max_top_k > 0 ? cfg->max_top_k + specv::kTieSlack : 0;
-    if (h->cand_cap > specv::kChunk) h->cand_cap = specv::kChunk;
+    h->cand_cap = cfg->max_top_k > 0 ? 2 * cfg->max_top_k + specv::kTieSlack : 0;
+    h->cand_cap = std::min(h->cand_cap, std::min(specv::kChunk, cfg->max_vocab));
+    h->kept_cap = std::min(specv::kKeptCap, cfg->max_vocab);
     const size_t rows = (size_t)cfg->max_batch * h->max_rows;
     const size_t rc = rows * h->max_chunks;
     specv::Workspace& ws = h->ws;
@@ -187,15 +187,15 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
-             alloc(&ws.cand_cnt, rc) == hipSuccess && alloc(&ws.trow, rows) == hipSuccess &&
-             alloc(&ws.kept, rows * specv::kKeptCap) == hipSuccess;
+             alloc(&ws.cand_meta, rc) == hipSuccess && alloc(&ws.trow, rows) == hipSuccess &&
+             alloc(&ws.kept, rows * h->kept_cap) == hipSuccess &&
+             alloc(&ws.counter_row, rows * specv::kCounterStride) == hipSuccess &&
+             hipMemset(ws.counter_row, 0, rows * specv::kCounterStride * sizeof(unsigned)) ==
+                 hipSuccess;
     const size_t counter_bytes = (size_t)cfg->max_batch * specv::kCounterStride * sizeof(unsigned);
     if (ok) ok = hipMemset(ws.counter, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipMemset(ws.counter2, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipMemset(ws.ready, 0, counter_bytes) == hipSuccess;
-    for (int v = 0; ok && v < 4; ++v)
-        ok = specv::verify_max_grid(v & 1, (v >> 1) & 1, &h->max_grid[v]) == hipSuccess &&
-             h->max_grid[v] > 0;
     if (ok) ok = hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
         free_ws(ws);

@@ -37,14 +37,26 @@ struct Cand {
 };
 
 // Result of the row-level truncation (top-k then top-p) for one logits row.
+// The kept set is {v : z_v >= tstar}, stored sorted (value desc, index asc).
 struct TruncRow {
     float zmax;     // largest raw logit
-    float tk;       // raw value of the top-k threshold
-    float tstar;    // raw value of the top-p threshold (>= tk)
+    float tstar;    // raw value of the last kept level
     float S;        // sum over the kept set of exp2((z - zmax) * scale)
-    int n_kept;     // kept entries (sorted by value desc, index asc) in Workspace::kept
-    unsigned flags; // SPECV_FLAG_* bits found while truncating
+    int n_kept;     // entries in Workspace::kept for the row
+    unsigned flags; // SPECV_FLAG_* bits found while truncating (overflow, top-p near)
+    unsigned bad;   // 1: NaN / +inf in the row, or no finite value
     int pad0, pad1;
+};
+
+// LDS scratch of the truncation steps (one per workgroup, reused).
+struct TruncScratch {
+    float v[kKeptCap];
+    int idx[kKeptCap];
+    float w[kKeptCap];
+    unsigned hist[256];
+    unsigned off[kMaxChunks + 1];
+    float red[kBlock / 64];
+    int misc[8];
 };
 
 // Outcome of one batch row's accept tests, handed from the streaming
@@ -71,10 +83,12 @@ struct Workspace {
     Dec* dec;             // [max_batch]
     unsigned* ready;      // [max_batch * kCounterStride]: epoch of the call whose decision
                           // for the row is published
-    Cand* cand;           // [max_batch * rows * max_chunks * cand_cap]
-    int* cand_cnt;        // [max_batch * rows * max_chunks]
+    Cand* cand;           // [max_batch * rows * max_chunks * cand_cap] chunk candidates
+    Cand* cand_meta;      // [max_batch * rows * max_chunks]: (lower bound L, count); count -1
+                          // when the chunk's candidates overflowed
     TruncRow* trow;       // [max_batch * rows]
-    Cand* kept;           // [max_batch * rows * kKeptCap]
+    Cand* kept;           // [max_batch * rows * kept_cap]
+    unsigned* counter_row;// [max_batch * rows * kCounterStride] unit arrivals per truncated row
 };
 
 struct Args {
@@ -88,6 +102,7 @@ struct Args {
     int R;                        // logits rows per batch row: 2 * gamma + 1
     int greedy_all;               // specv_verify_greedy
     int cand_cap;                 // candidates per (row, chunk); 0: no truncation
+    int kept_cap;                 // kept-set entries per row: min(kKeptCap, max_vocab)
     int max_top_k;
     const int* tokens;            // [B, gamma]
     const specv_row_params* params;
@@ -107,14 +122,10 @@ struct Args {
 };
 
 // Launch the whole verify step on ``stream`` as one kernel (one workgroup per
-// streaming unit and per sampling item; ``grid`` is unused).  ``bf16``
-// selects the element type, ``vec`` the 16-byte vector-load variant (row
-// starts 16-byte aligned).  ``ev`` (nullable) receives two event records
-// around the launch.
-hipError_t launch_verify(const Args& a, bool bf16, bool vec, int grid, hipStream_t stream,
-                         hipEvent_t* ev);
-
-// Largest co-resident grid of the verify kernel variant on the current device.
-hipError_t verify_max_grid(bool bf16, bool vec, int* grid);
+// streaming unit and per sampling item).  ``bf16`` selects the element type,
+// ``vec`` the 16-byte vector-load variant (row starts 16-byte aligned); the
+// truncation-capable variant is used when a.cand_cap > 0.  ``ev`` (nullable)
+// receives two event records around the launch.
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev);
 
 }  // namespace specv

@@ -340,6 +340,9 @@ struct Plan {
     float scale;    // log2(e) / T
     int top_k;
     float top_p;
+    int keff;       // truncated rows: candidates wanted per chunk (top_k, or the handle's
+                    // max_top_k for top-p alone)
+    int kmode;      // truncated rows: 1 when top-k is on (normaliser over the top-k set)
     unsigned flags;
 };
 
@@ -378,12 +381,18 @@ __device__ inline Plan make_plan(const Args& a, int b) {
     } else if (greedy) {
         p.mode = MODE_GREEDY;
     } else if (topk_on || topp_on) {
-        p.mode = MODE_SKIP;                   // truncated rows: candidate path
-        p.flags |= SPECV_FLAG_UNSUPPORTED;
+        if (a.cand_cap == 0 || (topk_on && k > a.max_top_k)) {
+            p.mode = MODE_SKIP;               // the handle reserved no room for these candidates
+            p.flags |= SPECV_FLAG_UNSUPPORTED;
+        } else {
+            p.mode = MODE_TRUNC;
+        }
     } else {
         p.mode = MODE_SAMPLE;
     }
     p.scale = greedy ? 0.f : kLog2e / T;
+    p.kmode = topk_on ? 1 : 0;
+    p.keff = topk_on ? k : a.max_top_k;
     p.nt = min(ce, a.gamma + 1);
     p.nd = p.mode == MODE_GREEDY ? 0 : min(ce, a.gamma);
     return p;
@@ -607,6 +616,636 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
 }
 
+// ---------------------------------------------------------------- truncation
+// Top-k / top-p rows ("11.1 核心原理" 11.1.2: p and q are the distributions
+// after truncation; q is the truncated proposal actually sampled).
+//   per chunk:   each thread keeps its top-j finite values (j = ceil(2k / 256)
+//                <= 8); the k-th largest of those 256 j values, L, has at
+//                least k chunk entries >= L, so every finite entry >= L is a
+//                superset of the chunk's top k (typically ~k entries);
+//   per row:     (last unit of the row) the row's top-k threshold is >= every
+//                chunk's L, so only candidates >= max L are gathered (at most
+//                2048); they are sorted (value desc, index asc), the k-th
+//                entry is the top-k threshold (ties kept), and the prefix is
+//                scanned for top-p: the first level whose cumulative mass
+//                reaches top_p ends the kept set (ties at a level all kept);
+//   per batch row: (last row) accept tests from the kept sets, and the
+//                correction / bonus sample from the (short) kept list of the
+//                sampled row, tokens in ascending index order.
+
+__device__ inline bool finite_logit(float x) { return x > -kInf && x <= 3.402823466e38f; }
+
+__device__ inline void publish_cand(Cand* p, float v, int idx) {
+    const unsigned long long w =
+        (unsigned long long)__float_as_uint(v) | ((unsigned long long)(unsigned)idx << 32);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), w, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline Cand published_cand(const Cand* p) {
+    const unsigned long long w = __hip_atomic_load(
+        reinterpret_cast<unsigned long long*>(const_cast<Cand*>(p)), __ATOMIC_RELAXED,
+        __HIP_MEMORY_SCOPE_AGENT);
+    Cand c;
+    c.v = __uint_as_float((unsigned)w);
+    c.idx = (int)(unsigned)(w >> 32);
+    return c;
+}
+
+__device__ inline int pow2_at_least(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+// (value desc, index asc)
+__device__ inline bool by_value(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+// index asc
+__device__ inline bool by_index(float, int ia, float, int ib) { return ia < ib; }
+
+// Block-wide bitonic sort of v / idx [0, n), n a power of two <= kKeptCap,
+// so that entry x comes before entry y when prec(x, y).  Entries must be
+// visible to the block (caller synchronised); result visible on return.
+template <typename Prec>
+__device__ void bitonic_sort(float* v, int* idx, int n, Prec prec) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += kBlock) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const float va = v[i], vb = v[ixj];
+                    const int ia = idx[i], ib = idx[ixj];
+                    const bool sw = (i & k) == 0 ? prec(vb, ib, va, ia) : prec(va, ia, vb, ib);
+                    if (sw) {
+                        v[i] = vb;
+                        v[ixj] = va;
+                        idx[i] = ib;
+                        idx[ixj] = ia;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Block-wide exclusive scan of one int per thread; returns this thread's
+// offset and writes the total to *total (both visible to all threads).
+__device__ inline int block_excl_scan(int x, int* scratch /* kWaves + 1 */, int* total) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) scratch[wave] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) base += scratch[w];
+        tot += scratch[w];
+    }
+    *total = tot;
+    __syncthreads();
+    return base + incl - x;
+}
+
+// In-place inclusive prefix sum of w[0, n), n <= kKeptCap: eight consecutive
+// entries per thread in order, then across threads.
+__device__ void block_inclusive_scan(float* w, int n, float* red) {
+    constexpr int per = kKeptCap / kBlock;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int base = threadIdx.x * per;
+    float loc[per];
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+        run += base + j < n ? w[base + j] : 0.f;
+        loc[j] = run;
+    }
+    float incl = run;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) red[wave] = incl;
+    __syncthreads();
+    float wbase = 0.f;
+    for (int w2 = 0; w2 < wave; ++w2) wbase += red[w2];
+    const float excl = wbase + incl - run;
+#pragma unroll
+    for (int j = 0; j < per; ++j)
+        if (base + j < n) w[base + j] = excl + loc[j];
+    __syncthreads();
+}
+
+__device__ inline long long cand_base(const Args& a, long long rowid, int c) {
+    return (rowid * a.C + c) * a.cand_cap;
+}
+
+// Order-preserving key of a raw logit (larger value -> larger key).  bf16
+// values are fp32 patterns with zero low halves, so their keys fit 16 bits.
+template <bool BF16>
+__device__ inline unsigned order_key(float x) {
+    unsigned u = __float_as_uint(x);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return BF16 ? (u >> 16) : u;
+}
+
+// Candidate f of a row (flat index over its chunks, offsets in sc.off).
+__device__ inline Cand row_candidate(const Args& a, long long rowid, const unsigned* off, int f) {
+    int lo = 0, hi = a.C - 1;                  // chunk c with off[c] <= f < off[c + 1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int)off[mid] <= f) lo = mid;
+        else hi = mid - 1;
+    }
+    return published_cand(a.ws.cand + cand_base(a, rowid, lo) + (f - (int)off[lo]));
+}
+
+// Radix select (8-bit digits from the top) of the K-th largest order key
+// among the row's candidates with value >= L, read from global memory.
+template <bool BF16>
+__device__ unsigned select_kth_key(const Args& a, long long rowid, int total, float L, int K,
+                                   TruncScratch& sc) {
+    constexpr int KB = BF16 ? 16 : 32;
+    const int tid = threadIdx.x;
+    __shared__ unsigned sPrefix, sDigit;
+    __shared__ int sRemaining, sAbove;
+    if (tid == 0) {
+        sPrefix = 0;
+        sRemaining = K;
+    }
+    for (int pass = 0; pass < KB / 8; ++pass) {
+        const int shift = KB - 8 * (pass + 1);
+        sc.hist[tid] = 0;                      // kBlock == 256 bins
+        __syncthreads();
+        const unsigned prefix = sPrefix;
+        const unsigned hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8)) & (BF16 ? 0xFFFFu : 0xFFFFFFFFu);
+        for (int f0 = 0; f0 < total; f0 += 4 * kBlock) {
+            Cand cv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = f0 + q * kBlock + tid;
+                cv[q] = f < total ? row_candidate(a, rowid, sc.off, f) : Cand{-kInf, 0};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (cv[q].v >= L && finite_logit(cv[q].v)) {
+                    const unsigned key = order_key<BF16>(cv[q].v);
+                    if ((key & hi_mask) == prefix) atomicAdd(&sc.hist[(key >> shift) & 255u], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        // bin t holds hist[t]; entries in bins >= t: total - (entries in bins < t)
+        const int h = (int)sc.hist[tid];
+        int binned;
+        const int below = block_excl_scan(h, sc.misc, &binned);
+        const int ge = binned - below;
+        const int need = sRemaining;
+        if (ge >= need && ge - h < need) {
+            sDigit = (unsigned)tid;
+            sAbove = ge - h;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            sPrefix |= sDigit << shift;
+            sRemaining -= sAbove;
+        }
+        __syncthreads();
+    }
+    return sPrefix;
+}
+
+// Candidates of one chunk (whole workgroup): every finite entry >= L.
+template <bool BF16>
+__device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff,
+                                 const float (&x)[kPerThread], TruncScratch& sc) {
+    const int tid = threadIdx.x;
+    // twice as many per-thread tops as needed keeps L close to the k-th value
+    const int jj = min(8, (2 * keff + kBlock - 1) / kBlock);
+    float tp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tp[j] = -kInf;                // this thread's top 8, desc
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        float v = x[k];
+        if (!(finite_logit(v) && v > tp[7])) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {                       // insertion, larger values first
+            if (v > tp[j]) {
+                const float s = tp[j];
+                tp[j] = v;
+                v = s;
+            }
+        }
+    }
+    const int n = kBlock * jj;
+    const int n2 = pow2_at_least(n);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < jj) {
+            sc.v[tid * jj + j] = tp[j];
+            sc.idx[tid * jj + j] = 0;
+        }
+    for (int i = n + tid; i < n2; i += kBlock) {
+        sc.v[i] = -kInf;
+        sc.idx[i] = 0;
+    }
+    __syncthreads();
+    bitonic_sort(sc.v, sc.idx, n2, by_value);
+    const float L = sc.v[keff - 1];        // keff <= 256 * jj / 2 <= n2
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) cnt += finite_logit(x[k]) && x[k] >= L;
+    int total;
+    const int off = block_excl_scan(cnt, sc.misc, &total);
+    if (total <= a.cand_cap) {
+        Cand* dst = a.ws.cand + cand_base(a, rowid, c);
+        int o = off;
+        const int v0 = c * kChunk;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k)
+            if (finite_logit(x[k]) && x[k] >= L) publish_cand(dst + o++, x[k], v0 + chunk_index<BF16>(k));
+    }
+    if (tid == 0)
+        publish_cand(a.ws.cand_meta + rowid * a.C + c, L, total <= a.cand_cap ? total : -1);
+}
+
+// Row-level truncation (whole workgroup), run by the last unit of the row.
+template <bool BF16>
+__device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScratch& sc) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const long long rowid = (long long)b * a.R + r;
+    __shared__ float sL, sM, sS, sZ1;
+    __shared__ unsigned sBad, sFlags;
+    __shared__ int sTotal, sN, sJ, sLevelStart;
+    unsigned* off = sc.off;                // chunk offsets [0, C]
+    if (tid == 0) {
+        sBad = 0;
+        sFlags = 0;
+        sN = 0;
+        sJ = 0x7fffffff;
+        sLevelStart = 0x7fffffff;
+    }
+    // chunk bounds and counts (lane c holds chunk c; C <= 64), and the row
+    // statistics (for top-p alone)
+    if (wave == 0) {
+        float L = -kInf;
+        int cnt = 0;
+        bool ovf = false;
+        if (lane < a.C) {
+            const Cand m = published_cand(a.ws.cand_meta + rowid * a.C + lane);
+            L = m.v;
+            ovf = m.idx < 0;
+            cnt = ovf ? 0 : m.idx;
+        }
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) L = fmaxf(L, __shfl_xor(L, o, kWave));
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int v = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += v;
+        }
+        if (lane < a.C) off[lane] = (unsigned)(incl - cnt);
+        if (lane == a.C - 1) {
+            off[a.C] = (unsigned)incl;
+            sTotal = incl;
+        }
+        const unsigned long long any_ovf = __ballot(ovf);
+        if (lane == 0) {
+            sL = L;
+            if (any_ovf) sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+        }
+    } else if (wave == 1) {
+        float m = -kInf, s = 0.f;
+        unsigned bad = 0;
+        for (int u = lane; u < a.U; u += kWave) {
+            const Part p = published_part(&a.ws.part[part_index(a, b, r, u)]);
+            merge_ms(m, s, p.m, p.s, pl.scale);
+            bad |= p.bad;
+        }
+        wave_merge_ms(m, s, pl.scale);
+        bad = wave_or(bad);
+        if (lane == 0) {
+            sM = m;
+            sS = s;
+            if (bad || m == -kInf) sBad = 1;
+        }
+    }
+    __syncthreads();
+    // gather the candidates >= max L into LDS
+    const float L = sL;
+    const int total = sTotal;
+    auto gather = [&](unsigned min_key) {
+        for (int f0 = 0; f0 < total; f0 += 4 * kBlock) {
+            Cand cv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = f0 + q * kBlock + tid;
+                cv[q] = f < total ? row_candidate(a, rowid, off, f) : Cand{-kInf, 0};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (cv[q].v >= L && finite_logit(cv[q].v) && order_key<BF16>(cv[q].v) >= min_key) {
+                    const int pos = atomicAdd(&sN, 1);
+                    if (pos < kKeptCap) {
+                        sc.v[pos] = cv[q].v;
+                        sc.idx[pos] = cv[q].idx;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    };
+    gather(0u);
+    if (sN > kKeptCap) {
+        // too many candidates above the chunk bounds: select the exact top-k
+        // key over them in global memory, then keep only entries >= it
+        const int K = min(pl.keff, sN);
+        const unsigned kkey = select_kth_key<BF16>(a, rowid, total, L, K, sc);
+        if (tid == 0) sN = 0;
+        __syncthreads();
+        gather(kkey);
+    }
+    const int n1 = sN;
+    if (n1 > kKeptCap && tid == 0) sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+    __syncthreads();
+    TruncRow* tr = &a.ws.trow[rowid];
+    if ((sFlags & SPECV_FLAG_CAND_OVERFLOW) || sBad || n1 == 0) {
+        if (tid == 0) {
+            publish(&tr->bad, (sBad || n1 == 0) ? 1u : 0u);
+            publish(&tr->flags, sFlags);
+            publish(&tr->n_kept, 0);
+        }
+        return;
+    }
+    // sort the gathered entries: value desc, index asc
+    const int n2 = pow2_at_least(n1);
+    for (int i = n1 + tid; i < n2; i += kBlock) {
+        sc.v[i] = -kInf;
+        sc.idx[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    bitonic_sort(sc.v, sc.idx, n2, by_value);
+    // top-k: the K-th largest (with multiplicity) ends the kept prefix; all
+    // entries equal to it are kept
+    const int K = min(pl.keff, n1);
+    const float tk = sc.v[K - 1];
+    // count of entries >= tk (a prefix of the sorted list)
+    int cnt = 0;
+    for (int i = tid; i < n1; i += kBlock) cnt += sc.v[i] >= tk;
+    int nk1;
+    (void)block_excl_scan(cnt, sc.misc, &nk1);
+    const float zmax = sc.v[0];
+    const float scale = pl.scale;
+    for (int i = tid; i < nk1; i += kBlock) sc.w[i] = fast_exp2(__fmul_rn(sc.v[i] - zmax, scale));
+    __syncthreads();
+    block_inclusive_scan(sc.w, nk1, sc.red);
+    if (tid == 0) {
+        // normaliser of the top-k-renormalised softmax: the kept top-k set, or
+        // the whole row when top-k is off
+        sZ1 = pl.kmode ? sc.w[nk1 - 1] : sS * fast_exp2(__fmul_rn(sM - zmax, scale));
+    }
+    __syncthreads();
+    const float Z1 = sZ1;
+    int jstar = nk1 - 1;
+    if (pl.top_p < 1.f) {
+        // first level end whose cumulative mass reaches top_p
+        for (int i = tid; i < nk1; i += kBlock) {
+            const bool level_end = i == nk1 - 1 || sc.v[i + 1] != sc.v[i];
+            if (level_end && sc.w[i] / Z1 >= pl.top_p) atomicMin(&sJ, i);
+        }
+        __syncthreads();
+        if (sJ == 0x7fffffff) {
+            if (!pl.kmode) {
+                // top-p alone: the candidates hold less than top_p of the mass
+                if (tid == 0) {
+                    sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+                    publish(&tr->bad, 0u);
+                    publish(&tr->flags, sFlags);
+                    publish(&tr->n_kept, 0);
+                }
+                return;
+            }
+            jstar = nk1 - 1;                // rounding: keep the whole top-k set
+        } else {
+            jstar = sJ;
+        }
+        const float tv = sc.v[jstar];
+        for (int i = tid; i <= jstar; i += kBlock)
+            if (sc.v[i] == tv) atomicMin(&sLevelStart, i);
+        __syncthreads();
+        if (tid == 0) {
+            const float cum = sc.w[jstar] / Z1;
+            const int ls = sLevelStart;
+            const float prev = ls > 0 ? sc.w[ls - 1] / Z1 : 0.f;
+            if (fabsf(cum - pl.top_p) < 1e-5f || (ls > 0 && fabsf(prev - pl.top_p) < 1e-5f))
+                sFlags |= SPECV_FLAG_TOPP_NEAR;
+        }
+    }
+    const int nkept = jstar + 1;
+    Cand* kept = a.ws.kept + rowid * a.kept_cap;
+    for (int i = tid; i < nkept; i += kBlock) publish_cand(kept + i, sc.v[i], sc.idx[i]);
+    __syncthreads();
+    if (tid == 0) {
+        publish(&tr->zmax, zmax);
+        publish(&tr->tstar, sc.v[jstar]);
+        publish(&tr->S, sc.w[jstar]);
+        publish(&tr->n_kept, nkept);
+        publish(&tr->flags, sFlags);
+        publish(&tr->bad, 0u);
+    }
+}
+
+// Decision and sampling of a truncated batch row (whole workgroup), run by
+// the last of its consulted rows to finish.
+template <bool BF16>
+__device__ void decide_trunc(const Args& a, int b, const Plan& pl, TruncScratch& sc) {
+    const int tid = threadIdx.x;
+    __shared__ float tZ[kMaxRows], tT[kMaxRows], tS[kMaxRows];
+    __shared__ int tN[kMaxRows];
+    __shared__ unsigned tF[kMaxRows], tBad[kMaxRows];
+    __shared__ float sP[SPECV_MAX_GAMMA], sQ[SPECV_MAX_GAMMA];
+    __shared__ int sQz[SPECV_MAX_GAMMA];
+    __shared__ float sUacc[SPECV_MAX_GAMMA], sUres[SPECV_MAX_GAMMA + 1];
+    __shared__ Dec sd;
+    __shared__ int sDead, sTok, sLastPos;
+    __shared__ float sWsum;
+    const float scale = pl.scale;
+    const int nrows = pl.nt + pl.nd;
+    for (int k = tid; k < nrows; k += kBlock) {
+        const int r = k < pl.nt ? k : a.gamma + 1 + (k - pl.nt);
+        const TruncRow* tr = &a.ws.trow[(long long)b * a.R + r];
+        tZ[r] = published(&tr->zmax);
+        tT[r] = published(&tr->tstar);
+        tS[r] = published(&tr->S);
+        tN[r] = published(&tr->n_kept);
+        tF[r] = published(&tr->flags);
+        tBad[r] = published(&tr->bad);
+    }
+    __syncthreads();
+    // membership in the kept set is decided on the raw value: z >= tstar
+    auto prob = [&](int r, float z) -> float {
+        if (!(finite_logit(z) && z >= tT[r])) return 0.f;
+        return fast_exp2(__fmul_rn(z - tZ[r], scale)) / tS[r];
+    };
+    auto row_dead = [&](int r) { return tBad[r] != 0 || (tF[r] & SPECV_FLAG_CAND_OVERFLOW) || tN[r] == 0; };
+    if (tid < pl.nd) {
+        const int i = tid;
+        const int d = a.tokens[(long long)b * a.gamma + i];
+        const float zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, i), d);
+        const float zq = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i), d);
+        const int rq = a.gamma + 1 + i;
+        sP[i] = row_dead(i) ? 0.f : prob(i, zt);
+        sQ[i] = row_dead(rq) ? 0.f : prob(rq, zq);
+        sQz[i] = !(finite_logit(zq) && zq >= tT[rq]);
+        sUacc[i] = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
+        sUres[i] = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
+    }
+    if (tid == kBlock - 1) sUres[a.gamma] = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
+    __syncthreads();
+    if (tid == 0) {
+        sd.kind = KIND_NONE;
+        sd.pos = -1;
+        sd.u = 0.f;
+        sd.nemit = 0;
+        sd.nacc = 0;
+        sd.flags = pl.flags;
+        int dead = 0, tested = 0;
+        const int* toks = a.tokens + (long long)b * a.gamma;
+        auto consult = [&](int r) {
+            sd.flags |= tF[r] & (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
+            if (tBad[r]) sd.flags |= SPECV_FLAG_NONFINITE_ROW;
+            return !row_dead(r);
+        };
+        int i = 0;
+        for (; i < a.gamma; ++i) {
+            if (sd.nemit >= pl.cap) break;
+            const bool okt = consult(i), okq = consult(a.gamma + 1 + i);
+            if (!okt || !okq) {
+                dead = 1;
+                break;
+            }
+            if (sQz[i]) sd.flags |= SPECV_FLAG_Q_ZERO;
+            tested = i + 1;
+            if (sUacc[i] * sQ[i] < sP[i]) {       // accept with probability min(1, p/q)
+                sd.emit[sd.nemit++] = toks[i];
+                sd.nacc++;
+                continue;
+            }
+            sd.kind = KIND_RESIDUAL;
+            sd.pos = i;
+            sd.u = sUres[i];
+            break;
+        }
+        if (!dead && sd.kind == KIND_NONE && i == a.gamma && sd.nemit < pl.cap) {
+            if (!consult(a.gamma)) {
+                dead = 1;
+            } else {
+                sd.kind = KIND_BONUS;
+                sd.pos = a.gamma;
+                sd.u = sUres[a.gamma];
+            }
+        }
+        for (int j = 0; j < tested; ++j) {
+            if (a.p_at) a.p_at[(long long)b * a.gamma + j] = sP[j];
+            if (a.q_at) a.q_at[(long long)b * a.gamma + j] = sQ[j];
+        }
+        write_diag_nan(a, b, tested);
+        if (dead) sd.kind = KIND_NONE;
+        sDead = dead;
+        sTok = 0x7fffffff;
+        sLastPos = -1;
+    }
+    __syncthreads();
+    int sampled = -1;
+    float wres = 0.f;
+    if (sd.kind != KIND_NONE) {
+        const int pos = sd.pos;
+        const bool res = sd.kind == KIND_RESIDUAL;
+        const int n = tN[pos];
+        const Cand* kept = a.ws.kept + ((long long)b * a.R + pos) * a.kept_cap;
+        const void* qrow = res ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+        const int rq = a.gamma + 1 + pos;
+        // weights over the kept set of p_pos (zero weight elsewhere):
+        // sc.v = weight, sc.idx = token, sc.w = p (fallback weight)
+        float part = 0.f, partp = 0.f;
+        for (int i = tid; i < n; i += kBlock) {
+            const Cand cv = published_cand(kept + i);
+            const float p = __fmul_rn(fast_exp2(__fmul_rn(cv.v - tZ[pos], scale)), 1.f / tS[pos]);
+            float w = p;
+            if (res) {
+                const float zq = load_elem<BF16>(qrow, cv.idx);
+                const float q = (finite_logit(zq) && zq >= tT[rq])
+                                    ? __fmul_rn(fast_exp2(__fmul_rn(zq - tZ[rq], scale)), 1.f / tS[rq])
+                                    : 0.f;
+                w = fmaxf(__fsub_rn(p, q), 0.f);
+            }
+            sc.v[i] = w;
+            sc.w[i] = p;
+            sc.idx[i] = cv.idx;
+            part += w;
+            partp += p;
+        }
+        part = wave_sum(part);
+        if (tid % kWave == 0) sc.red[tid / kWave] = part;
+        __syncthreads();
+        if (tid == 0) {
+            float W = 0.f;
+            for (int w2 = 0; w2 < kWaves; ++w2) W += sc.red[w2];
+            sWsum = W;
+        }
+        __syncthreads();
+        wres = res ? sWsum : 0.f;
+        if (res && (!(sWsum > 0.f) || !__builtin_isfinite(sWsum))) {
+            // the correction mass vanished: sample from p at that position
+            for (int i = tid; i < n; i += kBlock) sc.v[i] = sc.w[i];
+            if (tid == 0) sd.flags |= SPECV_FLAG_RESIDUAL_FALLBACK;
+        }
+        (void)partp;
+        // tokens in ascending index order, then the first running sum > u * W
+        const int n2 = pow2_at_least(n);
+        for (int i = n + tid; i < n2; i += kBlock) {
+            sc.v[i] = 0.f;
+            sc.idx[i] = 0x7fffffff;
+        }
+        __syncthreads();
+        bitonic_sort(sc.v, sc.idx, n2, by_index);
+        for (int i = tid; i < n; i += kBlock) sc.w[i] = sc.v[i];
+        __syncthreads();
+        block_inclusive_scan(sc.w, n, sc.red);
+        const float target = sd.u * sc.w[n - 1];
+        for (int i = tid; i < n; i += kBlock) {
+            if (sc.v[i] > 0.f) {
+                if (sc.w[i] > target) atomicMin(&sTok, i);
+                atomicMax(&sLastPos, i);
+            }
+        }
+        __syncthreads();
+        const int j = sTok != 0x7fffffff ? sTok : sLastPos;     // clamp: last positive weight
+        sampled = j >= 0 ? sc.idx[j] : -1;
+    }
+    if (tid == 0) {
+        bool dead = sDead;
+        unsigned flags = sd.flags;
+        if (!dead && sd.kind != KIND_NONE && sampled < 0) {
+            dead = true;
+            flags |= SPECV_FLAG_NONFINITE_ROW;
+        }
+        write_outputs(a, b, sd.emit, sd.nemit, sd.nacc, flags, dead, sampled, wres);
+        publish(&a.ws.dec[b].kind, (int)KIND_NONE);
+        wait_stores();
+        publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
+    }
+}
+
 // ---------------------------------------------------------------- streaming
 // Issue the 16-byte loads of one full chunk (this thread's four / eight groups).
 template <bool BF16>
@@ -626,8 +1265,8 @@ __device__ inline void issue_chunk(const void* row, int v0, uint4 (&q)[kPerThrea
 //   greedy rows:   running max and its lowest index.
 // The unit's statistics are published; the last unit of a batch row to
 // arrive runs the decision.
-template <bool BF16, bool VEC>
-__device__ void stream_unit(const Args& a, int t) {
+template <bool BF16, bool VEC, bool TRUNC>
+__device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
     constexpr int NG = kPerThread / (BF16 ? 8 : 4);
     const int unit = t % a.U;
     const int row = t / a.U;
@@ -654,6 +1293,8 @@ __device__ void stream_unit(const Args& a, int t) {
     const int c0 = unit * kUnitChunks;
     const int nfull = a.V / kChunk;                    // chunks without a tail
     const bool greedy = pl.mode == MODE_GREEDY;
+    const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
+    const long long rowid = (long long)b * a.R + r;
     const float scale = pl.scale;
     float m = -kInf, s = 0.f;                          // sampling rows
     float best = -kInf;                                // greedy rows
@@ -698,6 +1339,8 @@ __device__ void stream_unit(const Args& a, int t) {
             for (int k = 0; k < kPerThread; ++k) cs += fast_exp2(fmaf(x[k], scale, nms));
             s = cs;
             m = nm;
+            if constexpr (TRUNC)
+                if (trunc) chunk_candidates<BF16>(a, rowid, c, pl.keff, x, *sc);
         }
     }
 
@@ -740,6 +1383,28 @@ __device__ void stream_unit(const Args& a, int t) {
             out.arg = -1;
             out.bad = __builtin_isnan(s) ? 1u : 0u;      // NaN or +inf in the unit
         }
+    }
+    if constexpr (TRUNC) if (trunc) {
+        // the last unit of the logits row truncates it; the last truncated
+        // row of the batch row decides and samples
+        if (tid == 0) {
+            publish_part(&a.ws.part[part_index(a, b, r, unit)], out);
+            sLast = arrive(&a.ws.counter_row[rowid * kCounterStride]) == (unsigned)(a.U - 1);
+        }
+        __syncthreads();
+        if (!sLast) return;
+        if (tid == 0) publish(&a.ws.counter_row[rowid * kCounterStride], 0u);
+        row_merge<BF16>(a, b, r, pl, *sc);
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned expected = (unsigned)(pl.nt + pl.nd);
+            sLast = arrive(&a.ws.counter[(long long)b * kCounterStride]) == expected - 1;
+        }
+        __syncthreads();
+        if (!sLast) return;
+        if (tid == 0) publish(&a.ws.counter[(long long)b * kCounterStride], 0u);
+        decide_trunc<BF16>(a, b, pl, *sc);
+        return;
     }
     if (tid == 0) {
         publish_part(&a.ws.part[part_index(a, b, r, unit)], out);
@@ -1001,43 +1666,43 @@ __device__ void sample_item(const Args& a, int b, int c) {
 // streaming workgroup has been dispatched (and never waits) before any
 // sampling workgroup that could wait for it: the waits always end.  Sampling
 // of early rows overlaps the streaming of later ones.
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_verify(Args a) {
+//
+// TRUNC selects the variant with the truncation path (handles created with
+// max_top_k > 0); without it truncated rows are flagged unsupported and the
+// kernel stays lean (registers and LDS of the streaming path only).
+template <bool BF16, bool VEC, bool TRUNC>
+__global__ __launch_bounds__(kBlock, 4) void k_verify(Args a) {
     const int units = a.B * a.R * a.U;
     const int t = blockIdx.x;
-    if (t < units) stream_unit<BF16, VEC>(a, t);
-    else sample_item<BF16, VEC>(a, (t - units) / a.C, (t - units) % a.C);
+    if (t < units) {
+        if constexpr (TRUNC) {
+            __shared__ TruncScratch sc;
+            stream_unit<BF16, VEC, true>(a, t, &sc);
+        } else {
+            stream_unit<BF16, VEC, false>(a, t, nullptr);
+        }
+    } else {
+        sample_item<BF16, VEC>(a, (t - units) / a.C, (t - units) % a.C);
+    }
 }
 
 using KernelFn = void (*)(Args);
 
-KernelFn pick(bool bf16, bool vec) {
-    if (bf16) return vec ? k_verify<true, true> : k_verify<true, false>;
-    return vec ? k_verify<false, true> : k_verify<false, false>;
+KernelFn pick(bool bf16, bool vec, bool trunc) {
+    if (trunc) {
+        if (bf16) return vec ? k_verify<true, true, true> : k_verify<true, false, true>;
+        return vec ? k_verify<false, true, true> : k_verify<false, false, true>;
+    }
+    if (bf16) return vec ? k_verify<true, true, false> : k_verify<true, false, false>;
+    return vec ? k_verify<false, true, false> : k_verify<false, false, false>;
 }
 
 }  // namespace
 
-hipError_t verify_max_grid(bool bf16, bool vec, int* grid) {
-    int dev = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    hipDeviceProp_t prop;
-    e = hipGetDeviceProperties(&prop, dev);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(pick(bf16, vec)),
-                                                     kBlock, 0);
-    if (e != hipSuccess) return e;
-    *grid = per_cu * prop.multiProcessorCount;
-    return hipSuccess;
-}
-
-hipError_t launch_verify(const Args& a, bool bf16, bool vec, int grid, hipStream_t stream,
-                         hipEvent_t* ev) {
-    (void)grid;
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev) {
     const int blocks = a.B * a.R * a.U + a.B * a.C;
     if (ev) (void)hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL(pick(bf16, vec), dim3(blocks), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL(pick(bf16, vec, a.cand_cap > 0), dim3(blocks), dim3(kBlock), 0, stream, a);
     if (ev) (void)hipEventRecord(ev[1], stream);
     return hipGetLastError();
 }
