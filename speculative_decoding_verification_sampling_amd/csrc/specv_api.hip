@@ -75,6 +75,8 @@ void free_ws(specv::Workspace& ws) {
     if (ws.counter2) (void)hipFree(ws.counter2);
     if (ws.dec) (void)hipFree(ws.dec);
     if (ws.ready) (void)hipFree(ws.ready);
+    if (ws.counter1) (void)hipFree(ws.counter1);
+    if (ws.stage1) (void)hipFree(ws.stage1);
     if (ws.cand) (void)hipFree(ws.cand);
     if (ws.cand_meta) (void)hipFree(ws.cand_meta);
     if (ws.counter_row) (void)hipFree(ws.counter_row);
@@ -129,7 +131,7 @@ specv::Args base_args(specv_handle h, int B, int gamma, int V) {
 // One launch of the verify kernel; each call gets a new epoch tag.
 specv_status launch(specv_handle h, specv::Args& a, bool bf16, bool vec, void* stream) {
     if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
-    h->epoch = h->epoch + 1 == 0 ? 1 : h->epoch + 1;
+    h->epoch = h->epoch + 1 >= 0x80000000u ? 1 : h->epoch + 1;
     a.epoch = h->epoch;
     if (specv::launch_verify(a, bf16, vec, static_cast<hipStream_t>(stream), next_events(h)) !=
         hipSuccess)
@@ -183,7 +185,9 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
               alloc(&ws.counter, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
               alloc(&ws.counter2, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
               alloc(&ws.dec, (size_t)cfg->max_batch) == hipSuccess &&
-              alloc(&ws.ready, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess;
+              alloc(&ws.ready, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
+              alloc(&ws.counter1, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
+              alloc(&ws.stage1, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess;
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
@@ -196,6 +200,8 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     if (ok) ok = hipMemset(ws.counter, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipMemset(ws.counter2, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipMemset(ws.ready, 0, counter_bytes) == hipSuccess;
+    if (ok) ok = hipMemset(ws.counter1, 0, counter_bytes) == hipSuccess;
+    if (ok) ok = hipMemset(ws.stage1, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
         free_ws(ws);

@@ -14,6 +14,7 @@ constexpr int kWaves = kBlock / kWave;
 constexpr int kChunk = 8192;            // vocabulary entries per chunk (32 per thread)
 constexpr int kPerThread = kChunk / kBlock;
 constexpr int kUnitChunks = 4;          // chunks streamed by one workgroup (one "unit")
+constexpr int kDecideParts = 512;       // unit statistics a decision stages in LDS at once
 constexpr int kMaxChunks = 64;          // V <= 64 * 8192 = 524288
 constexpr int kMaxRows = 2 * SPECV_MAX_GAMMA + 1;
 constexpr int kCounterStride = 64;     // one arrival counter per 256-byte slot: atomics
@@ -83,6 +84,9 @@ struct Workspace {
     Dec* dec;             // [max_batch]
     unsigned* ready;      // [max_batch * kCounterStride]: epoch of the call whose decision
                           // for the row is published
+    unsigned* counter1;   // [max_batch * kCounterStride] arrivals of position-0 units
+    unsigned* stage1;     // [max_batch * kCounterStride]: 2 * epoch + 1 when the round goes on
+                          // past position 0, 2 * epoch when it ended there
     Cand* cand;           // [max_batch * rows * max_chunks * cand_cap] chunk candidates
     Cand* cand_meta;      // [max_batch * rows * max_chunks]: (lower bound L, count); count -1
                           // when the chunk's candidates overflowed

@@ -291,13 +291,57 @@ __device__ inline void merge_ms(float& m, float& s, float m2, float s2, float sc
     m = M;
 }
 
-__device__ inline void wave_merge_ms(float& m, float& s, float scale) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        const float m2 = __shfl_xor(m, off, kWave);
-        const float s2 = __shfl_xor(s, off, kWave);
-        merge_ms(m, s, m2, s2, scale);
+// ---------------------------------------------------------------- wave64 DPP
+// Cross-lane moves by DPP (VALU-speed, no LDS round trip).  Lanes whose
+// source is outside the pattern or masked off receive ``old``, the identity
+// of the operation being built.
+constexpr int kDppQuad1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuad2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+constexpr int kDppBcast15 = 0x142;    // lane 15 of a row -> the next row
+constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+constexpr int kDppShr = 0x110;        // + n: row_shr:n
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline int dpp_i(int v, int old) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline float dpp_f(float v, float old) {
+    return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(v), __float_as_int(old)));
+}
+
+// Wave reduction of a value pair with a combine functor: quads, half rows,
+// rows, then rows 0+1 -> 1, 2+3 -> 3, rows 0..2 -> 3; the total ends in lane
+// 63 and is broadcast.
+template <typename Comb>
+__device__ inline void wave_reduce2(float& x, int& y, float idx, int idy, Comb comb) {
+#define SPECV_DPP_STEP(CTRL, MASK)                                          \
+    {                                                                       \
+        const float x2 = dpp_f<CTRL, MASK>(x, idx);                         \
+        const int y2 = dpp_i<CTRL, MASK>(y, idy);                           \
+        comb(x, y, x2, y2);                                                 \
     }
+    SPECV_DPP_STEP(kDppQuad1, 0xF)
+    SPECV_DPP_STEP(kDppQuad2, 0xF)
+    SPECV_DPP_STEP(kDppHalfMirror, 0xF)
+    SPECV_DPP_STEP(kDppMirror, 0xF)
+    SPECV_DPP_STEP(kDppBcast15, 0xA)
+    SPECV_DPP_STEP(kDppBcast31, 0xC)
+#undef SPECV_DPP_STEP
+    x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+    y = __builtin_amdgcn_readlane(y, kWave - 1);
+}
+
+__device__ inline void wave_merge_ms(float& m, float& s, float scale) {
+    int si = __float_as_int(s);
+    wave_reduce2(m, si, -kInf, 0, [scale](float& m1, int& s1, float m2, int s2) {
+        float sa = __int_as_float(s1);
+        merge_ms(m1, sa, m2, __int_as_float(s2), scale);
+        s1 = __float_as_int(sa);
+    });
+    s = __int_as_float(si);
 }
 
 // (value, index) argmax merge: larger value wins, lower index on ties.
@@ -309,26 +353,56 @@ __device__ inline void merge_arg(float& v, int& i, float v2, int i2) {
 }
 
 __device__ inline void wave_merge_arg(float& v, int& i) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        const float v2 = __shfl_xor(v, off, kWave);
-        const int i2 = __shfl_xor(i, off, kWave);
-        merge_arg(v, i, v2, i2);
-    }
+    wave_reduce2(v, i, -kInf, 0x7fffffff, [](float& v1, int& i1, float v2, int i2) {
+        merge_arg(v1, i1, v2, i2);
+    });
 }
 
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    int dummy = 0;
+    wave_reduce2(x, dummy, 0.f, 0, [](float& a, int&, float b, int) { a += b; });
+    return x;
+}
+
+__device__ inline float wave_max(float x) {
+    int dummy = 0;
+    wave_reduce2(x, dummy, -kInf, 0, [](float& a, int&, float b, int) { a = fmaxf(a, b); });
     return x;
 }
 
 __device__ inline unsigned wave_or(unsigned x) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) x |= __shfl_xor(x, off, kWave);
+    float dummy = 0.f;
+    int xi = (int)x;
+    wave_reduce2(dummy, xi, 0.f, 0, [](float&, int& a, float, int b) { a |= b; });
+    return (unsigned)xi;
+}
+
+__device__ inline int wave_max_i(int x) {
+    float dummy = 0.f;
+    wave_reduce2(dummy, x, 0.f, (int)0x80000000, [](float&, int& a, float, int b) { a = max(a, b); });
     return x;
 }
 
+// Inclusive prefix sums across the wave (lane order).
+__device__ inline float wave_scan_incl(float x) {
+    x += dpp_f<kDppShr + 1>(x, 0.f);
+    x += dpp_f<kDppShr + 2>(x, 0.f);
+    x += dpp_f<kDppShr + 4>(x, 0.f);
+    x += dpp_f<kDppShr + 8>(x, 0.f);
+    x += dpp_f<kDppBcast15, 0xA>(x, 0.f);
+    x += dpp_f<kDppBcast31, 0xC>(x, 0.f);
+    return x;
+}
+
+__device__ inline int wave_scan_incl(int x) {
+    x += dpp_i<kDppShr + 1>(x, 0);
+    x += dpp_i<kDppShr + 2>(x, 0);
+    x += dpp_i<kDppShr + 4>(x, 0);
+    x += dpp_i<kDppShr + 8>(x, 0);
+    x += dpp_i<kDppBcast15, 0xA>(x, 0);
+    x += dpp_i<kDppBcast31, 0xC>(x, 0);
+    return x;
+}
 
 // ---------------------------------------------------------------- row plan
 // What one batch row needs, from its parameters and draft tokens alone.
@@ -472,8 +546,13 @@ __device__ inline bool wait_flag(const unsigned* flag, unsigned epoch) {
 // greedy rule.  Rows that need no sampled token get their outputs here; the
 // others publish a Dec record for the sampling phase.  Either way the row's
 // ready flag is set to this call's epoch.
+//
+// With ``first`` set it runs after the position-0 rows only: if the round
+// ends at position 0 the row is decided as above (and the stage flag says
+// "stop"); otherwise only the stage flag is published ("go on") and the
+// decision is left to the last unit of the later positions.
 template <bool BF16>
-__device__ void decide_row(const Args& a, int b, const Plan& pl) {
+__device__ void decide_row(const Args& a, int b, const Plan& pl, bool first) {
     __shared__ float sM[kMaxRows], sS[kMaxRows];
     __shared__ int sI[kMaxRows];
     __shared__ unsigned sBad[kMaxRows];
@@ -481,49 +560,65 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     __shared__ int sQz[SPECV_MAX_GAMMA];
     __shared__ float sUacc[SPECV_MAX_GAMMA], sUres[SPECV_MAX_GAMMA + 1];
     __shared__ Dec sd;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x;
     const bool greedy = pl.mode == MODE_GREEDY;
     const float scale = pl.scale;
-    const int nrows = pl.nt + pl.nd;
-    for (int k = wave; k < nrows; k += kWaves) {
-        const int r = k < pl.nt ? k : a.gamma + 1 + (k - pl.nt);
+    const int nt = first ? 1 : pl.nt;                 // rows merged at this point
+    const int nd = first ? min(pl.nd, 1) : pl.nd;
+    const int nrows = nt + nd;
+    // one memory round trip: every unit statistic, every z at d_i, and the
+    // uniforms, issued together by different threads
+    __shared__ Part sPart[kDecideParts];
+    __shared__ float sZt[SPECV_MAX_GAMMA], sZq[SPECV_MAX_GAMMA];
+    const int nparts = nrows * a.U;
+    for (int k = tid; k < nparts; k += kBlock) {
+        const int row = k / a.U;
+        const int r = row < nt ? row : a.gamma + 1 + (row - nt);
+        if (k < kDecideParts) sPart[k] = published_part(&a.ws.part[part_index(a, b, r, k - row * a.U)]);
+    }
+    if (!greedy && tid >= kBlock - kWave && tid - (kBlock - kWave) < nd) {
+        const int i = tid - (kBlock - kWave);
+        const int d = a.tokens[(long long)b * a.gamma + i];
+        sZt[i] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, i), d);
+        sZq[i] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i), d);
+    }
+    if (!greedy && tid >= kBlock - 2 * kWave && tid < kBlock - kWave) {
+        const int i = tid - (kBlock - 2 * kWave);
+        if (i < nd) {
+            sUacc[i] = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
+            sUres[i] = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
+        }
+        if (i == kWave - 1) sUres[a.gamma] = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
+    }
+    __syncthreads();
+    // merge the units of each row, one thread per row
+    for (int row = tid; row < nrows; row += kBlock) {
+        const int r = row < nt ? row : a.gamma + 1 + (row - nt);
         float m = -kInf, s = 0.f;
         int arg = 0x7fffffff;
         unsigned bad = 0;
-        for (int cc = lane; cc < a.U; cc += kWave) {
-            const Part p = published_part(&a.ws.part[part_index(a, b, r, cc)]);
+        for (int u = 0; u < a.U; ++u) {
+            const int k = row * a.U + u;
+            const Part p = k < kDecideParts ? sPart[k]
+                                            : published_part(&a.ws.part[part_index(a, b, r, u)]);
             if (greedy) merge_arg(m, arg, p.m, p.arg);
             else merge_ms(m, s, p.m, p.s, scale);
             bad |= p.bad;
         }
-        if (greedy) wave_merge_arg(m, arg);
-        else wave_merge_ms(m, s, scale);
-        bad = wave_or(bad);
-        if (lane == 0) {
-            sM[r] = m;
-            sS[r] = s;
-            sI[r] = arg;
-            sBad[r] = bad || m == -kInf || (!greedy && !(s > 0.f));
-        }
+        sM[r] = m;
+        sS[r] = s;
+        sI[r] = arg;
+        sBad[r] = bad || m == -kInf || (!greedy && !(s > 0.f));
     }
     __syncthreads();
-    if (!greedy && tid < pl.nd) {
-        // p_i(d_i) and q_i(d_i) from the raw logits at d_i, and the uniforms
-        // this position may need (drawn in parallel; only the ones the
-        // sequential rule reaches are used)
+    if (!greedy && tid < nd) {
+        // p_i(d_i) and q_i(d_i) from the raw logits at d_i
         const int i = tid;
-        const int d = a.tokens[(long long)b * a.gamma + i];
-        const float zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, i), d);
-        const float zq = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i), d);
         const int rq = a.gamma + 1 + i;
-        sP[i] = fast_exp2((zt - sM[i]) * scale) / sS[i];
-        sQ[i] = fast_exp2((zq - sM[rq]) * scale) / sS[rq];
-        sQz[i] = zq == -kInf;
-        sUacc[i] = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
-        sUres[i] = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
+        sP[i] = fast_exp2((sZt[i] - sM[i]) * scale) / sS[i];
+        sQ[i] = fast_exp2((sZq[i] - sM[rq]) * scale) / sS[rq];
+        sQz[i] = sZq[i] == -kInf;
     }
-    if (!greedy && tid == kBlock - 1)
-        sUres[a.gamma] = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
     __syncthreads();
     if (tid != 0) return;
 
@@ -534,12 +629,17 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     sd.nacc = 0;
     sd.flags = pl.flags;
     bool dead = false;
+    bool go_on = false;                                // first stage: the round continues
     int sampled = -1;
     int tested = 0;
     const int* toks = a.tokens + (long long)b * a.gamma;
     if (greedy) {
         for (int i = 0; i <= a.gamma; ++i) {
             if (sd.nemit >= pl.cap) break;
+            if (first && i >= 1) {
+                go_on = true;
+                break;
+            }
             if (sBad[i]) {
                 dead = true;
                 break;
@@ -557,6 +657,10 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
         int i = 0;
         for (; i < a.gamma; ++i) {
             if (sd.nemit >= pl.cap) break;
+            if (first && i >= 1) {
+                go_on = true;
+                break;
+            }
             if (sBad[i] || sBad[a.gamma + 1 + i]) {
                 dead = true;
                 break;
@@ -573,8 +677,10 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
             sd.u = sUres[i];
             break;
         }
-        if (!dead && sd.kind == KIND_NONE && i == a.gamma && sd.nemit < pl.cap) {
-            if (sBad[a.gamma]) {
+        if (!go_on && !dead && sd.kind == KIND_NONE && i == a.gamma && sd.nemit < pl.cap) {
+            if (first && a.gamma >= 1) {
+                go_on = true;                     // the bonus row is a later position
+            } else if (sBad[a.gamma]) {
                 dead = true;
             } else {
                 sd.kind = KIND_BONUS;
@@ -582,10 +688,16 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
                 sd.u = sUres[a.gamma];
             }
         }
-        for (int j = 0; j < tested; ++j) {
-            if (a.p_at) a.p_at[(long long)b * a.gamma + j] = sP[j];
-            if (a.q_at) a.q_at[(long long)b * a.gamma + j] = sQ[j];
+        if (!go_on) {
+            for (int j = 0; j < tested; ++j) {
+                if (a.p_at) a.p_at[(long long)b * a.gamma + j] = sP[j];
+                if (a.q_at) a.q_at[(long long)b * a.gamma + j] = sQ[j];
+            }
         }
+    }
+    if (go_on) {
+        publish(&a.ws.stage1[(long long)b * kCounterStride], 2u * a.epoch + 1u);
+        return;
     }
     write_diag_nan(a, b, tested);
     if (dead) {
@@ -614,6 +726,7 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl) {
     }
     wait_stores();
     publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
+    if (first) publish(&a.ws.stage1[(long long)b * kCounterStride], 2u * a.epoch);
 }
 
 // ---------------------------------------------------------------- truncation
@@ -695,12 +808,7 @@ __device__ void bitonic_sort(float* v, int* idx, int n, Prec prec) {
 // offset and writes the total to *total (both visible to all threads).
 __device__ inline int block_excl_scan(int x, int* scratch /* kWaves + 1 */, int* total) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-    }
+    const int incl = wave_scan_incl(x);
     if (lane == kWave - 1) scratch[wave] = incl;
     __syncthreads();
     int base = 0, tot = 0;
@@ -726,12 +834,7 @@ __device__ void block_inclusive_scan(float* w, int n, float* red) {
         run += base + j < n ? w[base + j] : 0.f;
         loc[j] = run;
     }
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const float o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-    }
+    const float incl = wave_scan_incl(run);
     if (lane == kWave - 1) red[wave] = incl;
     __syncthreads();
     float wbase = 0.f;
@@ -905,14 +1008,8 @@ __device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScra
             ovf = m.idx < 0;
             cnt = ovf ? 0 : m.idx;
         }
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) L = fmaxf(L, __shfl_xor(L, o, kWave));
-        int incl = cnt;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int v = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += v;
-        }
+        L = wave_max(L);
+        const int incl = wave_scan_incl(cnt);
         if (lane < a.C) off[lane] = (unsigned)(incl - cnt);
         if (lane == a.C - 1) {
             off[a.C] = (unsigned)incl;
@@ -1265,13 +1362,34 @@ __device__ inline void issue_chunk(const void* row, int v0, uint4 (&q)[kPerThrea
 //   greedy rows:   running max and its lowest index.
 // The unit's statistics are published; the last unit of a batch row to
 // arrive runs the decision.
+//
+// Units come in two stages.  Stage 1 holds the position-0 rows (target row 0
+// and draft row 0) of every batch row; stage 2 the later positions.  For
+// sampling and greedy rows the last stage-1 unit tests position 0; stage-2
+// units wait for that result and skip their rows when the round has already
+// ended (the rows past the first rejection are never needed), otherwise the
+// last stage-2 unit decides the row.  Truncated rows do not wait.
 template <bool BF16, bool VEC, bool TRUNC>
 __device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
     constexpr int NG = kPerThread / (BF16 ? 8 : 4);
-    const int unit = t % a.U;
-    const int row = t / a.U;
-    const int b = row / a.R;
-    const int r = row - b * a.R;
+    const int n1 = a.gamma >= 1 ? 2 : 1;            // position-0 rows per batch row
+    const int n2 = a.R - n1;
+    const int units1 = a.B * n1 * a.U;
+    const bool stage1 = t < units1;
+    int b, r, unit;
+    if (stage1) {
+        unit = t % a.U;
+        const int row = t / a.U;
+        b = row / n1;
+        r = (row - b * n1) == 0 ? 0 : a.gamma + 1;
+    } else {
+        const int t2 = t - units1;
+        unit = t2 % a.U;
+        const int row = t2 / a.U;
+        b = row / n2;
+        const int k = row - b * n2;                  // target rows 1..gamma, then draft rows 1..
+        r = k < a.gamma ? 1 + k : a.gamma + 2 + (k - a.gamma);
+    }
     const int tid = threadIdx.x;
     const Plan pl = make_plan(a, b);
     if (pl.mode == MODE_SKIP) {
@@ -1287,6 +1405,23 @@ __device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
     const bool is_target = r <= a.gamma;
     const int pos = is_target ? r : r - a.gamma - 1;
     if (pos >= (is_target ? pl.nt : pl.nd)) return;   // a row this round cannot consult
+    const bool staged = pl.mode == MODE_SAMPLE || pl.mode == MODE_GREEDY;
+    if (staged && !stage1) {
+        __shared__ unsigned sGo;
+        if (tid == 0) {
+            const unsigned* flag = &a.ws.stage1[(long long)b * kCounterStride];
+            unsigned v = 0;
+            for (int spin = 0; spin < (1 << 20); ++spin) {
+                v = published(flag);
+                if ((v >> 1) == a.epoch) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            sGo = (v >> 1) == a.epoch ? (v & 1u) : 0u;
+            if ((v >> 1) != a.epoch && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
+        }
+        __syncthreads();
+        if (!sGo) return;                              // the round ended at position 0
+    }
 
     const void* rp = is_target ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos)
                                : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos);
@@ -1406,15 +1541,17 @@ __device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
         decide_trunc<BF16>(a, b, pl, *sc);
         return;
     }
+    unsigned* counter = stage1 ? &a.ws.counter1[(long long)b * kCounterStride]
+                               : &a.ws.counter[(long long)b * kCounterStride];
     if (tid == 0) {
         publish_part(&a.ws.part[part_index(a, b, r, unit)], out);
-        const unsigned expected = (unsigned)((pl.nt + pl.nd) * a.U);
-        sLast = arrive(&a.ws.counter[(long long)b * kCounterStride]) == expected - 1;
+        const int rows = stage1 ? 1 + min(pl.nd, 1) : (pl.nt - 1) + max(pl.nd - 1, 0);
+        sLast = arrive(counter) == (unsigned)(rows * a.U) - 1;
     }
     __syncthreads();
     if (!sLast) return;
-    if (tid == 0) publish(&a.ws.counter[(long long)b * kCounterStride], 0u);   // ready for the next call
-    decide_row<BF16>(a, b, pl);
+    if (tid == 0) publish(counter, 0u);               // ready for the next call
+    decide_row<BF16>(a, b, pl, stage1);
 }
 
 // ---------------------------------------------------------------- sampling
@@ -1446,19 +1583,27 @@ __device__ void sample_item(const Args& a, int b, int c) {
     Dec* gd = &a.ws.dec[b];
     __shared__ int sKind, sPos;
     __shared__ float sU, sMt, sInvt, sMq, sInvq, sScale;
+    __shared__ int sOk;
     if (tid == 0) {
         const bool ok = wait_flag(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
-        sKind = ok ? published(&gd->kind) : (int)KIND_NONE;
-        if (ok && sKind != KIND_NONE) {
-            sPos = published(&gd->pos);
-            sU = published(&gd->u);
-            sMt = published(&gd->mt);
-            sInvt = published(&gd->invt);
-            sMq = published(&gd->mq);
-            sInvq = published(&gd->invq);
-            sScale = published(&gd->scale);
-        }
+        sOk = ok;
         if (!ok && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
+    }
+    __syncthreads();
+    // the record's fields, one thread each (one round trip)
+    if (sOk && tid < 8) {
+        switch (tid) {
+            case 0: sKind = published(&gd->kind); break;
+            case 1: sPos = published(&gd->pos); break;
+            case 2: sU = published(&gd->u); break;
+            case 3: sMt = published(&gd->mt); break;
+            case 4: sInvt = published(&gd->invt); break;
+            case 5: sMq = published(&gd->mq); break;
+            case 6: sInvq = published(&gd->invq); break;
+            case 7: sScale = published(&gd->scale); break;
+        }
+    } else if (!sOk && tid == 0) {
+        sKind = (int)KIND_NONE;
     }
     __syncthreads();
     const int kind = sKind;
@@ -1594,12 +1739,7 @@ __device__ void sample_item(const Args& a, int b, int c) {
             }
         }
         // inclusive scan of the per-thread totals (thread order = token order)
-        float incl = tot;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float o = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += o;
-        }
+        const float incl = wave_scan_incl(tot);
         __shared__ float wtot[kWaves];
         __shared__ int wlast[kWaves];
         if (lane == kWave - 1) wtot[wave] = incl;
@@ -1628,9 +1768,7 @@ __device__ void sample_item(const Args& a, int b, int c) {
                 atomicMin(&sTok, tk);
             }
         }
-        int lp = lastpos;
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) lp = max(lp, __shfl_xor(lp, off, kWave));
+        const int lp = wave_max_i(lastpos);
         if (lane == 0) wlast[wave] = lp;
         __syncthreads();
         if (tid == 0) {
