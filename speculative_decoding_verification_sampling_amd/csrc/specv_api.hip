@@ -74,7 +74,6 @@ void free_ws(specv::Workspace& ws) {
     if (ws.counter) (void)hipFree(ws.counter);
     if (ws.counter2) (void)hipFree(ws.counter2);
     if (ws.dec) (void)hipFree(ws.dec);
-    if (ws.ready) (void)hipFree(ws.ready);
     if (ws.counter1) (void)hipFree(ws.counter1);
     if (ws.stage1) (void)hipFree(ws.stage1);
     if (ws.cand) (void)hipFree(ws.cand);
@@ -185,7 +184,6 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
               alloc(&ws.counter, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
               alloc(&ws.counter2, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
               alloc(&ws.dec, (size_t)cfg->max_batch) == hipSuccess &&
-              alloc(&ws.ready, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
               alloc(&ws.counter1, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
               alloc(&ws.stage1, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess;
     // candidate storage for truncated rows, reserved only when asked for
@@ -199,7 +197,7 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     const size_t counter_bytes = (size_t)cfg->max_batch * specv::kCounterStride * sizeof(unsigned);
     if (ok) ok = hipMemset(ws.counter, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipMemset(ws.counter2, 0, counter_bytes) == hipSuccess;
-    if (ok) ok = hipMemset(ws.ready, 0, counter_bytes) == hipSuccess;
+    if (ok) ok = hipMemset(ws.dec, 0, (size_t)cfg->max_batch * sizeof(specv::Dec)) == hipSuccess;
     if (ok) ok = hipMemset(ws.counter1, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipMemset(ws.stage1, 0, counter_bytes) == hipSuccess;
     if (ok) ok = hipDeviceSynchronize() == hipSuccess;

@@ -60,19 +60,27 @@ struct TruncScratch {
     int misc[8];
 };
 
-// Outcome of one batch row's accept tests, handed from the streaming
-// kernel to the sampling kernel.
+// Outcome of one batch row's accept tests, handed from the workgroup that
+// decides the row to its sampling workgroups.  Every word holds
+// (epoch << 32) | value, written with one 64-bit store, so a reader polls all
+// the words it needs at once and knows each is this call's when its epoch
+// matches: no separate ready flag, no ordering between the words.
+enum DecWord {
+    DW_KIND = 0,          // 0: nothing to sample (outputs written); 1: correction; 2: bonus
+    DW_POS,               // rejected position, or gamma for the bonus
+    DW_U,                 // uniform of the correction / bonus draw (float bits)
+    DW_MT, DW_INVT,       // target row max and 1 / sum (exp2 units)
+    DW_MQ, DW_INVQ,       // draft row max and 1 / sum (correction only)
+    DW_SCALE,             // log2(e) / T
+    DW_NEMIT,             // tokens emitted before the sampled one
+    DW_NACC,
+    DW_FLAGS,
+    DW_EMIT,              // emitted tokens, gamma words (-1 past nemit)
+};
+constexpr int kDecWords = DW_EMIT + SPECV_MAX_GAMMA;
+static_assert(kDecWords <= 64, "one wave64 polls the whole record");
 struct Dec {
-    int kind;             // 0: nothing to sample (outputs written); 1: correction; 2: bonus
-    int pos;              // rejected position, or gamma for the bonus
-    float u;              // uniform of the correction / bonus draw
-    float mt, invt;       // target row max and 1 / sum (exp2 units)
-    float mq, invq;       // draft row max and 1 / sum (correction only)
-    float scale;          // log2(e) / T
-    int nemit;            // tokens emitted before the sampled one
-    int nacc;
-    unsigned flags;
-    int emit[SPECV_MAX_GAMMA + 1];
+    unsigned long long w[48];
 };
 
 struct Workspace {
@@ -81,9 +89,7 @@ struct Workspace {
     unsigned* counter;    // [max_batch * kCounterStride] arrivals in the streaming kernel
     unsigned* counter2;   // [max_batch * kCounterStride] arrivals in the sampling kernel;
                           // both zero between calls
-    Dec* dec;             // [max_batch]
-    unsigned* ready;      // [max_batch * kCounterStride]: epoch of the call whose decision
-                          // for the row is published
+    Dec* dec;             // [max_batch], zero before the first call
     unsigned* counter1;   // [max_batch * kCounterStride] arrivals of position-0 units
     unsigned* stage1;     // [max_batch * kCounterStride]: 2 * epoch + 1 when the round goes on
                           // past position 0, 2 * epoch when it ended there

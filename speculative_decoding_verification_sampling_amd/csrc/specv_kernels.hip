@@ -527,25 +527,54 @@ __device__ inline void write_outputs(const Args& a, int b, const int* emit, int 
     if (a.wres) a.wres[b] = wres;
 }
 
-// ---------------------------------------------------------------- decision
-// Wait (bounded) until ``flag`` holds ``epoch``; false on time-out.  The
-// workgroup that publishes the flag was dispatched before the waiting one
-// and never waits itself, so the wait ends; the bound only guards against a
-// dispatch order other than the hardware's in-order one.
-__device__ inline bool wait_flag(const unsigned* flag, unsigned epoch) {
-    for (int spin = 0; spin < (1 << 20); ++spin) {
-        if (published(flag) == epoch) return true;
-        __builtin_amdgcn_s_sleep(2);
-    }
-    return false;
+// A batch row's decision while it is being taken (LDS of the deciding
+// workgroup), and its publication as epoch-tagged words.
+struct DecLocal {
+    int kind;
+    int pos;
+    float u;
+    int nemit;
+    int nacc;
+    unsigned flags;
+    int emit[SPECV_MAX_GAMMA];
+};
+
+__device__ inline void dec_put(Dec* d, int word, unsigned v, unsigned epoch) {
+    __hip_atomic_store(&d->w[word], ((unsigned long long)epoch << 32) | v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Nothing to sample for the row (its outputs are written).
+__device__ inline void publish_dec_none(const Args& a, int b) {
+    dec_put(&a.ws.dec[b], DW_KIND, (unsigned)KIND_NONE, a.epoch);
+}
+
+// A correction / bonus draw for the sampling workgroups of the row.
+__device__ inline void publish_dec_draw(const Args& a, int b, const DecLocal& sd, float mt,
+                                        float invt, float mq, float invq, float scale) {
+    Dec* d = &a.ws.dec[b];
+    const unsigned e = a.epoch;
+    dec_put(d, DW_KIND, (unsigned)sd.kind, e);
+    dec_put(d, DW_POS, (unsigned)sd.pos, e);
+    dec_put(d, DW_U, __float_as_uint(sd.u), e);
+    dec_put(d, DW_MT, __float_as_uint(mt), e);
+    dec_put(d, DW_INVT, __float_as_uint(invt), e);
+    dec_put(d, DW_MQ, __float_as_uint(mq), e);
+    dec_put(d, DW_INVQ, __float_as_uint(invq), e);
+    dec_put(d, DW_SCALE, __float_as_uint(scale), e);
+    dec_put(d, DW_NEMIT, (unsigned)sd.nemit, e);
+    dec_put(d, DW_NACC, (unsigned)sd.nacc, e);
+    dec_put(d, DW_FLAGS, sd.flags, e);
+    for (int j = 0; j < a.gamma; ++j) dec_put(d, DW_EMIT + j, (unsigned)(j < sd.nemit ? sd.emit[j] : -1), e);
+}
+
+// ---------------------------------------------------------------- decision
 // Run by the last streaming workgroup of batch row b, once every consulted
 // row's unit statistics are published: combine them, take the accept tests
 // in order and stop at the first rejection (pseudo-code 10-1), or follow the
 // greedy rule.  Rows that need no sampled token get their outputs here; the
-// others publish a Dec record for the sampling phase.  Either way the row's
-// ready flag is set to this call's epoch.
+// others publish a decision record for the sampling phase; either way the
+// record's kind word carries this call's epoch.
 //
 // With ``first`` set it runs after the position-0 rows only: if the round
 // ends at position 0 the row is decided as above (and the stage flag says
@@ -559,7 +588,7 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl, bool first) {
     __shared__ float sP[SPECV_MAX_GAMMA], sQ[SPECV_MAX_GAMMA];
     __shared__ int sQz[SPECV_MAX_GAMMA];
     __shared__ float sUacc[SPECV_MAX_GAMMA], sUres[SPECV_MAX_GAMMA + 1];
-    __shared__ Dec sd;
+    __shared__ DecLocal sd;
     const int tid = threadIdx.x;
     const bool greedy = pl.mode == MODE_GREEDY;
     const float scale = pl.scale;
@@ -704,28 +733,15 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl, bool first) {
         sd.flags |= SPECV_FLAG_NONFINITE_ROW;
         sd.kind = KIND_NONE;
     }
-    Dec* gd = &a.ws.dec[b];
     if (sd.kind == KIND_NONE) {
         write_outputs(a, b, sd.emit, sd.nemit, sd.nacc, sd.flags, dead, sampled, 0.f);
-        publish(&gd->kind, (int)KIND_NONE);
+        publish_dec_none(a, b);
     } else {
         const int pos = sd.pos;
         const bool res = sd.kind == KIND_RESIDUAL;
-        publish(&gd->kind, sd.kind);
-        publish(&gd->pos, pos);
-        publish(&gd->u, sd.u);
-        publish(&gd->mt, sM[pos]);
-        publish(&gd->invt, 1.f / sS[pos]);
-        publish(&gd->mq, res ? sM[a.gamma + 1 + pos] : 0.f);
-        publish(&gd->invq, res ? 1.f / sS[a.gamma + 1 + pos] : 0.f);
-        publish(&gd->scale, scale);
-        publish(&gd->nemit, sd.nemit);
-        publish(&gd->nacc, sd.nacc);
-        publish(&gd->flags, sd.flags);
-        for (int j = 0; j < sd.nemit; ++j) publish(&gd->emit[j], sd.emit[j]);
+        publish_dec_draw(a, b, sd, sM[pos], 1.f / sS[pos], res ? sM[a.gamma + 1 + pos] : 0.f,
+                         res ? 1.f / sS[a.gamma + 1 + pos] : 0.f, scale);
     }
-    wait_stores();
-    publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
     if (first) publish(&a.ws.stage1[(long long)b * kCounterStride], 2u * a.epoch);
 }
 
@@ -1172,7 +1188,7 @@ __device__ void decide_trunc(const Args& a, int b, const Plan& pl, TruncScratch&
     __shared__ float sP[SPECV_MAX_GAMMA], sQ[SPECV_MAX_GAMMA];
     __shared__ int sQz[SPECV_MAX_GAMMA];
     __shared__ float sUacc[SPECV_MAX_GAMMA], sUres[SPECV_MAX_GAMMA + 1];
-    __shared__ Dec sd;
+    __shared__ DecLocal sd;
     __shared__ int sDead, sTok, sLastPos;
     __shared__ float sWsum;
     const float scale = pl.scale;
@@ -1337,26 +1353,63 @@ __device__ void decide_trunc(const Args& a, int b, const Plan& pl, TruncScratch&
             flags |= SPECV_FLAG_NONFINITE_ROW;
         }
         write_outputs(a, b, sd.emit, sd.nemit, sd.nacc, flags, dead, sampled, wres);
-        publish(&a.ws.dec[b].kind, (int)KIND_NONE);
-        wait_stores();
-        publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
+        publish_dec_none(a, b);
     }
 }
 
 // ---------------------------------------------------------------- streaming
-// Issue the 16-byte loads of one full chunk (this thread's four / eight groups).
+// The 16-byte loads of this thread's groups of chunk entries [v0, v0 + len),
+// in load_chunk's layout, split in two halves so that several chunks can be
+// in flight at once: ``issue_groups`` only issues the loads (groups past the
+// chunk's last whole group load group 0 instead), ``finish_groups`` unpacks
+// and masks them.  Needs len >= one group.
 template <bool BF16>
-__device__ inline void issue_chunk(const void* row, int v0, uint4 (&q)[kPerThread / (BF16 ? 8 : 4)]) {
-    constexpr int NG = kPerThread / (BF16 ? 8 : 4);
+__device__ inline void issue_groups(const void* row, int v0, int len,
+                                    uint4 (&q)[kPerThread / (BF16 ? 8 : 4)]) {
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int NG = kPerThread / G;
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
                                                     (size_t)v0 * (BF16 ? 2 : 4));
+    const int full = len / G;
 #pragma unroll
-    for (int j = 0; j < NG; ++j) q[j] = p[j * kBlock + threadIdx.x];
+    for (int j = 0; j < NG; ++j) {
+        const int g = j * kBlock + (int)threadIdx.x;
+        q[j] = p[g < full ? g : 0];
+    }
+}
+
+template <bool BF16>
+__device__ inline void finish_groups(const void* row, int v0, int len,
+                                     const uint4 (&q)[kPerThread / (BF16 ? 8 : 4)],
+                                     float (&x)[kPerThread]) {
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int NG = kPerThread / G;
+    const int tid = threadIdx.x;
+    const int full = len / G;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        unpack16<BF16>(q[j], &x[j * G]);
+        if (j * kBlock + tid >= full) {
+#pragma unroll
+            for (int e = 0; e < G; ++e) x[j * G + e] = -kInf;
+        }
+    }
+    const int rem = len - full * G;                 // entries of a last partial group
+    if (rem && tid == full % kBlock) {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            if (j == full / kBlock) {
+#pragma unroll
+                for (int e = 0; e < G; ++e)
+                    if (e < rem) x[j * G + e] = load_elem<BF16>(row, (long long)v0 + full * G + e);
+            }
+        }
+    }
 }
 
 // One streaming unit t = (b, r, unit): up to kUnitChunks chunks of one logits
-// row, the next chunk's loads issued before the current one is reduced, with
-// per-thread running statistics:
+// row, the loads of all of them (bfloat16) or of the next two (float32) in
+// flight before the first is reduced, with per-thread running statistics:
 //   sampling rows: running max m and sum s of exp2((z - m) * scale), the sum
 //                  rescaled when the max grows (one extra exp2 per chunk);
 //   greedy rows:   running max and its lowest index.
@@ -1396,9 +1449,7 @@ __device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
         if (r == 0 && unit == 0 && tid == 0) {
             write_outputs(a, b, nullptr, 0, 0, pl.flags, true, -1, 0.f);
             write_diag_nan(a, b, 0);
-            publish(&a.ws.dec[b].kind, (int)KIND_NONE);
-            wait_stores();
-            publish(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
+            publish_dec_none(a, b);
         }
         return;
     }
@@ -1426,7 +1477,6 @@ __device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
     const void* rp = is_target ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos)
                                : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos);
     const int c0 = unit * kUnitChunks;
-    const int nfull = a.V / kChunk;                    // chunks without a tail
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
     const long long rowid = (long long)b * a.R + r;
@@ -1436,22 +1486,25 @@ __device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
     int bi = 0x7fffffff;
     unsigned bad = 0;
 
-    uint4 q[NG];
-    if (VEC && c0 < nfull) issue_chunk<BF16>(rp, c0 * kChunk, q);
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int DEPTH = BF16 && !TRUNC ? kUnitChunks : 2;   // chunks in flight (registers)
+    auto chunk_len = [&](int c) { return c < a.C ? min(kChunk, a.V - c * kChunk) : 0; };
+    uint4 q[DEPTH][NG];
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+        if (VEC && chunk_len(c0 + u) >= G) issue_groups<BF16>(rp, (c0 + u) * kChunk, chunk_len(c0 + u), q[u]);
 #pragma unroll
     for (int u = 0; u < kUnitChunks; ++u) {
         const int c = c0 + u;
-        if (c >= a.C) break;
+        if (c >= a.C) continue;                       // (keeps the unrolled trip count)
+        const int len = chunk_len(c);
         float x[kPerThread];
-        if (VEC && c < nfull) {
-            uint4 cur[NG];
-#pragma unroll
-            for (int j = 0; j < NG; ++j) cur[j] = q[j];
-            if (u + 1 < kUnitChunks && c + 1 < nfull) issue_chunk<BF16>(rp, (c + 1) * kChunk, q);
-#pragma unroll
-            for (int j = 0; j < NG; ++j) unpack16<BF16>(cur[j], &x[j * (BF16 ? 8 : 4)]);
+        if (VEC && len >= G) {
+            finish_groups<BF16>(rp, c * kChunk, len, q[u % DEPTH], x);
+            if (u + DEPTH < kUnitChunks && chunk_len(c + DEPTH) >= G)
+                issue_groups<BF16>(rp, (c + DEPTH) * kChunk, chunk_len(c + DEPTH), q[u % DEPTH]);
         } else {
-            load_chunk<BF16, VEC>(rp, c * kChunk, min(kChunk, a.V - c * kChunk), x);
+            load_chunk<BF16, VEC>(rp, c * kChunk, len, x);
         }
         if (greedy) {
             const int v0 = c * kChunk;
@@ -1571,52 +1624,58 @@ struct Weights {
     }
 };
 
-// Sampling item (b, c), after b's decision is published: sum chunk c's
+// Sampling item (b, c), once b's decision is published: sum chunk c's
 // sampling weight (correction max(p - q, 0) from the two rows, or bonus p)
 // and its p mass.  The last item of the row to arrive picks the chunk
 // holding u * W, rescans it with a block prefix sum (tokens in ascending
 // order, first running sum > u * W) and writes the outputs.
+// The workgroup that decides the row was dispatched before every sampling
+// workgroup and never waits for one, so the (bounded) wait for the decision
+// ends; the bound only guards against a dispatch order other than the
+// hardware's in-order one, and its expiry flags the row INTERNAL.
 template <bool BF16, bool VEC>
 __device__ void sample_item(const Args& a, int b, int c) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
-    Dec* gd = &a.ws.dec[b];
-    __shared__ int sKind, sPos;
-    __shared__ float sU, sMt, sInvt, sMq, sInvq, sScale;
+    // the row's decision record: one wave polls every word it needs at once
+    // until all carry this call's epoch (or the kind word alone says there
+    // is nothing to sample)
+    __shared__ unsigned sDw[kDecWords];
     __shared__ int sOk;
-    if (tid == 0) {
-        const bool ok = wait_flag(&a.ws.ready[(long long)b * kCounterStride], a.epoch);
-        sOk = ok;
-        if (!ok && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
-    }
-    __syncthreads();
-    // the record's fields, one thread each (one round trip)
-    if (sOk && tid < 8) {
-        switch (tid) {
-            case 0: sKind = published(&gd->kind); break;
-            case 1: sPos = published(&gd->pos); break;
-            case 2: sU = published(&gd->u); break;
-            case 3: sMt = published(&gd->mt); break;
-            case 4: sInvt = published(&gd->invt); break;
-            case 5: sMq = published(&gd->mq); break;
-            case 6: sInvq = published(&gd->invq); break;
-            case 7: sScale = published(&gd->scale); break;
+    if (wave == 0) {
+        const int nw = DW_EMIT + a.gamma;
+        unsigned long long* src = a.ws.dec[b].w;
+        const unsigned long long tag = (unsigned long long)a.epoch << 32;
+        unsigned long long v = tag;
+        bool done = false;
+        for (int spin = 0; spin < (1 << 20); ++spin) {
+            v = lane < nw ? __hip_atomic_load(src + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : tag;
+            const unsigned long long mine = __ballot((unsigned)(v >> 32) == a.epoch);
+            const unsigned kind0 = __builtin_amdgcn_readfirstlane((unsigned)v);
+            if ((mine & 1ull) && (kind0 == (unsigned)KIND_NONE || mine == ~0ull)) {
+                done = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
         }
-    } else if (!sOk && tid == 0) {
-        sKind = (int)KIND_NONE;
+        if (lane < nw) sDw[lane] = (unsigned)v;
+        if (lane == 0) sOk = done;
+        if (!done && lane == 0 && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
     }
     __syncthreads();
-    const int kind = sKind;
+    if (!sOk) return;
+    const int kind = (int)sDw[DW_KIND];
     if (kind == KIND_NONE) return;
-    const int pos = sPos;
+    const int pos = (int)sDw[DW_POS];
     Weights wt;
     wt.residual = kind == KIND_RESIDUAL;
-    wt.mt = sMt;
-    wt.st = sScale;
-    wt.invt = sInvt;
-    wt.mq = sMq;
-    wt.invq = sInvq;
-    const float u = sU;
+    wt.mt = __uint_as_float(sDw[DW_MT]);
+    wt.st = __uint_as_float(sDw[DW_SCALE]);
+    wt.invt = __uint_as_float(sDw[DW_INVT]);
+    wt.mq = __uint_as_float(sDw[DW_MQ]);
+    wt.invq = __uint_as_float(sDw[DW_INVQ]);
+    const float u = __uint_as_float(sDw[DW_U]);
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos);
     const void* qrow = wt.residual ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
 
@@ -1670,7 +1729,7 @@ __device__ void sample_item(const Args& a, int b, int c) {
     __syncthreads();
     if (tid == 0) {
         publish(&a.ws.counter2[(long long)b * kCounterStride], 0u);   // ready for the next call
-        unsigned flags = published(&gd->flags);
+        unsigned flags = sDw[DW_FLAGS];
         float W = 0.f;
         for (int cc = 0; cc < a.C; ++cc) W += sW[cc];
         float wres = 0.f;
@@ -1783,13 +1842,11 @@ __device__ void sample_item(const Args& a, int b, int c) {
         sampled = sTok;
     }
     if (tid == 0) {
-        int emit[SPECV_MAX_GAMMA + 1];
-        const int nemit = published(&gd->nemit);
-        for (int j = 0; j < nemit; ++j) emit[j] = published(&gd->emit[j]);
         unsigned flags = sFlags;
         const bool dead = sampled < 0;        // no weight anywhere: cannot happen for finite rows
         if (dead) flags |= SPECV_FLAG_NONFINITE_ROW;
-        write_outputs(a, b, emit, nemit, published(&gd->nacc), flags, dead, sampled, sWres);
+        write_outputs(a, b, reinterpret_cast<const int*>(&sDw[DW_EMIT]), (int)sDw[DW_NEMIT],
+                      (int)sDw[DW_NACC], flags, dead, sampled, sWres);
     }
     __syncthreads();      // shared state is reused by the next item
 }
