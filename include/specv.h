@@ -93,7 +93,7 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype;
                                                   decision (a launch without co-residency): the
                                                   row's outputs are not valid                      */
 
-#define SPECV_MAX_GAMMA 32
+#define SPECV_MAX_GAMMA 31      /* one 64-bit status word holds a row's accept and stop bits */
 #define SPECV_MAX_TOP_K 1024
 #define SPECV_MAX_VOCAB 524288
 

@@ -16,7 +16,6 @@
 
 struct specv_ctx {
     specv_config cfg;
-    int max_rows;
     int max_chunks;
     int cand_cap;      // candidates per (row, chunk); 0 without truncation support
     int kept_cap;      // kept-set entries per row
@@ -69,16 +68,12 @@ hipError_t alloc(T** p, size_t count) {
 }
 
 void free_ws(specv::Workspace& ws) {
-    if (ws.part) (void)hipFree(ws.part);
+    if (ws.stats) (void)hipFree(ws.stats);
+    if (ws.pair) (void)hipFree(ws.pair);
     if (ws.wsum) (void)hipFree(ws.wsum);
-    if (ws.counter) (void)hipFree(ws.counter);
-    if (ws.counter2) (void)hipFree(ws.counter2);
-    if (ws.dec) (void)hipFree(ws.dec);
-    if (ws.counter1) (void)hipFree(ws.counter1);
-    if (ws.stage1) (void)hipFree(ws.stage1);
+    if (ws.ctr) (void)hipFree(ws.ctr);
     if (ws.cand) (void)hipFree(ws.cand);
     if (ws.cand_meta) (void)hipFree(ws.cand_meta);
-    if (ws.counter_row) (void)hipFree(ws.counter_row);
     if (ws.trow) (void)hipFree(ws.trow);
     if (ws.kept) (void)hipFree(ws.kept);
     ws = specv::Workspace{};
@@ -118,8 +113,7 @@ specv::Args base_args(specv_handle h, int B, int gamma, int V) {
     a.gamma = gamma;
     a.V = V;
     a.C = (V + specv::kChunk - 1) / specv::kChunk;
-    a.U = (a.C + specv::kUnitChunks - 1) / specv::kUnitChunks;
-    a.R = 2 * gamma + 1;
+    a.P = gamma + 1;
     a.ws = h->ws;
     a.cand_cap = h->cand_cap;
     a.kept_cap = h->kept_cap;
@@ -127,14 +121,36 @@ specv::Args base_args(specv_handle h, int B, int gamma, int V) {
     return a;
 }
 
-// One launch of the verify kernel; each call gets a new epoch tag.
+// Zero the epoch-tagged records and the arrival counters (handle creation,
+// and the rare epoch wrap).  Fresh allocations may
+// hold another handle's words with the same epoch numbers, so every tagged
+// array is cleared.
+hipError_t clear_ws(specv_ctx* h, hipStream_t stream) {
+    const specv::Workspace& ws = h->ws;
+    const size_t groups = (size_t)h->cfg.max_batch * (h->cfg.max_gamma + 1);
+    hipError_t e = hipMemsetAsync(ws.stats, 0, groups * 2 * h->max_chunks * 2 * sizeof(unsigned long long),
+                                  stream);
+    if (e == hipSuccess) e = hipMemsetAsync(ws.pair, 0, groups * sizeof(specv::PairRec), stream);
+    if (e == hipSuccess)
+        e = hipMemsetAsync(ws.wsum, 0,
+                           (size_t)h->cfg.max_batch * h->max_chunks * 2 * sizeof(unsigned long long), stream);
+    if (e == hipSuccess) e = hipMemsetAsync(ws.ctr, 0, groups * specv::kSlot * sizeof(unsigned), stream);
+    return e;
+}
+
+// One launch of the verify kernel with the next epoch tag.
 specv_status launch(specv_handle h, specv::Args& a, bool bf16, bool vec, void* stream) {
     if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
-    h->epoch = h->epoch + 1 >= 0x80000000u ? 1 : h->epoch + 1;
-    a.epoch = h->epoch;
-    if (specv::launch_verify(a, bf16, vec, static_cast<hipStream_t>(stream), next_events(h)) !=
-        hipSuccess)
-        return SPECV_E_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned next = h->epoch + 1;
+    if (next >= 0x7fffffffu) {
+        // epoch tags would repeat: start again from cleared records
+        if (clear_ws(h, s) != hipSuccess) return SPECV_E_HIP;
+        next = 1;
+    }
+    a.epoch = next;
+    if (specv::launch_verify(a, bf16, vec, s, next_events(h)) != hipSuccess) return SPECV_E_HIP;
+    h->epoch = next;
     return SPECV_OK;
 }
 
@@ -171,35 +187,23 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     specv_ctx* h = new (std::nothrow) specv_ctx{};
     if (!h) return SPECV_E_NOMEM;
     h->cfg = *cfg;
-    h->max_rows = 2 * cfg->max_gamma + 1;
     h->max_chunks = (cfg->max_vocab + specv::kChunk - 1) / specv::kChunk;
     h->cand_cap = cfg->max_top_k > 0 ? 2 * cfg->max_top_k + specv::kTieSlack : 0;
     h->cand_cap = std::min(h->cand_cap, std::min(specv::kChunk, cfg->max_vocab));
     h->kept_cap = std::min(specv::kKeptCap, cfg->max_vocab);
-    const size_t rows = (size_t)cfg->max_batch * h->max_rows;
+    const size_t groups = (size_t)cfg->max_batch * (cfg->max_gamma + 1);   // (b, position) pairs
+    const size_t rows = groups * 2;                                         // logits rows
     const size_t rc = rows * h->max_chunks;
     specv::Workspace& ws = h->ws;
-    bool ok = alloc(&ws.part, rc) == hipSuccess &&
+    bool ok = alloc(&ws.stats, rc * 2) == hipSuccess && alloc(&ws.pair, groups) == hipSuccess &&
               alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks * 2) == hipSuccess &&
-              alloc(&ws.counter, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
-              alloc(&ws.counter2, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
-              alloc(&ws.dec, (size_t)cfg->max_batch) == hipSuccess &&
-              alloc(&ws.counter1, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess &&
-              alloc(&ws.stage1, (size_t)cfg->max_batch * specv::kCounterStride) == hipSuccess;
+              alloc(&ws.ctr, groups * specv::kSlot) == hipSuccess;
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
              alloc(&ws.cand_meta, rc) == hipSuccess && alloc(&ws.trow, rows) == hipSuccess &&
-             alloc(&ws.kept, rows * h->kept_cap) == hipSuccess &&
-             alloc(&ws.counter_row, rows * specv::kCounterStride) == hipSuccess &&
-             hipMemset(ws.counter_row, 0, rows * specv::kCounterStride * sizeof(unsigned)) ==
-                 hipSuccess;
-    const size_t counter_bytes = (size_t)cfg->max_batch * specv::kCounterStride * sizeof(unsigned);
-    if (ok) ok = hipMemset(ws.counter, 0, counter_bytes) == hipSuccess;
-    if (ok) ok = hipMemset(ws.counter2, 0, counter_bytes) == hipSuccess;
-    if (ok) ok = hipMemset(ws.dec, 0, (size_t)cfg->max_batch * sizeof(specv::Dec)) == hipSuccess;
-    if (ok) ok = hipMemset(ws.counter1, 0, counter_bytes) == hipSuccess;
-    if (ok) ok = hipMemset(ws.stage1, 0, counter_bytes) == hipSuccess;
+             alloc(&ws.kept, rows * h->kept_cap) == hipSuccess;
+    if (ok) ok = clear_ws(h, nullptr) == hipSuccess;
     if (ok) ok = hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
         free_ws(ws);

@@ -1,29 +1,40 @@
 // libspecv kernels for gfx950 (CDNA4, wave64).
 //
-// The verify step is bandwidth-bound: every logits row that the round may
-// consult is streamed from HBM once with 16-byte loads, reduced to per-chunk
-// statistics, and the sequential part of the round (accept tests, stopping
-// at the first rejection) runs on those statistics.  Only the one row pair
-// that is actually sampled from is read a second time.
+// The verify step is bandwidth-bound, and the round it computes is
+// sequential: draft d_k only matters while every earlier draft was accepted
+// (pseudo-code 10-1 stops at the first rejection).  The kernel therefore
+// reads the logits lazily, in ONE launch of B x C workgroups: workgroup
+// (b, c) owns chunk c (8192 entries) of every logits row of batch row b and
+// walks the positions k = 0, 1, ... in order:
 //
-//   k_rowstats  grid (chunks, B * (2*gamma+1)): one workgroup per 8192-entry
-//               chunk of one logits row.  Sampling rows: chunk max and
-//               sum of exp2((z - max) * log2(e) / T).  Greedy rows: chunk max
-//               and its lowest index.  Rows a round cannot consult (past the
-//               cap / first EOS, draft rows of greedy rows) are skipped.
-//   k_decide    grid (chunks, B): every workgroup of a batch row combines
-//               the statistics, draws the accept uniforms and finds the first
-//               rejection (cheap, done redundantly); each then sums the
-//               correction weights max(p - q, 0) of its chunk (or takes the
-//               bonus row's chunk mass from the statistics).  The last
-//               workgroup of the row to finish (atomic counter) picks the
-//               chunk that holds u * W, rescans it with a block prefix sum and
-//               writes the outputs.
+//   stream : chunk c of target row k and, below gamma, of draft row k, with
+//            16-byte loads, reduced to chunk statistics (max / sum of exp2
+//            for sampling rows, max / lowest argmax for greedy rows, top-k
+//            candidates for truncated rows), published as epoch-tagged words;
+//   decide : every unit reads the C chunk statistics of the pair and runs the
+//            accept test of position k itself (the same arithmetic in every
+//            unit, so all units of the row agree); truncated pairs are
+//            decided once, by the last unit to arrive, which publishes the
+//            outcome;
+//   go on  : on acceptance the walk moves to position k + 1 (whose chunk was
+//            already pulled into the L2 while k was being decided); rows past
+//            the first rejection are never read;
+//   sample : at the first rejection (or the bonus position) the units still
+//            hold their chunk in registers: each sums its chunk's correction
+//            weight max(p - q, 0) (or bonus weight p), publishes it, reads
+//            every chunk's sum, and the unit whose chunk holds u * W finds the
+//            token with a block prefix sum.  Nothing is read twice.
+//
+// The C units of a row wait only for each other (bounded polls).  Workgroups
+// are dispatched in increasing ID order within each XCD and a row's units
+// have consecutive IDs, so every unit waited for is resident or done, and
+// the waits end; the bound only guards against a dispatch order other than
+// the hardware's, and its expiry flags the row.
 //
 // Sources: "11.1 核心原理: Draft + Verify 与 Rejection Sampling" (11.1.1
-// alignment, 11.1.2 acceptance / residual / greedy, pseudo-code 10-1) and
-// "Fast Inference from Transformers via Speculative Decoding" (speculative
-// sampling, bonus token).
+// alignment, 11.1.2 acceptance / residual / greedy / processed proposals,
+// pseudo-code 10-1) and "Fast Inference from Transformers via Speculative
+// Decoding" (speculative sampling, bonus token).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -36,10 +47,14 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInf = __builtin_huge_valf();
+constexpr int kSpinLimit = 1 << 18;
 
 enum Mode { MODE_SAMPLE = 0, MODE_GREEDY = 1, MODE_TRUNC = 2, MODE_SKIP = 3 };
 enum Kind { KIND_NONE = 0, KIND_RESIDUAL = 1, KIND_BONUS = 2 };
 enum Purpose { PURPOSE_ACCEPT = 1, PURPOSE_RESIDUAL = 2, PURPOSE_BONUS = 3 };
+// outcome of one pair (low byte of PW_STATE)
+enum Outcome { OUT_ACC = 1, OUT_REJ = 2, OUT_BAD = 3, OUT_BONUS = 4 };
+
 
 // ---------------------------------------------------------------- Philox
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
@@ -75,36 +90,38 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // and read with agent-scope atomic accesses, which are coherent across the
 // XCDs' L2 caches by themselves, so no L2 write-back / invalidate is needed
 // (a __threadfence() would flush the whole L2 of the XCD).  ``wait_stores``
-// makes this wave's outstanding stores complete before the arrival counter is
-// bumped, and keeps the compiler from moving memory accesses across it.
-__device__ inline void publish(float* p, float v) {
+// makes this wave's outstanding stores complete before a later atomic, and
+// keeps the compiler from moving memory accesses across it.
+template <typename T>
+__device__ inline void publish(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline void publish(int* p, int v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void publish(unsigned* p, unsigned v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float published(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int published(const int* p) {
-    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline unsigned published(const unsigned* p) {
-    return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+template <typename T>
+__device__ inline T published(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Bump the arrival counter after this thread's published stores completed;
-// returns the previous count.
-__device__ inline unsigned arrive(unsigned* counter) {
-    wait_stores();
-    const unsigned old =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_stores();
-    return old;
+// Bump an arrival counter; returns the previous count.  With ``ordered`` the
+// thread's earlier stores complete first, for readers that do not check
+// epoch tags; without it the atomic goes out behind them at once.
+__device__ inline unsigned arrive(unsigned* counter, bool ordered) {
+    if (ordered) wait_stores();
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Epoch-tagged 64-bit words: (epoch << 32) | value.
+__device__ inline void put_tagged(unsigned long long* p, unsigned v, unsigned epoch) {
+    publish(p, ((unsigned long long)epoch << 32) | v);
+}
+__device__ inline bool tag_is(unsigned long long w, unsigned epoch) {
+    return (unsigned)(w >> 32) == epoch;
+}
+
+__device__ inline unsigned long long readlane64(unsigned long long v, int lane) {
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, lane);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(v >> 32), lane);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
@@ -150,134 +167,111 @@ __device__ inline void unpack16(const uint4& q, float* x) {
     }
 }
 
-// Load this thread's 32 entries of a chunk into x[]; entries past ``len``
-// read as -inf.  Layout: 16-byte groups, group g = j * kBlock + tid, so each
-// load instruction of the workgroup covers one contiguous 4 KB span.  Every
-// load is issued before any value is used: out-of-range groups load a clamped
-// in-range address and are masked afterwards (no branch around a load).
-template <bool BF16, bool VEC>
-__device__ inline void load_chunk(const void* row, int v0, int len, float (&x)[kPerThread]) {
-    const int tid = threadIdx.x;
-    constexpr int G = BF16 ? 8 : 4;                 // entries per 16-byte group
-    constexpr int NG = kPerThread / G;              // groups per thread
-    if constexpr (VEC) {
-        const uint4* p = reinterpret_cast<const uint4*>(
-            static_cast<const char*>(row) + (size_t)v0 * (BF16 ? 2 : 4));
-        if (len == kChunk) {
-            uint4 q[NG];
-#pragma unroll
-            for (int j = 0; j < NG; ++j) q[j] = p[j * kBlock + tid];
-#pragma unroll
-            for (int j = 0; j < NG; ++j) unpack16<BF16>(q[j], &x[j * G]);
-            return;
-        }
-        if (len >= G) {
-            const int full = len / G;               // groups entirely inside the chunk
-            uint4 q[NG];
-#pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                const int g = j * kBlock + tid;
-                q[j] = p[g < full ? g : 0];
-            }
-#pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                unpack16<BF16>(q[j], &x[j * G]);
-                if (j * kBlock + tid >= full) {
-#pragma unroll
-                    for (int e = 0; e < G; ++e) x[j * G + e] = -kInf;
-                }
-            }
-            // entries of the one partial group at the end, if any
-            const int rem = len - full * G;
-            if (rem && tid == full % kBlock) {
-#pragma unroll
-                for (int j = 0; j < NG; ++j) {
-                    if (j == full / kBlock) {
-#pragma unroll
-                        for (int e = 0; e < G; ++e)
-                            if (e < rem) x[j * G + e] = load_elem<BF16>(row, (long long)v0 + full * G + e);
-                    }
-                }
-            }
-            return;
-        }
-    }
-    float t[kPerThread];
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-#pragma unroll
-        for (int e = 0; e < G; ++e) {
-            const int v = (j * kBlock + tid) * G + e;
-            t[j * G + e] = load_elem<BF16>(row, (long long)v0 + (v < len ? v : len - 1));
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-#pragma unroll
-        for (int e = 0; e < G; ++e) {
-            const int v = (j * kBlock + tid) * G + e;
-            x[j * G + e] = v < len ? t[j * G + e] : -kInf;
-        }
-    }
-}
-
-// Load entries [tid * 32, tid * 32 + 32) of a chunk (contiguous per thread,
-// for the in-order prefix sum); entries past ``len`` read as -inf.
-template <bool BF16, bool VEC>
-__device__ inline void load_contig(const void* row, int v0, int len, float (&x)[kPerThread]) {
-    const int tid = threadIdx.x;
-    constexpr int G = BF16 ? 8 : 4;
-    constexpr int NG = kPerThread / G;
-    const int base = tid * kPerThread;
-    if constexpr (VEC) {
-        if (len >= G) {
-            const uint4* p = reinterpret_cast<const uint4*>(
-                static_cast<const char*>(row) + (size_t)v0 * (BF16 ? 2 : 4));
-            const int full = len / G;
-            uint4 q[NG];
-#pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                const int g = base / G + j;
-                q[j] = p[g < full ? g : 0];
-            }
-#pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                unpack16<BF16>(q[j], &x[j * G]);
-                if (base / G + j >= full) {
-#pragma unroll
-                    for (int e = 0; e < G; ++e) x[j * G + e] = -kInf;
-                }
-            }
-            const int rem = len - full * G;
-            if (rem && full * G >= base && full * G < base + kPerThread) {
-#pragma unroll
-                for (int j = 0; j < NG; ++j) {
-                    if (base / G + j == full) {
-#pragma unroll
-                        for (int e = 0; e < G; ++e)
-                            if (e < rem) x[j * G + e] = load_elem<BF16>(row, (long long)v0 + full * G + e);
-                    }
-                }
-            }
-            return;
-        }
-    }
-    float t[kPerThread];
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const int v = base + k;
-        t[k] = load_elem<BF16>(row, (long long)v0 + (v < len ? v : len - 1));
-    }
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) x[k] = base + k < len ? t[k] : -kInf;
-}
-
-// Index (within the chunk) of entry k of this thread's x[] in load_chunk's layout.
+// Index (within the chunk) of entry k of this thread's x[]: 16-byte groups,
+// group g = j * kBlock + tid holds entries [g * G, g * G + G), so each load
+// instruction of the workgroup covers one contiguous 4 KB span.
 template <bool BF16>
 __device__ inline int chunk_index(int k) {
     constexpr int G = BF16 ? 8 : 4;
     return ((k / G) * kBlock + (int)threadIdx.x) * G + (k % G);
 }
+
+// One chunk of one logits row held in registers, in chunk_index's layout;
+// entries past the row's end read as -inf.
+//   VEC:  packed 16-byte groups (bfloat16: 8 entries, float32: 4); every
+//         load is issued before any is used (``issue``), groups past the last
+//         whole group load group 0 and are overwritten by ``finish``, which
+//         also fills a partial last group with scalar loads.
+//   !VEC: scalar loads (rows not 16-byte aligned), held as float.
+template <bool BF16, bool VEC>
+struct ChunkRegs;
+
+template <bool BF16>
+struct ChunkRegs<BF16, true> {
+    static constexpr int G = BF16 ? 8 : 4;
+    static constexpr int NG = kPerThread / G;
+    uint4 q[NG];
+
+    __device__ inline void issue(const void* row, int v0, int len) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
+                                                        (size_t)v0 * (BF16 ? 2 : 4));
+        const int full = len / G;
+        if (full == 0) return;                   // nothing 16-byte loadable (tiny tail)
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            const int g = j * kBlock + (int)threadIdx.x;
+            q[j] = p[g < full ? g : 0];
+        }
+    }
+    __device__ inline void finish(const void* row, int v0, int len) {
+        const int full = len / G;
+        const int rem = len - full * G;
+        const unsigned ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            const int g = j * kBlock + (int)threadIdx.x;
+            if (g >= full) {
+                q[j] = make_uint4(ninf, ninf, ninf, ninf);
+                if (g == full && rem) {
+                    unsigned w[4] = {ninf, ninf, ninf, ninf};
+#pragma unroll
+                    for (int e = 0; e < G; ++e) {
+                        if (e < rem) {
+                            if constexpr (BF16) {
+                                const unsigned h = static_cast<const unsigned short*>(row)[v0 + full * G + e];
+                                w[e / 2] = (e & 1) ? ((w[e / 2] & 0xFFFFu) | (h << 16))
+                                                   : ((w[e / 2] & 0xFFFF0000u) | h);
+                            } else {
+                                w[e] = __float_as_uint(static_cast<const float*>(row)[v0 + full * G + e]);
+                            }
+                        }
+                    }
+                    q[j] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+        }
+    }
+    __device__ inline void get(float (&x)[kPerThread]) const {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) unpack16<BF16>(q[j], &x[j * G]);
+    }
+    // entry i (a compile-time constant in unrolled loops) unpacked on the fly
+    __device__ inline float elem(int i) const {
+        const uint4& g = q[i / G];
+        const int e = i % G;
+        if constexpr (BF16) {
+            const unsigned w = (e / 2) == 0 ? g.x : (e / 2) == 1 ? g.y : (e / 2) == 2 ? g.z : g.w;
+            return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+        } else {
+            return __uint_as_float(e == 0 ? g.x : e == 1 ? g.y : e == 2 ? g.z : g.w);
+        }
+    }
+};
+
+template <bool BF16>
+struct ChunkRegs<BF16, false> {
+    static constexpr int G = BF16 ? 8 : 4;
+    static constexpr int NG = kPerThread / G;
+    float x[kPerThread];
+
+    __device__ inline void issue(const void* row, int v0, int len) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int v = chunk_index<BF16>(k);
+            x[k] = load_elem<BF16>(row, (long long)v0 + (v < len ? v : len - 1));
+        }
+    }
+    __device__ inline void finish(const void*, int, int len) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k)
+            if (chunk_index<BF16>(k) >= len) x[k] = -kInf;
+    }
+    __device__ inline void get(float (&y)[kPerThread]) const {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) y[k] = x[k];
+    }
+    __device__ inline float elem(int i) const { return x[i]; }
+};
 
 // Merge (m, s) statistics: s is relative to m in units of exp2(. * scale).
 __device__ inline void merge_ms(float& m, float& s, float m2, float s2, float scale) {
@@ -377,12 +371,6 @@ __device__ inline unsigned wave_or(unsigned x) {
     return (unsigned)xi;
 }
 
-__device__ inline int wave_max_i(int x) {
-    float dummy = 0.f;
-    wave_reduce2(dummy, x, 0.f, (int)0x80000000, [](float&, int& a, float, int b) { a = max(a, b); });
-    return x;
-}
-
 // Inclusive prefix sums across the wave (lane order).
 __device__ inline float wave_scan_incl(float x) {
     x += dpp_f<kDppShr + 1>(x, 0.f);
@@ -409,8 +397,8 @@ __device__ inline int wave_scan_incl(int x) {
 struct Plan {
     int mode;
     int cap;        // tokens the round may emit: max_new_tokens and the first EOS
-    int nt;         // target rows the round may consult
-    int nd;         // draft rows the round may consult
+    int nt;         // positions whose target row the round may consult: min(cap, gamma + 1)
+    int ntest;      // accept tests the round may run: min(cap, gamma)
     float scale;    // log2(e) / T
     int top_k;
     float top_p;
@@ -418,9 +406,13 @@ struct Plan {
                     // max_top_k for top-p alone)
     int kmode;      // truncated rows: 1 when top-k is on (normaliser over the top-k set)
     unsigned flags;
+    int tok;        // lane i < gamma: draft token d_i
 };
 
+// Computed by every wave on its own: lane i loads d_i, so the parameters and
+// all the tokens arrive in one memory round trip.
 __device__ inline Plan make_plan(const Args& a, int b) {
+    const int lane = threadIdx.x % kWave;
     Plan p;
     float T = 0.f;
     int k = 0;
@@ -435,15 +427,15 @@ __device__ inline Plan make_plan(const Args& a, int b) {
     } else if (a.caps) {
         cap = a.caps[b];
     }
+    const int d = lane < a.gamma ? a.tokens[(long long)b * a.gamma + lane] : 0;
+    p.tok = d;
     // emission ends after max_new_tokens tokens and after an emitted EOS; an
     // EOS among the drafts therefore caps the round at its position + 1
     int ce = cap >= 1 ? cap : 0x7fffffff;
-    p.flags = 0;
-    for (int i = 0; i < a.gamma; ++i) {
-        const int d = a.tokens[(long long)b * a.gamma + i];
-        if (d < 0 || d >= a.V) p.flags |= SPECV_FLAG_TOKEN_OOR;
-        else if (d == a.eos && i + 1 < ce) ce = i + 1;
-    }
+    const unsigned long long oor = __ballot(lane < a.gamma && (d < 0 || d >= a.V));
+    const unsigned long long eos = __ballot(lane < a.gamma && d == a.eos);
+    p.flags = oor ? SPECV_FLAG_TOKEN_OOR : 0u;
+    if (eos) ce = min(ce, __builtin_ctzll(eos) + 1);
     p.cap = ce;
     p.top_k = k;
     p.top_p = tp;
@@ -468,281 +460,93 @@ __device__ inline Plan make_plan(const Args& a, int b) {
     p.kmode = topk_on ? 1 : 0;
     p.keff = topk_on ? k : a.max_top_k;
     p.nt = min(ce, a.gamma + 1);
-    p.nd = p.mode == MODE_GREEDY ? 0 : min(ce, a.gamma);
+    p.ntest = min(ce, a.gamma);
     return p;
 }
 
-__device__ inline long long part_index(const Args& a, int b, int r, int unit) {
-    return ((long long)b * a.R + r) * a.U + unit;
+
+// ---------------------------------------------------------------- workspace
+__device__ inline long long pair_id(const Args& a, int b, int k) { return (long long)b * a.P + k; }
+
+// Draft token d_k of row b, by a load from the same (uniform) address in
+// every lane.  Never a cross-lane read of the plan's lane-distributed
+// tokens: in code that only some lanes execute, the compiler may reload a
+// spilled register for the active lanes alone, and a read of another lane
+// then returns garbage.
+__device__ inline int draft_token(const Args& a, int b, int k) {
+    return a.tokens[(long long)b * a.gamma + k];
+}
+__device__ inline long long side_row(const Args& a, int b, int k, int side) {
+    return pair_id(a, b, k) * 2 + side;
+}
+__device__ inline long long part_index(const Args& a, int b, int k, int side, int c) {
+    return side_row(a, b, k, side) * a.C + c;
 }
 
-// A Part moves as two 64-bit agent-scope accesses.
-__device__ inline void publish_part(Part* p, const Part& v) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
-    const unsigned long long lo =
-        (unsigned long long)__float_as_uint(v.m) | ((unsigned long long)__float_as_uint(v.s) << 32);
-    const unsigned long long hi =
-        (unsigned long long)(unsigned)v.arg | ((unsigned long long)v.bad << 32);
-    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// A chunk's statistics move as two epoch-tagged words: (max, sum) for
+// sampling and truncated rows, the sum NaN when the chunk held NaN / +inf;
+// (max, argmax) for greedy rows, the max NaN when the chunk held NaN / +inf.
+// Readers poll until both tags are this call's, so the writer never waits
+// for its stores to complete.
+__device__ inline unsigned long long* stats_words(const Args& a, int b, int k, int side, int c) {
+    return a.ws.stats + part_index(a, b, k, side, c) * 2;
+}
+__device__ inline void publish_stats(unsigned long long* w, float m, unsigned second, unsigned epoch) {
+    put_tagged(w, __float_as_uint(m), epoch);
+    put_tagged(w + 1, second, epoch);
+}
+// Returns false when the words did not carry this call's tag within the bound.
+__device__ inline bool published_stats(const unsigned long long* w, unsigned epoch, float& m,
+                                       unsigned& second) {
+    unsigned long long w0 = 0, w1 = 0;
+    bool ok = false;
+    for (int spin = 0; spin < kSpinLimit; ++spin) {
+        w0 = published(w);
+        w1 = published(w + 1);
+        if (tag_is(w0, epoch) && tag_is(w1, epoch)) {
+            ok = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    m = __uint_as_float((unsigned)w0);
+    second = (unsigned)w1;
+    return ok;
 }
 
-__device__ inline Part published_part(const Part* p) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<Part*>(p));
-    const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    Part v;
-    v.m = __uint_as_float((unsigned)lo);
-    v.s = __uint_as_float((unsigned)(lo >> 32));
-    v.arg = (int)(unsigned)hi;
-    v.bad = (unsigned)(hi >> 32);
-    return v;
-}
-
-__device__ inline void write_diag_nan(const Args& a, int b, int from) {
-    for (int i = from; i < a.gamma; ++i) {
-        if (a.p_at) a.p_at[(long long)b * a.gamma + i] = __builtin_nanf("");
-        if (a.q_at) a.q_at[(long long)b * a.gamma + i] = __builtin_nanf("");
+// Diagnostics of one row by one wave: lane i holds p_i(d_i), q_i(d_i).
+__device__ inline void write_diag_wave(const Args& a, int b, int tested, float p, float q) {
+    const int i = threadIdx.x % kWave;
+    if (i < a.gamma) {
+        const bool t = i < tested;
+        if (a.p_at) a.p_at[(long long)b * a.gamma + i] = t ? p : __builtin_nanf("");
+        if (a.q_at) a.q_at[(long long)b * a.gamma + i] = t ? q : __builtin_nanf("");
     }
 }
 
-// Final outputs of one row: emit[0..nemit) then ``sampled`` (if >= 0), -1 padding.
-__device__ inline void write_outputs(const Args& a, int b, const int* emit, int nemit, int nacc,
-                                     unsigned flags, bool dead, int sampled, float wres) {
+// Final outputs of one row by one wave (lane i holds d_i in ``tok``): the
+// first nemit drafts, then ``sampled`` (if >= 0), -1 padding.
+__device__ inline void write_outputs_wave(const Args& a, int b, int nemit, int nacc, unsigned flags,
+                                          bool dead, int sampled, float wres, int tok) {
+    const int lane = threadIdx.x % kWave;
     const int g1 = a.gamma + 1;
     if (dead) {
         nemit = 0;
         nacc = 0;
         sampled = -1;
     }
-    for (int j = 0; j < g1; ++j) {
+    if (lane < g1) {
         int t = -1;
-        if (j < nemit) t = emit[j];
-        else if (j == nemit && sampled >= 0) t = sampled;
-        a.out_tok[(long long)b * g1 + j] = t;
+        if (lane < nemit) t = tok;
+        else if (lane == nemit && sampled >= 0) t = sampled;
+        a.out_tok[(long long)b * g1 + lane] = t;
     }
-    a.out_emit[b] = nemit + (sampled >= 0 ? 1 : 0);
-    a.out_acc[b] = nacc;
-    if (a.out_flags) a.out_flags[b] = (int)flags;
-    if (a.wres) a.wres[b] = wres;
-}
-
-// A batch row's decision while it is being taken (LDS of the deciding
-// workgroup), and its publication as epoch-tagged words.
-struct DecLocal {
-    int kind;
-    int pos;
-    float u;
-    int nemit;
-    int nacc;
-    unsigned flags;
-    int emit[SPECV_MAX_GAMMA];
-};
-
-__device__ inline void dec_put(Dec* d, int word, unsigned v, unsigned epoch) {
-    __hip_atomic_store(&d->w[word], ((unsigned long long)epoch << 32) | v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Nothing to sample for the row (its outputs are written).
-__device__ inline void publish_dec_none(const Args& a, int b) {
-    dec_put(&a.ws.dec[b], DW_KIND, (unsigned)KIND_NONE, a.epoch);
-}
-
-// A correction / bonus draw for the sampling workgroups of the row.
-__device__ inline void publish_dec_draw(const Args& a, int b, const DecLocal& sd, float mt,
-                                        float invt, float mq, float invq, float scale) {
-    Dec* d = &a.ws.dec[b];
-    const unsigned e = a.epoch;
-    dec_put(d, DW_KIND, (unsigned)sd.kind, e);
-    dec_put(d, DW_POS, (unsigned)sd.pos, e);
-    dec_put(d, DW_U, __float_as_uint(sd.u), e);
-    dec_put(d, DW_MT, __float_as_uint(mt), e);
-    dec_put(d, DW_INVT, __float_as_uint(invt), e);
-    dec_put(d, DW_MQ, __float_as_uint(mq), e);
-    dec_put(d, DW_INVQ, __float_as_uint(invq), e);
-    dec_put(d, DW_SCALE, __float_as_uint(scale), e);
-    dec_put(d, DW_NEMIT, (unsigned)sd.nemit, e);
-    dec_put(d, DW_NACC, (unsigned)sd.nacc, e);
-    dec_put(d, DW_FLAGS, sd.flags, e);
-    for (int j = 0; j < a.gamma; ++j) dec_put(d, DW_EMIT + j, (unsigned)(j < sd.nemit ? sd.emit[j] : -1), e);
-}
-
-// ---------------------------------------------------------------- decision
-// Run by the last streaming workgroup of batch row b, once every consulted
-// row's unit statistics are published: combine them, take the accept tests
-// in order and stop at the first rejection (pseudo-code 10-1), or follow the
-// greedy rule.  Rows that need no sampled token get their outputs here; the
-// others publish a decision record for the sampling phase; either way the
-// record's kind word carries this call's epoch.
-//
-// With ``first`` set it runs after the position-0 rows only: if the round
-// ends at position 0 the row is decided as above (and the stage flag says
-// "stop"); otherwise only the stage flag is published ("go on") and the
-// decision is left to the last unit of the later positions.
-template <bool BF16>
-__device__ void decide_row(const Args& a, int b, const Plan& pl, bool first) {
-    __shared__ float sM[kMaxRows], sS[kMaxRows];
-    __shared__ int sI[kMaxRows];
-    __shared__ unsigned sBad[kMaxRows];
-    __shared__ float sP[SPECV_MAX_GAMMA], sQ[SPECV_MAX_GAMMA];
-    __shared__ int sQz[SPECV_MAX_GAMMA];
-    __shared__ float sUacc[SPECV_MAX_GAMMA], sUres[SPECV_MAX_GAMMA + 1];
-    __shared__ DecLocal sd;
-    const int tid = threadIdx.x;
-    const bool greedy = pl.mode == MODE_GREEDY;
-    const float scale = pl.scale;
-    const int nt = first ? 1 : pl.nt;                 // rows merged at this point
-    const int nd = first ? min(pl.nd, 1) : pl.nd;
-    const int nrows = nt + nd;
-    // one memory round trip: every unit statistic, every z at d_i, and the
-    // uniforms, issued together by different threads
-    __shared__ Part sPart[kDecideParts];
-    __shared__ float sZt[SPECV_MAX_GAMMA], sZq[SPECV_MAX_GAMMA];
-    const int nparts = nrows * a.U;
-    for (int k = tid; k < nparts; k += kBlock) {
-        const int row = k / a.U;
-        const int r = row < nt ? row : a.gamma + 1 + (row - nt);
-        if (k < kDecideParts) sPart[k] = published_part(&a.ws.part[part_index(a, b, r, k - row * a.U)]);
+    if (lane == 0) {
+        a.out_emit[b] = nemit + (sampled >= 0 ? 1 : 0);
+        a.out_acc[b] = nacc;
+        if (a.out_flags) a.out_flags[b] = (int)flags;
+        if (a.wres) a.wres[b] = wres;
     }
-    if (!greedy && tid >= kBlock - kWave && tid - (kBlock - kWave) < nd) {
-        const int i = tid - (kBlock - kWave);
-        const int d = a.tokens[(long long)b * a.gamma + i];
-        sZt[i] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, i), d);
-        sZq[i] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i), d);
-    }
-    if (!greedy && tid >= kBlock - 2 * kWave && tid < kBlock - kWave) {
-        const int i = tid - (kBlock - 2 * kWave);
-        if (i < nd) {
-            sUacc[i] = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
-            sUres[i] = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
-        }
-        if (i == kWave - 1) sUres[a.gamma] = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
-    }
-    __syncthreads();
-    // merge the units of each row, one thread per row
-    for (int row = tid; row < nrows; row += kBlock) {
-        const int r = row < nt ? row : a.gamma + 1 + (row - nt);
-        float m = -kInf, s = 0.f;
-        int arg = 0x7fffffff;
-        unsigned bad = 0;
-        for (int u = 0; u < a.U; ++u) {
-            const int k = row * a.U + u;
-            const Part p = k < kDecideParts ? sPart[k]
-                                            : published_part(&a.ws.part[part_index(a, b, r, u)]);
-            if (greedy) merge_arg(m, arg, p.m, p.arg);
-            else merge_ms(m, s, p.m, p.s, scale);
-            bad |= p.bad;
-        }
-        sM[r] = m;
-        sS[r] = s;
-        sI[r] = arg;
-        sBad[r] = bad || m == -kInf || (!greedy && !(s > 0.f));
-    }
-    __syncthreads();
-    if (!greedy && tid < nd) {
-        // p_i(d_i) and q_i(d_i) from the raw logits at d_i
-        const int i = tid;
-        const int rq = a.gamma + 1 + i;
-        sP[i] = fast_exp2((sZt[i] - sM[i]) * scale) / sS[i];
-        sQ[i] = fast_exp2((sZq[i] - sM[rq]) * scale) / sS[rq];
-        sQz[i] = sZq[i] == -kInf;
-    }
-    __syncthreads();
-    if (tid != 0) return;
-
-    sd.kind = KIND_NONE;
-    sd.pos = -1;
-    sd.u = 0.f;
-    sd.nemit = 0;
-    sd.nacc = 0;
-    sd.flags = pl.flags;
-    bool dead = false;
-    bool go_on = false;                                // first stage: the round continues
-    int sampled = -1;
-    int tested = 0;
-    const int* toks = a.tokens + (long long)b * a.gamma;
-    if (greedy) {
-        for (int i = 0; i <= a.gamma; ++i) {
-            if (sd.nemit >= pl.cap) break;
-            if (first && i >= 1) {
-                go_on = true;
-                break;
-            }
-            if (sBad[i]) {
-                dead = true;
-                break;
-            }
-            const int am = sI[i];
-            if (i < a.gamma && toks[i] == am) {
-                sd.emit[sd.nemit++] = am;
-                sd.nacc++;
-                continue;
-            }
-            sampled = am;        // first mismatch, or the bonus position
-            break;
-        }
-    } else {
-        int i = 0;
-        for (; i < a.gamma; ++i) {
-            if (sd.nemit >= pl.cap) break;
-            if (first && i >= 1) {
-                go_on = true;
-                break;
-            }
-            if (sBad[i] || sBad[a.gamma + 1 + i]) {
-                dead = true;
-                break;
-            }
-            if (sQz[i]) sd.flags |= SPECV_FLAG_Q_ZERO;
-            tested = i + 1;
-            if (sUacc[i] * sQ[i] < sP[i]) {       // accept with probability min(1, p/q)
-                sd.emit[sd.nemit++] = toks[i];
-                sd.nacc++;
-                continue;
-            }
-            sd.kind = KIND_RESIDUAL;
-            sd.pos = i;
-            sd.u = sUres[i];
-            break;
-        }
-        if (!go_on && !dead && sd.kind == KIND_NONE && i == a.gamma && sd.nemit < pl.cap) {
-            if (first && a.gamma >= 1) {
-                go_on = true;                     // the bonus row is a later position
-            } else if (sBad[a.gamma]) {
-                dead = true;
-            } else {
-                sd.kind = KIND_BONUS;
-                sd.pos = a.gamma;
-                sd.u = sUres[a.gamma];
-            }
-        }
-        if (!go_on) {
-            for (int j = 0; j < tested; ++j) {
-                if (a.p_at) a.p_at[(long long)b * a.gamma + j] = sP[j];
-                if (a.q_at) a.q_at[(long long)b * a.gamma + j] = sQ[j];
-            }
-        }
-    }
-    if (go_on) {
-        publish(&a.ws.stage1[(long long)b * kCounterStride], 2u * a.epoch + 1u);
-        return;
-    }
-    write_diag_nan(a, b, tested);
-    if (dead) {
-        sd.flags |= SPECV_FLAG_NONFINITE_ROW;
-        sd.kind = KIND_NONE;
-    }
-    if (sd.kind == KIND_NONE) {
-        write_outputs(a, b, sd.emit, sd.nemit, sd.nacc, sd.flags, dead, sampled, 0.f);
-        publish_dec_none(a, b);
-    } else {
-        const int pos = sd.pos;
-        const bool res = sd.kind == KIND_RESIDUAL;
-        publish_dec_draw(a, b, sd, sM[pos], 1.f / sS[pos], res ? sM[a.gamma + 1 + pos] : 0.f,
-                         res ? 1.f / sS[a.gamma + 1 + pos] : 0.f, scale);
-    }
-    if (first) publish(&a.ws.stage1[(long long)b * kCounterStride], 2u * a.epoch);
 }
 
 // ---------------------------------------------------------------- truncation
@@ -752,14 +556,15 @@ __device__ void decide_row(const Args& a, int b, const Plan& pl, bool first) {
 //                <= 8); the k-th largest of those 256 j values, L, has at
 //                least k chunk entries >= L, so every finite entry >= L is a
 //                superset of the chunk's top k (typically ~k entries);
-//   per row:     (last unit of the row) the row's top-k threshold is >= every
-//                chunk's L, so only candidates >= max L are gathered (at most
-//                2048); they are sorted (value desc, index asc), the k-th
-//                entry is the top-k threshold (ties kept), and the prefix is
-//                scanned for top-p: the first level whose cumulative mass
-//                reaches top_p ends the kept set (ties at a level all kept);
-//   per batch row: (last row) accept tests from the kept sets, and the
-//                correction / bonus sample from the (short) kept list of the
+//   per row:     (the workgroup deciding the position) the row's top-k
+//                threshold is >= every chunk's L, so only candidates >= max L
+//                are gathered (at most 2048); they are sorted (value desc,
+//                index asc), the k-th entry is the top-k threshold (ties
+//                kept), and the prefix is scanned for top-p: the first level
+//                whose cumulative mass reaches top_p ends the kept set (ties
+//                at a level all kept);
+//   per batch row: the accept tests use the kept sets, and the correction /
+//                bonus sample is drawn from the (short) kept list of the
 //                sampled row, tokens in ascending index order.
 
 __device__ inline bool finite_logit(float x) { return x > -kInf && x <= 3.402823466e38f; }
@@ -767,14 +572,11 @@ __device__ inline bool finite_logit(float x) { return x > -kInf && x <= 3.402823
 __device__ inline void publish_cand(Cand* p, float v, int idx) {
     const unsigned long long w =
         (unsigned long long)__float_as_uint(v) | ((unsigned long long)(unsigned)idx << 32);
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), w, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    publish(reinterpret_cast<unsigned long long*>(p), w);
 }
 
 __device__ inline Cand published_cand(const Cand* p) {
-    const unsigned long long w = __hip_atomic_load(
-        reinterpret_cast<unsigned long long*>(const_cast<Cand*>(p)), __ATOMIC_RELAXED,
-        __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long w = published(reinterpret_cast<const unsigned long long*>(p));
     Cand c;
     c.v = __uint_as_float((unsigned)w);
     c.idx = (int)(unsigned)(w >> 32);
@@ -966,6 +768,7 @@ __device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff
     }
     const int n = kBlock * jj;
     const int n2 = pow2_at_least(n);
+    __syncthreads();                                        // sc may still be read
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         if (j < jj) {
@@ -996,21 +799,32 @@ __device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff
         publish_cand(a.ws.cand_meta + rowid * a.C + c, L, total <= a.cand_cap ? total : -1);
 }
 
-// Row-level truncation (whole workgroup), run by the last unit of the row.
+// Row-level truncation (whole workgroup) of logits row (b, k, side), once
+// every chunk's candidates are published.  Publishes the kept list and the
+// row's TruncRow, and returns the TruncRow to every thread.
 template <bool BF16>
-__device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScratch& sc) {
+__device__ TruncRow row_merge(const Args& a, int b, int k, int side, const Plan& pl,
+                              TruncScratch& sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const long long rowid = (long long)b * a.R + r;
+    const long long rowid = side_row(a, b, k, side);
     __shared__ float sL, sM, sS, sZ1;
     __shared__ unsigned sBad, sFlags;
     __shared__ int sTotal, sN, sJ, sLevelStart;
+    __shared__ TruncRow sOut;
     unsigned* off = sc.off;                // chunk offsets [0, C]
+    __syncthreads();                       // shared state may still be read
     if (tid == 0) {
         sBad = 0;
         sFlags = 0;
         sN = 0;
         sJ = 0x7fffffff;
         sLevelStart = 0x7fffffff;
+        sOut.zmax = -kInf;
+        sOut.tstar = kInf;
+        sOut.S = 0.f;
+        sOut.n_kept = 0;
+        sOut.flags = 0;
+        sOut.bad = 0;
     }
     // chunk bounds and counts (lane c holds chunk c; C <= 64), and the row
     // statistics (for top-p alone)
@@ -1038,18 +852,16 @@ __device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScra
         }
     } else if (wave == 1) {
         float m = -kInf, s = 0.f;
-        unsigned bad = 0;
-        for (int u = lane; u < a.U; u += kWave) {
-            const Part p = published_part(&a.ws.part[part_index(a, b, r, u)]);
-            merge_ms(m, s, p.m, p.s, pl.scale);
-            bad |= p.bad;
+        if (lane < a.C) {
+            unsigned sw = 0;
+            (void)published_stats(stats_words(a, b, k, side, lane), a.epoch, m, sw);
+            s = __uint_as_float(sw);
         }
         wave_merge_ms(m, s, pl.scale);
-        bad = wave_or(bad);
         if (lane == 0) {
             sM = m;
             sS = s;
-            if (bad || m == -kInf) sBad = 1;
+            if (__builtin_isnan(s) || m == -kInf) sBad = 1;
         }
     }
     __syncthreads();
@@ -1093,11 +905,15 @@ __device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScra
     TruncRow* tr = &a.ws.trow[rowid];
     if ((sFlags & SPECV_FLAG_CAND_OVERFLOW) || sBad || n1 == 0) {
         if (tid == 0) {
-            publish(&tr->bad, (sBad || n1 == 0) ? 1u : 0u);
+            sOut.bad = (sBad || n1 == 0) ? 1u : 0u;
+            sOut.flags = sFlags;
+            sOut.n_kept = 0;
+            publish(&tr->bad, sOut.bad);
             publish(&tr->flags, sFlags);
             publish(&tr->n_kept, 0);
         }
-        return;
+        __syncthreads();
+        return sOut;
     }
     // sort the gathered entries: value desc, index asc
     const int n2 = pow2_at_least(n1);
@@ -1141,11 +957,15 @@ __device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScra
                 // top-p alone: the candidates hold less than top_p of the mass
                 if (tid == 0) {
                     sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+                    sOut.bad = 0;
+                    sOut.flags = sFlags;
+                    sOut.n_kept = 0;
                     publish(&tr->bad, 0u);
                     publish(&tr->flags, sFlags);
                     publish(&tr->n_kept, 0);
                 }
-                return;
+                __syncthreads();
+                return sOut;
             }
             jstar = nk1 - 1;                // rounding: keep the whole top-k set
         } else {
@@ -1168,6 +988,12 @@ __device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScra
     for (int i = tid; i < nkept; i += kBlock) publish_cand(kept + i, sc.v[i], sc.idx[i]);
     __syncthreads();
     if (tid == 0) {
+        sOut.zmax = zmax;
+        sOut.tstar = sc.v[jstar];
+        sOut.S = sc.w[jstar];
+        sOut.n_kept = nkept;
+        sOut.flags = sFlags;
+        sOut.bad = 0;
         publish(&tr->zmax, zmax);
         publish(&tr->tstar, sc.v[jstar]);
         publish(&tr->S, sc.w[jstar]);
@@ -1175,436 +1001,191 @@ __device__ void row_merge(const Args& a, int b, int r, const Plan& pl, TruncScra
         publish(&tr->flags, sFlags);
         publish(&tr->bad, 0u);
     }
+    __syncthreads();
+    return sOut;
 }
 
-// Decision and sampling of a truncated batch row (whole workgroup), run by
-// the last of its consulted rows to finish.
+__device__ inline bool trow_dead(const TruncRow& t) {
+    return t.bad != 0 || (t.flags & SPECV_FLAG_CAND_OVERFLOW) || t.n_kept == 0;
+}
+
+// Probability of raw logit z under a truncated row: membership in the kept
+// set is decided on the raw value (z >= tstar).
+__device__ inline float trunc_prob(const TruncRow& t, float z, float scale) {
+    if (!(finite_logit(z) && z >= t.tstar)) return 0.f;
+    return fast_exp2(__fmul_rn(z - t.zmax, scale)) / t.S;
+}
+
+__device__ inline TruncRow published_trow(const TruncRow* p) {
+    TruncRow t;
+    t.zmax = published(&p->zmax);
+    t.tstar = published(&p->tstar);
+    t.S = published(&p->S);
+    t.n_kept = published(&p->n_kept);
+    t.flags = published(&p->flags);
+    t.bad = published(&p->bad);
+    return t;
+}
+
+// Correction / bonus sample of a truncated row (whole workgroup) at position
+// pos: weights over the kept set of p_pos (zero weight elsewhere), tokens in
+// ascending index order, first running sum > u * W.  Returns the token (-1 if
+// no weight anywhere) to every thread; *wres gets W of a correction, and
+// *fallback is set when the correction mass vanished and p was used.
 template <bool BF16>
-__device__ void decide_trunc(const Args& a, int b, const Plan& pl, TruncScratch& sc) {
+__device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, const Plan& pl,
+                            TruncScratch& sc, float* wres, bool* fallback) {
     const int tid = threadIdx.x;
-    __shared__ float tZ[kMaxRows], tT[kMaxRows], tS[kMaxRows];
-    __shared__ int tN[kMaxRows];
-    __shared__ unsigned tF[kMaxRows], tBad[kMaxRows];
-    __shared__ float sP[SPECV_MAX_GAMMA], sQ[SPECV_MAX_GAMMA];
-    __shared__ int sQz[SPECV_MAX_GAMMA];
-    __shared__ float sUacc[SPECV_MAX_GAMMA], sUres[SPECV_MAX_GAMMA + 1];
-    __shared__ DecLocal sd;
-    __shared__ int sDead, sTok, sLastPos;
+    __shared__ TruncRow tT, tQ;
     __shared__ float sWsum;
+    __shared__ int sTok, sLastPos, sFb;
     const float scale = pl.scale;
-    const int nrows = pl.nt + pl.nd;
-    for (int k = tid; k < nrows; k += kBlock) {
-        const int r = k < pl.nt ? k : a.gamma + 1 + (k - pl.nt);
-        const TruncRow* tr = &a.ws.trow[(long long)b * a.R + r];
-        tZ[r] = published(&tr->zmax);
-        tT[r] = published(&tr->tstar);
-        tS[r] = published(&tr->S);
-        tN[r] = published(&tr->n_kept);
-        tF[r] = published(&tr->flags);
-        tBad[r] = published(&tr->bad);
-    }
-    __syncthreads();
-    // membership in the kept set is decided on the raw value: z >= tstar
-    auto prob = [&](int r, float z) -> float {
-        if (!(finite_logit(z) && z >= tT[r])) return 0.f;
-        return fast_exp2(__fmul_rn(z - tZ[r], scale)) / tS[r];
-    };
-    auto row_dead = [&](int r) { return tBad[r] != 0 || (tF[r] & SPECV_FLAG_CAND_OVERFLOW) || tN[r] == 0; };
-    if (tid < pl.nd) {
-        const int i = tid;
-        const int d = a.tokens[(long long)b * a.gamma + i];
-        const float zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, i), d);
-        const float zq = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i), d);
-        const int rq = a.gamma + 1 + i;
-        sP[i] = row_dead(i) ? 0.f : prob(i, zt);
-        sQ[i] = row_dead(rq) ? 0.f : prob(rq, zq);
-        sQz[i] = !(finite_logit(zq) && zq >= tT[rq]);
-        sUacc[i] = uniform24(a.seed, b, i, PURPOSE_ACCEPT, a.step);
-        sUres[i] = uniform24(a.seed, b, i, PURPOSE_RESIDUAL, a.step);
-    }
-    if (tid == kBlock - 1) sUres[a.gamma] = uniform24(a.seed, b, a.gamma, PURPOSE_BONUS, a.step);
     __syncthreads();
     if (tid == 0) {
-        sd.kind = KIND_NONE;
-        sd.pos = -1;
-        sd.u = 0.f;
-        sd.nemit = 0;
-        sd.nacc = 0;
-        sd.flags = pl.flags;
-        int dead = 0, tested = 0;
-        const int* toks = a.tokens + (long long)b * a.gamma;
-        auto consult = [&](int r) {
-            sd.flags |= tF[r] & (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
-            if (tBad[r]) sd.flags |= SPECV_FLAG_NONFINITE_ROW;
-            return !row_dead(r);
-        };
-        int i = 0;
-        for (; i < a.gamma; ++i) {
-            if (sd.nemit >= pl.cap) break;
-            const bool okt = consult(i), okq = consult(a.gamma + 1 + i);
-            if (!okt || !okq) {
-                dead = 1;
-                break;
-            }
-            if (sQz[i]) sd.flags |= SPECV_FLAG_Q_ZERO;
-            tested = i + 1;
-            if (sUacc[i] * sQ[i] < sP[i]) {       // accept with probability min(1, p/q)
-                sd.emit[sd.nemit++] = toks[i];
-                sd.nacc++;
-                continue;
-            }
-            sd.kind = KIND_RESIDUAL;
-            sd.pos = i;
-            sd.u = sUres[i];
-            break;
-        }
-        if (!dead && sd.kind == KIND_NONE && i == a.gamma && sd.nemit < pl.cap) {
-            if (!consult(a.gamma)) {
-                dead = 1;
-            } else {
-                sd.kind = KIND_BONUS;
-                sd.pos = a.gamma;
-                sd.u = sUres[a.gamma];
-            }
-        }
-        for (int j = 0; j < tested; ++j) {
-            if (a.p_at) a.p_at[(long long)b * a.gamma + j] = sP[j];
-            if (a.q_at) a.q_at[(long long)b * a.gamma + j] = sQ[j];
-        }
-        write_diag_nan(a, b, tested);
-        if (dead) sd.kind = KIND_NONE;
-        sDead = dead;
+        tT = published_trow(&a.ws.trow[side_row(a, b, pos, 0)]);
+        if (res) tQ = published_trow(&a.ws.trow[side_row(a, b, pos, 1)]);
         sTok = 0x7fffffff;
         sLastPos = -1;
+        sFb = 0;
     }
     __syncthreads();
-    int sampled = -1;
-    float wres = 0.f;
-    if (sd.kind != KIND_NONE) {
-        const int pos = sd.pos;
-        const bool res = sd.kind == KIND_RESIDUAL;
-        const int n = tN[pos];
-        const Cand* kept = a.ws.kept + ((long long)b * a.R + pos) * a.kept_cap;
-        const void* qrow = res ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
-        const int rq = a.gamma + 1 + pos;
-        // weights over the kept set of p_pos (zero weight elsewhere):
-        // sc.v = weight, sc.idx = token, sc.w = p (fallback weight)
-        float part = 0.f, partp = 0.f;
-        for (int i = tid; i < n; i += kBlock) {
-            const Cand cv = published_cand(kept + i);
-            const float p = __fmul_rn(fast_exp2(__fmul_rn(cv.v - tZ[pos], scale)), 1.f / tS[pos]);
-            float w = p;
-            if (res) {
-                const float zq = load_elem<BF16>(qrow, cv.idx);
-                const float q = (finite_logit(zq) && zq >= tT[rq])
-                                    ? __fmul_rn(fast_exp2(__fmul_rn(zq - tZ[rq], scale)), 1.f / tS[rq])
-                                    : 0.f;
-                w = fmaxf(__fsub_rn(p, q), 0.f);
-            }
-            sc.v[i] = w;
-            sc.w[i] = p;
-            sc.idx[i] = cv.idx;
-            part += w;
-            partp += p;
+    const int n = tT.n_kept;
+    if (n <= 0) return -1;                  // (a dead row is never sampled)
+    const Cand* kept = a.ws.kept + side_row(a, b, pos, 0) * a.kept_cap;
+    const void* qrow = res ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+    // sc.v = weight, sc.idx = token, sc.w = p (fallback weight)
+    float part = 0.f;
+    for (int i = tid; i < n; i += kBlock) {
+        const Cand cv = published_cand(kept + i);
+        const float p = __fmul_rn(fast_exp2(__fmul_rn(cv.v - tT.zmax, scale)), 1.f / tT.S);
+        float w = p;
+        if (res) {
+            const float zq = load_elem<BF16>(qrow, cv.idx);
+            const float q = (finite_logit(zq) && zq >= tQ.tstar)
+                                ? __fmul_rn(fast_exp2(__fmul_rn(zq - tQ.zmax, scale)), 1.f / tQ.S)
+                                : 0.f;
+            w = fmaxf(__fsub_rn(p, q), 0.f);
         }
-        part = wave_sum(part);
-        if (tid % kWave == 0) sc.red[tid / kWave] = part;
-        __syncthreads();
-        if (tid == 0) {
-            float W = 0.f;
-            for (int w2 = 0; w2 < kWaves; ++w2) W += sc.red[w2];
-            sWsum = W;
-        }
-        __syncthreads();
-        wres = res ? sWsum : 0.f;
-        if (res && (!(sWsum > 0.f) || !__builtin_isfinite(sWsum))) {
-            // the correction mass vanished: sample from p at that position
-            for (int i = tid; i < n; i += kBlock) sc.v[i] = sc.w[i];
-            if (tid == 0) sd.flags |= SPECV_FLAG_RESIDUAL_FALLBACK;
-        }
-        (void)partp;
-        // tokens in ascending index order, then the first running sum > u * W
-        const int n2 = pow2_at_least(n);
-        for (int i = n + tid; i < n2; i += kBlock) {
-            sc.v[i] = 0.f;
-            sc.idx[i] = 0x7fffffff;
-        }
-        __syncthreads();
-        bitonic_sort(sc.v, sc.idx, n2, by_index);
-        for (int i = tid; i < n; i += kBlock) sc.w[i] = sc.v[i];
-        __syncthreads();
-        block_inclusive_scan(sc.w, n, sc.red);
-        const float target = sd.u * sc.w[n - 1];
-        for (int i = tid; i < n; i += kBlock) {
-            if (sc.v[i] > 0.f) {
-                if (sc.w[i] > target) atomicMin(&sTok, i);
-                atomicMax(&sLastPos, i);
-            }
-        }
-        __syncthreads();
-        const int j = sTok != 0x7fffffff ? sTok : sLastPos;     // clamp: last positive weight
-        sampled = j >= 0 ? sc.idx[j] : -1;
+        sc.v[i] = w;
+        sc.w[i] = p;
+        sc.idx[i] = cv.idx;
+        part += w;
     }
+    part = wave_sum(part);
+    if (tid % kWave == 0) sc.red[tid / kWave] = part;
+    __syncthreads();
     if (tid == 0) {
-        bool dead = sDead;
-        unsigned flags = sd.flags;
-        if (!dead && sd.kind != KIND_NONE && sampled < 0) {
-            dead = true;
-            flags |= SPECV_FLAG_NONFINITE_ROW;
-        }
-        write_outputs(a, b, sd.emit, sd.nemit, sd.nacc, flags, dead, sampled, wres);
-        publish_dec_none(a, b);
+        float W = 0.f;
+        for (int w2 = 0; w2 < kWaves; ++w2) W += sc.red[w2];
+        sWsum = W;
+        sFb = res && (!(W > 0.f) || !__builtin_isfinite(W));
     }
+    __syncthreads();
+    *wres = res ? sWsum : 0.f;
+    *fallback = sFb != 0;
+    if (sFb) {
+        // the correction mass vanished: sample from p at that position
+        for (int i = tid; i < n; i += kBlock) sc.v[i] = sc.w[i];
+    }
+    // tokens in ascending index order, then the first running sum > u * W
+    const int n2 = pow2_at_least(n);
+    for (int i = n + tid; i < n2; i += kBlock) {
+        sc.v[i] = 0.f;
+        sc.idx[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    bitonic_sort(sc.v, sc.idx, n2, by_index);
+    for (int i = tid; i < n; i += kBlock) sc.w[i] = sc.v[i];
+    __syncthreads();
+    block_inclusive_scan(sc.w, n, sc.red);
+    const float target = u * sc.w[n - 1];
+    for (int i = tid; i < n; i += kBlock) {
+        if (sc.v[i] > 0.f) {
+            if (sc.w[i] > target) atomicMin(&sTok, i);
+            atomicMax(&sLastPos, i);
+        }
+    }
+    __syncthreads();
+    const int j = sTok != 0x7fffffff ? sTok : sLastPos;     // clamp: last positive weight
+    const int tok = j >= 0 ? sc.idx[j] : -1;
+    __syncthreads();
+    return tok;
 }
 
-// ---------------------------------------------------------------- streaming
-// The 16-byte loads of this thread's groups of chunk entries [v0, v0 + len),
-// in load_chunk's layout, split in two halves so that several chunks can be
-// in flight at once: ``issue_groups`` only issues the loads (groups past the
-// chunk's last whole group load group 0 instead), ``finish_groups`` unpacks
-// and masks them.  Needs len >= one group.
+// ---------------------------------------------------------------- row finish
+// Outputs and diagnostics of row b, by wave 0 of the calling workgroup: the
+// first nacc drafts, then ``sampled`` (if >= 0); p_i(d_i), q_i(d_i) of the
+// ``tested`` positions from the walk's history (hp, hq in LDS).
+__device__ inline void finish_row(const Args& a, int b, const Plan& pl, int nacc, int tested,
+                                  unsigned flags, bool dead, int sampled, float wres,
+                                  const float* hp, const float* hq) {
+    if (threadIdx.x / kWave != 0) return;
+    const int lane = threadIdx.x % kWave;
+    write_outputs_wave(a, b, nacc, nacc, flags, dead, sampled, wres, pl.tok);
+    write_diag_wave(a, b, tested, lane < kMaxPos ? hp[lane] : 0.f, lane < kMaxPos ? hq[lane] : 0.f);
+}
+
+// Accept test of a sampling pair from its merged statistics (pseudo-code
+// 10-1: accept with probability min(1, p / q), i.e. u * q < p).
+__device__ inline unsigned sample_outcome(bool test, float mt, float st, float mq, float sq,
+                                          bool badT, bool badQ, float zt, float zq, float u,
+                                          float scale, unsigned& flags, float& p, float& q) {
+    flags = 0;
+    p = 0.f;
+    q = 0.f;
+    if (badT || badQ) {
+        flags = SPECV_FLAG_NONFINITE_ROW;
+        return OUT_BAD;
+    }
+    if (!test) return OUT_BONUS;
+    p = fast_exp2((zt - mt) * scale) / st;
+    q = fast_exp2((zq - mq) * scale) / sq;
+    if (zq == -kInf) flags |= SPECV_FLAG_Q_ZERO;
+    return u * q < p ? OUT_ACC : OUT_REJ;
+}
+
+// Decision of a truncated pair (k, b) by the last of its units to arrive
+// (whole workgroup): the row-level truncation of target row k (and draft row
+// k), then the accept test on the kept sets; the outcome goes to the pair's
+// record, which the pair's other units wait for.
 template <bool BF16>
-__device__ inline void issue_groups(const void* row, int v0, int len,
-                                    uint4 (&q)[kPerThread / (BF16 ? 8 : 4)]) {
-    constexpr int G = BF16 ? 8 : 4;
-    constexpr int NG = kPerThread / G;
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
-                                                    (size_t)v0 * (BF16 ? 2 : 4));
-    const int full = len / G;
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        const int g = j * kBlock + (int)threadIdx.x;
-        q[j] = p[g < full ? g : 0];
-    }
-}
-
-template <bool BF16>
-__device__ inline void finish_groups(const void* row, int v0, int len,
-                                     const uint4 (&q)[kPerThread / (BF16 ? 8 : 4)],
-                                     float (&x)[kPerThread]) {
-    constexpr int G = BF16 ? 8 : 4;
-    constexpr int NG = kPerThread / G;
+__device__ void decide_trunc(const Args& a, int b, int k, const Plan& pl, TruncScratch& sc,
+                             unsigned* out, unsigned* flags_out, float* p_out, float* q_out) {
     const int tid = threadIdx.x;
-    const int full = len / G;
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        unpack16<BF16>(q[j], &x[j * G]);
-        if (j * kBlock + tid >= full) {
-#pragma unroll
-            for (int e = 0; e < G; ++e) x[j * G + e] = -kInf;
-        }
-    }
-    const int rem = len - full * G;                 // entries of a last partial group
-    if (rem && tid == full % kBlock) {
-#pragma unroll
-        for (int j = 0; j < NG; ++j) {
-            if (j == full / kBlock) {
-#pragma unroll
-                for (int e = 0; e < G; ++e)
-                    if (e < rem) x[j * G + e] = load_elem<BF16>(row, (long long)v0 + full * G + e);
-            }
-        }
-    }
-}
-
-// One streaming unit t = (b, r, unit): up to kUnitChunks chunks of one logits
-// row, the loads of all of them (bfloat16) or of the next two (float32) in
-// flight before the first is reduced, with per-thread running statistics:
-//   sampling rows: running max m and sum s of exp2((z - m) * scale), the sum
-//                  rescaled when the max grows (one extra exp2 per chunk);
-//   greedy rows:   running max and its lowest index.
-// The unit's statistics are published; the last unit of a batch row to
-// arrive runs the decision.
-//
-// Units come in two stages.  Stage 1 holds the position-0 rows (target row 0
-// and draft row 0) of every batch row; stage 2 the later positions.  For
-// sampling and greedy rows the last stage-1 unit tests position 0; stage-2
-// units wait for that result and skip their rows when the round has already
-// ended (the rows past the first rejection are never needed), otherwise the
-// last stage-2 unit decides the row.  Truncated rows do not wait.
-template <bool BF16, bool VEC, bool TRUNC>
-__device__ void stream_unit(const Args& a, int t, TruncScratch* sc) {
-    constexpr int NG = kPerThread / (BF16 ? 8 : 4);
-    const int n1 = a.gamma >= 1 ? 2 : 1;            // position-0 rows per batch row
-    const int n2 = a.R - n1;
-    const int units1 = a.B * n1 * a.U;
-    const bool stage1 = t < units1;
-    int b, r, unit;
-    if (stage1) {
-        unit = t % a.U;
-        const int row = t / a.U;
-        b = row / n1;
-        r = (row - b * n1) == 0 ? 0 : a.gamma + 1;
-    } else {
-        const int t2 = t - units1;
-        unit = t2 % a.U;
-        const int row = t2 / a.U;
-        b = row / n2;
-        const int k = row - b * n2;                  // target rows 1..gamma, then draft rows 1..
-        r = k < a.gamma ? 1 + k : a.gamma + 2 + (k - a.gamma);
-    }
-    const int tid = threadIdx.x;
-    const Plan pl = make_plan(a, b);
-    if (pl.mode == MODE_SKIP) {
-        if (r == 0 && unit == 0 && tid == 0) {
-            write_outputs(a, b, nullptr, 0, 0, pl.flags, true, -1, 0.f);
-            write_diag_nan(a, b, 0);
-            publish_dec_none(a, b);
-        }
-        return;
-    }
-    const bool is_target = r <= a.gamma;
-    const int pos = is_target ? r : r - a.gamma - 1;
-    if (pos >= (is_target ? pl.nt : pl.nd)) return;   // a row this round cannot consult
-    const bool staged = pl.mode == MODE_SAMPLE || pl.mode == MODE_GREEDY;
-    if (staged && !stage1) {
-        __shared__ unsigned sGo;
-        if (tid == 0) {
-            const unsigned* flag = &a.ws.stage1[(long long)b * kCounterStride];
-            unsigned v = 0;
-            for (int spin = 0; spin < (1 << 20); ++spin) {
-                v = published(flag);
-                if ((v >> 1) == a.epoch) break;
-                __builtin_amdgcn_s_sleep(2);
-            }
-            sGo = (v >> 1) == a.epoch ? (v & 1u) : 0u;
-            if ((v >> 1) != a.epoch && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
-        }
-        __syncthreads();
-        if (!sGo) return;                              // the round ended at position 0
-    }
-
-    const void* rp = is_target ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos)
-                               : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos);
-    const int c0 = unit * kUnitChunks;
-    const bool greedy = pl.mode == MODE_GREEDY;
-    const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
-    const long long rowid = (long long)b * a.R + r;
+    const bool test = k < a.gamma;
     const float scale = pl.scale;
-    float m = -kInf, s = 0.f;                          // sampling rows
-    float best = -kInf;                                // greedy rows
-    int bi = 0x7fffffff;
-    unsigned bad = 0;
-
-    constexpr int G = BF16 ? 8 : 4;
-    constexpr int DEPTH = BF16 && !TRUNC ? kUnitChunks : 2;   // chunks in flight (registers)
-    auto chunk_len = [&](int c) { return c < a.C ? min(kChunk, a.V - c * kChunk) : 0; };
-    uint4 q[DEPTH][NG];
-#pragma unroll
-    for (int u = 0; u < DEPTH; ++u)
-        if (VEC && chunk_len(c0 + u) >= G) issue_groups<BF16>(rp, (c0 + u) * kChunk, chunk_len(c0 + u), q[u]);
-#pragma unroll
-    for (int u = 0; u < kUnitChunks; ++u) {
-        const int c = c0 + u;
-        if (c >= a.C) continue;                       // (keeps the unrolled trip count)
-        const int len = chunk_len(c);
-        float x[kPerThread];
-        if (VEC && len >= G) {
-            finish_groups<BF16>(rp, c * kChunk, len, q[u % DEPTH], x);
-            if (u + DEPTH < kUnitChunks && chunk_len(c + DEPTH) >= G)
-                issue_groups<BF16>(rp, (c + DEPTH) * kChunk, chunk_len(c + DEPTH), q[u % DEPTH]);
-        } else {
-            load_chunk<BF16, VEC>(rp, c * kChunk, len, x);
-        }
-        if (greedy) {
-            const int v0 = c * kChunk;
-#pragma unroll
-            for (int k = 0; k < kPerThread; ++k) {
-                bad |= !(x[k] <= 3.402823466e38f);        // NaN or +inf
-                if (x[k] > best) {                        // strict: keeps the lowest index
-                    best = x[k];
-                    bi = v0 + chunk_index<BF16>(k);
-                }
-            }
-        } else {
-            float cm = -kInf;
-#pragma unroll
-            for (int k = 0; k < kPerThread; ++k) cm = fmaxf(cm, x[k]);
-            const float nm = fmaxf(m, cm);
-            const float nms = nm == -kInf ? 0.f : -nm * scale;
-            float cs = s * fast_exp2(fmaf(m, scale, nms));
-#pragma unroll
-            for (int k = 0; k < kPerThread; ++k) cs += fast_exp2(fmaf(x[k], scale, nms));
-            s = cs;
-            m = nm;
-            if constexpr (TRUNC)
-                if (trunc) chunk_candidates<BF16>(a, rowid, c, pl.keff, x, *sc);
-        }
-    }
-
-    __shared__ float sm[kWaves], ss[kWaves];
-    __shared__ int si[kWaves];
-    __shared__ unsigned sb[kWaves];
-    __shared__ int sLast;
-    const int lane = tid % kWave, wave = tid / kWave;
-    Part out;
-    if (greedy) {
-        wave_merge_arg(best, bi);
-        bad = wave_or(bad);
-        if (lane == 0) {
-            sm[wave] = best;
-            si[wave] = bi;
-            sb[wave] = bad;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            for (int w = 1; w < kWaves; ++w) {
-                merge_arg(best, bi, sm[w], si[w]);
-                bad |= sb[w];
-            }
-            out.m = best;
-            out.s = 0.f;
-            out.arg = bi;
-            out.bad = bad;
-        }
-    } else {
-        wave_merge_ms(m, s, scale);
-        if (lane == 0) {
-            sm[wave] = m;
-            ss[wave] = s;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[w], ss[w], scale);
-            out.m = m;
-            out.s = s;
-            out.arg = -1;
-            out.bad = __builtin_isnan(s) ? 1u : 0u;      // NaN or +inf in the unit
-        }
-    }
-    if constexpr (TRUNC) if (trunc) {
-        // the last unit of the logits row truncates it; the last truncated
-        // row of the batch row decides and samples
-        if (tid == 0) {
-            publish_part(&a.ws.part[part_index(a, b, r, unit)], out);
-            sLast = arrive(&a.ws.counter_row[rowid * kCounterStride]) == (unsigned)(a.U - 1);
-        }
-        __syncthreads();
-        if (!sLast) return;
-        if (tid == 0) publish(&a.ws.counter_row[rowid * kCounterStride], 0u);
-        row_merge<BF16>(a, b, r, pl, *sc);
-        __syncthreads();
-        if (tid == 0) {
-            const unsigned expected = (unsigned)(pl.nt + pl.nd);
-            sLast = arrive(&a.ws.counter[(long long)b * kCounterStride]) == expected - 1;
-        }
-        __syncthreads();
-        if (!sLast) return;
-        if (tid == 0) publish(&a.ws.counter[(long long)b * kCounterStride], 0u);
-        decide_trunc<BF16>(a, b, pl, *sc);
-        return;
-    }
-    unsigned* counter = stage1 ? &a.ws.counter1[(long long)b * kCounterStride]
-                               : &a.ws.counter[(long long)b * kCounterStride];
+    const int d = test ? draft_token(a, b, k) : 0;
+    const TruncRow t0 = row_merge<BF16>(a, b, k, 0, pl, sc);
+    TruncRow t1 = t0;
+    if (test) t1 = row_merge<BF16>(a, b, k, 1, pl, sc);
     if (tid == 0) {
-        publish_part(&a.ws.part[part_index(a, b, r, unit)], out);
-        const int rows = stage1 ? 1 + min(pl.nd, 1) : (pl.nt - 1) + max(pl.nd - 1, 0);
-        sLast = arrive(counter) == (unsigned)(rows * a.U) - 1;
+        unsigned flags = (t0.flags | (test ? t1.flags : 0u)) &
+                         (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
+        if (t0.bad || (test && t1.bad)) flags |= SPECV_FLAG_NONFINITE_ROW;
+        unsigned outcome;
+        float p = 0.f, q = 0.f;
+        if (trow_dead(t0) || (test && trow_dead(t1))) {
+            outcome = OUT_BAD;
+        } else if (!test) {
+            outcome = OUT_BONUS;
+        } else {
+            const float zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), d);
+            const float zq = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
+            p = trunc_prob(t0, zt, scale);
+            q = trunc_prob(t1, zq, scale);
+            if (!(finite_logit(zq) && zq >= t1.tstar)) flags |= SPECV_FLAG_Q_ZERO;
+            const float u = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
+            outcome = u * q < p ? OUT_ACC : OUT_REJ;       // accept with probability min(1, p/q)
+        }
+        PairRec* pr = &a.ws.pair[pair_id(a, b, k)];
+        put_tagged(&pr->w[PW_P], __float_as_uint(p), a.epoch);
+        put_tagged(&pr->w[PW_Q], __float_as_uint(q), a.epoch);
+        put_tagged(&pr->w[PW_STATE], outcome | (flags << 8), a.epoch);
+        *out = outcome;
+        *flags_out = flags;
+        *p_out = p;
+        *q_out = q;
     }
-    __syncthreads();
-    if (!sLast) return;
-    if (tid == 0) publish(counter, 0u);               // ready for the next call
-    decide_row<BF16>(a, b, pl, stage1);
 }
 
 // ---------------------------------------------------------------- sampling
@@ -1616,135 +1197,116 @@ struct Weights {
     float mq, invq;      // draft row max, 1 / sum
     // Products are rounded separately (no fused multiply-add) so that equal
     // p and q rows give exactly zero correction weight.
+    __device__ inline float p(float z) const {
+        return __fmul_rn(fast_exp2(__fmul_rn(z - mt, st)), invt);
+    }
     __device__ inline float w(float z, float zq) const {
-        const float p = __fmul_rn(fast_exp2(__fmul_rn(z - mt, st)), invt);
-        if (!residual) return p;
+        const float pz = p(z);
+        if (!residual) return pz;
         const float q = __fmul_rn(fast_exp2(__fmul_rn(zq - mq, st)), invq);
-        return fmaxf(__fsub_rn(p, q), 0.f);
+        return fmaxf(__fsub_rn(pz, q), 0.f);
     }
 };
 
-// Sampling item (b, c), once b's decision is published: sum chunk c's
-// sampling weight (correction max(p - q, 0) from the two rows, or bonus p)
-// and its p mass.  The last item of the row to arrive picks the chunk
-// holding u * W, rescans it with a block prefix sum (tokens in ascending
-// order, first running sum > u * W) and writes the outputs.
-// The workgroup that decides the row was dispatched before every sampling
-// workgroup and never waits for one, so the (bounded) wait for the decision
-// ends; the bound only guards against a dispatch order other than the
-// hardware's in-order one, and its expiry flags the row INTERNAL.
+// Correction (position k < gamma) or bonus (k == gamma) sample from the
+// chunk in registers, by every unit of the row once the walk stopped at k:
+// each publishes its chunk's weight sum and p mass, reads all of them, and
+// the unit whose chunk holds u * W scans it (tokens in ascending order, first
+// running sum > u * W) and writes the outputs.  ``flags``: the row's flags
+// so far.  Whole workgroup.
 template <bool BF16, bool VEC>
-__device__ void sample_item(const Args& a, int b, int c) {
-    const int tid = threadIdx.x;
-    const int lane = tid % kWave, wave = tid / kWave;
-    // the row's decision record: one wave polls every word it needs at once
-    // until all carry this call's epoch (or the kind word alone says there
-    // is nothing to sample)
-    __shared__ unsigned sDw[kDecWords];
-    __shared__ int sOk;
-    if (wave == 0) {
-        const int nw = DW_EMIT + a.gamma;
-        unsigned long long* src = a.ws.dec[b].w;
-        const unsigned long long tag = (unsigned long long)a.epoch << 32;
-        unsigned long long v = tag;
-        bool done = false;
-        for (int spin = 0; spin < (1 << 20); ++spin) {
-            v = lane < nw ? __hip_atomic_load(src + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                          : tag;
-            const unsigned long long mine = __ballot((unsigned)(v >> 32) == a.epoch);
-            const unsigned kind0 = __builtin_amdgcn_readfirstlane((unsigned)v);
-            if ((mine & 1ull) && (kind0 == (unsigned)KIND_NONE || mine == ~0ull)) {
-                done = true;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (lane < nw) sDw[lane] = (unsigned)v;
-        if (lane == 0) sOk = done;
-        if (!done && lane == 0 && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
-    }
-    __syncthreads();
-    if (!sOk) return;
-    const int kind = (int)sDw[DW_KIND];
-    if (kind == KIND_NONE) return;
-    const int pos = (int)sDw[DW_POS];
-    Weights wt;
-    wt.residual = kind == KIND_RESIDUAL;
-    wt.mt = __uint_as_float(sDw[DW_MT]);
-    wt.st = __uint_as_float(sDw[DW_SCALE]);
-    wt.invt = __uint_as_float(sDw[DW_INVT]);
-    wt.mq = __uint_as_float(sDw[DW_MQ]);
-    wt.invq = __uint_as_float(sDw[DW_INVQ]);
-    const float u = __uint_as_float(sDw[DW_U]);
-    const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos);
-    const void* qrow = wt.residual ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+__device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan& pl, Weights wt,
+                                 unsigned flags_in, const ChunkRegs<BF16, VEC>& rt,
+                                 const ChunkRegs<BF16, VEC>& rd) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int NG = kPerThread / G;
+    const float u = uniform24(a.seed, b, k, wt.residual ? PURPOSE_RESIDUAL : PURPOSE_BONUS, a.step);
 
-    __shared__ float red[2][kWaves];
-    __shared__ int sLast;
-    {
-        const int v0 = c * kChunk;
-        const int len = min(kChunk, a.V - v0);
-        float x[kPerThread], y[kPerThread];
-        load_chunk<BF16, VEC>(trow, v0, len, x);
-        if (wt.residual) load_chunk<BF16, VEC>(qrow, v0, len, y);
-        float sw = 0.f, sp = 0.f;
+    // per-group weight sums (group j of this thread: entries [j * G, j * G + G));
+    // entries are unpacked from the chunk registers where they are used
+    float gw[NG], sw = 0.f, sp = 0.f;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-            const float p = __fmul_rn(fast_exp2(__fmul_rn(x[k] - wt.mt, wt.st)), wt.invt);
-            sp += p;
-            sw += wt.residual ? wt.w(x[k], y[k]) : p;
+    for (int j = 0; j < NG; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const int i = j * G + e;
+            const float pz = wt.p(rt.elem(i));
+            sp += pz;
+            s += wt.residual ? wt.w(rt.elem(i), rd.elem(i)) : pz;
         }
-        sw = wave_sum(sw);
-        sp = wave_sum(sp);
-        if (lane == 0) {
-            red[0][wave] = sw;
-            red[1][wave] = sp;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            float wc = red[0][0], pc = red[1][0];
-            for (int w = 1; w < kWaves; ++w) {
-                wc += red[0][w];
-                pc += red[1][w];
-            }
-            float* slot = a.ws.wsum + ((long long)b * a.C + c) * 2;
-            publish(slot, wc);
-            publish(slot + 1, pc);
-            sLast = arrive(&a.ws.counter2[(long long)b * kCounterStride]) == (unsigned)(a.C - 1);
-        }
+        gw[j] = s;
+        sw += s;
     }
-    __syncthreads();
-    if (!sLast) return;
-
-    // last item of the row
+    __shared__ float red[2][kWaves];
     __shared__ float sW[kMaxChunks], sPm[kMaxChunks];
-    __shared__ float sWres, sBase, sTarget;
-    __shared__ int sChunk, sRes, sTok;
-    __shared__ unsigned sFlags;
-    for (int cc = tid; cc < a.C; cc += kBlock) {
-        const float* slot = a.ws.wsum + ((long long)b * a.C + cc) * 2;
-        sW[cc] = published(slot);
-        sPm[cc] = published(slot + 1);
+    __shared__ int sOk;
+    sw = wave_sum(sw);
+    sp = wave_sum(sp);
+    __syncthreads();                               // shared state may still be read
+    if (lane == 0) {
+        red[0][wave] = sw;
+        red[1][wave] = sp;
     }
     __syncthreads();
     if (tid == 0) {
-        publish(&a.ws.counter2[(long long)b * kCounterStride], 0u);   // ready for the next call
-        unsigned flags = sDw[DW_FLAGS];
+        float wc = red[0][0], pc = red[1][0];
+        for (int w2 = 1; w2 < kWaves; ++w2) {
+            wc += red[0][w2];
+            pc += red[1][w2];
+        }
+        unsigned long long* slot = a.ws.wsum + ((long long)b * a.C + c) * 2;
+        put_tagged(slot, __float_as_uint(wc), a.epoch);
+        put_tagged(slot + 1, __float_as_uint(pc), a.epoch);
+    }
+    if (wave == 0) {
+        // every chunk's sums (lane c: chunk c)
+        const unsigned long long* base = a.ws.wsum + (long long)b * a.C * 2;
+        bool done = false;
+        unsigned long long w0 = 0, w1 = 0;
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+            if (lane < a.C) {
+                w0 = published(base + lane * 2);
+                w1 = published(base + lane * 2 + 1);
+            }
+            const bool mine = lane >= a.C || (tag_is(w0, a.epoch) && tag_is(w1, a.epoch));
+            if (__ballot(mine) == ~0ull) {
+                done = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane < a.C) {
+            sW[lane] = __uint_as_float((unsigned)w0);
+            sPm[lane] = __uint_as_float((unsigned)w1);
+        }
+        if (lane == 0) sOk = done;
+        if (!done && lane == 0 && c == 0 && a.out_flags)
+            atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
+    }
+    __syncthreads();
+    if (!sOk) return;
+
+    // the chunk holding u * W: the same sequential sums in every unit
+    __shared__ float sBase, sTarget, sWres;
+    __shared__ int sChunk, sRes, sTok, sLast;
+    __shared__ unsigned sFlags;
+    if (tid == 0) {
+        unsigned flags = flags_in;
         float W = 0.f;
         for (int cc = 0; cc < a.C; ++cc) W += sW[cc];
-        float wres = 0.f;
-        if (wt.residual) {
-            wres = W;
-            if (!(W > 0.f) || !__builtin_isfinite(W)) {
-                // the correction mass vanished (p == q where the draft was
-                // rejected, or rounding): sample from p at that position
-                flags |= SPECV_FLAG_RESIDUAL_FALLBACK;
-                wt.residual = 0;
-                W = 0.f;
-                for (int cc = 0; cc < a.C; ++cc) {
-                    sW[cc] = sPm[cc];
-                    W += sW[cc];
-                }
+        const float wres = wt.residual ? W : 0.f;
+        int res = wt.residual;
+        if (res && (!(W > 0.f) || !__builtin_isfinite(W))) {
+            // the correction mass vanished (p == q where the draft was
+            // rejected, or rounding): sample from p at that position
+            flags |= SPECV_FLAG_RESIDUAL_FALLBACK;
+            res = 0;
+            W = 0.f;
+            for (int cc = 0; cc < a.C; ++cc) {
+                sW[cc] = sPm[cc];
+                W += sW[cc];
             }
         }
         const float target = u * W;
@@ -1769,135 +1331,429 @@ __device__ void sample_item(const Args& a, int b, int c) {
         sChunk = chosen;
         sBase = base;
         sTarget = target;
-        sRes = wt.residual;
+        sRes = res;
         sWres = wres;
         sFlags = flags;
         sTok = 0x7fffffff;
+        sLast = -1;
     }
     __syncthreads();
-    wt.residual = sRes;
-    const int cs = sChunk;
-    int sampled = -1;
-    if (cs >= 0) {
-        const int v0 = cs * kChunk;
-        const int len = min(kChunk, a.V - v0);
-        float w[kPerThread];
-        float tot = 0.f;
-        int lastpos = -1;
-        {
-            float zt[kPerThread], zq[kPerThread];
-            load_contig<BF16, VEC>(trow, v0, len, zt);
-            if (wt.residual) load_contig<BF16, VEC>(qrow, v0, len, zq);
+    const int chosen = sChunk;
+    if (chosen < 0) {
+        // no weight anywhere: cannot happen for finite rows
+        if (c == 0 && wave == 0)
+            write_outputs_wave(a, b, k, k, sFlags | SPECV_FLAG_NONFINITE_ROW, true, -1, sWres, pl.tok);
+        return;
+    }
+    if (chosen != c) return;
+    if (sRes != wt.residual) {
+        // fallback weights p
 #pragma unroll
-            for (int k = 0; k < kPerThread; ++k) {
-                const int v = tid * kPerThread + k;
-                const float wk = v < len ? wt.w(zt[k], wt.residual ? zq[k] : 0.f) : 0.f;
-                w[k] = wk;
-                tot += wk;
-                if (wk > 0.f) lastpos = v;
+        for (int j = 0; j < NG; ++j) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < G; ++e) s += wt.p(rt.elem(j * G + e));
+            gw[j] = s;
+        }
+        wt.residual = 0;
+    }
+    // prefix sums of the group weights in token order: group (j, tid) comes
+    // after every group (j', *) with j' < j and every (j, tid') with tid' < tid
+    __shared__ float gtot[NG][kWaves];
+    float incl[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        incl[j] = wave_scan_incl(gw[j]);
+        if (lane == kWave - 1) gtot[j][wave] = incl[j];
+    }
+    __syncthreads();
+    const float target = sTarget;
+    float gbase = sBase;
+    int tok = 0x7fffffff, lastpos = -1;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        float before = 0.f, tot = 0.f;
+        for (int w2 = 0; w2 < kWaves; ++w2) {
+            if (w2 < wave) before += gtot[j][w2];
+            tot += gtot[j][w2];
+        }
+        const float start = gbase + before + (incl[j] - gw[j]);
+        float run = start;
+        int first = -1, lastin = -1;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const int i = j * G + e;
+            const float wk = wt.w(rt.elem(i), wt.residual ? rd.elem(i) : 0.f);
+            run += wk;
+            if (wk > 0.f) {
+                lastin = e;
+                if (first < 0 && run > target) first = e;
             }
         }
-        // inclusive scan of the per-thread totals (thread order = token order)
-        const float incl = wave_scan_incl(tot);
-        __shared__ float wtot[kWaves];
-        __shared__ int wlast[kWaves];
-        if (lane == kWave - 1) wtot[wave] = incl;
-        __syncthreads();
-        float wbase = 0.f;
-        for (int w2 = 0; w2 < wave; ++w2) wbase += wtot[w2];
-        const float excl = sBase + wbase + (incl - tot);
-        const float inc = sBase + wbase + incl;
-        const float target = sTarget;
-        // the first thread whose range crosses the target finds the token
-        const unsigned long long hit = __ballot(inc > target && tot > 0.f);
-        if (hit) {
-            const int first = __ffsll((unsigned long long)hit) - 1;
-            if (lane == first) {
-                float run = 0.f;
-                int tk = lastpos;
-                bool found = false;
+        const int g = j * kBlock + tid;
+        if (lastin >= 0) lastpos = g * G + lastin;
+        if (tok == 0x7fffffff && gw[j] > 0.f && start + gw[j] > target)
+            tok = g * G + (first >= 0 ? first : lastin);
+        gbase += tot;
+    }
+    if (tok != 0x7fffffff) atomicMin(&sTok, tok);
+    if (lastpos >= 0) atomicMax(&sLast, lastpos);
+    __syncthreads();
+    if (wave == 0) {
+        const int t = sTok != 0x7fffffff ? sTok : sLast;     // rounding: the last token with weight
+        const bool dead = t < 0;
+        unsigned flags = sFlags;
+        if (dead) flags |= SPECV_FLAG_NONFINITE_ROW;
+        write_outputs_wave(a, b, k, k, flags, dead, dead ? -1 : c * kChunk + t, sWres, pl.tok);
+    }
+}
+
+// ---------------------------------------------------------------- the walk
+// Every chunk statistic of row ``side`` of pair (k, b), polled by one wave
+// (lane c: chunk c) until all carry this call's tag; returns false when some
+// did not within the bound.
+__device__ inline bool gather_stats(const Args& a, int b, int k, int side, float& m, unsigned& second) {
+    const int lane = threadIdx.x % kWave;
+    bool ok = true;
+    m = -kInf;
+    second = 0;
+    if (lane < a.C) ok = published_stats(stats_words(a, b, k, side, lane), a.epoch, m, second);
+    return __ballot(!ok) == 0;
+}
+
+// Touch every 128-byte line of chunk [v0, v0 + len) of a row with one dword
+// load each (threads 128..255), so that the chunk is in the L2 when it is
+// loaded for real; returns the loaded words folded together (the caller
+// keeps them live).
+template <bool BF16>
+__device__ inline unsigned prefetch_chunk(const void* row, int v0, int len) {
+    constexpr int per_line = BF16 ? 64 : 32;          // entries per 128-byte line
+    const int t = (int)threadIdx.x - kBlock / 2;
+    const unsigned* base = reinterpret_cast<const unsigned*>(static_cast<const char*>(row) +
+                                                            (size_t)v0 * (BF16 ? 2 : 4));
+    const int lines = (len + per_line - 1) / per_line;
+    unsigned acc = 0;
+    for (int i = t; i < lines; i += kBlock / 2) acc ^= base[i * 32];   // 32 dwords per line
+    return acc;
+}
+
+// Workgroup (b, c): chunk c of every position of batch row b, walked in
+// order while the round goes on (pseudo-code 10-1 stops at the first
+// rejection, so later rows are never read).  At each position k the unit
+// streams chunk c of target row k (and draft row k), publishes its chunk
+// statistics, reads every chunk's statistics of the pair, and takes the
+// accept test itself (the same arithmetic in every unit of the row).
+// Truncated pairs are decided by the last unit to arrive.  From position 1
+// on, the next position's chunk is pulled into the L2 while the current
+// position is decided.
+#ifndef SPECV_PREFETCH_FROM
+#define SPECV_PREFETCH_FROM 1
+#endif
+template <bool BF16, bool VEC, bool TRUNC>
+__device__ void walk_row(const Args& a, int b, int c, TruncScratch* sc) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const Plan pl = make_plan(a, b);
+    if (pl.mode == MODE_SKIP) {
+        if (c == 0 && wave == 0) {
+            write_outputs_wave(a, b, 0, 0, pl.flags, true, -1, 0.f, pl.tok);
+            write_diag_wave(a, b, 0, 0.f, 0.f);
+        }
+        return;
+    }
+    const bool greedy = pl.mode == MODE_GREEDY;
+    const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
+    const float scale = pl.scale;
+    const int v0 = c * kChunk;
+    const int len = min(kChunk, a.V - v0);
+    __shared__ float hp[kMaxPos], hq[kMaxPos];        // p_k(d_k), q_k(d_k) along the walk
+    __shared__ float sm[2][kWaves], ss[2][kWaves];
+    __shared__ int si[kWaves];
+    __shared__ unsigned sb[kWaves];
+    __shared__ float pM[2], pS[2], pZ[2], pP, pQ;
+    __shared__ int pLate[2], pArg, pLast;
+    __shared__ unsigned pOut, pFlags;
+    unsigned flags_acc = pl.flags;
+    unsigned sink = 0;
+    for (int k = 0; k < pl.nt; ++k) {
+        const bool test = k < a.gamma;
+        const bool two = !greedy && test;
+        const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
+        const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
+        ChunkRegs<BF16, VEC> rt, rd;
+        rt.issue(trow, v0, len);
+        if (two) rd.issue(drow, v0, len);
+        // d_k and z at d_k for the accept test, fetched alongside
+        const int dk = test ? draft_token(a, b, k) : 0;
+        float zt = 0.f, zq = 0.f;
+        if (two && !trunc && tid == 0) {
+            zt = load_elem<BF16>(trow, dk);
+            zq = load_elem<BF16>(drow, dk);
+        }
+        rt.finish(trow, v0, len);
+        if (two) rd.finish(drow, v0, len);
+        __syncthreads();                              // the previous position's LDS is read
+        if (greedy) {
+            float best = -kInf;
+            int bi = 0x7fffffff;
+            unsigned bad = 0;
 #pragma unroll
-                for (int k = 0; k < kPerThread; ++k) {
-                    run += w[k];
-                    if (!found && w[k] > 0.f && excl + run > target) {
-                        tk = tid * kPerThread + k;
-                        found = true;
+            for (int i = 0; i < kPerThread; ++i) {
+                const float x = rt.elem(i);
+                bad |= !(x <= 3.402823466e38f);           // NaN or +inf
+                if (x > best) {                           // strict: keeps the lowest index
+                    best = x;
+                    bi = v0 + chunk_index<BF16>(i);
+                }
+            }
+            wave_merge_arg(best, bi);
+            bad = wave_or(bad);
+            if (lane == 0) {
+                sm[0][wave] = best;
+                si[wave] = bi;
+                sb[wave] = bad;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                for (int w = 1; w < kWaves; ++w) {
+                    merge_arg(best, bi, sm[0][w], si[w]);
+                    bad |= sb[w];
+                }
+                publish_stats(stats_words(a, b, k, 0, c), bad ? __builtin_nanf("") : best,
+                              (unsigned)bi, a.epoch);
+            }
+        } else {
+#pragma unroll
+            for (int side = 0; side < 2; ++side) {
+                if (side == 1 && !two) break;
+                const ChunkRegs<BF16, VEC>& r = side == 0 ? rt : rd;
+                float cm = -kInf;
+#pragma unroll
+                for (int i = 0; i < kPerThread; ++i) cm = fmaxf(cm, r.elem(i));
+                const float nms = cm == -kInf ? 0.f : -cm * scale;
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < kPerThread; ++i) s += fast_exp2(fmaf(r.elem(i), scale, nms));
+                float m = cm;
+                wave_merge_ms(m, s, scale);
+                if (lane == 0) {
+                    sm[side][wave] = m;
+                    ss[side][wave] = s;
+                }
+                if constexpr (TRUNC) {
+                    if (trunc) {
+                        float x[kPerThread];
+                        r.get(x);
+                        chunk_candidates<BF16>(a, side_row(a, b, k, side), c, pl.keff, x, *sc);
                     }
                 }
-                atomicMin(&sTok, tk);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                for (int side = 0; side < (two ? 2 : 1); ++side) {
+                    float m = sm[side][0], s = ss[side][0];
+                    for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[side][w], ss[side][w], scale);
+                    publish_stats(stats_words(a, b, k, side, c), m, __float_as_uint(s), a.epoch);
+                }
+                pZ[0] = zt;
+                pZ[1] = zq;
             }
         }
-        const int lp = wave_max_i(lastpos);
-        if (lane == 0) wlast[wave] = lp;
-        __syncthreads();
+        // the next position's chunk heads for the L2 meanwhile (waves 2 and 3)
+        if (VEC && k >= SPECV_PREFETCH_FROM && k + 1 < pl.nt && wave >= 2) {
+            const bool two1 = !greedy && k + 1 < a.gamma;
+            sink ^= prefetch_chunk<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k + 1), v0, len);
+            if (two1) sink ^= prefetch_chunk<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k + 1), v0, len);
+        }
+        // the pair's outcome
+        unsigned outcome = OUT_BAD, flags = 0;
+        float p = 0.f, q = 0.f;
+        bool decider = c == 0;                        // the unit that finishes the row
+        if (trunc) {
+            if constexpr (TRUNC) {
+                if (tid == 0) {
+                    unsigned* ctr = a.ws.ctr + pair_id(a, b, k) * kSlot;
+                    pLast = arrive(ctr, true) == (unsigned)(a.C - 1);
+                    if (pLast) publish(ctr, 0u);          // ready for the next call
+                }
+                __syncthreads();
+                decider = pLast != 0;
+                if (decider) {
+                    decide_trunc<BF16>(a, b, k, pl, *sc, &pOut, &pFlags, &pP, &pQ);
+                } else if (wave == 0) {
+                    // the decider's record
+                    const PairRec* pr = &a.ws.pair[pair_id(a, b, k)];
+                    unsigned long long v = 0;
+                    bool ok = false;
+                    for (int spin = 0; spin < kSpinLimit; ++spin) {
+                        v = 0;
+                        if (lane == 0) v = published(&pr->w[PW_STATE]);
+                        else if (lane == 1) v = published(&pr->w[PW_P]);
+                        else if (lane == 2) v = published(&pr->w[PW_Q]);
+                        if ((__ballot(lane < 3 && tag_is(v, a.epoch)) & 7ull) == 7ull) {
+                            ok = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    const unsigned st = (unsigned)readlane64(v, 0);
+                    if (lane == 0) {
+                        pOut = ok ? (st & 0xffu) : OUT_BAD;
+                        pFlags = ok ? (st >> 8) : SPECV_FLAG_INTERNAL;
+                        pP = __uint_as_float((unsigned)readlane64(v, 1));
+                        pQ = __uint_as_float((unsigned)readlane64(v, 2));
+                    }
+                }
+                __syncthreads();
+                outcome = pOut;
+                flags = pFlags;
+                p = pP;
+                q = pQ;
+            }
+        } else if (greedy) {
+            if (wave == 0) {
+                float m;
+                unsigned second;
+                const bool ok = gather_stats(a, b, k, 0, m, second);
+                int arg = (int)second;
+                const bool nan = __builtin_isnan(m);
+                const bool anybad = __ballot(nan) != 0;
+                if (nan || lane >= a.C) {
+                    m = -kInf;
+                    arg = 0x7fffffff;
+                }
+                wave_merge_arg(m, arg);
+                if (lane == 0) {
+                    pArg = arg;
+                    pOut = !ok ? OUT_BAD : ((anybad || m == -kInf) ? OUT_BAD : OUT_ACC);
+                    pFlags = !ok ? SPECV_FLAG_INTERNAL : ((anybad || m == -kInf) ? SPECV_FLAG_NONFINITE_ROW : 0u);
+                }
+            }
+            __syncthreads();
+            outcome = pOut;
+            flags = pFlags;
+            if (outcome != OUT_BAD)
+                outcome = !test ? OUT_BONUS : (dk == pArg ? OUT_ACC : OUT_REJ);
+        } else {
+            // every unit merges the pair's statistics and runs the test itself
+            if (wave < (two ? 2 : 1)) {
+                float m;
+                unsigned second;
+                const bool ok = gather_stats(a, b, k, wave, m, second);
+                float s = lane < a.C ? __uint_as_float(second) : 0.f;
+                wave_merge_ms(m, s, scale);
+                if (lane == 0) {
+                    pM[wave] = m;
+                    pS[wave] = s;
+                    pLate[wave] = !ok;
+                }
+            }
+            __syncthreads();
+            const bool badT = __builtin_isnan(pS[0]) || pM[0] == -kInf || !(pS[0] > 0.f);
+            const bool badQ = two && (__builtin_isnan(pS[1]) || pM[1] == -kInf || !(pS[1] > 0.f));
+            const float u = two ? uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step) : 0.f;
+            outcome = sample_outcome(test, pM[0], pS[0], pM[1], pS[1], badT, badQ, pZ[0], pZ[1], u,
+                                     scale, flags, p, q);
+            if (pLate[0] || (two && pLate[1])) {
+                outcome = OUT_BAD;
+                flags = SPECV_FLAG_INTERNAL;
+            }
+        }
         if (tid == 0) {
-            int tk = sTok;
-            if (tk == 0x7fffffff) {                 // rounding: the last token with weight
-                tk = -1;
-                for (int w2 = 0; w2 < kWaves; ++w2) tk = max(tk, wlast[w2]);
-            }
-            sTok = tk < 0 ? -1 : v0 + tk;
+            hp[k] = p;
+            hq[k] = q;
         }
+        flags_acc |= flags;
+        if (outcome == OUT_BAD) {
+            // a consulted row with NaN / +inf or nothing finite: no emission
+            __syncthreads();
+            if (decider) finish_row(a, b, pl, k, greedy ? 0 : k, flags_acc, true, -1, 0.f, hp, hq);
+            break;
+        }
+        if (test && outcome == OUT_ACC) {
+            if (k + 1 < pl.nt) continue;
+            // every draft the cap allows was accepted, and no bonus position
+            __syncthreads();
+            if (decider) finish_row(a, b, pl, k + 1, greedy ? 0 : k + 1, flags_acc, false, -1, 0.f, hp, hq);
+            break;
+        }
+        // the round stops at k: a correction (rejection) or the bonus token
         __syncthreads();
-        sampled = sTok;
+        const int tested = test ? k + 1 : k;
+        if (greedy) {
+            if (decider) finish_row(a, b, pl, k, 0, flags_acc, false, pArg, 0.f, hp, hq);
+            break;
+        }
+        if (trunc) {
+            if constexpr (TRUNC) {
+                if (decider) {
+                    const float u = uniform24(a.seed, b, k, test ? PURPOSE_RESIDUAL : PURPOSE_BONUS, a.step);
+                    float wres;
+                    bool fb;
+                    const int tok = trunc_sample<BF16>(a, b, k, test, u, pl, *sc, &wres, &fb);
+                    const unsigned f = flags_acc | (fb ? SPECV_FLAG_RESIDUAL_FALLBACK : 0u) |
+                                       (tok < 0 ? SPECV_FLAG_NONFINITE_ROW : 0u);
+                    finish_row(a, b, pl, k, tested, f, tok < 0, tok, wres, hp, hq);
+                }
+            }
+            break;
+        }
+        if (c == 0 && wave == 0) write_diag_wave(a, b, tested, lane < kMaxPos ? hp[lane] : 0.f,
+                                                  lane < kMaxPos ? hq[lane] : 0.f);
+        Weights wt;
+        wt.residual = test;
+        wt.mt = pM[0];
+        wt.invt = 1.f / pS[0];
+        wt.mq = two ? pM[1] : 0.f;
+        wt.invq = two ? 1.f / pS[1] : 0.f;
+        wt.st = scale;
+        sample_from_regs<BF16, VEC>(a, b, k, c, pl, wt, flags_acc, rt, rd);
+        break;
     }
-    if (tid == 0) {
-        unsigned flags = sFlags;
-        const bool dead = sampled < 0;        // no weight anywhere: cannot happen for finite rows
-        if (dead) flags |= SPECV_FLAG_NONFINITE_ROW;
-        write_outputs(a, b, reinterpret_cast<const int*>(&sDw[DW_EMIT]), (int)sDw[DW_NEMIT],
-                      (int)sDw[DW_NACC], flags, dead, sampled, sWres);
-    }
-    __syncthreads();      // shared state is reused by the next item
+    // keep the prefetch loads (their values are never needed)
+    if (sink == 0x9E3779B9u && a.V < 0) a.out_acc[0] = (int)sink;
 }
 
 // ---------------------------------------------------------------- k_verify
-// One launch per call, one workgroup per piece of work:
-//   blocks [0, units):            streaming unit t = (b, r, unit), in batch-row
-//                                 order; the last unit of a row decides it;
-//   blocks [units, units + items): sampling item (b, c), waiting for its row's
-//                                 decision.
-// Workgroups are dispatched in increasing order within each XCD, so every
-// streaming workgroup has been dispatched (and never waits) before any
-// sampling workgroup that could wait for it: the waits always end.  Sampling
-// of early rows overlaps the streaming of later ones.
-//
-// TRUNC selects the variant with the truncation path (handles created with
-// max_top_k > 0); without it truncated rows are flagged unsupported and the
-// kernel stays lean (registers and LDS of the streaming path only).
-template <bool BF16, bool VEC, bool TRUNC>
-__global__ __launch_bounds__(kBlock, 4) void k_verify(Args a) {
-    const int units = a.B * a.R * a.U;
-    const int t = blockIdx.x;
-    if (t < units) {
-        if constexpr (TRUNC) {
-            __shared__ TruncScratch sc;
-            stream_unit<BF16, VEC, true>(a, t, &sc);
-        } else {
-            stream_unit<BF16, VEC, false>(a, t, nullptr);
-        }
-    } else {
-        sample_item<BF16, VEC>(a, (t - units) / a.C, (t - units) % a.C);
-    }
+// One launch per call, one workgroup per (batch row, chunk).  The lean
+// variant (no truncation) is held to 128 VGPRs so that four workgroups share
+// a CU: 1024 resident units, a whole B=64 x V=128256 batch at once.
+// k_verify_trunc carries the truncation path (handles created with
+// max_top_k > 0) and its LDS scratch; without it truncated rows are flagged
+// unsupported.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_verify(Args a) {
+    const int b = blockIdx.x / a.C;
+    const int c = blockIdx.x - b * a.C;
+    walk_row<BF16, VEC, false>(a, b, c, nullptr);
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_verify_trunc(Args a) {
+    const int b = blockIdx.x / a.C;
+    const int c = blockIdx.x - b * a.C;
+    __shared__ TruncScratch sc;
+    walk_row<BF16, VEC, true>(a, b, c, &sc);
 }
 
 using KernelFn = void (*)(Args);
 
 KernelFn pick(bool bf16, bool vec, bool trunc) {
     if (trunc) {
-        if (bf16) return vec ? k_verify<true, true, true> : k_verify<true, false, true>;
-        return vec ? k_verify<false, true, true> : k_verify<false, false, true>;
+        if (bf16) return vec ? k_verify_trunc<true, true> : k_verify_trunc<true, false>;
+        return vec ? k_verify_trunc<false, true> : k_verify_trunc<false, false>;
     }
-    if (bf16) return vec ? k_verify<true, true, false> : k_verify<true, false, false>;
-    return vec ? k_verify<false, true, false> : k_verify<false, false, false>;
+    if (bf16) return vec ? k_verify<true, true> : k_verify<true, false>;
+    return vec ? k_verify<false, true> : k_verify<false, false>;
 }
 
 }  // namespace
 
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev) {
-    const int blocks = a.B * a.R * a.U + a.B * a.C;
+    const long long blocks = (long long)a.B * a.C;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    KernelFn fn = pick(bf16, vec, a.cand_cap > 0);
     if (ev) (void)hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL(pick(bf16, vec, a.cand_cap > 0), dim3(blocks), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
     if (ev) (void)hipEventRecord(ev[1], stream);
     return hipGetLastError();
 }
