@@ -70,6 +70,8 @@ hipError_t alloc(T** p, size_t count) {
 void free_ws(specv::Workspace& ws) {
     if (ws.stats) (void)hipFree(ws.stats);
     if (ws.pair) (void)hipFree(ws.pair);
+    if (ws.rowrec) (void)hipFree(ws.rowrec);
+    if (ws.status) (void)hipFree(ws.status);
     if (ws.wsum) (void)hipFree(ws.wsum);
     if (ws.ctr) (void)hipFree(ws.ctr);
     if (ws.cand) (void)hipFree(ws.cand);
@@ -130,15 +132,22 @@ hipError_t clear_ws(specv_ctx* h, hipStream_t stream) {
     const size_t groups = (size_t)h->cfg.max_batch * (h->cfg.max_gamma + 1);
     hipError_t e = hipMemsetAsync(ws.stats, 0, groups * 2 * h->max_chunks * 2 * sizeof(unsigned long long),
                                   stream);
+    const size_t rows = (size_t)h->cfg.max_batch;
     if (e == hipSuccess) e = hipMemsetAsync(ws.pair, 0, groups * sizeof(specv::PairRec), stream);
     if (e == hipSuccess)
-        e = hipMemsetAsync(ws.wsum, 0,
-                           (size_t)h->cfg.max_batch * h->max_chunks * 2 * sizeof(unsigned long long), stream);
-    if (e == hipSuccess) e = hipMemsetAsync(ws.ctr, 0, groups * specv::kSlot * sizeof(unsigned), stream);
+        e = hipMemsetAsync(ws.rowrec, 0, rows * specv::kRowWords * sizeof(unsigned long long), stream);
+    if (e == hipSuccess)
+        e = hipMemsetAsync(ws.wsum, 0, rows * h->max_chunks * 2 * sizeof(unsigned long long), stream);
+    if (e == hipSuccess) e = hipMemsetAsync(ws.ctr, 0, 2 * groups * specv::kSlot * sizeof(unsigned), stream);
+    if (e == hipSuccess)
+        e = hipMemsetAsync(ws.status, 0, 2 * rows * specv::kSlot * sizeof(unsigned), stream);
     return e;
 }
 
-// One launch of the verify kernel with the next epoch tag.
+// One launch of the verify kernel with the next epoch tag.  The epoch
+// advances only when the launch succeeded: a call clears the counters and
+// status words of the other parity for the next call, so the next call must
+// use the other parity exactly when this one ran.
 specv_status launch(specv_handle h, specv::Args& a, bool bf16, bool vec, void* stream) {
     if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -195,9 +204,13 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     const size_t rows = groups * 2;                                         // logits rows
     const size_t rc = rows * h->max_chunks;
     specv::Workspace& ws = h->ws;
+    ws.n_groups = (int)groups;
+    ws.n_rows = cfg->max_batch;
     bool ok = alloc(&ws.stats, rc * 2) == hipSuccess && alloc(&ws.pair, groups) == hipSuccess &&
+              alloc(&ws.rowrec, (size_t)cfg->max_batch * specv::kRowWords) == hipSuccess &&
               alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks * 2) == hipSuccess &&
-              alloc(&ws.ctr, groups * specv::kSlot) == hipSuccess;
+              alloc(&ws.ctr, 2 * groups * specv::kSlot) == hipSuccess &&
+              alloc(&ws.status, (size_t)2 * cfg->max_batch * (specv::kSlot / 2)) == hipSuccess;
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&

@@ -49,26 +49,43 @@ struct TruncScratch {
     int misc[8];
 };
 
-// Outcome of one position of one truncated batch row (its "pair": target
-// row k and, below gamma, draft row k), published by the workgroup that
-// truncated the pair's rows.  Every word holds (epoch << 32) | value, so a
-// reader knows a word is this call's when its epoch matches.
+// Outcome of one position of one batch row (its "pair": target row k and,
+// below gamma, draft row k), published by the workgroup that decided it.
+// Every word holds (epoch << 32) | value, so a reader knows a word is this
+// call's when its epoch matches.
 enum PairWord {
     PW_STATE = 0,         // outcome | (SPECV_FLAG_* bits << 8)
     PW_P, PW_Q,           // p_k(d_k), q_k(d_k) (float bits)
+    PW_ARG,               // target argmax (greedy rows)
+    PW_MT, PW_INVT,       // target row max and 1 / sum (exp2 units)
+    PW_MQ, PW_INVQ,       // draft row max and 1 / sum
     kPairWords
 };
 struct PairRec {
     unsigned long long w[kPairWords];
 };
 
+// How a sampling row's round ended, for its sampling workgroups: which
+// position draws the correction / bonus token, the row's flags so far, and
+// that position's normalisers.  Epoch-tagged words like PairRec.
+enum RowWord {
+    RW_REC = 0,           // kind | (position << 3) | (flags << 8)
+    RW_MT, RW_INVT, RW_MQ, RW_INVQ,
+    kRowWords = 8
+};
+
 struct Workspace {
     unsigned long long* stats;  // [max_batch * max_pos * 2 * max_chunks][2]: per (row, chunk)
                                 // epoch-tagged (max, sum) or (max, argmax)
-    PairRec* pair;              // [max_batch * max_pos]: truncated pairs' outcomes
+    PairRec* pair;              // [max_batch * max_pos]
+    unsigned long long* rowrec; // [max_batch * kRowWords]
     unsigned long long* wsum;   // [max_batch * max_chunks * 2]: chunk sampling weight, p mass
-    unsigned* ctr;              // [max_batch * max_pos][kSlot]: arrivals per truncated pair,
-                                // zero between calls
+    unsigned* ctr;              // [2][max_batch * max_pos][kSlot]: arrivals per pair, one set
+                                // per call parity; a call clears the other parity's set
+    unsigned long long* status; // [2][max_batch][kSlot / 2]: per-row accept / stop bits, one
+                                // set per call parity
+    int n_groups;               // max_batch * max_pos
+    int n_rows;                 // max_batch
     Cand* cand;                 // [max_batch * max_pos * 2 * max_chunks * cand_cap]
     Cand* cand_meta;            // [max_batch * max_pos * 2 * max_chunks]: (bound L, count);
                                 // count -1 when the chunk's candidates overflowed
@@ -105,8 +122,9 @@ struct Args {
     Workspace ws;
 };
 
-// Launch the whole verify step on ``stream`` as one kernel: one workgroup per
-// (batch row, chunk), walking the row's positions.  ``bf16`` selects the element
+// Launch the whole verify step on ``stream`` as one kernel: one streaming
+// workgroup per (position, batch row, chunk), position-major, then one
+// sampling workgroup per (batch row, chunk).  ``bf16`` selects the element
 // type, ``vec`` the 16-byte vector-load variant (row starts 16-byte aligned);
 // the truncation-capable variant is used when a.cand_cap > 0.  ``ev``
 // (nullable) receives two event records around the launch.

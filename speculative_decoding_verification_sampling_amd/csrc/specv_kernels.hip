@@ -2,34 +2,42 @@
 //
 // The verify step is bandwidth-bound, and the round it computes is
 // sequential: draft d_k only matters while every earlier draft was accepted
-// (pseudo-code 10-1 stops at the first rejection).  The kernel therefore
-// reads the logits lazily, in ONE launch of B x C workgroups: workgroup
-// (b, c) owns chunk c (8192 entries) of every logits row of batch row b and
-// walks the positions k = 0, 1, ... in order:
+// (pseudo-code 10-1 stops at the first rejection), so rows past the first
+// rejection need not be read.  One launch does the whole step with two kinds
+// of workgroup:
 //
-//   stream : chunk c of target row k and, below gamma, of draft row k, with
-//            16-byte loads, reduced to chunk statistics (max / sum of exp2
-//            for sampling rows, max / lowest argmax for greedy rows, top-k
-//            candidates for truncated rows), published as epoch-tagged words;
-//   decide : every unit reads the C chunk statistics of the pair and runs the
-//            accept test of position k itself (the same arithmetic in every
-//            unit, so all units of the row agree); truncated pairs are
-//            decided once, by the last unit to arrive, which publishes the
-//            outcome;
-//   go on  : on acceptance the walk moves to position k + 1 (whose chunk was
-//            already pulled into the L2 while k was being decided); rows past
-//            the first rejection are never read;
-//   sample : at the first rejection (or the bonus position) the units still
-//            hold their chunk in registers: each sums its chunk's correction
-//            weight max(p - q, 0) (or bonus weight p), publishes it, reads
-//            every chunk's sum, and the unit whose chunk holds u * W finds the
-//            token with a block prefix sum.  Nothing is read twice.
+//   streaming unit (k, b, c), position-major, P x B x C of them: reads chunk
+//            c (8192 entries) of target row k and, for sampling and
+//            truncated rows below gamma, of draft row k, with 16-byte loads;
+//            reduces it to chunk statistics (max / sum of exp2 for sampling
+//            rows, max / lowest argmax for greedy rows, top-k candidates for
+//            truncated rows), published as epoch-tagged words; bumps the
+//            pair's arrival counter.  The last of the C units to arrive
+//            merges the statistics and takes position k's accept test,
+//            publishes the pair record and sets the position's bit in the
+//            row's status word.  Units of position k >= 2 first read that
+//            word and skip their chunk when the round stopped before k; the
+//            stream itself never waits for a decision, so positions that are
+//            still open are read speculatively.
+//   row finish: the decider whose bit resolves the row (first rejection, a
+//            bad row, the cap, or the bonus position reached) gathers the
+//            consulted pair records, writes diagnostics and, for greedy,
+//            capped, dead and truncated rows, the outputs; for sampling rows
+//            it publishes the row record (where the round stopped and that
+//            position's normalisers).
+//   sampling workgroup (b, c), B x C of them after the stream: waits for
+//            the row record, reads chunk c of the stopping position's target
+//            (and draft) row, sums the correction weight max(p - q, 0) (or
+//            the bonus weight p), publishes the sum, reads every chunk's sum,
+//            and the workgroup whose chunk holds u * W finds the token with a
+//            block prefix sum.
 //
-// The C units of a row wait only for each other (bounded polls).  Workgroups
-// are dispatched in increasing ID order within each XCD and a row's units
-// have consecutive IDs, so every unit waited for is resident or done, and
-// the waits end; the bound only guards against a dispatch order other than
-// the hardware's, and its expiry flags the row.
+// Hand-offs use agent-scope atomics on epoch-tagged words, polled with a
+// bound (the expiry flags the row, it never hangs the launch).  Workgroups
+// are dispatched in increasing ID order within each XCD, and every wait is
+// for words that a workgroup with a lower ID writes (the stream's decisions,
+// for the sampling workgroups) or that were stored before the status bit the
+// waiter saw (pair records, for the row finish), so the waits end.
 //
 // Sources: "11.1 核心原理: Draft + Verify 与 Rejection Sampling" (11.1.1
 // alignment, 11.1.2 acceptance / residual / greedy / processed proposals,
@@ -1112,80 +1120,336 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     return tok;
 }
 
+// ---------------------------------------------------------------- row status
+// Row status word (one per batch row and call parity):
+//   bit k        accept test of position k passed        (k < gamma <= 31)
+//   bit 31       bonus row merged and usable
+//   bit 32 + k   position k stopped the round: rejected, or a consulted row is bad
+//   bit 63       bonus row bad
+constexpr unsigned long long kBonusOk = 1ull << 31;
+constexpr unsigned long long kBonusBad = 1ull << 63;
+
+// Where the round stands, from a row status word.
+enum How { H_OPEN = 0, H_STOP, H_CAPPED, H_BONUS, H_BONUS_BAD };
+struct Res {
+    int how;
+    int n;          // H_STOP: the stopping position; H_CAPPED: accepted drafts
+};
+
+__device__ inline Res resolve(unsigned long long st, const Plan& pl, int gamma) {
+    const unsigned acc = (unsigned)st & 0x7fffffffu;
+    const unsigned stop = (unsigned)(st >> 32) & 0x7fffffffu;
+    Res r;
+    const int j = __builtin_ctz(~acc);          // first position not (yet) accepted; <= 31
+    if (j < pl.ntest) {
+        r.n = j;
+        r.how = ((stop >> j) & 1u) ? H_STOP : H_OPEN;
+        return r;
+    }
+    r.n = pl.ntest;
+    if (pl.nt <= gamma) r.how = H_CAPPED;       // the cap leaves no bonus position
+    else if (st & kBonusOk) r.how = H_BONUS;
+    else if (st & kBonusBad) r.how = H_BONUS_BAD;
+    else r.how = H_OPEN;
+    return r;
+}
+
+__device__ inline bool stopped_before(unsigned long long st, int k) {
+    const unsigned stop = (unsigned)(st >> 32) & 0x7fffffffu;
+    return (stop & ((1u << k) - 1u)) != 0;      // k <= 31
+}
+
+__device__ inline unsigned* pair_counter(const Args& a, unsigned par, int b, int k) {
+    return a.ws.ctr + ((long long)par * a.ws.n_groups + pair_id(a, b, k)) * kSlot;
+}
+__device__ inline unsigned long long* status_word(const Args& a, unsigned par, int b) {
+    return a.ws.status + ((long long)par * a.ws.n_rows + b) * (kSlot / 2);
+}
+
 // ---------------------------------------------------------------- row finish
-// Outputs and diagnostics of row b, by wave 0 of the calling workgroup: the
-// first nacc drafts, then ``sampled`` (if >= 0); p_i(d_i), q_i(d_i) of the
-// ``tested`` positions from the walk's history (hp, hq in LDS).
-__device__ inline void finish_row(const Args& a, int b, const Plan& pl, int nacc, int tested,
-                                  unsigned flags, bool dead, int sampled, float wres,
-                                  const float* hp, const float* hq) {
-    if (threadIdx.x / kWave != 0) return;
-    const int lane = threadIdx.x % kWave;
-    write_outputs_wave(a, b, nacc, nacc, flags, dead, sampled, wres, pl.tok);
-    write_diag_wave(a, b, tested, lane < kMaxPos ? hp[lane] : 0.f, lane < kMaxPos ? hq[lane] : 0.f);
-}
+// A pair record in registers.
+struct PairVals {
+    unsigned state;
+    float p, q;
+    int arg;
+    float mt, invt, mq, invq;
+};
 
-// Accept test of a sampling pair from its merged statistics (pseudo-code
-// 10-1: accept with probability min(1, p / q), i.e. u * q < p).
-__device__ inline unsigned sample_outcome(bool test, float mt, float st, float mq, float sq,
-                                          bool badT, bool badQ, float zt, float zq, float u,
-                                          float scale, unsigned& flags, float& p, float& q) {
-    flags = 0;
-    p = 0.f;
-    q = 0.f;
-    if (badT || badQ) {
-        flags = SPECV_FLAG_NONFINITE_ROW;
-        return OUT_BAD;
-    }
-    if (!test) return OUT_BONUS;
-    p = fast_exp2((zt - mt) * scale) / st;
-    q = fast_exp2((zq - mq) * scale) / sq;
-    if (zq == -kInf) flags |= SPECV_FLAG_Q_ZERO;
-    return u * q < p ? OUT_ACC : OUT_REJ;
-}
-
-// Decision of a truncated pair (k, b) by the last of its units to arrive
-// (whole workgroup): the row-level truncation of target row k (and draft row
-// k), then the accept test on the kept sets; the outcome goes to the pair's
-// record, which the pair's other units wait for.
-template <bool BF16>
-__device__ void decide_trunc(const Args& a, int b, int k, const Plan& pl, TruncScratch& sc,
-                             unsigned* out, unsigned* flags_out, float* p_out, float* q_out) {
-    const int tid = threadIdx.x;
-    const bool test = k < a.gamma;
-    const float scale = pl.scale;
-    const int d = test ? draft_token(a, b, k) : 0;
-    const TruncRow t0 = row_merge<BF16>(a, b, k, 0, pl, sc);
-    TruncRow t1 = t0;
-    if (test) t1 = row_merge<BF16>(a, b, k, 1, pl, sc);
-    if (tid == 0) {
-        unsigned flags = (t0.flags | (test ? t1.flags : 0u)) &
-                         (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
-        if (t0.bad || (test && t1.bad)) flags |= SPECV_FLAG_NONFINITE_ROW;
-        unsigned outcome;
-        float p = 0.f, q = 0.f;
-        if (trow_dead(t0) || (test && trow_dead(t1))) {
-            outcome = OUT_BAD;
-        } else if (!test) {
-            outcome = OUT_BONUS;
-        } else {
-            const float zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), d);
-            const float zq = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
-            p = trunc_prob(t0, zt, scale);
-            q = trunc_prob(t1, zq, scale);
-            if (!(finite_logit(zq) && zq >= t1.tstar)) flags |= SPECV_FLAG_Q_ZERO;
-            const float u = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
-            outcome = u * q < p ? OUT_ACC : OUT_REJ;       // accept with probability min(1, p/q)
+// Run by the workgroup whose status update resolved row b (whole
+// workgroup; wave 0 does the row's bookkeeping, lane i for position i): the
+// records of the positions the round consulted give the flags and the
+// diagnostics; greedy, capped and dead rows get their outputs here,
+// truncated rows draw their token here from the kept lists, and sampling rows
+// hand the draw to their sampling workgroups through the row record.
+template <bool BF16, bool TRUNC>
+__device__ void finish_row(const Args& a, int b, int k, const PairVals& own, const Plan& pl,
+                           unsigned long long st, TruncScratch* sc) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const Res r = resolve(st, pl, a.gamma);
+    const bool greedy = pl.mode == MODE_GREEDY;
+    // highest position whose record is read
+    const int last = r.how == H_STOP ? r.n : (r.how == H_CAPPED ? r.n - 1 : a.gamma);
+    const int nacc = r.how == H_STOP || r.how == H_CAPPED ? r.n : a.gamma;
+    __shared__ int fKind, fDead, fAt;
+    __shared__ unsigned fFlags;
+    if (wave == 0) {
+        unsigned long long w[kPairWords];
+#pragma unroll
+        for (int i = 0; i < kPairWords; ++i) w[i] = 0;
+        bool ok = true;
+        if (lane <= last) {
+            if (lane == k) {
+                w[PW_STATE] = own.state;
+                w[PW_P] = __float_as_uint(own.p);
+                w[PW_Q] = __float_as_uint(own.q);
+                w[PW_ARG] = (unsigned)own.arg;
+                w[PW_MT] = __float_as_uint(own.mt);
+                w[PW_INVT] = __float_as_uint(own.invt);
+                w[PW_MQ] = __float_as_uint(own.mq);
+                w[PW_INVQ] = __float_as_uint(own.invq);
+            } else {
+                const PairRec* pr = &a.ws.pair[pair_id(a, b, lane)];
+                ok = false;
+#pragma unroll 1
+                for (int spin = 0; spin < kSpinLimit; ++spin) {
+                    bool all = true;
+#pragma unroll
+                    for (int i = 0; i < kPairWords; ++i) {
+                        w[i] = published(&pr->w[i]);
+                        all = all && tag_is(w[i], a.epoch);
+                    }
+                    if (all) {
+                        ok = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
         }
-        PairRec* pr = &a.ws.pair[pair_id(a, b, k)];
-        put_tagged(&pr->w[PW_P], __float_as_uint(p), a.epoch);
-        put_tagged(&pr->w[PW_Q], __float_as_uint(q), a.epoch);
-        put_tagged(&pr->w[PW_STATE], outcome | (flags << 8), a.epoch);
-        *out = outcome;
-        *flags_out = flags;
-        *p_out = p;
-        *q_out = q;
+        const unsigned rs = (unsigned)w[PW_STATE];
+        unsigned flags = pl.flags | wave_or(lane < nacc ? (rs >> 8) : 0u);
+        if (__ballot(!ok)) flags |= SPECV_FLAG_INTERNAL;
+        int kind = KIND_NONE, sampled = -1, tested = nacc;
+        bool dead = false;
+        // the record of the position that ended the round, read from its lane
+        // here, with every lane active (a cross-lane read inside a branch that
+        // only some lanes take can see registers the branch never restored)
+        const int at = r.how == H_STOP ? r.n : a.gamma;
+        const unsigned s_at = __builtin_amdgcn_readlane(rs, at);
+        const int a_at = __builtin_amdgcn_readlane((int)(unsigned)w[PW_ARG], at);
+        const unsigned mt_at = __builtin_amdgcn_readlane((unsigned)w[PW_MT], at);
+        const unsigned invt_at = __builtin_amdgcn_readlane((unsigned)w[PW_INVT], at);
+        const unsigned mq_at = __builtin_amdgcn_readlane((unsigned)w[PW_MQ], at);
+        const unsigned invq_at = __builtin_amdgcn_readlane((unsigned)w[PW_INVQ], at);
+        if (r.how == H_STOP || r.how == H_BONUS || r.how == H_BONUS_BAD) {
+            flags |= s_at >> 8;
+            if (r.how == H_BONUS_BAD || (s_at & 0xffu) == OUT_BAD) {
+                dead = true;
+            } else {
+                if (r.how == H_STOP) tested = r.n + 1;
+                if (greedy) sampled = a_at;
+                else kind = r.how == H_STOP ? KIND_RESIDUAL : KIND_BONUS;
+            }
+        }
+        if (greedy) tested = 0;
+        write_diag_wave(a, b, tested, __uint_as_float((unsigned)w[PW_P]),
+                        __uint_as_float((unsigned)w[PW_Q]));
+        const bool samp = pl.mode == MODE_SAMPLE && kind != KIND_NONE;
+        if (kind == KIND_NONE) write_outputs_wave(a, b, nacc, nacc, flags, dead, sampled, 0.f, pl.tok);
+        if (pl.mode == MODE_SAMPLE) {
+            // the row record: lane i < kRowWords writes word i
+            const unsigned rec = (unsigned)(samp ? kind : KIND_NONE) | ((unsigned)(samp ? at : 0) << 3) |
+                                 ((flags & 0xffu) << 8);
+            const unsigned v = lane == RW_MT ? mt_at : lane == RW_INVT ? invt_at
+                             : lane == RW_MQ ? mq_at : lane == RW_INVQ ? invq_at : rec;
+            if (lane <= RW_INVQ) put_tagged(&a.ws.rowrec[(long long)b * kRowWords + lane], v, a.epoch);
+        }
+        if (lane == 0) {
+            fKind = kind;
+            fDead = dead;
+            fFlags = flags;
+            fAt = at;
+        }
     }
+    __syncthreads();
+    if constexpr (TRUNC) {
+        if (pl.mode == MODE_TRUNC && fKind != KIND_NONE) {
+            const bool res = fKind == KIND_RESIDUAL;
+            const int pos = fAt;
+            const float u = uniform24(a.seed, b, pos, res ? PURPOSE_RESIDUAL : PURPOSE_BONUS, a.step);
+            float wres;
+            bool fb;
+            const int tok = trunc_sample<BF16>(a, b, pos, res, u, pl, *sc, &wres, &fb);
+            if (wave == 0) {
+                unsigned flags = fFlags | (fb ? SPECV_FLAG_RESIDUAL_FALLBACK : 0u);
+                bool dead = fDead;
+                if (tok < 0) {
+                    dead = true;
+                    flags |= SPECV_FLAG_NONFINITE_ROW;
+                }
+                write_outputs_wave(a, b, nacc, nacc, flags, dead, tok, wres, pl.tok);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- pair decision
+// Run by the last unit of pair (k, b) to arrive (whole workgroup): merge the
+// chunk statistics of target row k (and draft row k), or truncate the two
+// rows, and take the accept test of position k (pseudo-code 10-1: accept
+// with probability min(1, p / q), i.e. u * q < p; greedy rows compare with the
+// argmax); publish the pair record, set the pair's status bit, and finish
+// the row when that resolves it.  Readers of the pair record check its tags,
+// so its stores need not complete first, except for truncated rows, whose
+// kept lists and TruncRows are read untagged.
+template <bool BF16, bool TRUNC>
+__device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncScratch* sc) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const bool greedy = pl.mode == MODE_GREEDY;
+    const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
+    const bool test = k < a.gamma;
+    const bool two = !greedy && test;
+    const float scale = pl.scale;
+    __shared__ float dM[2], dS[2], dZ[2], dU;
+    __shared__ int dA, dBad[2], dLate[2];
+    __shared__ TruncRow dT[2];
+    __shared__ int dFinish;
+    __shared__ unsigned long long dNew;
+    __shared__ PairVals dOwn;
+    const int d = test ? draft_token(a, b, k) : 0;
+    if (trunc) {
+        if constexpr (TRUNC) {
+            const TruncRow t0 = row_merge<BF16>(a, b, k, 0, pl, *sc);
+            TruncRow t1 = t0;
+            if (two) t1 = row_merge<BF16>(a, b, k, 1, pl, *sc);
+            if (tid == 0) {
+                dT[0] = t0;
+                dT[1] = t1;
+                dLate[0] = dLate[1] = 0;
+                if (two) {
+                    dZ[0] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), d);
+                    dZ[1] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
+                    dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
+                }
+            }
+        }
+    } else {
+        // one wave per row merges the chunk statistics (lane c: chunk c);
+        // wave 2 fetches z at d_k and draws the accept uniform meanwhile
+        if (wave < (two ? 2 : 1)) {
+            const int side = wave;
+            float m = -kInf;
+            unsigned second = 0;
+            bool ok = true;
+            if (lane < a.C) ok = published_stats(stats_words(a, b, k, side, lane), a.epoch, m, second);
+            float s = 0.f;
+            int arg = 0x7fffffff;
+            bool nan = false;
+            if (lane < a.C) {
+                if (greedy) {
+                    arg = (int)second;
+                    nan = __builtin_isnan(m);
+                    if (nan) m = -kInf;
+                } else {
+                    s = __uint_as_float(second);
+                }
+            }
+            if (greedy) wave_merge_arg(m, arg);
+            else wave_merge_ms(m, s, scale);
+            const bool anybad = __ballot(nan) != 0;
+            const bool late = __ballot(!ok) != 0;
+            if (lane == 0) {
+                dM[side] = m;
+                dS[side] = s;
+                dBad[side] = anybad || (greedy ? false : __builtin_isnan(s));
+                dLate[side] = late;
+                if (side == 0) dA = arg;
+            }
+        } else if (wave == 2 && two) {
+            if (lane < 2) dZ[lane] = load_elem<BF16>(lane == 0 ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k)
+                                                               : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
+            if (lane == 2) dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        PairVals v{};
+        unsigned outcome, flags = 0;
+        if (greedy) {
+            const bool bad = dBad[0] || dM[0] == -kInf;
+            if (bad) {
+                outcome = OUT_BAD;
+                flags = SPECV_FLAG_NONFINITE_ROW;
+            } else {
+                outcome = !test ? OUT_BONUS : (d == dA ? OUT_ACC : OUT_REJ);
+            }
+            v.arg = dA;
+        } else if (trunc) {
+            const TruncRow& t0 = dT[0];
+            const TruncRow& t1 = dT[1];
+            flags = (t0.flags | (two ? t1.flags : 0u)) & (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
+            if (t0.bad || (two && t1.bad)) flags |= SPECV_FLAG_NONFINITE_ROW;
+            if (trow_dead(t0) || (two && trow_dead(t1))) {
+                outcome = OUT_BAD;
+            } else if (!test) {
+                outcome = OUT_BONUS;
+            } else {
+                v.p = trunc_prob(t0, dZ[0], scale);
+                v.q = trunc_prob(t1, dZ[1], scale);
+                if (!(finite_logit(dZ[1]) && dZ[1] >= t1.tstar)) flags |= SPECV_FLAG_Q_ZERO;
+                outcome = dU * v.q < v.p ? OUT_ACC : OUT_REJ;
+            }
+        } else {
+            const bool badT = dBad[0] || dM[0] == -kInf || !(dS[0] > 0.f);
+            const bool badQ = two && (dBad[1] || dM[1] == -kInf || !(dS[1] > 0.f));
+            v.mt = dM[0];
+            v.invt = 1.f / dS[0];
+            if (two) {
+                v.mq = dM[1];
+                v.invq = 1.f / dS[1];
+            }
+            if (badT || badQ) {
+                outcome = OUT_BAD;
+                flags = SPECV_FLAG_NONFINITE_ROW;
+            } else if (!test) {
+                outcome = OUT_BONUS;
+            } else {
+                v.p = fast_exp2((dZ[0] - dM[0]) * scale) / dS[0];
+                v.q = fast_exp2((dZ[1] - dM[1]) * scale) / dS[1];
+                if (dZ[1] == -kInf) flags |= SPECV_FLAG_Q_ZERO;
+                outcome = dU * v.q < v.p ? OUT_ACC : OUT_REJ;
+            }
+        }
+        if (dLate[0] || (two && dLate[1])) {
+            // statistics that never arrived (a dispatch order other than the
+            // hardware's): the row emits nothing
+            outcome = OUT_BAD;
+            flags |= SPECV_FLAG_INTERNAL;
+        }
+        v.state = outcome | (flags << 8);
+        PairRec* pr = &a.ws.pair[pair_id(a, b, k)];
+        const unsigned e = a.epoch;
+        put_tagged(&pr->w[PW_P], __float_as_uint(v.p), e);
+        put_tagged(&pr->w[PW_Q], __float_as_uint(v.q), e);
+        put_tagged(&pr->w[PW_ARG], (unsigned)v.arg, e);
+        put_tagged(&pr->w[PW_MT], __float_as_uint(v.mt), e);
+        put_tagged(&pr->w[PW_INVT], __float_as_uint(v.invt), e);
+        put_tagged(&pr->w[PW_MQ], __float_as_uint(v.mq), e);
+        put_tagged(&pr->w[PW_INVQ], __float_as_uint(v.invq), e);
+        put_tagged(&pr->w[PW_STATE], v.state, e);
+        dOwn = v;
+        unsigned long long bit;
+        if (test) bit = outcome == OUT_ACC ? (1ull << k) : (1ull << (32 + k));
+        else bit = outcome == OUT_BONUS ? kBonusOk : kBonusBad;
+        if (trunc) wait_stores();
+        const unsigned long long old = __hip_atomic_fetch_or(
+            status_word(a, a.epoch & 1u, b), bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long now = old | bit;
+        dNew = now;
+        dFinish = resolve(old, pl, a.gamma).how == H_OPEN && resolve(now, pl, a.gamma).how != H_OPEN;
+    }
+    __syncthreads();
+    if (dFinish) finish_row<BF16, TRUNC>(a, b, k, dOwn, pl, dNew, sc);
 }
 
 // ---------------------------------------------------------------- sampling
@@ -1208,12 +1472,12 @@ struct Weights {
     }
 };
 
-// Correction (position k < gamma) or bonus (k == gamma) sample from the
-// chunk in registers, by every unit of the row once the walk stopped at k:
-// each publishes its chunk's weight sum and p mass, reads all of them, and
-// the unit whose chunk holds u * W scans it (tokens in ascending order, first
-// running sum > u * W) and writes the outputs.  ``flags``: the row's flags
-// so far.  Whole workgroup.
+// Correction (position k < gamma) or bonus (k == gamma) sample of row b, by
+// its C sampling workgroups, each holding chunk c of the sampled row pair in
+// registers: each publishes its chunk's weight sum and p mass, reads all of
+// them, and the workgroup whose chunk holds u * W scans it (tokens in
+// ascending order, first running sum > u * W) and writes the outputs.
+// ``flags_in``: the row's flags so far.  Whole workgroup.
 template <bool BF16, bool VEC>
 __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan& pl, Weights wt,
                                  unsigned flags_in, const ChunkRegs<BF16, VEC>& rt,
@@ -1222,10 +1486,9 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
     constexpr int G = BF16 ? 8 : 4;
     constexpr int NG = kPerThread / G;
     const float u = uniform24(a.seed, b, k, wt.residual ? PURPOSE_RESIDUAL : PURPOSE_BONUS, a.step);
-
-    // per-group weight sums (group j of this thread: entries [j * G, j * G + G));
-    // entries are unpacked from the chunk registers where they are used
-    float gw[NG], sw = 0.f, sp = 0.f;
+    // the weights of this thread's entries (kept for the scan), their group
+    // sums, and the p mass
+    float w[kPerThread], gw[NG], sw = 0.f, sp = 0.f;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
         float s = 0.f;
@@ -1234,7 +1497,8 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
             const int i = j * G + e;
             const float pz = wt.p(rt.elem(i));
             sp += pz;
-            s += wt.residual ? wt.w(rt.elem(i), rd.elem(i)) : pz;
+            w[i] = wt.residual ? wt.w(rt.elem(i), rd.elem(i)) : pz;
+            s += w[i];
         }
         gw[j] = s;
         sw += s;
@@ -1244,7 +1508,6 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
     __shared__ int sOk;
     sw = wave_sum(sw);
     sp = wave_sum(sp);
-    __syncthreads();                               // shared state may still be read
     if (lane == 0) {
         red[0][wave] = sw;
         red[1][wave] = sp;
@@ -1265,6 +1528,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         const unsigned long long* base = a.ws.wsum + (long long)b * a.C * 2;
         bool done = false;
         unsigned long long w0 = 0, w1 = 0;
+#pragma unroll 1
         for (int spin = 0; spin < kSpinLimit; ++spin) {
             if (lane < a.C) {
                 w0 = published(base + lane * 2);
@@ -1288,7 +1552,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
     __syncthreads();
     if (!sOk) return;
 
-    // the chunk holding u * W: the same sequential sums in every unit
+    // the chunk holding u * W: the same sequential sums in every workgroup
     __shared__ float sBase, sTarget, sWres;
     __shared__ int sChunk, sRes, sTok, sLast;
     __shared__ unsigned sFlags;
@@ -1352,10 +1616,12 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         for (int j = 0; j < NG; ++j) {
             float s = 0.f;
 #pragma unroll
-            for (int e = 0; e < G; ++e) s += wt.p(rt.elem(j * G + e));
+            for (int e = 0; e < G; ++e) {
+                w[j * G + e] = wt.p(rt.elem(j * G + e));
+                s += w[j * G + e];
+            }
             gw[j] = s;
         }
-        wt.residual = 0;
     }
     // prefix sums of the group weights in token order: group (j, tid) comes
     // after every group (j', *) with j' < j and every (j, tid') with tid' < tid
@@ -1382,8 +1648,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         int first = -1, lastin = -1;
 #pragma unroll
         for (int e = 0; e < G; ++e) {
-            const int i = j * G + e;
-            const float wk = wt.w(rt.elem(i), wt.residual ? rd.elem(i) : 0.f);
+            const float wk = w[j * G + e];
             run += wk;
             if (wk > 0.f) {
                 lastin = e;
@@ -1408,331 +1673,224 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
     }
 }
 
-// ---------------------------------------------------------------- the walk
-// Every chunk statistic of row ``side`` of pair (k, b), polled by one wave
-// (lane c: chunk c) until all carry this call's tag; returns false when some
-// did not within the bound.
-__device__ inline bool gather_stats(const Args& a, int b, int k, int side, float& m, unsigned& second) {
-    const int lane = threadIdx.x % kWave;
-    bool ok = true;
-    m = -kInf;
-    second = 0;
-    if (lane < a.C) ok = published_stats(stats_words(a, b, k, side, lane), a.epoch, m, second);
-    return __ballot(!ok) == 0;
-}
-
-// Touch every 128-byte line of chunk [v0, v0 + len) of a row with one dword
-// load each (threads 128..255), so that the chunk is in the L2 when it is
-// loaded for real; returns the loaded words folded together (the caller
-// keeps them live).
-template <bool BF16>
-__device__ inline unsigned prefetch_chunk(const void* row, int v0, int len) {
-    constexpr int per_line = BF16 ? 64 : 32;          // entries per 128-byte line
-    const int t = (int)threadIdx.x - kBlock / 2;
-    const unsigned* base = reinterpret_cast<const unsigned*>(static_cast<const char*>(row) +
-                                                            (size_t)v0 * (BF16 ? 2 : 4));
-    const int lines = (len + per_line - 1) / per_line;
-    unsigned acc = 0;
-    for (int i = t; i < lines; i += kBlock / 2) acc ^= base[i * 32];   // 32 dwords per line
-    return acc;
-}
-
-// Workgroup (b, c): chunk c of every position of batch row b, walked in
-// order while the round goes on (pseudo-code 10-1 stops at the first
-// rejection, so later rows are never read).  At each position k the unit
-// streams chunk c of target row k (and draft row k), publishes its chunk
-// statistics, reads every chunk's statistics of the pair, and takes the
-// accept test itself (the same arithmetic in every unit of the row).
-// Truncated pairs are decided by the last unit to arrive.  From position 1
-// on, the next position's chunk is pulled into the L2 while the current
-// position is decided.
-#ifndef SPECV_PREFETCH_FROM
-#define SPECV_PREFETCH_FROM 1
+// ---------------------------------------------------------------- streaming
+// Unit (k, b, c): chunk c of target row k and (sampling and truncated rows,
+// k < gamma) of draft row k, reduced to chunk statistics that are published
+// for the pair's decision; the last unit of the pair to arrive decides it.
+// A unit at position k >= kSkipFrom first reads its row's status and skips
+// its chunk when the round is known to have stopped before k; otherwise it
+// reads (speculatively when earlier positions are undecided), so the stream
+// never waits for a decision.
+#ifndef SPECV_SKIP_FROM
+#define SPECV_SKIP_FROM 2
 #endif
+constexpr int kSkipFrom = SPECV_SKIP_FROM;
+
 template <bool BF16, bool VEC, bool TRUNC>
-__device__ void walk_row(const Args& a, int b, int c, TruncScratch* sc) {
+__device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const unsigned par = a.epoch & 1u;
+    const bool check = k >= kSkipFrom;
+    // the row's status is fetched by one thread in the same memory round
+    // trip as the plan, and the skip decision shared through LDS
+    __shared__ int sSkip;
+    unsigned long long st = 0;
+    if (check && tid == 0) st = published(status_word(a, par, b));
     const Plan pl = make_plan(a, b);
     if (pl.mode == MODE_SKIP) {
-        if (c == 0 && wave == 0) {
+        if (k == 0 && c == 0 && wave == 0) {
             write_outputs_wave(a, b, 0, 0, pl.flags, true, -1, 0.f, pl.tok);
             write_diag_wave(a, b, 0, 0.f, 0.f);
         }
         return;
     }
+    if (k >= pl.nt) return;                         // a position the round cannot consult
+    if (check) {
+        if (tid == 0) sSkip = stopped_before(st, k);
+        __syncthreads();
+        if (sSkip) return;
+    }
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
-    const float scale = pl.scale;
+    const bool two = !greedy && k < a.gamma;
+    const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
+    const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
     const int v0 = c * kChunk;
     const int len = min(kChunk, a.V - v0);
-    __shared__ float hp[kMaxPos], hq[kMaxPos];        // p_k(d_k), q_k(d_k) along the walk
+    ChunkRegs<BF16, VEC> rt, rd;
+    rt.issue(trow, v0, len);
+    if (two) rd.issue(drow, v0, len);
+    rt.finish(trow, v0, len);
+    if (two) rd.finish(drow, v0, len);
+
     __shared__ float sm[2][kWaves], ss[2][kWaves];
     __shared__ int si[kWaves];
     __shared__ unsigned sb[kWaves];
-    __shared__ float pM[2], pS[2], pZ[2], pP, pQ;
-    __shared__ int pLate[2], pArg, pLast;
-    __shared__ unsigned pOut, pFlags;
-    unsigned flags_acc = pl.flags;
-    unsigned sink = 0;
-    for (int k = 0; k < pl.nt; ++k) {
-        const bool test = k < a.gamma;
-        const bool two = !greedy && test;
-        const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
-        const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
-        ChunkRegs<BF16, VEC> rt, rd;
-        rt.issue(trow, v0, len);
-        if (two) rd.issue(drow, v0, len);
-        // d_k and z at d_k for the accept test, fetched alongside
-        const int dk = test ? draft_token(a, b, k) : 0;
-        float zt = 0.f, zq = 0.f;
-        if (two && !trunc && tid == 0) {
-            zt = load_elem<BF16>(trow, dk);
-            zq = load_elem<BF16>(drow, dk);
-        }
-        rt.finish(trow, v0, len);
-        if (two) rd.finish(drow, v0, len);
-        __syncthreads();                              // the previous position's LDS is read
-        if (greedy) {
-            float best = -kInf;
-            int bi = 0x7fffffff;
-            unsigned bad = 0;
+    __shared__ int sLast;
+    const float scale = pl.scale;
+    if (greedy) {
+        float best = -kInf;
+        int bi = 0x7fffffff;
+        unsigned bad = 0;
 #pragma unroll
-            for (int i = 0; i < kPerThread; ++i) {
-                const float x = rt.elem(i);
-                bad |= !(x <= 3.402823466e38f);           // NaN or +inf
-                if (x > best) {                           // strict: keeps the lowest index
-                    best = x;
-                    bi = v0 + chunk_index<BF16>(i);
-                }
-            }
-            wave_merge_arg(best, bi);
-            bad = wave_or(bad);
-            if (lane == 0) {
-                sm[0][wave] = best;
-                si[wave] = bi;
-                sb[wave] = bad;
-            }
-            __syncthreads();
-            if (tid == 0) {
-                for (int w = 1; w < kWaves; ++w) {
-                    merge_arg(best, bi, sm[0][w], si[w]);
-                    bad |= sb[w];
-                }
-                publish_stats(stats_words(a, b, k, 0, c), bad ? __builtin_nanf("") : best,
-                              (unsigned)bi, a.epoch);
-            }
-        } else {
-#pragma unroll
-            for (int side = 0; side < 2; ++side) {
-                if (side == 1 && !two) break;
-                const ChunkRegs<BF16, VEC>& r = side == 0 ? rt : rd;
-                float cm = -kInf;
-#pragma unroll
-                for (int i = 0; i < kPerThread; ++i) cm = fmaxf(cm, r.elem(i));
-                const float nms = cm == -kInf ? 0.f : -cm * scale;
-                float s = 0.f;
-#pragma unroll
-                for (int i = 0; i < kPerThread; ++i) s += fast_exp2(fmaf(r.elem(i), scale, nms));
-                float m = cm;
-                wave_merge_ms(m, s, scale);
-                if (lane == 0) {
-                    sm[side][wave] = m;
-                    ss[side][wave] = s;
-                }
-                if constexpr (TRUNC) {
-                    if (trunc) {
-                        float x[kPerThread];
-                        r.get(x);
-                        chunk_candidates<BF16>(a, side_row(a, b, k, side), c, pl.keff, x, *sc);
-                    }
-                }
-            }
-            __syncthreads();
-            if (tid == 0) {
-                for (int side = 0; side < (two ? 2 : 1); ++side) {
-                    float m = sm[side][0], s = ss[side][0];
-                    for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[side][w], ss[side][w], scale);
-                    publish_stats(stats_words(a, b, k, side, c), m, __float_as_uint(s), a.epoch);
-                }
-                pZ[0] = zt;
-                pZ[1] = zq;
+        for (int i = 0; i < kPerThread; ++i) {
+            const float x = rt.elem(i);
+            bad |= !(x <= 3.402823466e38f);           // NaN or +inf
+            if (x > best) {                           // strict: keeps the lowest index
+                best = x;
+                bi = v0 + chunk_index<BF16>(i);
             }
         }
-        // the next position's chunk heads for the L2 meanwhile (waves 2 and 3)
-        if (VEC && k >= SPECV_PREFETCH_FROM && k + 1 < pl.nt && wave >= 2) {
-            const bool two1 = !greedy && k + 1 < a.gamma;
-            sink ^= prefetch_chunk<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k + 1), v0, len);
-            if (two1) sink ^= prefetch_chunk<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k + 1), v0, len);
+        wave_merge_arg(best, bi);
+        bad = wave_or(bad);
+        if (lane == 0) {
+            sm[0][wave] = best;
+            si[wave] = bi;
+            sb[wave] = bad;
         }
-        // the pair's outcome
-        unsigned outcome = OUT_BAD, flags = 0;
-        float p = 0.f, q = 0.f;
-        bool decider = c == 0;                        // the unit that finishes the row
-        if (trunc) {
-            if constexpr (TRUNC) {
-                if (tid == 0) {
-                    unsigned* ctr = a.ws.ctr + pair_id(a, b, k) * kSlot;
-                    pLast = arrive(ctr, true) == (unsigned)(a.C - 1);
-                    if (pLast) publish(ctr, 0u);          // ready for the next call
-                }
-                __syncthreads();
-                decider = pLast != 0;
-                if (decider) {
-                    decide_trunc<BF16>(a, b, k, pl, *sc, &pOut, &pFlags, &pP, &pQ);
-                } else if (wave == 0) {
-                    // the decider's record
-                    const PairRec* pr = &a.ws.pair[pair_id(a, b, k)];
-                    unsigned long long v = 0;
-                    bool ok = false;
-                    for (int spin = 0; spin < kSpinLimit; ++spin) {
-                        v = 0;
-                        if (lane == 0) v = published(&pr->w[PW_STATE]);
-                        else if (lane == 1) v = published(&pr->w[PW_P]);
-                        else if (lane == 2) v = published(&pr->w[PW_Q]);
-                        if ((__ballot(lane < 3 && tag_is(v, a.epoch)) & 7ull) == 7ull) {
-                            ok = true;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                    const unsigned st = (unsigned)readlane64(v, 0);
-                    if (lane == 0) {
-                        pOut = ok ? (st & 0xffu) : OUT_BAD;
-                        pFlags = ok ? (st >> 8) : SPECV_FLAG_INTERNAL;
-                        pP = __uint_as_float((unsigned)readlane64(v, 1));
-                        pQ = __uint_as_float((unsigned)readlane64(v, 2));
-                    }
-                }
-                __syncthreads();
-                outcome = pOut;
-                flags = pFlags;
-                p = pP;
-                q = pQ;
-            }
-        } else if (greedy) {
-            if (wave == 0) {
-                float m;
-                unsigned second;
-                const bool ok = gather_stats(a, b, k, 0, m, second);
-                int arg = (int)second;
-                const bool nan = __builtin_isnan(m);
-                const bool anybad = __ballot(nan) != 0;
-                if (nan || lane >= a.C) {
-                    m = -kInf;
-                    arg = 0x7fffffff;
-                }
-                wave_merge_arg(m, arg);
-                if (lane == 0) {
-                    pArg = arg;
-                    pOut = !ok ? OUT_BAD : ((anybad || m == -kInf) ? OUT_BAD : OUT_ACC);
-                    pFlags = !ok ? SPECV_FLAG_INTERNAL : ((anybad || m == -kInf) ? SPECV_FLAG_NONFINITE_ROW : 0u);
-                }
-            }
-            __syncthreads();
-            outcome = pOut;
-            flags = pFlags;
-            if (outcome != OUT_BAD)
-                outcome = !test ? OUT_BONUS : (dk == pArg ? OUT_ACC : OUT_REJ);
-        } else {
-            // every unit merges the pair's statistics and runs the test itself
-            if (wave < (two ? 2 : 1)) {
-                float m;
-                unsigned second;
-                const bool ok = gather_stats(a, b, k, wave, m, second);
-                float s = lane < a.C ? __uint_as_float(second) : 0.f;
-                wave_merge_ms(m, s, scale);
-                if (lane == 0) {
-                    pM[wave] = m;
-                    pS[wave] = s;
-                    pLate[wave] = !ok;
-                }
-            }
-            __syncthreads();
-            const bool badT = __builtin_isnan(pS[0]) || pM[0] == -kInf || !(pS[0] > 0.f);
-            const bool badQ = two && (__builtin_isnan(pS[1]) || pM[1] == -kInf || !(pS[1] > 0.f));
-            const float u = two ? uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step) : 0.f;
-            outcome = sample_outcome(test, pM[0], pS[0], pM[1], pS[1], badT, badQ, pZ[0], pZ[1], u,
-                                     scale, flags, p, q);
-            if (pLate[0] || (two && pLate[1])) {
-                outcome = OUT_BAD;
-                flags = SPECV_FLAG_INTERNAL;
-            }
-        }
-        if (tid == 0) {
-            hp[k] = p;
-            hq[k] = q;
-        }
-        flags_acc |= flags;
-        if (outcome == OUT_BAD) {
-            // a consulted row with NaN / +inf or nothing finite: no emission
-            __syncthreads();
-            if (decider) finish_row(a, b, pl, k, greedy ? 0 : k, flags_acc, true, -1, 0.f, hp, hq);
-            break;
-        }
-        if (test && outcome == OUT_ACC) {
-            if (k + 1 < pl.nt) continue;
-            // every draft the cap allows was accepted, and no bonus position
-            __syncthreads();
-            if (decider) finish_row(a, b, pl, k + 1, greedy ? 0 : k + 1, flags_acc, false, -1, 0.f, hp, hq);
-            break;
-        }
-        // the round stops at k: a correction (rejection) or the bonus token
         __syncthreads();
-        const int tested = test ? k + 1 : k;
-        if (greedy) {
-            if (decider) finish_row(a, b, pl, k, 0, flags_acc, false, pArg, 0.f, hp, hq);
-            break;
+        if (tid == 0) {
+            for (int w = 1; w < kWaves; ++w) {
+                merge_arg(best, bi, sm[0][w], si[w]);
+                bad |= sb[w];
+            }
+            publish_stats(stats_words(a, b, k, 0, c), bad ? __builtin_nanf("") : best, (unsigned)bi,
+                          a.epoch);
         }
-        if (trunc) {
+    } else {
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            if (side == 1 && !two) break;
+            const ChunkRegs<BF16, VEC>& r = side == 0 ? rt : rd;
+            float cm = -kInf;
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) cm = fmaxf(cm, r.elem(i));
+            const float nms = cm == -kInf ? 0.f : -cm * scale;
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) s += fast_exp2(fmaf(r.elem(i), scale, nms));
+            float m = cm;
+            wave_merge_ms(m, s, scale);
+            if (lane == 0) {
+                sm[side][wave] = m;
+                ss[side][wave] = s;
+            }
             if constexpr (TRUNC) {
-                if (decider) {
-                    const float u = uniform24(a.seed, b, k, test ? PURPOSE_RESIDUAL : PURPOSE_BONUS, a.step);
-                    float wres;
-                    bool fb;
-                    const int tok = trunc_sample<BF16>(a, b, k, test, u, pl, *sc, &wres, &fb);
-                    const unsigned f = flags_acc | (fb ? SPECV_FLAG_RESIDUAL_FALLBACK : 0u) |
-                                       (tok < 0 ? SPECV_FLAG_NONFINITE_ROW : 0u);
-                    finish_row(a, b, pl, k, tested, f, tok < 0, tok, wres, hp, hq);
+                if (trunc) {
+                    float x[kPerThread];
+                    r.get(x);
+                    chunk_candidates<BF16>(a, side_row(a, b, k, side), c, pl.keff, x, *sc);
                 }
             }
-            break;
         }
-        if (c == 0 && wave == 0) write_diag_wave(a, b, tested, lane < kMaxPos ? hp[lane] : 0.f,
-                                                  lane < kMaxPos ? hq[lane] : 0.f);
-        Weights wt;
-        wt.residual = test;
-        wt.mt = pM[0];
-        wt.invt = 1.f / pS[0];
-        wt.mq = two ? pM[1] : 0.f;
-        wt.invq = two ? 1.f / pS[1] : 0.f;
-        wt.st = scale;
-        sample_from_regs<BF16, VEC>(a, b, k, c, pl, wt, flags_acc, rt, rd);
-        break;
+        __syncthreads();
+        if (tid == 0) {
+            for (int side = 0; side < (two ? 2 : 1); ++side) {
+                float m = sm[side][0], s = ss[side][0];
+                for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[side][w], ss[side][w], scale);
+                publish_stats(stats_words(a, b, k, side, c), m, __float_as_uint(s), a.epoch);
+            }
+        }
     }
-    // keep the prefetch loads (their values are never needed)
-    if (sink == 0x9E3779B9u && a.V < 0) a.out_acc[0] = (int)sink;
+    if (tid == 0) sLast = arrive(pair_counter(a, par, b, k), trunc) == (unsigned)(a.C - 1);
+    __syncthreads();
+    if (sLast) decide_pair<BF16, TRUNC>(a, b, k, pl, sc);
+}
+
+// Sampling workgroup (b, c) of a sampling row: waits for the row record,
+// then reads chunk c of the target (and draft) row of the position the round
+// stopped at, or of the bonus row, and takes part in the sample.  Rows of
+// other modes never need one.
+template <bool BF16, bool VEC>
+__device__ void sample_item(const Args& a, int b, int c) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const Plan pl = make_plan(a, b);
+    if (pl.mode != MODE_SAMPLE) return;
+    __shared__ unsigned sRec[kRowWords];
+    __shared__ int sGo;
+    if (wave == 0) {
+        const unsigned long long* rr = a.ws.rowrec + (long long)b * kRowWords;
+        int go = 0;
+        unsigned long long v = 0;
+#pragma unroll 1
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+            v = lane <= RW_INVQ ? published(rr + lane) : 0ull;
+            if ((__ballot(lane <= RW_INVQ && tag_is(v, a.epoch)) & 0x1full) == 0x1full) {
+                go = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane < kRowWords) sRec[lane] = (unsigned)v;
+        if (lane == 0) sGo = go;
+        if (!go && lane == 0 && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
+    }
+    __syncthreads();
+    if (!sGo) return;
+    const unsigned rec = sRec[RW_REC];
+    const int kind = (int)(rec & 7u);
+    if (kind != KIND_RESIDUAL && kind != KIND_BONUS) return;
+    const int k = (int)((rec >> 3) & 31u);
+    const bool two = kind == KIND_RESIDUAL;
+    const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
+    const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
+    const int v0 = c * kChunk;
+    const int len = min(kChunk, a.V - v0);
+    ChunkRegs<BF16, VEC> rt, rd;
+    rt.issue(trow, v0, len);
+    if (two) rd.issue(drow, v0, len);
+    rt.finish(trow, v0, len);
+    if (two) rd.finish(drow, v0, len);
+    Weights wt;
+    wt.residual = two;
+    wt.mt = __uint_as_float(sRec[RW_MT]);
+    wt.invt = __uint_as_float(sRec[RW_INVT]);
+    wt.mq = __uint_as_float(sRec[RW_MQ]);
+    wt.invq = __uint_as_float(sRec[RW_INVQ]);
+    wt.st = pl.scale;
+    sample_from_regs<BF16, VEC>(a, b, k, c, pl, wt, (rec >> 8) & 0xffu, rt, rd);
 }
 
 // ---------------------------------------------------------------- k_verify
-// One launch per call, one workgroup per (batch row, chunk).  The lean
-// variant (no truncation) is held to 128 VGPRs so that four workgroups share
-// a CU: 1024 resident units, a whole B=64 x V=128256 batch at once.
+// One launch per call:
+//   blocks [0, P * B * C):        streaming unit (k, b, c), position-major;
+//   blocks [P * B * C, + B * C):  sampling workgroup (b, c).
+// Every workgroup also clears its share of the other call parity's arrival
+// counters and status words, which the next call starts from.
 // k_verify_trunc carries the truncation path (handles created with
 // max_top_k > 0) and its LDS scratch; without it truncated rows are flagged
-// unsupported.
+// unsupported and the kernel stays lean.
+__device__ inline void clear_other_parity(const Args& a) {
+    const unsigned other = (a.epoch & 1u) ^ 1u;
+    const long long stride = (long long)gridDim.x * kBlock;
+    for (long long i = (long long)blockIdx.x * kBlock + threadIdx.x; i < a.ws.n_groups; i += stride)
+        publish(a.ws.ctr + ((long long)other * a.ws.n_groups + i) * kSlot, 0u);
+    for (long long i = (long long)blockIdx.x * kBlock + threadIdx.x; i < a.ws.n_rows; i += stride)
+        publish(a.ws.status + ((long long)other * a.ws.n_rows + i) * (kSlot / 2), 0ull);
+}
+
+template <bool BF16, bool VEC, bool TRUNC>
+__device__ inline void verify_block(const Args& a, TruncScratch* sc) {
+    clear_other_parity(a);
+    const int per_pos = a.B * a.C;
+    const int t = blockIdx.x;
+    const int k = t / per_pos;
+    const int rem = t - k * per_pos;
+    const int b = rem / a.C;
+    const int c = rem - b * a.C;
+    if (k < a.P) stream_unit<BF16, VEC, TRUNC>(a, k, b, c, sc);
+    else sample_item<BF16, VEC>(a, b, c);
+}
+
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_verify(Args a) {
-    const int b = blockIdx.x / a.C;
-    const int c = blockIdx.x - b * a.C;
-    walk_row<BF16, VEC, false>(a, b, c, nullptr);
+__global__ __launch_bounds__(kBlock) void k_verify(Args a) {
+    verify_block<BF16, VEC, false>(a, nullptr);
 }
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_verify_trunc(Args a) {
-    const int b = blockIdx.x / a.C;
-    const int c = blockIdx.x - b * a.C;
     __shared__ TruncScratch sc;
-    walk_row<BF16, VEC, true>(a, b, c, &sc);
+    verify_block<BF16, VEC, true>(a, &sc);
 }
 
 using KernelFn = void (*)(Args);
@@ -1749,7 +1907,7 @@ KernelFn pick(bool bf16, bool vec, bool trunc) {
 }  // namespace
 
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev) {
-    const long long blocks = (long long)a.B * a.C;
+    const long long blocks = (long long)(a.P + 1) * a.B * a.C;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     KernelFn fn = pick(bf16, vec, a.cand_cap > 0);
     if (ev) (void)hipEventRecord(ev[0], stream);
