@@ -379,6 +379,18 @@ __device__ inline unsigned wave_or(unsigned x) {
     return (unsigned)xi;
 }
 
+__device__ inline int wave_min_int(int x) {
+    float dummy = 0.f;
+    wave_reduce2(dummy, x, 0.f, 0x7fffffff, [](float&, int& a, float, int b) { a = min(a, b); });
+    return x;
+}
+
+__device__ inline int wave_max_int(int x) {
+    float dummy = 0.f;
+    wave_reduce2(dummy, x, 0.f, (int)0x80000000, [](float&, int& a, float, int b) { a = max(a, b); });
+    return x;
+}
+
 // Inclusive prefix sums across the wave (lane order).
 __device__ inline float wave_scan_incl(float x) {
     x += dpp_f<kDppShr + 1>(x, 0.f);
@@ -1504,8 +1516,6 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         sw += s;
     }
     __shared__ float red[2][kWaves];
-    __shared__ float sW[kMaxChunks], sPm[kMaxChunks];
-    __shared__ int sOk;
     sw = wave_sum(sw);
     sp = wave_sum(sp);
     if (lane == 0) {
@@ -1513,19 +1523,21 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         red[1][wave] = sp;
     }
     __syncthreads();
-    if (tid == 0) {
+
+    // wave 0 publishes this chunk's sums, reads every chunk's (lane c: chunk
+    // c) and picks the chunk holding u * W from their prefix sums; the same
+    // arithmetic in every workgroup of the row, so all pick the same chunk
+    __shared__ float sBase, sTarget, sWres;
+    __shared__ int sChunk, sRes, sOk;
+    __shared__ unsigned sFlags;
+    if (wave == 0) {
         float wc = red[0][0], pc = red[1][0];
         for (int w2 = 1; w2 < kWaves; ++w2) {
             wc += red[0][w2];
             pc += red[1][w2];
         }
-        unsigned long long* slot = a.ws.wsum + ((long long)b * a.C + c) * 2;
-        put_tagged(slot, __float_as_uint(wc), a.epoch);
-        put_tagged(slot + 1, __float_as_uint(pc), a.epoch);
-    }
-    if (wave == 0) {
-        // every chunk's sums (lane c: chunk c)
-        const unsigned long long* base = a.ws.wsum + (long long)b * a.C * 2;
+        unsigned long long* base = a.ws.wsum + (long long)b * a.C * 2;
+        if (lane < 2) put_tagged(base + c * 2 + lane, __float_as_uint(lane == 0 ? wc : pc), a.epoch);
         bool done = false;
         unsigned long long w0 = 0, w1 = 0;
 #pragma unroll 1
@@ -1541,67 +1553,40 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        if (lane < a.C) {
-            sW[lane] = __uint_as_float((unsigned)w0);
-            sPm[lane] = __uint_as_float((unsigned)w1);
-        }
-        if (lane == 0) sOk = done;
-        if (!done && lane == 0 && c == 0 && a.out_flags)
-            atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
-    }
-    __syncthreads();
-    if (!sOk) return;
-
-    // the chunk holding u * W: the same sequential sums in every workgroup
-    __shared__ float sBase, sTarget, sWres;
-    __shared__ int sChunk, sRes, sTok, sLast;
-    __shared__ unsigned sFlags;
-    if (tid == 0) {
+        float vw = lane < a.C ? __uint_as_float((unsigned)w0) : 0.f;
+        const float vp = lane < a.C ? __uint_as_float((unsigned)w1) : 0.f;
         unsigned flags = flags_in;
-        float W = 0.f;
-        for (int cc = 0; cc < a.C; ++cc) W += sW[cc];
-        const float wres = wt.residual ? W : 0.f;
         int res = wt.residual;
+        float W = wave_sum(vw);
+        const float wres = res ? W : 0.f;
         if (res && (!(W > 0.f) || !__builtin_isfinite(W))) {
             // the correction mass vanished (p == q where the draft was
             // rejected, or rounding): sample from p at that position
             flags |= SPECV_FLAG_RESIDUAL_FALLBACK;
             res = 0;
-            W = 0.f;
-            for (int cc = 0; cc < a.C; ++cc) {
-                sW[cc] = sPm[cc];
-                W += sW[cc];
-            }
+            vw = vp;
+            W = wave_sum(vw);
         }
         const float target = u * W;
-        float acc = 0.f, base = 0.f, lastbase = 0.f;
-        int chosen = -1, lastc = -1;
-        for (int cc = 0; cc < a.C; ++cc) {
-            const float v = sW[cc];
-            if (v > 0.f) {
-                lastc = cc;
-                lastbase = acc;
-            }
-            if (chosen < 0 && acc + v > target) {
-                chosen = cc;
-                base = acc;
-            }
-            acc += v;
+        const float incl = wave_scan_incl(vw);
+        const unsigned long long hit = __ballot(lane < a.C && vw > 0.f && incl > target);
+        const unsigned long long pos = __ballot(lane < a.C && vw > 0.f);
+        // rounding: without a hit, the last chunk with weight
+        const int chosen = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : -1);
+        const float before = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), chosen > 0 ? chosen - 1 : 0));
+        if (lane == 0) {
+            sOk = done;
+            sChunk = chosen;
+            sBase = chosen > 0 ? before : 0.f;
+            sTarget = target;
+            sRes = res;
+            sWres = wres;
+            sFlags = flags;
+            if (!done && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
         }
-        if (chosen < 0) {        // rounding: clamp to the last chunk with weight
-            chosen = lastc;
-            base = lastbase;
-        }
-        sChunk = chosen;
-        sBase = base;
-        sTarget = target;
-        sRes = res;
-        sWres = wres;
-        sFlags = flags;
-        sTok = 0x7fffffff;
-        sLast = -1;
     }
     __syncthreads();
+    if (!sOk) return;
     const int chosen = sChunk;
     if (chosen < 0) {
         // no weight anywhere: cannot happen for finite rows
@@ -1626,6 +1611,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
     // prefix sums of the group weights in token order: group (j, tid) comes
     // after every group (j', *) with j' < j and every (j, tid') with tid' < tid
     __shared__ float gtot[NG][kWaves];
+    __shared__ int tokW[kWaves], lastW[kWaves];
     float incl[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -1639,9 +1625,11 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
         float before = 0.f, tot = 0.f;
+#pragma unroll
         for (int w2 = 0; w2 < kWaves; ++w2) {
-            if (w2 < wave) before += gtot[j][w2];
-            tot += gtot[j][w2];
+            const float g = gtot[j][w2];
+            if (w2 < wave) before += g;
+            tot += g;
         }
         const float start = gbase + before + (incl[j] - gw[j]);
         float run = start;
@@ -1661,11 +1649,22 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
             tok = g * G + (first >= 0 ? first : lastin);
         gbase += tot;
     }
-    if (tok != 0x7fffffff) atomicMin(&sTok, tok);
-    if (lastpos >= 0) atomicMax(&sLast, lastpos);
+    // the first token past u * W, and the last token with weight (for
+    // rounding), reduced per wave then across the four waves
+    tok = wave_min_int(tok);
+    lastpos = wave_max_int(lastpos);
+    if (lane == 0) {
+        tokW[wave] = tok;
+        lastW[wave] = lastpos;
+    }
     __syncthreads();
     if (wave == 0) {
-        const int t = sTok != 0x7fffffff ? sTok : sLast;     // rounding: the last token with weight
+        int t = tokW[0], l = lastW[0];
+        for (int w2 = 1; w2 < kWaves; ++w2) {
+            t = min(t, tokW[w2]);
+            l = max(l, lastW[w2]);
+        }
+        if (t == 0x7fffffff) t = l;        // rounding: the last token with weight
         const bool dead = t < 0;
         unsigned flags = sFlags;
         if (dead) flags |= SPECV_FLAG_NONFINITE_ROW;
