@@ -127,7 +127,8 @@ struct Args {
 // sampling workgroup per (batch row, chunk).  ``bf16`` selects the element
 // type, ``vec`` the 16-byte vector-load variant (row starts 16-byte aligned);
 // the truncation-capable variant is used when a.cand_cap > 0.  ``ev``
-// (nullable) receives two event records around the launch.
+// (nullable) holds two events that the launch records at the kernel's start
+// and end.
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev);
 
 }  // namespace specv
