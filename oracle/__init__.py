@@ -31,6 +31,7 @@ from .philox import philox4x32_10, uniform, PURPOSE_DRAFT, PURPOSE_ACCEPT, PURPO
 from .process import process_row, ProcessedRow, greedy_argmax
 from .verify import (
     verify_sample,
+    verify_point_mass,
     verify_greedy,
     inverse_cdf,
     cdf_interval,

@@ -32,6 +32,15 @@ token with positive weight, so a zero-weight token is never returned.
 Uniforms: Philox4x32-10 keyed by (seed, row b, position i, purpose, step);
 see ``oracle.philox``.
 
+Deterministic proposals (n-gram or prompt-lookup drafts: section 2.1 and
+4.2 of the "投机解码 Speculative Decoding" tutorial; the ICML summary's
+remark that the approximation model may be an n-gram model or a
+context-repeat heuristic) propose d_i with probability one, so their actual
+proposal distribution is the point mass on d_i.  ``verify_point_mass`` runs
+the same round with q_i = delta(d_i): the test reads u < p_i(d_i), and the
+correction distribution norm(max(p_i - delta(d_i), 0)) is p_i with d_i
+removed.  No draft logits exist.
+
 Pins (``tests/test_oracle_*.py``): the worked example of 11.1.3, exact
 enumeration over all 2^24 uniforms on small rows, the 11.1.3 identities,
 E[N] against the closed form of the ICML summary and the tutorial's printed
@@ -169,6 +178,66 @@ def _sample_row(b, trow, drow, toks, T, k, p, cap, eos_id, seed, step, keep_weig
     return emitted, n_acc, flags, p_at, q_at, W_out, ev
 
 
+def _point_mass_row(b, trow, toks, T, k, p, cap, eos_id, seed, step, keep_weights):
+    """Stochastic verification of one row against a deterministic proposal:
+    pseudo-code 10-1 with q_i the point mass on d_i."""
+    gamma = len(toks)
+    emitted = []
+    n_acc = 0
+    flags = 0
+    p_at = np.full(gamma, np.nan)
+    q_at = np.full(gamma, np.nan)
+    W_out = 0.0
+    ev = {"accept_tests": [], "sample": None}
+    for i in range(gamma):
+        if len(emitted) >= cap:
+            return emitted, n_acc, flags, p_at, q_at, W_out, ev
+        P = process_row(trow[i], T, k, p)
+        if P.nonfinite:
+            return [], 0, flags | FLAG_NONFINITE_ROW, p_at, q_at, 0.0, ev
+        if P.topp_near:
+            flags |= FLAG_TOPP_NEAR
+        d = int(toks[i])
+        delta = np.zeros_like(P.probs)
+        delta[d] = 1.0                        # q_i: all mass on the proposed token
+        pd, qd = P.probs[d], delta[d]
+        p_at[i], q_at[i] = pd, qd
+        u = float(uniform(seed, b, i, PURPOSE_ACCEPT, step))
+        ev["accept_tests"].append((i, u, pd, qd))
+        if u * qd < pd:                       # accept with probability min(1, p/q) = p(d)
+            emitted.append(d)
+            n_acc += 1
+            if d == eos_id:
+                return emitted, n_acc, flags, p_at, q_at, W_out, ev
+            continue
+        # first rejection: correction sample from norm(max(p - delta, 0))
+        w = residual_weights(P.probs, delta)
+        W = w.sum()
+        W_out = W
+        if not (np.isfinite(W) and W > 0):
+            flags |= FLAG_RESIDUAL_FALLBACK
+            w = P.probs
+        u2 = float(uniform(seed, b, i, PURPOSE_RESIDUAL, step))
+        t = inverse_cdf(w, u2)
+        ev["sample"] = {"kind": "residual", "pos": i, "u": u2, "W": float(w.sum()),
+                        "weights": w if keep_weights else None}
+        emitted.append(t)
+        return emitted, n_acc, flags, p_at, q_at, W_out, ev
+    if len(emitted) >= cap:
+        return emitted, n_acc, flags, p_at, q_at, W_out, ev
+    P = process_row(trow[gamma], T, k, p)
+    if P.nonfinite:
+        return [], 0, flags | FLAG_NONFINITE_ROW, p_at, q_at, 0.0, ev
+    if P.topp_near:
+        flags |= FLAG_TOPP_NEAR
+    u3 = float(uniform(seed, b, gamma, PURPOSE_BONUS, step))
+    t = inverse_cdf(P.probs, u3)
+    ev["sample"] = {"kind": "bonus", "pos": gamma, "u": u3, "W": float(P.probs.sum()),
+                    "weights": P.probs if keep_weights else None}
+    emitted.append(t)
+    return emitted, n_acc, flags, p_at, q_at, W_out, ev
+
+
 def _finish(results, B, gamma):
     out = {
         "num_accepted": np.zeros(B, np.int32),
@@ -232,6 +301,38 @@ def verify_sample(target, draft, tokens, temperature, top_k, top_p, max_new_toke
             continue
         results.append(_sample_row(b, target[b], draft[b], toks, T[b], K[b], Pp[b], caps[b],
                                    eos_id, seed, step, keep_weights))
+    return _finish(results, B, gamma)
+
+
+def verify_point_mass(target, tokens, temperature, top_k, top_p, max_new_tokens, seed, step=0,
+                      eos_id=-1, keep_weights=False):
+    """One verification round for every batch row against deterministic
+    drafts (q_i = the point mass on d_i; no draft logits).  Arguments and
+    result as ``verify_sample`` without ``draft``; temperature 0 rows are
+    verified greedily."""
+    target = np.asarray(target)
+    tokens = np.asarray(tokens)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    assert tokens.shape == (B, gamma)
+    T = _broadcast(temperature, B, np.float64)
+    K = _broadcast(top_k, B, np.int64)
+    Pp = _broadcast(top_p, B, np.float64)
+    caps = _caps(max_new_tokens, B)
+    results = []
+    for b in range(B):
+        toks = tokens[b]
+        if ((toks < 0) | (toks >= V)).any():
+            results.append(([], 0, FLAG_TOKEN_OOR, np.full(gamma, np.nan),
+                            np.full(gamma, np.nan), 0.0, {"accept_tests": [], "sample": None}))
+            continue
+        if T[b] == 0.0:
+            em, na, fl = _greedy_row(target[b], toks, caps[b], eos_id)
+            results.append((em, na, fl, np.full(gamma, np.nan), np.full(gamma, np.nan), 0.0,
+                            {"accept_tests": [], "sample": None}))
+            continue
+        results.append(_point_mass_row(b, target[b], toks, T[b], K[b], Pp[b], caps[b], eos_id,
+                                       seed, step, keep_weights))
     return _finish(results, B, gamma)
 
 
