@@ -151,6 +151,26 @@ SPECV_API specv_status specv_verify_sample(specv_handle h, void* stream,
                                  int32_t* out_num_emitted, int32_t* out_row_flags,
                                  const specv_diag* diag);
 
+/* Stochastic verification against deterministic drafts: n-gram or
+ * prompt-lookup proposals ("投机解码 Speculative Decoding" tutorial, sections
+ * 2.1 and 4.2; the ICML summary's remark that the approximation model may be
+ * an n-gram model or a context-repeat heuristic).  Such a draft proposes d_i
+ * with probability one, so q_i is the point mass on d_i and the round above
+ * reads: accept d_i with probability p_i(d_i); at the first rejection emit
+ * t ~ p_i with d_i removed (norm(max(p_i - q_i, 0))); after full acceptance
+ * the bonus t ~ p_gamma.  Temperature-0 rows are verified greedily.  No
+ * draft logits are read; q_at_draft reports 1 for every test run.
+ * Arguments, layouts, ownership and errors as specv_verify_sample without
+ * the draft logits. */
+SPECV_API specv_status specv_verify_point_mass(specv_handle h, void* stream,
+                                 const void* target_logits, int64_t t_stride_b, int64_t t_stride_pos,
+                                 specv_dtype dtype, int B, int gamma, int V,
+                                 const int32_t* draft_tokens, const specv_row_params* row_params,
+                                 uint64_t seed, uint32_t step, int32_t eos_id,
+                                 int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags,
+                                 const specv_diag* diag);
+
 /* Greedy verification (11.1.2): accept while d_i == argmax of the raw target
  * logits (lowest index on ties), emit the argmax at the first mismatch or as
  * the bonus.  Draft logits are not read.

@@ -50,7 +50,7 @@ FLAG_INTERNAL = 1 << 7
 SPECV_F32 = 0
 SPECV_BF16 = 1
 
-EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_greedy",
+EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_point_mass", "specv_verify_greedy",
                     "specv_destroy", "specv_status_string", "specv_set_profiling",
                     "specv_get_profile")
 
@@ -105,6 +105,15 @@ def load_library():
         vp, vp, vp, vp,
         ctypes.POINTER(_Diag)]
     lib.specv_verify_sample.restype = ctypes.c_int
+    lib.specv_verify_point_mass.argtypes = [
+        vp, vp,
+        vp, i64, i64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, vp,
+        u64, u32, i32,
+        vp, vp, vp, vp,
+        ctypes.POINTER(_Diag)]
+    lib.specv_verify_point_mass.restype = ctypes.c_int
     lib.specv_verify_greedy.argtypes = [
         vp, vp,
         vp, i64, i64,
@@ -257,6 +266,40 @@ class Verifier:
             _ptr(o.get("row_flags")),
             ctypes.byref(d) if d is not None else None)
         _check(st, "specv_verify_sample")
+        return o
+
+    def verify_point_mass(self, target, tokens, row_params, seed, step=0, eos_id=-1, out=None,
+                          diag=False):
+        """Stochastic verification against deterministic drafts (q_i is the
+        point mass on d_i; no draft logits).  target [B, gamma+1, V], tokens
+        int32 [B, gamma], row_params from make_row_params.  Returns a dict of
+        device tensors as verify_sample."""
+        B, g1, V = target.shape
+        gamma = g1 - 1
+        tsb, tsp = _rows(target, "target", None)
+        for t, n in ((tokens, "tokens"), (row_params, "row_params")):
+            if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+                raise SpecvError(f"{n} must be a contiguous int32 device tensor")
+        if tokens.shape != (B, gamma) or row_params.shape != (B, 4):
+            raise SpecvError("tokens must be [B, gamma] and row_params [B, 4]")
+        o = self._outputs(B, gamma, target.device, out)
+        d = None
+        if diag:
+            o["p_at_draft"] = torch.empty(B, gamma, dtype=torch.float32, device=target.device)
+            o["q_at_draft"] = torch.empty(B, gamma, dtype=torch.float32, device=target.device)
+            o["residual_sum"] = torch.empty(B, dtype=torch.float32, device=target.device)
+            d = _Diag(o["p_at_draft"].data_ptr(), o["q_at_draft"].data_ptr(),
+                      o["residual_sum"].data_ptr())
+        st = load_library().specv_verify_point_mass(
+            self._h, self._stream(),
+            _ptr(target), tsb, tsp,
+            _dtype_code(target), B, gamma, V,
+            _ptr(tokens), _ptr(row_params),
+            int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF, int(eos_id),
+            _ptr(o["num_accepted"]), _ptr(o["out_tokens"]), _ptr(o["num_emitted"]),
+            _ptr(o.get("row_flags")),
+            ctypes.byref(d) if d is not None else None)
+        _check(st, "specv_verify_point_mass")
         return o
 
     def verify_greedy(self, target, tokens, max_new_tokens=None, eos_id=-1, out=None):

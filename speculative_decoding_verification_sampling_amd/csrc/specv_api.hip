@@ -265,23 +265,31 @@ specv_status specv_destroy(specv_handle h) {
     return SPECV_OK;
 }
 
-specv_status specv_verify_sample(specv_handle h, void* stream, const void* target_logits,
-                                 int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
-                                 int64_t d_stride_b, int64_t d_stride_pos, specv_dtype dtype, int B,
-                                 int gamma, int V, const int32_t* draft_tokens,
-                                 const specv_row_params* row_params, uint64_t seed, uint32_t step,
-                                 int32_t eos_id, int32_t* out_num_accepted, int32_t* out_tokens,
-                                 int32_t* out_num_emitted, int32_t* out_row_flags,
-                                 const specv_diag* diag) {
+}  // extern "C"
+
+namespace {
+
+// Stochastic verification (specv_verify_sample; with point_mass, the draft
+// logits are absent and q_i is the point mass on d_i).
+specv_status verify_sampling(specv_handle h, void* stream, const void* target_logits,
+                             int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
+                             int64_t d_stride_b, int64_t d_stride_pos, specv_dtype dtype, int B,
+                             int gamma, int V, const int32_t* draft_tokens,
+                             const specv_row_params* row_params, uint64_t seed, uint32_t step,
+                             int32_t eos_id, int32_t* out_num_accepted, int32_t* out_tokens,
+                             int32_t* out_num_emitted, int32_t* out_row_flags, const specv_diag* diag,
+                             bool point_mass) {
     specv_status st = check_common(h, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
                                    draft_tokens, out_num_accepted, out_tokens, out_num_emitted,
                                    out_row_flags);
     if (st != SPECV_OK || B == 0) return st;
     if (!row_params) return SPECV_E_NULL;
-    if (gamma > 0 && !draft_logits) return SPECV_E_NULL;
-    if (d_stride_b < 0 || d_stride_pos < 0) return SPECV_E_SHAPE;
     const size_t es = dtype == SPECV_BF16 ? 2 : 4;
-    if (gamma > 0 && !aligned(draft_logits, es)) return SPECV_E_ALIGN;
+    if (!point_mass) {
+        if (gamma > 0 && !draft_logits) return SPECV_E_NULL;
+        if (d_stride_b < 0 || d_stride_pos < 0) return SPECV_E_SHAPE;
+        if (gamma > 0 && !aligned(draft_logits, es)) return SPECV_E_ALIGN;
+    }
     if (!aligned(row_params, 16)) return SPECV_E_ALIGN;
     if (diag && ((diag->p_at_draft && !aligned(diag->p_at_draft, 4)) ||
                  (diag->q_at_draft && !aligned(diag->q_at_draft, 4)) ||
@@ -292,10 +300,11 @@ specv_status specv_verify_sample(specv_handle h, void* stream, const void* targe
     a.tgt = target_logits;
     a.t_sb = t_stride_b;
     a.t_sp = t_stride_pos;
-    a.drf = draft_logits;
-    a.d_sb = d_stride_b;
-    a.d_sp = d_stride_pos;
+    a.drf = point_mass ? nullptr : draft_logits;
+    a.d_sb = point_mass ? 0 : d_stride_b;
+    a.d_sp = point_mass ? 0 : d_stride_pos;
     a.greedy_all = 0;
+    a.point_mass = point_mass ? 1 : 0;
     a.tokens = draft_tokens;
     a.params = row_params;
     a.caps = nullptr;
@@ -310,9 +319,37 @@ specv_status specv_verify_sample(specv_handle h, void* stream, const void* targe
     a.q_at = diag ? diag->q_at_draft : nullptr;
     a.wres = diag ? diag->residual_sum : nullptr;
     const bool vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es) &&
-                     (gamma == 0 || rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es));
+                     (point_mass || gamma == 0 || rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es));
     return launch(h, a, dtype == SPECV_BF16, vec, stream);
-    return SPECV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+specv_status specv_verify_sample(specv_handle h, void* stream, const void* target_logits,
+                                 int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
+                                 int64_t d_stride_b, int64_t d_stride_pos, specv_dtype dtype, int B,
+                                 int gamma, int V, const int32_t* draft_tokens,
+                                 const specv_row_params* row_params, uint64_t seed, uint32_t step,
+                                 int32_t eos_id, int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags,
+                                 const specv_diag* diag) {
+    return verify_sampling(h, stream, target_logits, t_stride_b, t_stride_pos, draft_logits, d_stride_b,
+                           d_stride_pos, dtype, B, gamma, V, draft_tokens, row_params, seed, step, eos_id,
+                           out_num_accepted, out_tokens, out_num_emitted, out_row_flags, diag, false);
+}
+
+specv_status specv_verify_point_mass(specv_handle h, void* stream, const void* target_logits,
+                                     int64_t t_stride_b, int64_t t_stride_pos, specv_dtype dtype, int B,
+                                     int gamma, int V, const int32_t* draft_tokens,
+                                     const specv_row_params* row_params, uint64_t seed, uint32_t step,
+                                     int32_t eos_id, int32_t* out_num_accepted, int32_t* out_tokens,
+                                     int32_t* out_num_emitted, int32_t* out_row_flags,
+                                     const specv_diag* diag) {
+    return verify_sampling(h, stream, target_logits, t_stride_b, t_stride_pos, nullptr, 0, 0, dtype, B,
+                           gamma, V, draft_tokens, row_params, seed, step, eos_id, out_num_accepted,
+                           out_tokens, out_num_emitted, out_row_flags, diag, true);
 }
 
 specv_status specv_verify_greedy(specv_handle h, void* stream, const void* target_logits,

@@ -102,6 +102,8 @@ struct Args {
     int C;                        // chunks per row
     int P;                        // positions per batch row: gamma + 1
     int greedy_all;               // specv_verify_greedy
+    int point_mass;               // specv_verify_point_mass: q_i is the point mass on d_i and
+                                  // no draft logits are read
     int cand_cap;                 // candidates per (row, chunk); 0: no truncation
     int kept_cap;                 // kept-set entries per row: min(kKeptCap, max_vocab)
     int max_top_k;

@@ -1061,10 +1061,11 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     __shared__ float sWsum;
     __shared__ int sTok, sLastPos, sFb;
     const float scale = pl.scale;
+    const bool pm = a.point_mass != 0;      // q = the point mass on d_pos
     __syncthreads();
     if (tid == 0) {
         tT = published_trow(&a.ws.trow[side_row(a, b, pos, 0)]);
-        if (res) tQ = published_trow(&a.ws.trow[side_row(a, b, pos, 1)]);
+        if (res && !pm) tQ = published_trow(&a.ws.trow[side_row(a, b, pos, 1)]);
         sTok = 0x7fffffff;
         sLastPos = -1;
         sFb = 0;
@@ -1073,7 +1074,8 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     const int n = tT.n_kept;
     if (n <= 0) return -1;                  // (a dead row is never sampled)
     const Cand* kept = a.ws.kept + side_row(a, b, pos, 0) * a.kept_cap;
-    const void* qrow = res ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+    const int dpm = res && pm ? draft_token(a, b, pos) : -1;
+    const void* qrow = res && !pm ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
     // sc.v = weight, sc.idx = token, sc.w = p (fallback weight)
     float part = 0.f;
     for (int i = tid; i < n; i += kBlock) {
@@ -1081,10 +1083,15 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
         const float p = __fmul_rn(fast_exp2(__fmul_rn(cv.v - tT.zmax, scale)), 1.f / tT.S);
         float w = p;
         if (res) {
-            const float zq = load_elem<BF16>(qrow, cv.idx);
-            const float q = (finite_logit(zq) && zq >= tQ.tstar)
-                                ? __fmul_rn(fast_exp2(__fmul_rn(zq - tQ.zmax, scale)), 1.f / tQ.S)
-                                : 0.f;
+            float q;
+            if (pm) {
+                q = cv.idx == dpm ? 1.f : 0.f;
+            } else {
+                const float zq = load_elem<BF16>(qrow, cv.idx);
+                q = (finite_logit(zq) && zq >= tQ.tstar)
+                        ? __fmul_rn(fast_exp2(__fmul_rn(zq - tQ.zmax, scale)), 1.f / tQ.S)
+                        : 0.f;
+            }
             w = fmaxf(__fsub_rn(p, q), 0.f);
         }
         sc.v[i] = w;
@@ -1321,7 +1328,9 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
     const bool test = k < a.gamma;
-    const bool two = !greedy && test;
+    const bool pm = a.point_mass != 0;      // q_k is the point mass on d_k
+    const bool zneed = !greedy && test;     // z at d_k and the accept uniform
+    const bool two = zneed && !pm;          // the draft row is consulted
     const float scale = pl.scale;
     __shared__ float dM[2], dS[2], dZ[2], dU;
     __shared__ int dA, dBad[2], dLate[2];
@@ -1339,9 +1348,9 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
                 dT[0] = t0;
                 dT[1] = t1;
                 dLate[0] = dLate[1] = 0;
-                if (two) {
+                if (zneed) {
                     dZ[0] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), d);
-                    dZ[1] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
+                    if (two) dZ[1] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
                     dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
                 }
             }
@@ -1378,9 +1387,9 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
                 dLate[side] = late;
                 if (side == 0) dA = arg;
             }
-        } else if (wave == 2 && two) {
-            if (lane < 2) dZ[lane] = load_elem<BF16>(lane == 0 ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k)
-                                                               : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
+        } else if (wave == 2 && zneed) {
+            if (lane == 0) dZ[0] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), d);
+            if (lane == 1 && two) dZ[1] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
             if (lane == 2) dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
         }
     }
@@ -1408,8 +1417,8 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
                 outcome = OUT_BONUS;
             } else {
                 v.p = trunc_prob(t0, dZ[0], scale);
-                v.q = trunc_prob(t1, dZ[1], scale);
-                if (!(finite_logit(dZ[1]) && dZ[1] >= t1.tstar)) flags |= SPECV_FLAG_Q_ZERO;
+                v.q = pm ? 1.f : trunc_prob(t1, dZ[1], scale);
+                if (!pm && !(finite_logit(dZ[1]) && dZ[1] >= t1.tstar)) flags |= SPECV_FLAG_Q_ZERO;
                 outcome = dU * v.q < v.p ? OUT_ACC : OUT_REJ;
             }
         } else {
@@ -1428,8 +1437,8 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
                 outcome = OUT_BONUS;
             } else {
                 v.p = fast_exp2((dZ[0] - dM[0]) * scale) / dS[0];
-                v.q = fast_exp2((dZ[1] - dM[1]) * scale) / dS[1];
-                if (dZ[1] == -kInf) flags |= SPECV_FLAG_Q_ZERO;
+                v.q = pm ? 1.f : fast_exp2((dZ[1] - dM[1]) * scale) / dS[1];
+                if (!pm && dZ[1] == -kInf) flags |= SPECV_FLAG_Q_ZERO;
                 outcome = dU * v.q < v.p ? OUT_ACC : OUT_REJ;
             }
         }
@@ -1470,6 +1479,8 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
 // pair being sampled.
 struct Weights {
     int residual;        // 1: max(p - q, 0); 0: p
+    int dpm;             // point-mass proposal: q = delta(dpm), so the correction weight
+                         // is p except 0 at dpm; -1 otherwise
     float mt, st, invt;  // target row max, scale, 1 / sum
     float mq, invq;      // draft row max, 1 / sum
     // Products are rounded separately (no fused multiply-add) so that equal
@@ -1510,7 +1521,9 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
             const int i = j * G + e;
             const float pz = wt.p(rt.elem(i));
             sp += pz;
-            w[i] = wt.residual ? wt.w(rt.elem(i), rd.elem(i)) : pz;
+            if (!wt.residual) w[i] = pz;
+            else if (wt.dpm >= 0) w[i] = c * kChunk + chunk_index<BF16>(i) == wt.dpm ? 0.f : pz;
+            else w[i] = wt.w(rt.elem(i), rd.elem(i));
             s += w[i];
         }
         gw[j] = s;
@@ -1712,7 +1725,7 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
     }
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
-    const bool two = !greedy && k < a.gamma;
+    const bool two = !greedy && k < a.gamma && !a.point_mass;
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
     const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
     const int v0 = c * kChunk;
@@ -1831,7 +1844,7 @@ __device__ void sample_item(const Args& a, int b, int c) {
     const int kind = (int)(rec & 7u);
     if (kind != KIND_RESIDUAL && kind != KIND_BONUS) return;
     const int k = (int)((rec >> 3) & 31u);
-    const bool two = kind == KIND_RESIDUAL;
+    const bool two = kind == KIND_RESIDUAL && !a.point_mass;      // the draft row is read
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
     const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
     const int v0 = c * kChunk;
@@ -1842,7 +1855,8 @@ __device__ void sample_item(const Args& a, int b, int c) {
     rt.finish(trow, v0, len);
     if (two) rd.finish(drow, v0, len);
     Weights wt;
-    wt.residual = two;
+    wt.residual = kind == KIND_RESIDUAL;
+    wt.dpm = kind == KIND_RESIDUAL && a.point_mass ? draft_token(a, b, k) : -1;
     wt.mt = __uint_as_float(sRec[RW_MT]);
     wt.invt = __uint_as_float(sRec[RW_INVT]);
     wt.mq = __uint_as_float(sRec[RW_MQ]);

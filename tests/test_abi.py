@@ -61,6 +61,9 @@ def test_verify_rejects_null_handle(lib):
     rc = lib.specv_verify_greedy(None, None, None, 0, 0, 1, 1, 1, 1, None, None, -1,
                                  None, None, None, None)
     assert rc == 1
+    rc = lib.specv_verify_point_mass(None, None, None, 0, 0, 1, 1, 1, 1, None, None, 0, 0, -1,
+                                     None, None, None, None, None)
+    assert rc == 1
     assert lib.specv_destroy(None) == 0
 
 
