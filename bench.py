@@ -1,6 +1,7 @@
 """Throughput of the speculative-sampling verify step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu-baseline]
+                    [--workload serving|point-mass]
 
 Workload: the serving batch, B=64 rows, gamma=5 drafts, V=128256 bfloat16
 logits (target [64, 6, 128256], draft [64, 5, 128256]), T=0.7, synthetic
@@ -9,6 +10,11 @@ N(0, 1.5^2)), draft tokens drawn from the draft distribution.  A step is one
 call of the whole verify path over one batch.  Inputs are resident in HBM;
 ``--sets`` distinct copies of them are rotated so that the 256 MB
 memory-side cache cannot serve a call from the previous one.
+
+``--workload point-mass`` runs the same target logits against deterministic
+drafts (the argmax of the draft logits, standing in for n-gram /
+prompt-lookup proposals) through ``specv_verify_point_mass``, which reads no
+draft logits.
 
 Prints one JSON line: verified rows/s (``value``), the achieved HBM bandwidth
 of the dominant kernel (the streaming statistics kernel) on its algorithmic
@@ -26,21 +32,27 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "verified rows/sec + achieved HBM GB/s (% peak), V=128256 γ=5 B=64 bf16"
+METRIC_POINT_MASS = ("verified rows/sec + achieved HBM GB/s (% peak), point-mass drafts, "
+                     "V=128256 γ=5 B=64 bf16")
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_sampling_amd", "csrc",
                           "specv_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_verify_serving_batch.json")
+TRAFFIC_FILES = {
+    "serving": os.path.join(ROOT, "profiles", "traffic_k_verify_serving_batch.json"),
+    "point-mass": os.path.join(ROOT, "profiles", "traffic_k_verify_point_mass.json"),
+}
 
 
-def algorithmic_bytes(B, gamma, V, es, caps, eos_cut, greedy):
+def algorithmic_bytes(B, gamma, V, es, caps, eos_cut, greedy, point_mass=False):
     """Logits bytes the round may consult: per row, target rows
-    min(cap, gamma+1) and (stochastic rows) draft rows min(cap, gamma)."""
+    min(cap, gamma+1) and (stochastic rows with draft logits) draft rows
+    min(cap, gamma)."""
     total = 0
     for b in range(B):
         cap = caps[b] if caps[b] >= 1 else 1 << 30
         cap = min(cap, eos_cut[b])
         nt = min(cap, gamma + 1)
-        nd = 0 if greedy[b] else min(cap, gamma)
+        nd = 0 if greedy[b] or point_mass else min(cap, gamma)
         total += (nt + nd) * V * es
     return total
 
@@ -53,11 +65,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch of the statistics kernel from committed rocprofv3
-    counter runs, or None when absent or taken on different kernel sources."""
+def stored_traffic(workload):
+    """HBM bytes per launch of the verify kernel on ``workload`` from
+    committed rocprofv3 counter runs, or None when absent or taken on
+    different kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[workload]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -66,7 +79,7 @@ def stored_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s=15.0):
+def cpu_baseline(w, tokens, point_mass, budget_s=15.0):
     """The oracle as it stands, on this host, over whole batches of the same
     workload at successive steps until about ``budget_s`` seconds."""
     import oracle
@@ -75,8 +88,12 @@ def cpu_baseline(w, budget_s=15.0):
     steps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.verify_sample(tf, df, w.tokens, w.temperature, w.top_k, w.top_p,
-                             w.max_new_tokens, w.seed, steps)
+        if point_mass:
+            oracle.verify_point_mass(tf, tokens, w.temperature, w.top_k, w.top_p,
+                                     w.max_new_tokens, w.seed, steps)
+        else:
+            oracle.verify_sample(tf, df, tokens, w.temperature, w.top_k, w.top_p,
+                                 w.max_new_tokens, w.seed, steps)
         rows += w.B
         steps += 1
         el = time.perf_counter() - t0
@@ -94,6 +111,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("serving", "point-mass"), default="serving")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run --steps device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -125,18 +143,24 @@ def main():
         return
     sv.load_library()
 
+    point_mass = args.workload == "point-mass"
     w = synth.serving_batch()
     B, gamma, V = w.B, w.gamma, w.V
+    # deterministic drafts stand in for n-gram / prompt-lookup proposals
+    tok_np = (w.draft.to(torch.float32).numpy().argmax(-1).astype(np.int32) if point_mass
+              else w.tokens)
     sets = []
     for _ in range(max(1, args.sets)):
-        sets.append((w.target.to(dev), w.draft.to(dev)))
-    tokens = torch.from_numpy(w.tokens).to(dev)
+        sets.append((w.target.to(dev), None if point_mass else w.draft.to(dev)))
+    tokens = torch.from_numpy(tok_np).to(dev)
     params = sv.make_row_params(B, w.temperature, w.top_k, w.top_p, w.max_new_tokens, dev)
     out = None
     v = sv.Verifier(B, gamma, V)
 
     def call(k, step):
         t, d = sets[k % len(sets)]
+        if point_mass:
+            return v.verify_point_mass(t, tokens, params, w.seed, step, -1, out=out)
         return v.verify_sample(t, d, tokens, params, w.seed, step, -1, out=out)
 
     out = call(0, 0)
@@ -179,13 +203,13 @@ def main():
     es = w.bytes_per_element()
     eos_cut = [1 << 30] * B
     greedy = [bool(t == 0) for t in w.temperature]
-    abytes = algorithmic_bytes(B, gamma, V, es, w.max_new_tokens, eos_cut, greedy)
+    abytes = algorithmic_bytes(B, gamma, V, es, w.max_new_tokens, eos_cut, greedy, point_mass)
     achieved = abytes / (avg_kernel * 1e-3) / 1e9
-    traffic = stored_traffic()
+    traffic = stored_traffic(args.workload)
 
     rows_per_s = B / (ms_step * 1e-3)
     line = {
-        "metric": METRIC,
+        "metric": METRIC_POINT_MASS if point_mass else METRIC,
         "value": rows_per_s,
         "unit": "verified rows/s",
         "n_gpus": 1,
@@ -197,8 +221,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"serving batch B={B} gamma={gamma} V={V} bf16 T=0.7, "
-                               "20 boosted tokens, draft noise 1.5",
+        "config": {"workload": (f"serving batch B={B} gamma={gamma} V={V} bf16 T=0.7, "
+                                "20 boosted tokens, " +
+                                ("deterministic drafts (argmax of target + noise 1.5), no draft logits"
+                                 if point_mass else "draft noise 1.5")),
                    "B": B, "gamma": gamma, "V": V, "rotated_input_sets": len(sets)},
         "emitted_tokens_per_s": tokens_per_call / (ms_step * 1e-3),
         "step_hbm_gbps_algorithmic": abytes / (ms_step * 1e-3) / 1e9,
@@ -215,7 +241,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(w, tok_np, point_mass)
     v.close()
     print(json.dumps(line), flush=True)
 

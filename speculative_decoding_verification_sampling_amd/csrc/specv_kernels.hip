@@ -1053,7 +1053,7 @@ __device__ inline TruncRow published_trow(const TruncRow* p) {
 // ascending index order, first running sum > u * W.  Returns the token (-1 if
 // no weight anywhere) to every thread; *wres gets W of a correction, and
 // *fallback is set when the correction mass vanished and p was used.
-template <bool BF16>
+template <bool BF16, bool PM>
 __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, const Plan& pl,
                             TruncScratch& sc, float* wres, bool* fallback) {
     const int tid = threadIdx.x;
@@ -1061,7 +1061,7 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     __shared__ float sWsum;
     __shared__ int sTok, sLastPos, sFb;
     const float scale = pl.scale;
-    const bool pm = a.point_mass != 0;      // q = the point mass on d_pos
+    constexpr bool pm = PM;                 // q = the point mass on d_pos
     __syncthreads();
     if (tid == 0) {
         tT = published_trow(&a.ws.trow[side_row(a, b, pos, 0)]);
@@ -1201,7 +1201,7 @@ struct PairVals {
 // diagnostics; greedy, capped and dead rows get their outputs here,
 // truncated rows draw their token here from the kept lists, and sampling rows
 // hand the draw to their sampling workgroups through the row record.
-template <bool BF16, bool TRUNC>
+template <bool BF16, bool TRUNC, bool PM>
 __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, const Plan& pl,
                            unsigned long long st, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -1299,7 +1299,7 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
             const float u = uniform24(a.seed, b, pos, res ? PURPOSE_RESIDUAL : PURPOSE_BONUS, a.step);
             float wres;
             bool fb;
-            const int tok = trunc_sample<BF16>(a, b, pos, res, u, pl, *sc, &wres, &fb);
+            const int tok = trunc_sample<BF16, PM>(a, b, pos, res, u, pl, *sc, &wres, &fb);
             if (wave == 0) {
                 unsigned flags = fFlags | (fb ? SPECV_FLAG_RESIDUAL_FALLBACK : 0u);
                 bool dead = fDead;
@@ -1322,13 +1322,13 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
 // the row when that resolves it.  Readers of the pair record check its tags,
 // so its stores need not complete first, except for truncated rows, whose
 // kept lists and TruncRows are read untagged.
-template <bool BF16, bool TRUNC>
+template <bool BF16, bool TRUNC, bool PM>
 __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
     const bool test = k < a.gamma;
-    const bool pm = a.point_mass != 0;      // q_k is the point mass on d_k
+    constexpr bool pm = PM;                 // q_k is the point mass on d_k
     const bool zneed = !greedy && test;     // z at d_k and the accept uniform
     const bool two = zneed && !pm;          // the draft row is consulted
     const float scale = pl.scale;
@@ -1388,8 +1388,11 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
                 if (side == 0) dA = arg;
             }
         } else if (wave == 2 && zneed) {
-            if (lane == 0) dZ[0] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), d);
-            if (lane == 1 && two) dZ[1] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
+            // one load instruction for both rows' z at d_k (lane 0: target,
+            // lane 1: draft), so that they share a round trip
+            if (lane == 0 || (lane == 1 && two))
+                dZ[lane] = load_elem<BF16>(lane == 0 ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k)
+                                                     : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
             if (lane == 2) dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
         }
     }
@@ -1471,7 +1474,7 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
         dFinish = resolve(old, pl, a.gamma).how == H_OPEN && resolve(now, pl, a.gamma).how != H_OPEN;
     }
     __syncthreads();
-    if (dFinish) finish_row<BF16, TRUNC>(a, b, k, dOwn, pl, dNew, sc);
+    if (dFinish) finish_row<BF16, TRUNC, PM>(a, b, k, dOwn, pl, dNew, sc);
 }
 
 // ---------------------------------------------------------------- sampling
@@ -1502,7 +1505,7 @@ struct Weights {
 // them, and the workgroup whose chunk holds u * W scans it (tokens in
 // ascending order, first running sum > u * W) and writes the outputs.
 // ``flags_in``: the row's flags so far.  Whole workgroup.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool PM>
 __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan& pl, Weights wt,
                                  unsigned flags_in, const ChunkRegs<BF16, VEC>& rt,
                                  const ChunkRegs<BF16, VEC>& rd) {
@@ -1513,21 +1516,37 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
     // the weights of this thread's entries (kept for the scan), their group
     // sums, and the p mass
     float w[kPerThread], gw[NG], sw = 0.f, sp = 0.f;
+    if (PM && wt.dpm >= 0) {
+        // point-mass proposal: p, except 0 at the proposed token
 #pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        float s = 0.f;
+        for (int j = 0; j < NG; ++j) {
+            float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < G; ++e) {
-            const int i = j * G + e;
-            const float pz = wt.p(rt.elem(i));
-            sp += pz;
-            if (!wt.residual) w[i] = pz;
-            else if (wt.dpm >= 0) w[i] = c * kChunk + chunk_index<BF16>(i) == wt.dpm ? 0.f : pz;
-            else w[i] = wt.w(rt.elem(i), rd.elem(i));
-            s += w[i];
+            for (int e = 0; e < G; ++e) {
+                const int i = j * G + e;
+                const float pz = wt.p(rt.elem(i));
+                sp += pz;
+                w[i] = c * kChunk + chunk_index<BF16>(i) == wt.dpm ? 0.f : pz;
+                s += w[i];
+            }
+            gw[j] = s;
+            sw += s;
         }
-        gw[j] = s;
-        sw += s;
+    } else {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < G; ++e) {
+                const int i = j * G + e;
+                const float pz = wt.p(rt.elem(i));
+                sp += pz;
+                w[i] = wt.residual ? wt.w(rt.elem(i), rd.elem(i)) : pz;
+                s += w[i];
+            }
+            gw[j] = s;
+            sw += s;
+        }
     }
     __shared__ float red[2][kWaves];
     sw = wave_sum(sw);
@@ -1699,7 +1718,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
 #endif
 constexpr int kSkipFrom = SPECV_SKIP_FROM;
 
-template <bool BF16, bool VEC, bool TRUNC>
+template <bool BF16, bool VEC, bool TRUNC, bool PM>
 __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const unsigned par = a.epoch & 1u;
@@ -1725,7 +1744,7 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
     }
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
-    const bool two = !greedy && k < a.gamma && !a.point_mass;
+    const bool two = !greedy && k < a.gamma && !PM;
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
     const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
     const int v0 = c * kChunk;
@@ -1807,14 +1826,14 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
     }
     if (tid == 0) sLast = arrive(pair_counter(a, par, b, k), trunc) == (unsigned)(a.C - 1);
     __syncthreads();
-    if (sLast) decide_pair<BF16, TRUNC>(a, b, k, pl, sc);
+    if (sLast) decide_pair<BF16, TRUNC, PM>(a, b, k, pl, sc);
 }
 
 // Sampling workgroup (b, c) of a sampling row: waits for the row record,
 // then reads chunk c of the target (and draft) row of the position the round
 // stopped at, or of the bonus row, and takes part in the sample.  Rows of
 // other modes never need one.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool PM>
 __device__ void sample_item(const Args& a, int b, int c) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const Plan pl = make_plan(a, b);
@@ -1844,7 +1863,7 @@ __device__ void sample_item(const Args& a, int b, int c) {
     const int kind = (int)(rec & 7u);
     if (kind != KIND_RESIDUAL && kind != KIND_BONUS) return;
     const int k = (int)((rec >> 3) & 31u);
-    const bool two = kind == KIND_RESIDUAL && !a.point_mass;      // the draft row is read
+    const bool two = kind == KIND_RESIDUAL && !PM;                // the draft row is read
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
     const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
     const int v0 = c * kChunk;
@@ -1856,13 +1875,13 @@ __device__ void sample_item(const Args& a, int b, int c) {
     if (two) rd.finish(drow, v0, len);
     Weights wt;
     wt.residual = kind == KIND_RESIDUAL;
-    wt.dpm = kind == KIND_RESIDUAL && a.point_mass ? draft_token(a, b, k) : -1;
+    wt.dpm = PM && kind == KIND_RESIDUAL ? draft_token(a, b, k) : -1;
     wt.mt = __uint_as_float(sRec[RW_MT]);
     wt.invt = __uint_as_float(sRec[RW_INVT]);
     wt.mq = __uint_as_float(sRec[RW_MQ]);
     wt.invq = __uint_as_float(sRec[RW_INVQ]);
     wt.st = pl.scale;
-    sample_from_regs<BF16, VEC>(a, b, k, c, pl, wt, (rec >> 8) & 0xffu, rt, rd);
+    sample_from_regs<BF16, VEC, PM>(a, b, k, c, pl, wt, (rec >> 8) & 0xffu, rt, rd);
 }
 
 // ---------------------------------------------------------------- k_verify
@@ -1883,7 +1902,7 @@ __device__ inline void clear_other_parity(const Args& a) {
         publish(a.ws.status + ((long long)other * a.ws.n_rows + i) * (kSlot / 2), 0ull);
 }
 
-template <bool BF16, bool VEC, bool TRUNC>
+template <bool BF16, bool VEC, bool TRUNC, bool PM>
 __device__ inline void verify_block(const Args& a, TruncScratch* sc) {
     clear_other_parity(a);
     const int per_pos = a.B * a.C;
@@ -1892,30 +1911,37 @@ __device__ inline void verify_block(const Args& a, TruncScratch* sc) {
     const int rem = t - k * per_pos;
     const int b = rem / a.C;
     const int c = rem - b * a.C;
-    if (k < a.P) stream_unit<BF16, VEC, TRUNC>(a, k, b, c, sc);
-    else sample_item<BF16, VEC>(a, b, c);
+    if (k < a.P) stream_unit<BF16, VEC, TRUNC, PM>(a, k, b, c, sc);
+    else sample_item<BF16, VEC, PM>(a, b, c);
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool PM>
 __global__ __launch_bounds__(kBlock) void k_verify(Args a) {
-    verify_block<BF16, VEC, false>(a, nullptr);
+    verify_block<BF16, VEC, false, PM>(a, nullptr);
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool PM>
 __global__ __launch_bounds__(kBlock) void k_verify_trunc(Args a) {
     __shared__ TruncScratch sc;
-    verify_block<BF16, VEC, true>(a, &sc);
+    verify_block<BF16, VEC, true, PM>(a, &sc);
 }
 
 using KernelFn = void (*)(Args);
 
-KernelFn pick(bool bf16, bool vec, bool trunc) {
+// The point-mass variants (PM) are separate instantiations, so that the
+// two-model kernels carry none of their code.
+template <bool PM>
+KernelFn pick_pm(bool bf16, bool vec, bool trunc) {
     if (trunc) {
-        if (bf16) return vec ? k_verify_trunc<true, true> : k_verify_trunc<true, false>;
-        return vec ? k_verify_trunc<false, true> : k_verify_trunc<false, false>;
+        if (bf16) return vec ? k_verify_trunc<true, true, PM> : k_verify_trunc<true, false, PM>;
+        return vec ? k_verify_trunc<false, true, PM> : k_verify_trunc<false, false, PM>;
     }
-    if (bf16) return vec ? k_verify<true, true> : k_verify<true, false>;
-    return vec ? k_verify<false, true> : k_verify<false, false>;
+    if (bf16) return vec ? k_verify<true, true, PM> : k_verify<true, false, PM>;
+    return vec ? k_verify<false, true, PM> : k_verify<false, false, PM>;
+}
+
+KernelFn pick(bool bf16, bool vec, bool trunc, bool pm) {
+    return pm ? pick_pm<true>(bf16, vec, trunc) : pick_pm<false>(bf16, vec, trunc);
 }
 
 }  // namespace
@@ -1923,7 +1949,7 @@ KernelFn pick(bool bf16, bool vec, bool trunc) {
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev) {
     const long long blocks = (long long)(a.P + 1) * a.B * a.C;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    KernelFn fn = pick(bf16, vec, a.cand_cap > 0);
+    KernelFn fn = pick(bf16, vec, a.cand_cap > 0, a.point_mass != 0);
     // the events (when profiling) are attached to the dispatch itself, so
     // that they time the kernel and not the packets around it
     hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev ? ev[0] : nullptr,
