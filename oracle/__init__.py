@@ -36,6 +36,7 @@ from .verify import (
     inverse_cdf,
     cdf_interval,
     sample_draft_tokens,
+    draft_row_stats,
     FLAG_TOKEN_OOR,
     FLAG_NONFINITE_ROW,
     FLAG_Q_ZERO,

@@ -41,11 +41,19 @@ the same round with q_i = delta(d_i): the test reads u < p_i(d_i), and the
 correction distribution norm(max(p_i - delta(d_i), 0)) is p_i with d_i
 removed.  No draft logits exist.
 
+The drafter's side: ``sample_draft_tokens`` draws d_i ~ q_i (the processed
+draft distribution, inverse CDF with the uniform of purpose DRAFT), and
+``draft_row_stats`` gives the statistics a drafter that sampled q_i can hand
+to the verifier, m = max z and s = sum exp((z - m) / T), from which
+q_i(v) = exp((z_v - m) / T) / s on an untruncated row.
+
 Pins (``tests/test_oracle_*.py``): the worked example of 11.1.3, exact
 enumeration over all 2^24 uniforms on small rows, the 11.1.3 identities,
 E[N] against the closed form of the ICML summary and the tutorial's printed
 E(4), E(8) at alpha = 0.7, chi-square tests of the emitted distribution, and
-the greedy path against ``torch.argmax``.
+the greedy path against ``torch.argmax``; the drafter's draw by exact
+enumeration against ``torch.softmax``, its statistics against
+``torch.logsumexp``.
 """
 
 import numpy as np
@@ -356,12 +364,40 @@ def verify_greedy(target, tokens, max_new_tokens=0, eos_id=-1):
     return _finish(results, B, gamma)
 
 
-def sample_draft_tokens(draft, temperature, top_k, top_p, seed, step=0):
+def draft_row_stats(draft, temperature):
+    """Statistics of each draft row, as a drafter that samples q_i can hand
+    them to the verifier: m = the largest logit and s = sum_v exp((z_v - m)/T),
+    so that q_i(v) = exp((z_v - m)/T) / s for an untruncated row (the
+    temperature division of the tutorial's section 3.3).  Rows with
+    temperature 0, or with NaN / +inf / no finite logit, get NaN for both.
+    Returns float64 [B, gamma, 2]."""
+    draft = np.asarray(draft, np.float64)
+    B, gamma, V = draft.shape
+    T = _broadcast(temperature, B, np.float64)
+    out = np.full((B, gamma, 2), np.nan)
+    for b in range(B):
+        if T[b] == 0.0:
+            continue
+        for i in range(gamma):
+            z = draft[b, i]
+            if np.isnan(z).any() or np.isposinf(z).any() or not np.isfinite(z).any():
+                continue
+            m = z.max()
+            out[b, i, 0] = m
+            out[b, i, 1] = np.exp((z - m) / T[b]).sum()
+    return out
+
+
+def sample_draft_tokens(draft, temperature, top_k, top_p, seed, step=0, pos0=0):
     """Harness stand-in for the draft model's sampling: d_i ~ q_i.
 
     Each d_i is drawn by inverse CDF from the processed draft distribution
     with the uniform of purpose DRAFT.  Rows with temperature 0 take the
-    draft argmax (what a greedy drafter emits).
+    draft argmax (what a greedy drafter emits).  A row with NaN / +inf or
+    no finite logit defines no distribution, and gets -1 (no token).
+    ``draft[:, i]`` is the round's draft position pos0 + i (the uniform's
+    counter), so a drafter that samples one position at a time passes one
+    column and its position.
     """
     draft = np.asarray(draft)
     B, gamma, V = draft.shape
@@ -372,9 +408,13 @@ def sample_draft_tokens(draft, temperature, top_k, top_p, seed, step=0):
     for b in range(B):
         for i in range(gamma):
             if T[b] == 0.0:
-                toks[b, i] = greedy_argmax(draft[b, i])
+                g = greedy_argmax(draft[b, i])
+                toks[b, i] = -1 if g is None else g
                 continue
             Q = process_row(draft[b, i], T[b], K[b], Pp[b])
-            u = float(uniform(seed, b, i, PURPOSE_DRAFT, step))
+            if Q.nonfinite:
+                toks[b, i] = -1
+                continue
+            u = float(uniform(seed, b, pos0 + i, PURPOSE_DRAFT, step))
             toks[b, i] = inverse_cdf(Q.probs, u)
     return toks
