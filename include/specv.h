@@ -32,8 +32,9 @@
  *
  * Random numbers: Philox4x32-10 (Salmon et al., SC'11), key = seed (low word
  * first), counter = (b, i, purpose, step), u = (word0 >> 8) * 2^-24.
- * Purposes: 1 accept test, 2 correction sample, 3 bonus sample (0 is left to
- * the caller's draft sampler).  b is the row index within the call.
+ * Purposes: 0 draft sample (specv_sample_draft), 1 accept test, 2 correction
+ * sample, 3 bonus sample.  b is the row index within the call and i the
+ * position within the round.
  *
  * Ownership: the caller owns every input and output buffer.  A handle owns a
  * device workspace allocated once by specv_create and freed by
@@ -171,6 +172,67 @@ SPECV_API specv_status specv_verify_point_mass(specv_handle h, void* stream,
                                  int32_t* out_num_emitted, int32_t* out_row_flags,
                                  const specv_diag* diag);
 
+/* Draft-side sampler: draws d_i ~ q_i for positions pos0 .. pos0+n_pos-1 of
+ * B rows in one pass over the draft logits, and returns each row's
+ * statistics for specv_verify_sample_qstats.  q_i is the draft distribution
+ * after the row's temperature ("11.1 核心原理" 11.1.2: the proposal is the
+ * distribution actually sampled; the "投机解码 Speculative Decoding"
+ * tutorial, section 3.3, for the temperature); the draw is the inverse CDF at
+ * the Philox uniform of purpose 0 with counter (b, pos0 + i, 0, step):
+ * ascending token order, the first token whose running mass exceeds u * W.
+ * A drafter that produces one position at a time calls this once per
+ * position (n_pos = 1, pos0 = the position).
+ *   draft_logits    [B, n_pos, V] of dtype; row (b, i) is position pos0 + i
+ *                   and starts at draft + b*d_stride_b + i*d_stride_pos
+ *   row_params      specv_row_params [B] (max_new_tokens is not used)
+ *   out_tokens      int32 [B, out_stride]: entry (b, pos0 + i) gets d_i, or -1
+ *                   for a row that defines no draw (below)
+ *   out_stats       float [B, out_stride, 2] or NULL: entry (b, pos0 + i) gets
+ *                   (m, s), m = max_v z_v and s = sum_v exp((z_v - m) / T) in
+ *                   float32, so that q_i(v) = exp((z_v - m) / T) / s; NaN for
+ *                   greedy and undrawn rows
+ *   out_flags       int32 [B, out_stride] or NULL: SPECV_FLAG_NONFINITE_ROW
+ *                   (NaN / +inf or no finite logit: token -1),
+ *                   SPECV_FLAG_UNSUPPORTED (top-k or top-p on: this sampler
+ *                   draws untruncated and greedy rows only; token -1),
+ *                   SPECV_FLAG_INTERNAL (a bounded wait expired), else 0
+ * Rows with temperature 0 take the draft argmax (lowest index on ties).
+ * Other entries of the outputs are left as they are.  0 <= pos0,
+ * pos0 + n_pos <= out_stride, n_pos <= max(max_gamma, 1), B <= max_batch,
+ * V <= max_vocab (SPECV_E_SHAPE / SPECV_E_CAPACITY); n_pos == 0 or B == 0 is
+ * a no-op.  Calls on a handle, sampler or verify, must not overlap. */
+SPECV_API specv_status specv_sample_draft(specv_handle h, void* stream,
+                                 const void* draft_logits, int64_t d_stride_b, int64_t d_stride_pos,
+                                 specv_dtype dtype, int B, int n_pos, int V, int pos0,
+                                 const specv_row_params* row_params, uint64_t seed, uint32_t step,
+                                 int32_t* out_tokens, float* out_stats, int32_t* out_flags,
+                                 int64_t out_stride);
+
+/* Stochastic verification reusing the drafter's row statistics: the round of
+ * specv_verify_sample, with draft_stats [B, s_stride_b, 2] (float32; entry
+ * (b, i) for position i, as specv_sample_draft writes them) standing for the
+ * normalisers of the untruncated sampling rows' draft distributions:
+ * q_i(v) = exp((z_v - m) / T) / s.  Such rows read no draft row for their
+ * accept tests (only the entry at d_i); the draft row where the round stops
+ * is read for the correction draw.  The statistics must come from the same
+ * draft logits and temperatures as this call's; a NaN, a zero s or an m of
+ * -inf marks the row non-finite.  Greedy and truncated rows ignore the
+ * statistics (truncated rows reduce their draft rows as specv_verify_sample
+ * does).  With statistics from specv_sample_draft the outputs equal
+ * specv_verify_sample's bit for bit.  s_stride_b >= gamma; draft_stats
+ * 8-byte aligned.  Other arguments, layouts, ownership and errors as
+ * specv_verify_sample. */
+SPECV_API specv_status specv_verify_sample_qstats(specv_handle h, void* stream,
+                                 const void* target_logits, int64_t t_stride_b, int64_t t_stride_pos,
+                                 const void* draft_logits, int64_t d_stride_b, int64_t d_stride_pos,
+                                 const float* draft_stats, int64_t s_stride_b,
+                                 specv_dtype dtype, int B, int gamma, int V,
+                                 const int32_t* draft_tokens, const specv_row_params* row_params,
+                                 uint64_t seed, uint32_t step, int32_t eos_id,
+                                 int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags,
+                                 const specv_diag* diag);
+
 /* Greedy verification (11.1.2): accept while d_i == argmax of the raw target
  * logits (lowest index on ties), emit the argmax at the first mismatch or as
  * the bonus.  Draft logits are not read.
@@ -183,9 +245,9 @@ SPECV_API specv_status specv_verify_greedy(specv_handle h, void* stream,
                                  int32_t* out_num_accepted, int32_t* out_tokens,
                                  int32_t* out_num_emitted, int32_t* out_row_flags);
 
-/* Kernel timing for measurement.  With enable != 0 every later verify call
- * records HIP events on its stream around its kernel (each call is one
- * kernel launch); the events are created here, not in the verify calls.
+/* Kernel timing for measurement.  With enable != 0 every later call (verify
+ * or sampler) records HIP events on its stream around its kernel (each call
+ * is one kernel launch); the events are created here, not in the verify calls.
  * specv_get_profile waits for the recorded events and returns the number of
  * profiled calls and their summed kernel milliseconds since the last reset,
  * and resets the sums when reset != 0.  Errors: SPECV_E_NULL, SPECV_E_HIP. */

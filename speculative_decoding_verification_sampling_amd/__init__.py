@@ -50,7 +50,8 @@ FLAG_INTERNAL = 1 << 7
 SPECV_F32 = 0
 SPECV_BF16 = 1
 
-EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_point_mass", "specv_verify_greedy",
+EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_point_mass",
+                    "specv_verify_sample_qstats", "specv_sample_draft", "specv_verify_greedy",
                     "specv_destroy", "specv_status_string", "specv_set_profiling",
                     "specv_get_profile")
 
@@ -114,6 +115,24 @@ def load_library():
         vp, vp, vp, vp,
         ctypes.POINTER(_Diag)]
     lib.specv_verify_point_mass.restype = ctypes.c_int
+    lib.specv_verify_sample_qstats.argtypes = [
+        vp, vp,
+        vp, i64, i64,
+        vp, i64, i64,
+        vp, i64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, vp,
+        u64, u32, i32,
+        vp, vp, vp, vp,
+        ctypes.POINTER(_Diag)]
+    lib.specv_verify_sample_qstats.restype = ctypes.c_int
+    lib.specv_sample_draft.argtypes = [
+        vp, vp,
+        vp, i64, i64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, u64, u32,
+        vp, vp, vp, i64]
+    lib.specv_sample_draft.restype = ctypes.c_int
     lib.specv_verify_greedy.argtypes = [
         vp, vp,
         vp, i64, i64,
@@ -234,6 +253,19 @@ class Verifier:
         (same dtype), tokens int32 [B, gamma], row_params from make_row_params.
         Returns a dict of device tensors (plus p_at_draft, q_at_draft,
         residual_sum when ``diag``).  Asynchronous on the current stream."""
+        return self._verify_two_model(target, draft, None, tokens, row_params, seed, step, eos_id,
+                                      out, diag)
+
+    def verify_sample_qstats(self, target, draft, draft_stats, tokens, row_params, seed, step=0,
+                             eos_id=-1, out=None, diag=False):
+        """Stochastic verification reusing the drafter's row statistics:
+        draft_stats float32 [B, >= gamma, 2] (max, sum) per draft row, as
+        ``sample_draft`` returns them.  Otherwise as verify_sample."""
+        return self._verify_two_model(target, draft, draft_stats, tokens, row_params, seed, step,
+                                      eos_id, out, diag)
+
+    def _verify_two_model(self, target, draft, draft_stats, tokens, row_params, seed, step, eos_id,
+                          out, diag):
         B, g1, V = target.shape
         gamma = g1 - 1
         tsb, tsp = _rows(target, "target", None)
@@ -255,18 +287,58 @@ class Verifier:
             o["residual_sum"] = torch.empty(B, dtype=torch.float32, device=target.device)
             d = _Diag(o["p_at_draft"].data_ptr(), o["q_at_draft"].data_ptr(),
                       o["residual_sum"].data_ptr())
-        st = load_library().specv_verify_sample(
-            self._h, self._stream(),
-            _ptr(target), tsb, tsp,
-            _ptr(draft if gamma > 0 else None), dsb, dsp,
-            _dtype_code(target), B, gamma, V,
-            _ptr(tokens), _ptr(row_params),
-            int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF, int(eos_id),
-            _ptr(o["num_accepted"]), _ptr(o["out_tokens"]), _ptr(o["num_emitted"]),
-            _ptr(o.get("row_flags")),
-            ctypes.byref(d) if d is not None else None)
-        _check(st, "specv_verify_sample")
+        common = (_dtype_code(target), B, gamma, V,
+                  _ptr(tokens), _ptr(row_params),
+                  int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF, int(eos_id),
+                  _ptr(o["num_accepted"]), _ptr(o["out_tokens"]), _ptr(o["num_emitted"]),
+                  _ptr(o.get("row_flags")),
+                  ctypes.byref(d) if d is not None else None)
+        drows = (_ptr(target), tsb, tsp, _ptr(draft if gamma > 0 else None), dsb, dsp)
+        if draft_stats is None:
+            st = load_library().specv_verify_sample(self._h, self._stream(), *drows, *common)
+            _check(st, "specv_verify_sample")
+            return o
+        if (draft_stats.dtype != torch.float32 or not draft_stats.is_cuda or draft_stats.dim() != 3
+                or draft_stats.shape[0] != B or draft_stats.shape[1] < gamma
+                or draft_stats.shape[2] != 2 or not draft_stats.is_contiguous()):
+            raise SpecvError("draft_stats must be a contiguous float32 [B, >= gamma, 2] device tensor")
+        st = load_library().specv_verify_sample_qstats(
+            self._h, self._stream(), *drows, _ptr(draft_stats), draft_stats.shape[1], *common)
+        _check(st, "specv_verify_sample_qstats")
         return o
+
+    def sample_draft(self, draft, row_params, seed, step=0, pos0=0, width=None, out=None):
+        """Draft-side sampler: d_i ~ q_i for positions pos0 .. pos0 + n - 1
+        of the round, from draft logits [B, n, V] (float32 or bfloat16), with
+        each row's statistics (max, sum) for verify_sample_qstats.  Returns
+        {"tokens": int32 [B, width], "stats": float32 [B, width, 2],
+        "flags": int32 [B, width]} (``width`` defaults to pos0 + n); pass
+        ``out`` (such a dict) to fill columns of existing tensors, e.g. one
+        position per call.  Asynchronous on the current stream."""
+        B, n, V = draft.shape
+        dsb, dsp = _rows(draft, "draft", None)
+        if row_params.dtype != torch.int32 or not row_params.is_contiguous() or row_params.shape != (B, 4):
+            raise SpecvError("row_params must be a contiguous int32 [B, 4] device tensor")
+        if out is None:
+            w = pos0 + n if width is None else int(width)
+            out = {"tokens": torch.full((B, w), -1, dtype=torch.int32, device=draft.device),
+                   "stats": torch.full((B, w, 2), float("nan"), dtype=torch.float32, device=draft.device),
+                   "flags": torch.zeros(B, w, dtype=torch.int32, device=draft.device)}
+        tok, sts, fl = out["tokens"], out.get("stats"), out.get("flags")
+        w = tok.shape[1]
+        if tok.dtype != torch.int32 or not tok.is_contiguous() or tok.shape[0] != B:
+            raise SpecvError("tokens output must be a contiguous int32 [B, width] tensor")
+        if sts is not None and (sts.dtype != torch.float32 or not sts.is_contiguous()
+                                or tuple(sts.shape) != (B, w, 2)):
+            raise SpecvError("stats output must be a contiguous float32 [B, width, 2] tensor")
+        if fl is not None and (fl.dtype != torch.int32 or not fl.is_contiguous() or tuple(fl.shape) != (B, w)):
+            raise SpecvError("flags output must be a contiguous int32 [B, width] tensor")
+        st = load_library().specv_sample_draft(
+            self._h, self._stream(), _ptr(draft), dsb, dsp, _dtype_code(draft), B, n, V, int(pos0),
+            _ptr(row_params), int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF,
+            _ptr(tok), _ptr(sts), _ptr(fl), w)
+        _check(st, "specv_sample_draft")
+        return out
 
     def verify_point_mass(self, target, tokens, row_params, seed, step=0, eos_id=-1, out=None,
                           diag=False):

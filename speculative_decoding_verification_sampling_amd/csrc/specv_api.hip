@@ -29,6 +29,7 @@ struct specv_ctx {
     int prof_calls = 0;
     double ms_kernel = 0.0;
     unsigned epoch = 0;             // call number; the kernel tags published decisions with it
+    unsigned draft_epoch = 0;       // draft sampler call number (its own tagged words)
 };
 
 namespace {
@@ -78,6 +79,7 @@ void free_ws(specv::Workspace& ws) {
     if (ws.cand_meta) (void)hipFree(ws.cand_meta);
     if (ws.trow) (void)hipFree(ws.trow);
     if (ws.kept) (void)hipFree(ws.kept);
+    if (ws.dstats) (void)hipFree(ws.dstats);
     ws = specv::Workspace{};
 }
 
@@ -123,6 +125,14 @@ specv::Args base_args(specv_handle h, int B, int gamma, int V) {
     return a;
 }
 
+size_t draft_stats_words(const specv_ctx* h) {
+    return (size_t)h->cfg.max_batch * std::max(h->cfg.max_gamma, 1) * h->max_chunks * 2;
+}
+
+hipError_t clear_draft_ws(specv_ctx* h, hipStream_t stream) {
+    return hipMemsetAsync(h->ws.dstats, 0, draft_stats_words(h) * sizeof(unsigned long long), stream);
+}
+
 // Zero the epoch-tagged records and the arrival counters (handle creation,
 // and the rare epoch wrap).  Fresh allocations may
 // hold another handle's words with the same epoch numbers, so every tagged
@@ -141,6 +151,7 @@ hipError_t clear_ws(specv_ctx* h, hipStream_t stream) {
     if (e == hipSuccess) e = hipMemsetAsync(ws.ctr, 0, 2 * groups * specv::kSlot * sizeof(unsigned), stream);
     if (e == hipSuccess)
         e = hipMemsetAsync(ws.status, 0, 2 * rows * specv::kSlot * sizeof(unsigned), stream);
+    if (e == hipSuccess) e = clear_draft_ws(h, stream);
     return e;
 }
 
@@ -210,7 +221,8 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
               alloc(&ws.rowrec, (size_t)cfg->max_batch * specv::kRowWords) == hipSuccess &&
               alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks * 2) == hipSuccess &&
               alloc(&ws.ctr, 2 * groups * specv::kSlot) == hipSuccess &&
-              alloc(&ws.status, (size_t)2 * cfg->max_batch * (specv::kSlot / 2)) == hipSuccess;
+              alloc(&ws.status, (size_t)2 * cfg->max_batch * (specv::kSlot / 2)) == hipSuccess &&
+              alloc(&ws.dstats, draft_stats_words(h)) == hipSuccess;
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
@@ -269,16 +281,18 @@ specv_status specv_destroy(specv_handle h) {
 
 namespace {
 
-// Stochastic verification (specv_verify_sample; with point_mass, the draft
-// logits are absent and q_i is the point mass on d_i).
+// Stochastic verification.  prop: 0 draft logits (specv_verify_sample);
+// 1 no draft logits, q_i is the point mass on d_i (specv_verify_point_mass);
+// 2 draft logits plus the drafter's row statistics (specv_verify_sample_qstats).
 specv_status verify_sampling(specv_handle h, void* stream, const void* target_logits,
                              int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
-                             int64_t d_stride_b, int64_t d_stride_pos, specv_dtype dtype, int B,
-                             int gamma, int V, const int32_t* draft_tokens,
-                             const specv_row_params* row_params, uint64_t seed, uint32_t step,
-                             int32_t eos_id, int32_t* out_num_accepted, int32_t* out_tokens,
-                             int32_t* out_num_emitted, int32_t* out_row_flags, const specv_diag* diag,
-                             bool point_mass) {
+                             int64_t d_stride_b, int64_t d_stride_pos, const float* draft_stats,
+                             int64_t s_stride_b, specv_dtype dtype, int B, int gamma, int V,
+                             const int32_t* draft_tokens, const specv_row_params* row_params,
+                             uint64_t seed, uint32_t step, int32_t eos_id, int32_t* out_num_accepted,
+                             int32_t* out_tokens, int32_t* out_num_emitted, int32_t* out_row_flags,
+                             const specv_diag* diag, int prop) {
+    const bool point_mass = prop == 1;
     specv_status st = check_common(h, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
                                    draft_tokens, out_num_accepted, out_tokens, out_num_emitted,
                                    out_row_flags);
@@ -289,6 +303,11 @@ specv_status verify_sampling(specv_handle h, void* stream, const void* target_lo
         if (gamma > 0 && !draft_logits) return SPECV_E_NULL;
         if (d_stride_b < 0 || d_stride_pos < 0) return SPECV_E_SHAPE;
         if (gamma > 0 && !aligned(draft_logits, es)) return SPECV_E_ALIGN;
+    }
+    if (prop == 2 && gamma > 0) {
+        if (!draft_stats) return SPECV_E_NULL;
+        if (s_stride_b < gamma) return SPECV_E_SHAPE;
+        if (!aligned(draft_stats, 8)) return SPECV_E_ALIGN;
     }
     if (!aligned(row_params, 16)) return SPECV_E_ALIGN;
     if (diag && ((diag->p_at_draft && !aligned(diag->p_at_draft, 4)) ||
@@ -304,7 +323,9 @@ specv_status verify_sampling(specv_handle h, void* stream, const void* target_lo
     a.d_sb = point_mass ? 0 : d_stride_b;
     a.d_sp = point_mass ? 0 : d_stride_pos;
     a.greedy_all = 0;
-    a.point_mass = point_mass ? 1 : 0;
+    a.prop = prop;
+    a.qstats = prop == 2 ? draft_stats : nullptr;
+    a.qs_sb = prop == 2 ? s_stride_b : 0;
     a.tokens = draft_tokens;
     a.params = row_params;
     a.caps = nullptr;
@@ -336,8 +357,25 @@ specv_status specv_verify_sample(specv_handle h, void* stream, const void* targe
                                  int32_t* out_num_emitted, int32_t* out_row_flags,
                                  const specv_diag* diag) {
     return verify_sampling(h, stream, target_logits, t_stride_b, t_stride_pos, draft_logits, d_stride_b,
-                           d_stride_pos, dtype, B, gamma, V, draft_tokens, row_params, seed, step, eos_id,
-                           out_num_accepted, out_tokens, out_num_emitted, out_row_flags, diag, false);
+                           d_stride_pos, nullptr, 0, dtype, B, gamma, V, draft_tokens, row_params, seed,
+                           step, eos_id, out_num_accepted, out_tokens, out_num_emitted, out_row_flags,
+                           diag, 0);
+}
+
+specv_status specv_verify_sample_qstats(specv_handle h, void* stream, const void* target_logits,
+                                        int64_t t_stride_b, int64_t t_stride_pos,
+                                        const void* draft_logits, int64_t d_stride_b,
+                                        int64_t d_stride_pos, const float* draft_stats,
+                                        int64_t s_stride_b, specv_dtype dtype, int B, int gamma, int V,
+                                        const int32_t* draft_tokens,
+                                        const specv_row_params* row_params, uint64_t seed,
+                                        uint32_t step, int32_t eos_id, int32_t* out_num_accepted,
+                                        int32_t* out_tokens, int32_t* out_num_emitted,
+                                        int32_t* out_row_flags, const specv_diag* diag) {
+    return verify_sampling(h, stream, target_logits, t_stride_b, t_stride_pos, draft_logits, d_stride_b,
+                           d_stride_pos, draft_stats, s_stride_b, dtype, B, gamma, V, draft_tokens,
+                           row_params, seed, step, eos_id, out_num_accepted, out_tokens, out_num_emitted,
+                           out_row_flags, diag, 2);
 }
 
 specv_status specv_verify_point_mass(specv_handle h, void* stream, const void* target_logits,
@@ -347,9 +385,59 @@ specv_status specv_verify_point_mass(specv_handle h, void* stream, const void* t
                                      int32_t eos_id, int32_t* out_num_accepted, int32_t* out_tokens,
                                      int32_t* out_num_emitted, int32_t* out_row_flags,
                                      const specv_diag* diag) {
-    return verify_sampling(h, stream, target_logits, t_stride_b, t_stride_pos, nullptr, 0, 0, dtype, B,
-                           gamma, V, draft_tokens, row_params, seed, step, eos_id, out_num_accepted,
-                           out_tokens, out_num_emitted, out_row_flags, diag, true);
+    return verify_sampling(h, stream, target_logits, t_stride_b, t_stride_pos, nullptr, 0, 0, nullptr, 0,
+                           dtype, B, gamma, V, draft_tokens, row_params, seed, step, eos_id,
+                           out_num_accepted, out_tokens, out_num_emitted, out_row_flags, diag, 1);
+}
+
+specv_status specv_sample_draft(specv_handle h, void* stream, const void* draft_logits,
+                                int64_t d_stride_b, int64_t d_stride_pos, specv_dtype dtype, int B,
+                                int n_pos, int V, int pos0, const specv_row_params* row_params,
+                                uint64_t seed, uint32_t step, int32_t* out_tokens, float* out_stats,
+                                int32_t* out_flags, int64_t out_stride) {
+    if (!h) return SPECV_E_NULL;
+    if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
+    if (B < 0 || n_pos < 0 || V < 1 || pos0 < 0 || d_stride_b < 0 || d_stride_pos < 0)
+        return SPECV_E_SHAPE;
+    if (out_stride < (int64_t)pos0 + n_pos) return SPECV_E_SHAPE;
+    if (B > h->cfg.max_batch || n_pos > std::max(h->cfg.max_gamma, 1) || V > h->cfg.max_vocab)
+        return SPECV_E_CAPACITY;
+    if (B == 0 || n_pos == 0) return SPECV_OK;
+    if (!draft_logits || !row_params || !out_tokens) return SPECV_E_NULL;
+    const size_t es = dtype == SPECV_BF16 ? 2 : 4;
+    if (!aligned(draft_logits, es) || !aligned(row_params, 16) || !aligned(out_tokens, 4) ||
+        (out_stats && !aligned(out_stats, 8)) || (out_flags && !aligned(out_flags, 4)))
+        return SPECV_E_ALIGN;
+    if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    specv::DraftArgs a{};
+    a.drf = draft_logits;
+    a.d_sb = d_stride_b;
+    a.d_sp = d_stride_pos;
+    a.B = B;
+    a.n = n_pos;
+    a.V = V;
+    a.C = (V + specv::kChunk - 1) / specv::kChunk;
+    a.pos0 = pos0;
+    a.out_stride = out_stride;
+    a.params = row_params;
+    a.seed = seed;
+    a.step = step;
+    a.out_tok = out_tokens;
+    a.out_stats = out_stats;
+    a.out_flags = out_flags;
+    a.stats = h->ws.dstats;
+    unsigned next = h->draft_epoch + 1;
+    if (next >= 0x7fffffffu) {
+        if (clear_draft_ws(h, s) != hipSuccess) return SPECV_E_HIP;
+        next = 1;
+    }
+    a.epoch = next;
+    const bool vec = rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es);
+    if (specv::launch_sample_draft(a, dtype == SPECV_BF16, vec, s, next_events(h)) != hipSuccess)
+        return SPECV_E_HIP;
+    h->draft_epoch = next;
+    return SPECV_OK;
 }
 
 specv_status specv_verify_greedy(specv_handle h, void* stream, const void* target_logits,

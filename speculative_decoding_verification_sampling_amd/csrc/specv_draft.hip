@@ -1,0 +1,215 @@
+// libspecv draft-side sampler for gfx950: d_i ~ q_i in one pass over the
+// draft logits, plus the row statistics the verifier can reuse.
+//
+// q_i is the draft model's distribution after its temperature ("11.1 核心原理"
+// 11.1.2: the proposal is the distribution actually sampled; the tutorial's
+// section 3.3 divides the logits by the temperature).  The draw is the
+// inverse CDF of q_i at a Philox uniform of purpose 0 (DRAFT): tokens in
+// ascending index order, the first whose running mass exceeds u * W.
+//
+// Workgroup (i, b, c), position-major, one per 8192-entry chunk of draft row
+// (b, i):
+//   1. reads its chunk once (16-byte loads) and reduces it to (max, sum of
+//      exp2((z - max) * log2(e) / T)), or (max, lowest argmax) for greedy
+//      rows, published as two epoch-tagged words;
+//   2. wave 0 reads every chunk's words of the row (lane c: chunk c), merges
+//      them into the row's (m, s), and turns them into chunk masses
+//      s_c * exp2((m_c - m) * scale) whose prefix sums locate the chunk
+//      holding u * W; every workgroup of the row computes the same thing;
+//   3. the workgroup owning that chunk finds the token in its registers with
+//      a block prefix sum and writes the token and the row's (m, s).
+// One hand-off per row, and the row is read once.  The chunk statistics and
+// their merge are the verify kernel's, so the (m, s) written here equal the
+// normalisers the verify step computes from the same row.
+//
+// Waits: a row's C workgroups have consecutive IDs and each waits only for
+// its own row.  Workgroups are dispatched in increasing ID order within each
+// XCD, and an XCD holds far more than C of them, so the lowest row with a
+// waiting workgroup always has all its workgroups dispatched.  The wait is
+// bounded; expiry flags the entry INTERNAL.
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "specv_device.hpp"
+#include "specv_internal.hpp"
+
+namespace specv {
+namespace {
+
+__device__ inline void write_draft(const DraftArgs& a, long long o, int tok, float m, float s,
+                                   unsigned flags) {
+    a.out_tok[o] = tok;
+    if (a.out_stats) {
+        a.out_stats[o * 2] = m;
+        a.out_stats[o * 2 + 1] = s;
+    }
+    if (a.out_flags) a.out_flags[o] = (int)flags;
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int per = a.B * a.C;
+    const int i = blockIdx.x / per;
+    const int rem = blockIdx.x - i * per;
+    const int b = rem / a.C;
+    const int c = rem - b * a.C;
+    const float nan = __builtin_nanf("");
+    const specv_row_params rp = a.params[b];
+    const bool greedy = !(rp.temperature > 0.f);
+    const bool trunc = !greedy && ((rp.top_k > 0 && rp.top_k < a.V) || rp.top_p < 1.f);
+    const int pos = a.pos0 + i;
+    const long long o = (long long)b * a.out_stride + pos;
+    if (trunc) {
+        if (c == 0 && tid == 0) write_draft(a, o, -1, nan, nan, SPECV_FLAG_UNSUPPORTED);
+        return;
+    }
+    const float scale = greedy ? 0.f : kLog2e / rp.temperature;
+    const void* row = row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i);
+    const int v0 = c * kChunk;
+    const int len = min(kChunk, a.V - v0);
+    ChunkRegs<BF16, VEC> r;
+    r.issue(row, v0, len);
+    r.finish(row, v0, len);
+
+    // 1. chunk statistics, merged across the four waves as the verify's
+    //    streaming units merge them
+    unsigned long long* words = a.stats + ((long long)i * a.B + b) * a.C * 2;
+    __shared__ float sm[kWaves], ss[kWaves];
+    __shared__ int si[kWaves];
+    __shared__ unsigned sb[kWaves];
+    if (greedy) {
+        float best;
+        int bi;
+        unsigned bad;
+        wave_chunk_argmax<BF16>(r, v0, best, bi, bad);
+        if (lane == 0) {
+            sm[wave] = best;
+            si[wave] = bi;
+            sb[wave] = bad;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 1; w < kWaves; ++w) {
+                merge_arg(best, bi, sm[w], si[w]);
+                bad |= sb[w];
+            }
+            publish_stats(words + c * 2, bad ? nan : best, (unsigned)bi, a.epoch);
+        }
+    } else {
+        float m, s;
+        wave_chunk_ms(r, scale, m, s);
+        if (lane == 0) {
+            sm[wave] = m;
+            ss[wave] = s;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            m = sm[0];
+            s = ss[0];
+            for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[w], ss[w], scale);
+            publish_stats(words + c * 2, m, __float_as_uint(s), a.epoch);
+        }
+    }
+
+    // 2. the row's statistics and the chunk holding u * W (wave 0)
+    __shared__ int sChosen, sDone;
+    __shared__ float sBase, sTarget, sM, sS;
+    if (wave == 0) {
+        float m = -kInf;
+        unsigned second = 0;
+        bool ok = true;
+        if (lane < a.C) ok = published_stats(words + lane * 2, a.epoch, m, second);
+        const bool late = __ballot(!ok) != 0;
+        int chosen = -1, tok = -1;
+        unsigned flags = 0;
+        float M = nan, S = nan, base = 0.f, target = 0.f;
+        if (greedy) {
+            int arg = lane < a.C ? (int)second : 0x7fffffff;
+            const bool isnan_m = lane < a.C && __builtin_isnan(m);
+            if (isnan_m || lane >= a.C) m = -kInf;
+            wave_merge_arg(m, arg);
+            if (__ballot(isnan_m) != 0 || m == -kInf) flags = SPECV_FLAG_NONFINITE_ROW;
+            else tok = arg;
+        } else {
+            const float s = lane < a.C ? __uint_as_float(second) : 0.f;
+            if (lane >= a.C) m = -kInf;
+            float Mr = m, Sr = s;
+            wave_merge_ms(Mr, Sr, scale);
+            if (__builtin_isnan(Sr) || Mr == -kInf || !(Sr > 0.f)) {
+                flags = SPECV_FLAG_NONFINITE_ROW;
+            } else {
+                M = Mr;
+                S = Sr;
+                const float wc = m > -kInf ? s * fast_exp2((m - M) * scale) : 0.f;
+                const float incl = wave_scan_incl(wc);
+                const float W = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), kWave - 1));
+                target = uniform24(a.seed, b, pos, PURPOSE_DRAFT, a.step) * W;
+                const unsigned long long hit = __ballot(wc > 0.f && incl > target);
+                const unsigned long long any = __ballot(wc > 0.f);
+                // rounding: without a hit, the last chunk with mass
+                chosen = hit ? __builtin_ctzll(hit) : (any ? 63 - __builtin_clzll(any) : -1);
+                const float before = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(incl), chosen > 0 ? chosen - 1 : 0));
+                base = chosen > 0 ? before : 0.f;
+            }
+        }
+        if (late) {
+            flags = SPECV_FLAG_INTERNAL;
+            chosen = -1;
+            tok = -1;
+        }
+        if (lane == 0) {
+            sChosen = chosen;
+            sDone = chosen < 0;
+            sBase = base;
+            sTarget = target;
+            sM = M;
+            sS = S;
+            // rows with nothing left to draw (greedy, bad, late) are written by
+            // chunk 0's workgroup
+            if (chosen < 0 && c == 0) write_draft(a, o, tok, nan, nan, flags);
+        }
+    }
+    __syncthreads();
+    if (sDone || sChosen != c) return;
+
+    // 3. the owner of the chunk finds the token
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int NG = kPerThread / G;
+    const float M = sM;
+    float w[kPerThread], gw[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            w[j * G + e] = fast_exp2(__fmul_rn(r.elem(j * G + e) - M, scale));
+            s += w[j * G + e];
+        }
+        gw[j] = s;
+    }
+    const int t = chunk_inverse_cdf<BF16>(w, gw, sBase, sTarget);
+    if (tid == 0) {
+        if (t < 0) write_draft(a, o, -1, nan, nan, SPECV_FLAG_NONFINITE_ROW);
+        else write_draft(a, o, c * kChunk + t, M, sS, 0u);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStream_t stream,
+                               hipEvent_t* ev) {
+    const long long blocks = (long long)a.n * a.B * a.C;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    void (*fn)(DraftArgs) = bf16 ? (vec ? k_sample_draft<true, true> : k_sample_draft<true, false>)
+                                 : (vec ? k_sample_draft<false, true> : k_sample_draft<false, false>);
+    hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev ? ev[0] : nullptr,
+                          ev ? ev[1] : nullptr, 0, a);
+    return hipGetLastError();
+}
+
+}  // namespace specv

@@ -91,6 +91,8 @@ struct Workspace {
                                 // count -1 when the chunk's candidates overflowed
     TruncRow* trow;             // [max_batch * max_pos * 2]
     Cand* kept;                 // [max_batch * max_pos * 2 * kept_cap]
+    unsigned long long* dstats; // [max_batch * max(max_gamma, 1) * max_chunks][2]: the draft
+                                // sampler's chunk statistics (its own epochs)
 };
 
 struct Args {
@@ -102,8 +104,12 @@ struct Args {
     int C;                        // chunks per row
     int P;                        // positions per batch row: gamma + 1
     int greedy_all;               // specv_verify_greedy
-    int point_mass;               // specv_verify_point_mass: q_i is the point mass on d_i and
-                                  // no draft logits are read
+    int prop;                     // the proposal: 0 draft logits; 1 (specv_verify_point_mass)
+                                  // q_i is the point mass on d_i and no draft logits are read;
+                                  // 2 (specv_verify_sample_qstats) draft logits plus the
+                                  // drafter's row statistics
+    const float* qstats;          // prop 2: [B][qs_sb][2] (max, sum) of draft row (b, i)
+    long long qs_sb;
     int cand_cap;                 // candidates per (row, chunk); 0: no truncation
     int kept_cap;                 // kept-set entries per row: min(kKeptCap, max_vocab)
     int max_top_k;
@@ -123,6 +129,28 @@ struct Args {
     float* wres;
     Workspace ws;
 };
+
+// The draft-side sampler (specv_sample_draft): draws positions pos0 ..
+// pos0 + n - 1 of B batch rows.
+struct DraftArgs {
+    const void* drf;
+    long long d_sb, d_sp;         // element strides of draft rows: row (b, i) is position pos0 + i
+    int B, n, V;
+    int C;                        // chunks per row
+    int pos0;
+    long long out_stride;         // entries per batch row of the outputs
+    const specv_row_params* params;
+    unsigned long long seed;
+    unsigned step;
+    unsigned epoch;               // per-handle sampler call number (never 0)
+    int* out_tok;                 // [B][out_stride]
+    float* out_stats;             // [B][out_stride][2] or nullptr
+    int* out_flags;               // [B][out_stride] or nullptr
+    unsigned long long* stats;    // [n * B][C][2] epoch-tagged chunk statistics
+};
+
+hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStream_t stream,
+                               hipEvent_t* ev);
 
 // Launch the whole verify step on ``stream`` as one kernel: one streaming
 // workgroup per (position, batch row, chunk), position-major, then one

@@ -49,369 +49,27 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "specv_device.hpp"
 #include "specv_internal.hpp"
 
 namespace specv {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kInf = __builtin_huge_valf();
-constexpr int kSpinLimit = 1 << 18;
-
 enum Mode { MODE_SAMPLE = 0, MODE_GREEDY = 1, MODE_TRUNC = 2, MODE_SKIP = 3 };
+// What stands for the proposal q (a template parameter, so that each kind
+// is a kernel of its own):
+//   kPropLogits: draft logits rows, reduced by the stream like the target's;
+//   kPropPoint:  q_i is the point mass on d_i, no draft rows exist;
+//   kPropStats:  draft logits rows plus the drafter's row statistics (max,
+//                sum) of untruncated sampling rows, so the stream reads no
+//                draft row of such rows: the accept test loads q's entry at
+//                d_i, and only the row where the round stops is read whole,
+//                for the correction draw.  Truncated rows stream their draft
+//                rows as with kPropLogits.
+constexpr int kPropLogits = 0, kPropPoint = 1, kPropStats = 2;
 enum Kind { KIND_NONE = 0, KIND_RESIDUAL = 1, KIND_BONUS = 2 };
-enum Purpose { PURPOSE_ACCEPT = 1, PURPOSE_RESIDUAL = 2, PURPOSE_BONUS = 3 };
 // outcome of one pair (low byte of PW_STATE)
 enum Outcome { OUT_ACC = 1, OUT_REJ = 2, OUT_BAD = 3, OUT_BONUS = 4 };
-
-
-// ---------------------------------------------------------------- Philox
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
-// 32x32->64 multiplies, key bumped by the Weyl constants between rounds.
-__device__ inline uint4 philox4x32_10(uint4 c, unsigned k0, unsigned k1) {
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r) {
-            k0 += 0x9E3779B9u;
-            k1 += 0xBB67AE85u;
-        }
-        const unsigned lo0 = 0xD2511F53u * c.x;
-        const unsigned hi0 = __umulhi(0xD2511F53u, c.x);
-        const unsigned lo1 = 0xCD9E8D57u * c.z;
-        const unsigned hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
-    }
-    return c;
-}
-
-// u = (word0 >> 8) * 2^-24 for counter (b, i, purpose, step).
-__device__ inline float uniform24(unsigned long long seed, unsigned b, unsigned i,
-                                  unsigned purpose, unsigned step) {
-    const uint4 r = philox4x32_10(make_uint4(b, i, purpose, step), (unsigned)seed,
-                                  (unsigned)(seed >> 32));
-    return (float)(r.x >> 8) * 5.9604644775390625e-08f;
-}
-
-// ---------------------------------------------------------------- helpers
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Hand-off between workgroups of one launch.  Published values are written
-// and read with agent-scope atomic accesses, which are coherent across the
-// XCDs' L2 caches by themselves, so no L2 write-back / invalidate is needed
-// (a __threadfence() would flush the whole L2 of the XCD).  ``wait_stores``
-// makes this wave's outstanding stores complete before a later atomic, and
-// keeps the compiler from moving memory accesses across it.
-template <typename T>
-__device__ inline void publish(T* p, T v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ inline T published(const T* p) {
-    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Bump an arrival counter; returns the previous count.  With ``ordered`` the
-// thread's earlier stores complete first, for readers that do not check
-// epoch tags; without it the atomic goes out behind them at once.
-__device__ inline unsigned arrive(unsigned* counter, bool ordered) {
-    if (ordered) wait_stores();
-    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Epoch-tagged 64-bit words: (epoch << 32) | value.
-__device__ inline void put_tagged(unsigned long long* p, unsigned v, unsigned epoch) {
-    publish(p, ((unsigned long long)epoch << 32) | v);
-}
-__device__ inline bool tag_is(unsigned long long w, unsigned epoch) {
-    return (unsigned)(w >> 32) == epoch;
-}
-
-__device__ inline unsigned long long readlane64(unsigned long long v, int lane) {
-    const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, lane);
-    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(v >> 32), lane);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
-__device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <bool BF16>
-__device__ inline float load_elem(const void* row, long long v) {
-    if constexpr (BF16) {
-        const unsigned short h = static_cast<const unsigned short*>(row)[v];
-        return __uint_as_float((unsigned)h << 16);
-    } else {
-        return static_cast<const float*>(row)[v];
-    }
-}
-
-template <bool BF16>
-__device__ inline const void* row_ptr(const void* base, long long stride_b, long long stride_p,
-                                      int b, int i) {
-    const long long off = (long long)b * stride_b + (long long)i * stride_p;
-    if constexpr (BF16) {
-        return static_cast<const unsigned short*>(base) + off;
-    } else {
-        return static_cast<const float*>(base) + off;
-    }
-}
-
-template <bool BF16>
-__device__ inline void unpack16(const uint4& q, float* x) {
-    if constexpr (BF16) {
-        x[0] = bf16_lo(q.x);
-        x[1] = bf16_hi(q.x);
-        x[2] = bf16_lo(q.y);
-        x[3] = bf16_hi(q.y);
-        x[4] = bf16_lo(q.z);
-        x[5] = bf16_hi(q.z);
-        x[6] = bf16_lo(q.w);
-        x[7] = bf16_hi(q.w);
-    } else {
-        x[0] = __uint_as_float(q.x);
-        x[1] = __uint_as_float(q.y);
-        x[2] = __uint_as_float(q.z);
-        x[3] = __uint_as_float(q.w);
-    }
-}
-
-// Index (within the chunk) of entry k of this thread's x[]: 16-byte groups,
-// group g = j * kBlock + tid holds entries [g * G, g * G + G), so each load
-// instruction of the workgroup covers one contiguous 4 KB span.
-template <bool BF16>
-__device__ inline int chunk_index(int k) {
-    constexpr int G = BF16 ? 8 : 4;
-    return ((k / G) * kBlock + (int)threadIdx.x) * G + (k % G);
-}
-
-// One chunk of one logits row held in registers, in chunk_index's layout;
-// entries past the row's end read as -inf.
-//   VEC:  packed 16-byte groups (bfloat16: 8 entries, float32: 4); every
-//         load is issued before any is used (``issue``), groups past the last
-//         whole group load group 0 and are overwritten by ``finish``, which
-//         also fills a partial last group with scalar loads.
-//   !VEC: scalar loads (rows not 16-byte aligned), held as float.
-template <bool BF16, bool VEC>
-struct ChunkRegs;
-
-template <bool BF16>
-struct ChunkRegs<BF16, true> {
-    static constexpr int G = BF16 ? 8 : 4;
-    static constexpr int NG = kPerThread / G;
-    uint4 q[NG];
-
-    __device__ inline void issue(const void* row, int v0, int len) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
-                                                        (size_t)v0 * (BF16 ? 2 : 4));
-        const int full = len / G;
-        if (full == 0) return;                   // nothing 16-byte loadable (tiny tail)
-#pragma unroll
-        for (int j = 0; j < NG; ++j) {
-            const int g = j * kBlock + (int)threadIdx.x;
-            q[j] = p[g < full ? g : 0];
-        }
-    }
-    __device__ inline void finish(const void* row, int v0, int len) {
-        const int full = len / G;
-        const int rem = len - full * G;
-        const unsigned ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
-#pragma unroll
-        for (int j = 0; j < NG; ++j) {
-            const int g = j * kBlock + (int)threadIdx.x;
-            if (g >= full) {
-                q[j] = make_uint4(ninf, ninf, ninf, ninf);
-                if (g == full && rem) {
-                    unsigned w[4] = {ninf, ninf, ninf, ninf};
-#pragma unroll
-                    for (int e = 0; e < G; ++e) {
-                        if (e < rem) {
-                            if constexpr (BF16) {
-                                const unsigned h = static_cast<const unsigned short*>(row)[v0 + full * G + e];
-                                w[e / 2] = (e & 1) ? ((w[e / 2] & 0xFFFFu) | (h << 16))
-                                                   : ((w[e / 2] & 0xFFFF0000u) | h);
-                            } else {
-                                w[e] = __float_as_uint(static_cast<const float*>(row)[v0 + full * G + e]);
-                            }
-                        }
-                    }
-                    q[j] = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            }
-        }
-    }
-    __device__ inline void get(float (&x)[kPerThread]) const {
-#pragma unroll
-        for (int j = 0; j < NG; ++j) unpack16<BF16>(q[j], &x[j * G]);
-    }
-    // entry i (a compile-time constant in unrolled loops) unpacked on the fly
-    __device__ inline float elem(int i) const {
-        const uint4& g = q[i / G];
-        const int e = i % G;
-        if constexpr (BF16) {
-            const unsigned w = (e / 2) == 0 ? g.x : (e / 2) == 1 ? g.y : (e / 2) == 2 ? g.z : g.w;
-            return (e & 1) ? bf16_hi(w) : bf16_lo(w);
-        } else {
-            return __uint_as_float(e == 0 ? g.x : e == 1 ? g.y : e == 2 ? g.z : g.w);
-        }
-    }
-};
-
-template <bool BF16>
-struct ChunkRegs<BF16, false> {
-    static constexpr int G = BF16 ? 8 : 4;
-    static constexpr int NG = kPerThread / G;
-    float x[kPerThread];
-
-    __device__ inline void issue(const void* row, int v0, int len) {
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-            const int v = chunk_index<BF16>(k);
-            x[k] = load_elem<BF16>(row, (long long)v0 + (v < len ? v : len - 1));
-        }
-    }
-    __device__ inline void finish(const void*, int, int len) {
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k)
-            if (chunk_index<BF16>(k) >= len) x[k] = -kInf;
-    }
-    __device__ inline void get(float (&y)[kPerThread]) const {
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) y[k] = x[k];
-    }
-    __device__ inline float elem(int i) const { return x[i]; }
-};
-
-// Merge (m, s) statistics: s is relative to m in units of exp2(. * scale).
-__device__ inline void merge_ms(float& m, float& s, float m2, float s2, float scale) {
-    const float M = fmaxf(m, m2);
-    if (M == -kInf) {            // both empty; keep NaN visible
-        s = s + s2;
-        m = M;
-        return;
-    }
-    s = s * fast_exp2((m - M) * scale) + s2 * fast_exp2((m2 - M) * scale);
-    m = M;
-}
-
-// ---------------------------------------------------------------- wave64 DPP
-// Cross-lane moves by DPP (VALU-speed, no LDS round trip).  Lanes whose
-// source is outside the pattern or masked off receive ``old``, the identity
-// of the operation being built.
-constexpr int kDppQuad1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kDppQuad2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
-constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
-constexpr int kDppBcast15 = 0x142;    // lane 15 of a row -> the next row
-constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3
-constexpr int kDppShr = 0x110;        // + n: row_shr:n
-
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ inline int dpp_i(int v, int old) {
-    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
-}
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ inline float dpp_f(float v, float old) {
-    return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(v), __float_as_int(old)));
-}
-
-// Wave reduction of a value pair with a combine functor: quads, half rows,
-// rows, then rows 0+1 -> 1, 2+3 -> 3, rows 0..2 -> 3; the total ends in lane
-// 63 and is broadcast.
-template <typename Comb>
-__device__ inline void wave_reduce2(float& x, int& y, float idx, int idy, Comb comb) {
-#define SPECV_DPP_STEP(CTRL, MASK)                                          \
-    {                                                                       \
-        const float x2 = dpp_f<CTRL, MASK>(x, idx);                         \
-        const int y2 = dpp_i<CTRL, MASK>(y, idy);                           \
-        comb(x, y, x2, y2);                                                 \
-    }
-    SPECV_DPP_STEP(kDppQuad1, 0xF)
-    SPECV_DPP_STEP(kDppQuad2, 0xF)
-    SPECV_DPP_STEP(kDppHalfMirror, 0xF)
-    SPECV_DPP_STEP(kDppMirror, 0xF)
-    SPECV_DPP_STEP(kDppBcast15, 0xA)
-    SPECV_DPP_STEP(kDppBcast31, 0xC)
-#undef SPECV_DPP_STEP
-    x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
-    y = __builtin_amdgcn_readlane(y, kWave - 1);
-}
-
-__device__ inline void wave_merge_ms(float& m, float& s, float scale) {
-    int si = __float_as_int(s);
-    wave_reduce2(m, si, -kInf, 0, [scale](float& m1, int& s1, float m2, int s2) {
-        float sa = __int_as_float(s1);
-        merge_ms(m1, sa, m2, __int_as_float(s2), scale);
-        s1 = __float_as_int(sa);
-    });
-    s = __int_as_float(si);
-}
-
-// (value, index) argmax merge: larger value wins, lower index on ties.
-__device__ inline void merge_arg(float& v, int& i, float v2, int i2) {
-    if (v2 > v || (v2 == v && i2 < i)) {
-        v = v2;
-        i = i2;
-    }
-}
-
-__device__ inline void wave_merge_arg(float& v, int& i) {
-    wave_reduce2(v, i, -kInf, 0x7fffffff, [](float& v1, int& i1, float v2, int i2) {
-        merge_arg(v1, i1, v2, i2);
-    });
-}
-
-__device__ inline float wave_sum(float x) {
-    int dummy = 0;
-    wave_reduce2(x, dummy, 0.f, 0, [](float& a, int&, float b, int) { a += b; });
-    return x;
-}
-
-__device__ inline float wave_max(float x) {
-    int dummy = 0;
-    wave_reduce2(x, dummy, -kInf, 0, [](float& a, int&, float b, int) { a = fmaxf(a, b); });
-    return x;
-}
-
-__device__ inline unsigned wave_or(unsigned x) {
-    float dummy = 0.f;
-    int xi = (int)x;
-    wave_reduce2(dummy, xi, 0.f, 0, [](float&, int& a, float, int b) { a |= b; });
-    return (unsigned)xi;
-}
-
-__device__ inline int wave_min_int(int x) {
-    float dummy = 0.f;
-    wave_reduce2(dummy, x, 0.f, 0x7fffffff, [](float&, int& a, float, int b) { a = min(a, b); });
-    return x;
-}
-
-__device__ inline int wave_max_int(int x) {
-    float dummy = 0.f;
-    wave_reduce2(dummy, x, 0.f, (int)0x80000000, [](float&, int& a, float, int b) { a = max(a, b); });
-    return x;
-}
-
-// Inclusive prefix sums across the wave (lane order).
-__device__ inline float wave_scan_incl(float x) {
-    x += dpp_f<kDppShr + 1>(x, 0.f);
-    x += dpp_f<kDppShr + 2>(x, 0.f);
-    x += dpp_f<kDppShr + 4>(x, 0.f);
-    x += dpp_f<kDppShr + 8>(x, 0.f);
-    x += dpp_f<kDppBcast15, 0xA>(x, 0.f);
-    x += dpp_f<kDppBcast31, 0xC>(x, 0.f);
-    return x;
-}
-
-__device__ inline int wave_scan_incl(int x) {
-    x += dpp_i<kDppShr + 1>(x, 0);
-    x += dpp_i<kDppShr + 2>(x, 0);
-    x += dpp_i<kDppShr + 4>(x, 0);
-    x += dpp_i<kDppShr + 8>(x, 0);
-    x += dpp_i<kDppBcast15, 0xA>(x, 0);
-    x += dpp_i<kDppBcast31, 0xC>(x, 0);
-    return x;
-}
 
 // ---------------------------------------------------------------- row plan
 // What one batch row needs, from its parameters and draft tokens alone.
@@ -511,28 +169,6 @@ __device__ inline long long part_index(const Args& a, int b, int k, int side, in
 // for its stores to complete.
 __device__ inline unsigned long long* stats_words(const Args& a, int b, int k, int side, int c) {
     return a.ws.stats + part_index(a, b, k, side, c) * 2;
-}
-__device__ inline void publish_stats(unsigned long long* w, float m, unsigned second, unsigned epoch) {
-    put_tagged(w, __float_as_uint(m), epoch);
-    put_tagged(w + 1, second, epoch);
-}
-// Returns false when the words did not carry this call's tag within the bound.
-__device__ inline bool published_stats(const unsigned long long* w, unsigned epoch, float& m,
-                                       unsigned& second) {
-    unsigned long long w0 = 0, w1 = 0;
-    bool ok = false;
-    for (int spin = 0; spin < kSpinLimit; ++spin) {
-        w0 = published(w);
-        w1 = published(w + 1);
-        if (tag_is(w0, epoch) && tag_is(w1, epoch)) {
-            ok = true;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    m = __uint_as_float((unsigned)w0);
-    second = (unsigned)w1;
-    return ok;
 }
 
 // Diagnostics of one row by one wave: lane i holds p_i(d_i), q_i(d_i).
@@ -1053,7 +689,7 @@ __device__ inline TruncRow published_trow(const TruncRow* p) {
 // ascending index order, first running sum > u * W.  Returns the token (-1 if
 // no weight anywhere) to every thread; *wres gets W of a correction, and
 // *fallback is set when the correction mass vanished and p was used.
-template <bool BF16, bool PM>
+template <bool BF16, int PROP>
 __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, const Plan& pl,
                             TruncScratch& sc, float* wres, bool* fallback) {
     const int tid = threadIdx.x;
@@ -1061,7 +697,7 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     __shared__ float sWsum;
     __shared__ int sTok, sLastPos, sFb;
     const float scale = pl.scale;
-    constexpr bool pm = PM;                 // q = the point mass on d_pos
+    constexpr bool pm = PROP == kPropPoint;  // q = the point mass on d_pos
     __syncthreads();
     if (tid == 0) {
         tT = published_trow(&a.ws.trow[side_row(a, b, pos, 0)]);
@@ -1201,7 +837,7 @@ struct PairVals {
 // diagnostics; greedy, capped and dead rows get their outputs here,
 // truncated rows draw their token here from the kept lists, and sampling rows
 // hand the draw to their sampling workgroups through the row record.
-template <bool BF16, bool TRUNC, bool PM>
+template <bool BF16, bool TRUNC, int PROP>
 __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, const Plan& pl,
                            unsigned long long st, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -1299,7 +935,7 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
             const float u = uniform24(a.seed, b, pos, res ? PURPOSE_RESIDUAL : PURPOSE_BONUS, a.step);
             float wres;
             bool fb;
-            const int tok = trunc_sample<BF16, PM>(a, b, pos, res, u, pl, *sc, &wres, &fb);
+            const int tok = trunc_sample<BF16, PROP>(a, b, pos, res, u, pl, *sc, &wres, &fb);
             if (wave == 0) {
                 unsigned flags = fFlags | (fb ? SPECV_FLAG_RESIDUAL_FALLBACK : 0u);
                 bool dead = fDead;
@@ -1322,15 +958,17 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
 // the row when that resolves it.  Readers of the pair record check its tags,
 // so its stores need not complete first, except for truncated rows, whose
 // kept lists and TruncRows are read untagged.
-template <bool BF16, bool TRUNC, bool PM>
+template <bool BF16, bool TRUNC, int PROP>
 __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
     const bool test = k < a.gamma;
-    constexpr bool pm = PM;                 // q_k is the point mass on d_k
+    constexpr bool pm = PROP == kPropPoint;  // q_k is the point mass on d_k
+    const bool qs = PROP == kPropStats && !trunc;   // q_k's statistics come from the drafter
     const bool zneed = !greedy && test;     // z at d_k and the accept uniform
-    const bool two = zneed && !pm;          // the draft row is consulted
+    const bool qside = zneed && !pm;        // the draft row's entry at d_k is consulted
+    const bool two = qside && !qs;          // the draft row's chunk statistics are merged
     const float scale = pl.scale;
     __shared__ float dM[2], dS[2], dZ[2], dU;
     __shared__ int dA, dBad[2], dLate[2];
@@ -1389,11 +1027,22 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
             }
         } else if (wave == 2 && zneed) {
             // one load instruction for both rows' z at d_k (lane 0: target,
-            // lane 1: draft), so that they share a round trip
-            if (lane == 0 || (lane == 1 && two))
+            // lane 1: draft) and the drafter's statistics (lanes 3, 4), so
+            // that they share a round trip
+            if (lane == 0 || (lane == 1 && qside))
                 dZ[lane] = load_elem<BF16>(lane == 0 ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k)
                                                      : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
             if (lane == 2) dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
+            if (qs && (lane == 3 || lane == 4)) {
+                const float x = a.qstats[((long long)b * a.qs_sb + k) * 2 + (lane - 3)];
+                if (lane == 3) {
+                    dM[1] = x;
+                    dLate[1] = 0;
+                } else {
+                    dS[1] = x;
+                    dBad[1] = __builtin_isnan(x);
+                }
+            }
         }
     }
     __syncthreads();
@@ -1426,10 +1075,10 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
             }
         } else {
             const bool badT = dBad[0] || dM[0] == -kInf || !(dS[0] > 0.f);
-            const bool badQ = two && (dBad[1] || dM[1] == -kInf || !(dS[1] > 0.f));
+            const bool badQ = qside && (dBad[1] || dM[1] == -kInf || !(dS[1] > 0.f));
             v.mt = dM[0];
             v.invt = 1.f / dS[0];
-            if (two) {
+            if (qside) {
                 v.mq = dM[1];
                 v.invq = 1.f / dS[1];
             }
@@ -1474,7 +1123,7 @@ __device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncSc
         dFinish = resolve(old, pl, a.gamma).how == H_OPEN && resolve(now, pl, a.gamma).how != H_OPEN;
     }
     __syncthreads();
-    if (dFinish) finish_row<BF16, TRUNC, PM>(a, b, k, dOwn, pl, dNew, sc);
+    if (dFinish) finish_row<BF16, TRUNC, PROP>(a, b, k, dOwn, pl, dNew, sc);
 }
 
 // ---------------------------------------------------------------- sampling
@@ -1505,7 +1154,7 @@ struct Weights {
 // them, and the workgroup whose chunk holds u * W scans it (tokens in
 // ascending order, first running sum > u * W) and writes the outputs.
 // ``flags_in``: the row's flags so far.  Whole workgroup.
-template <bool BF16, bool VEC, bool PM>
+template <bool BF16, bool VEC, int PROP>
 __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan& pl, Weights wt,
                                  unsigned flags_in, const ChunkRegs<BF16, VEC>& rt,
                                  const ChunkRegs<BF16, VEC>& rd) {
@@ -1516,7 +1165,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
     // the weights of this thread's entries (kept for the scan), their group
     // sums, and the p mass
     float w[kPerThread], gw[NG], sw = 0.f, sp = 0.f;
-    if (PM && wt.dpm >= 0) {
+    if (PROP == kPropPoint && wt.dpm >= 0) {
         // point-mass proposal: p, except 0 at the proposed token
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
@@ -1641,63 +1290,8 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
             gw[j] = s;
         }
     }
-    // prefix sums of the group weights in token order: group (j, tid) comes
-    // after every group (j', *) with j' < j and every (j, tid') with tid' < tid
-    __shared__ float gtot[NG][kWaves];
-    __shared__ int tokW[kWaves], lastW[kWaves];
-    float incl[NG];
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        incl[j] = wave_scan_incl(gw[j]);
-        if (lane == kWave - 1) gtot[j][wave] = incl[j];
-    }
-    __syncthreads();
-    const float target = sTarget;
-    float gbase = sBase;
-    int tok = 0x7fffffff, lastpos = -1;
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        float before = 0.f, tot = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < kWaves; ++w2) {
-            const float g = gtot[j][w2];
-            if (w2 < wave) before += g;
-            tot += g;
-        }
-        const float start = gbase + before + (incl[j] - gw[j]);
-        float run = start;
-        int first = -1, lastin = -1;
-#pragma unroll
-        for (int e = 0; e < G; ++e) {
-            const float wk = w[j * G + e];
-            run += wk;
-            if (wk > 0.f) {
-                lastin = e;
-                if (first < 0 && run > target) first = e;
-            }
-        }
-        const int g = j * kBlock + tid;
-        if (lastin >= 0) lastpos = g * G + lastin;
-        if (tok == 0x7fffffff && gw[j] > 0.f && start + gw[j] > target)
-            tok = g * G + (first >= 0 ? first : lastin);
-        gbase += tot;
-    }
-    // the first token past u * W, and the last token with weight (for
-    // rounding), reduced per wave then across the four waves
-    tok = wave_min_int(tok);
-    lastpos = wave_max_int(lastpos);
-    if (lane == 0) {
-        tokW[wave] = tok;
-        lastW[wave] = lastpos;
-    }
-    __syncthreads();
+    const int t = chunk_inverse_cdf<BF16>(w, gw, sBase, sTarget);
     if (wave == 0) {
-        int t = tokW[0], l = lastW[0];
-        for (int w2 = 1; w2 < kWaves; ++w2) {
-            t = min(t, tokW[w2]);
-            l = max(l, lastW[w2]);
-        }
-        if (t == 0x7fffffff) t = l;        // rounding: the last token with weight
         const bool dead = t < 0;
         unsigned flags = sFlags;
         if (dead) flags |= SPECV_FLAG_NONFINITE_ROW;
@@ -1718,7 +1312,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
 #endif
 constexpr int kSkipFrom = SPECV_SKIP_FROM;
 
-template <bool BF16, bool VEC, bool TRUNC, bool PM>
+template <bool BF16, bool VEC, bool TRUNC, int PROP>
 __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const unsigned par = a.epoch & 1u;
@@ -1744,7 +1338,8 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
     }
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
-    const bool two = !greedy && k < a.gamma && !PM;
+    const bool two = !greedy && k < a.gamma &&
+                     (PROP == kPropLogits || (PROP == kPropStats && trunc));
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
     const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
     const int v0 = c * kChunk;
@@ -1761,20 +1356,10 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
     __shared__ int sLast;
     const float scale = pl.scale;
     if (greedy) {
-        float best = -kInf;
-        int bi = 0x7fffffff;
-        unsigned bad = 0;
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const float x = rt.elem(i);
-            bad |= !(x <= 3.402823466e38f);           // NaN or +inf
-            if (x > best) {                           // strict: keeps the lowest index
-                best = x;
-                bi = v0 + chunk_index<BF16>(i);
-            }
-        }
-        wave_merge_arg(best, bi);
-        bad = wave_or(bad);
+        float best;
+        int bi;
+        unsigned bad;
+        wave_chunk_argmax<BF16>(rt, v0, best, bi, bad);
         if (lane == 0) {
             sm[0][wave] = best;
             si[wave] = bi;
@@ -1794,15 +1379,8 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
         for (int side = 0; side < 2; ++side) {
             if (side == 1 && !two) break;
             const ChunkRegs<BF16, VEC>& r = side == 0 ? rt : rd;
-            float cm = -kInf;
-#pragma unroll
-            for (int i = 0; i < kPerThread; ++i) cm = fmaxf(cm, r.elem(i));
-            const float nms = cm == -kInf ? 0.f : -cm * scale;
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < kPerThread; ++i) s += fast_exp2(fmaf(r.elem(i), scale, nms));
-            float m = cm;
-            wave_merge_ms(m, s, scale);
+            float m, s;
+            wave_chunk_ms(r, scale, m, s);
             if (lane == 0) {
                 sm[side][wave] = m;
                 ss[side][wave] = s;
@@ -1826,14 +1404,14 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
     }
     if (tid == 0) sLast = arrive(pair_counter(a, par, b, k), trunc) == (unsigned)(a.C - 1);
     __syncthreads();
-    if (sLast) decide_pair<BF16, TRUNC, PM>(a, b, k, pl, sc);
+    if (sLast) decide_pair<BF16, TRUNC, PROP>(a, b, k, pl, sc);
 }
 
 // Sampling workgroup (b, c) of a sampling row: waits for the row record,
 // then reads chunk c of the target (and draft) row of the position the round
 // stopped at, or of the bonus row, and takes part in the sample.  Rows of
 // other modes never need one.
-template <bool BF16, bool VEC, bool PM>
+template <bool BF16, bool VEC, int PROP>
 __device__ void sample_item(const Args& a, int b, int c) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const Plan pl = make_plan(a, b);
@@ -1863,7 +1441,7 @@ __device__ void sample_item(const Args& a, int b, int c) {
     const int kind = (int)(rec & 7u);
     if (kind != KIND_RESIDUAL && kind != KIND_BONUS) return;
     const int k = (int)((rec >> 3) & 31u);
-    const bool two = kind == KIND_RESIDUAL && !PM;                // the draft row is read
+    const bool two = kind == KIND_RESIDUAL && PROP != kPropPoint;  // the draft row is read
     const void* trow = row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
     const void* drow = two ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : nullptr;
     const int v0 = c * kChunk;
@@ -1875,13 +1453,13 @@ __device__ void sample_item(const Args& a, int b, int c) {
     if (two) rd.finish(drow, v0, len);
     Weights wt;
     wt.residual = kind == KIND_RESIDUAL;
-    wt.dpm = PM && kind == KIND_RESIDUAL ? draft_token(a, b, k) : -1;
+    wt.dpm = PROP == kPropPoint && kind == KIND_RESIDUAL ? draft_token(a, b, k) : -1;
     wt.mt = __uint_as_float(sRec[RW_MT]);
     wt.invt = __uint_as_float(sRec[RW_INVT]);
     wt.mq = __uint_as_float(sRec[RW_MQ]);
     wt.invq = __uint_as_float(sRec[RW_INVQ]);
     wt.st = pl.scale;
-    sample_from_regs<BF16, VEC, PM>(a, b, k, c, pl, wt, (rec >> 8) & 0xffu, rt, rd);
+    sample_from_regs<BF16, VEC, PROP>(a, b, k, c, pl, wt, (rec >> 8) & 0xffu, rt, rd);
 }
 
 // ---------------------------------------------------------------- k_verify
@@ -1902,7 +1480,7 @@ __device__ inline void clear_other_parity(const Args& a) {
         publish(a.ws.status + ((long long)other * a.ws.n_rows + i) * (kSlot / 2), 0ull);
 }
 
-template <bool BF16, bool VEC, bool TRUNC, bool PM>
+template <bool BF16, bool VEC, bool TRUNC, int PROP>
 __device__ inline void verify_block(const Args& a, TruncScratch* sc) {
     clear_other_parity(a);
     const int per_pos = a.B * a.C;
@@ -1911,37 +1489,39 @@ __device__ inline void verify_block(const Args& a, TruncScratch* sc) {
     const int rem = t - k * per_pos;
     const int b = rem / a.C;
     const int c = rem - b * a.C;
-    if (k < a.P) stream_unit<BF16, VEC, TRUNC, PM>(a, k, b, c, sc);
-    else sample_item<BF16, VEC, PM>(a, b, c);
+    if (k < a.P) stream_unit<BF16, VEC, TRUNC, PROP>(a, k, b, c, sc);
+    else sample_item<BF16, VEC, PROP>(a, b, c);
 }
 
-template <bool BF16, bool VEC, bool PM>
+template <bool BF16, bool VEC, int PROP>
 __global__ __launch_bounds__(kBlock) void k_verify(Args a) {
-    verify_block<BF16, VEC, false, PM>(a, nullptr);
+    verify_block<BF16, VEC, false, PROP>(a, nullptr);
 }
 
-template <bool BF16, bool VEC, bool PM>
+template <bool BF16, bool VEC, int PROP>
 __global__ __launch_bounds__(kBlock) void k_verify_trunc(Args a) {
     __shared__ TruncScratch sc;
-    verify_block<BF16, VEC, true, PM>(a, &sc);
+    verify_block<BF16, VEC, true, PROP>(a, &sc);
 }
 
 using KernelFn = void (*)(Args);
 
-// The point-mass variants (PM) are separate instantiations, so that the
-// two-model kernels carry none of their code.
-template <bool PM>
-KernelFn pick_pm(bool bf16, bool vec, bool trunc) {
+// Each proposal kind is a separate instantiation, so that the two-model
+// kernels carry none of the other kinds' code.
+template <int PROP>
+KernelFn pick_prop(bool bf16, bool vec, bool trunc) {
     if (trunc) {
-        if (bf16) return vec ? k_verify_trunc<true, true, PM> : k_verify_trunc<true, false, PM>;
-        return vec ? k_verify_trunc<false, true, PM> : k_verify_trunc<false, false, PM>;
+        if (bf16) return vec ? k_verify_trunc<true, true, PROP> : k_verify_trunc<true, false, PROP>;
+        return vec ? k_verify_trunc<false, true, PROP> : k_verify_trunc<false, false, PROP>;
     }
-    if (bf16) return vec ? k_verify<true, true, PM> : k_verify<true, false, PM>;
-    return vec ? k_verify<false, true, PM> : k_verify<false, false, PM>;
+    if (bf16) return vec ? k_verify<true, true, PROP> : k_verify<true, false, PROP>;
+    return vec ? k_verify<false, true, PROP> : k_verify<false, false, PROP>;
 }
 
-KernelFn pick(bool bf16, bool vec, bool trunc, bool pm) {
-    return pm ? pick_pm<true>(bf16, vec, trunc) : pick_pm<false>(bf16, vec, trunc);
+KernelFn pick(bool bf16, bool vec, bool trunc, int prop) {
+    if (prop == kPropPoint) return pick_prop<kPropPoint>(bf16, vec, trunc);
+    if (prop == kPropStats) return pick_prop<kPropStats>(bf16, vec, trunc);
+    return pick_prop<kPropLogits>(bf16, vec, trunc);
 }
 
 }  // namespace
@@ -1949,7 +1529,7 @@ KernelFn pick(bool bf16, bool vec, bool trunc, bool pm) {
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev) {
     const long long blocks = (long long)(a.P + 1) * a.B * a.C;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    KernelFn fn = pick(bf16, vec, a.cand_cap > 0, a.point_mass != 0);
+    KernelFn fn = pick(bf16, vec, a.cand_cap > 0, a.prop);
     // the events (when profiling) are attached to the dispatch itself, so
     // that they time the kernel and not the packets around it
     hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev ? ev[0] : nullptr,

@@ -166,3 +166,56 @@ def _check_values(rep, b, gpu, orc, eo, greedy):
             rep.fail(b, f"residual sum gpu={gw} oracle={ow}")
         elif err > W_REL * ow:
             rep.w_floor_only += 1
+
+
+def compare_draft(gpu_tok, gpu_stats, gpu_flags, draft_f32, temperature, seed, step=0, pos0=0,
+                  report=None, skip_rows=()):
+    """Compare the draft sampler's outputs for positions pos0 .. pos0+n-1
+    (arrays already sliced to those columns) with the oracle's draw and row
+    statistics.  Tokens: identical, or (sampled rows) inside the CDF window;
+    greedy tokens bit-exact; m exact; s within REL_TOL; flags exact.  Batch
+    rows in ``skip_rows`` are not compared."""
+    rep = report or Report()
+    d = np.asarray(draft_f32)
+    B, n, V = d.shape
+    T = np.broadcast_to(np.asarray(temperature, np.float64), (B,))
+    o_tok = oracle.sample_draft_tokens(d, T, 0, 1.0, seed, step, pos0)
+    o_st = oracle.draft_row_stats(d, T)
+    g_tok, g_st, g_fl = _np(gpu_tok), _np(gpu_stats), _np(gpu_flags)
+    for b in range(B):
+        if b in skip_rows:
+            continue
+        for i in range(n):
+            rep.rows += 1
+            t, o = int(g_tok[b, i]), int(o_tok[b, i])
+            want_flag = oracle.FLAG_NONFINITE_ROW if o < 0 else 0
+            if int(g_fl[b, i]) != want_flag:
+                rep.fail(b, f"pos {pos0 + i}: flags {int(g_fl[b, i])} want {want_flag}")
+                continue
+            if T[b] > 0 and o >= 0:
+                m, s = float(g_st[b, i, 0]), float(g_st[b, i, 1])
+                rep.value_checks += 1
+                if m != o_st[b, i, 0] or not abs(s - o_st[b, i, 1]) <= REL_TOL * o_st[b, i, 1]:
+                    rep.fail(b, f"pos {pos0 + i}: stats ({m}, {s}) oracle {tuple(o_st[b, i])}")
+                    continue
+            elif not np.isnan(g_st[b, i]).all():
+                rep.fail(b, f"pos {pos0 + i}: stats {g_st[b, i]} written for a greedy / undrawn row")
+                continue
+            if t == o:
+                rep.exact += 1
+                continue
+            if T[b] == 0 or o < 0:
+                rep.fail(b, f"pos {pos0 + i}: token {t} oracle {o}")
+                continue
+            q = oracle.process_row(d[b, i], T[b]).probs
+            if not (0 <= t < V) or q[t] <= 0:
+                rep.fail(b, f"pos {pos0 + i}: token {t} has no draft mass")
+                continue
+            lo, hi = oracle.cdf_interval(q, t)
+            u = float(oracle.philox.uniform(seed, b, pos0 + i, oracle.philox.PURPOSE_DRAFT, step))
+            dist = 0.0 if lo <= u <= hi else min(abs(u - lo), abs(u - hi))
+            if dist < CDF_WINDOW:
+                rep.tolerated["cdf_window"] += 1
+            else:
+                rep.fail(b, f"pos {pos0 + i}: token {t} [{lo},{hi}] oracle {o} u={u}")
+    return rep

@@ -64,6 +64,12 @@ def test_verify_rejects_null_handle(lib):
     rc = lib.specv_verify_point_mass(None, None, None, 0, 0, 1, 1, 1, 1, None, None, 0, 0, -1,
                                      None, None, None, None, None)
     assert rc == 1
+    rc = lib.specv_verify_sample_qstats(None, None, None, 0, 0, None, 0, 0, None, 0, 1, 1, 1, 1,
+                                        None, None, 0, 0, -1, None, None, None, None, None)
+    assert rc == 1
+    rc = lib.specv_sample_draft(None, None, None, 0, 0, 1, 1, 1, 1, 0, None, 0, 0,
+                                None, None, None, 1)
+    assert rc == 1
     assert lib.specv_destroy(None) == 0
 
 

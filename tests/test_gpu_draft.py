@@ -1,0 +1,234 @@
+"""GPU parity of the draft-side sampler (``specv_sample_draft``) with the
+oracle's draw and row statistics, and of verification that reuses those
+statistics (``specv_verify_sample_qstats``) with ``specv_verify_sample``
+(bit for bit) and the oracle.
+
+Covered: the tiny workload over 20,000 rows with a chi-square test of the
+draws, the serving batch at full size (all positions in one call, and one
+position per call), greedy rows, ragged vocabularies and unaligned rows,
+gamma at its maximum, rows that define no draw, truncated rows (flagged, and
+verified from their draft rows), and statistics that mark a row non-finite.
+"""
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+import synth
+import speculative_decoding_verification_sampling_amd as sv
+from parity import compare, compare_draft
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sv.load_library()          # raises loudly when the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def _prm(B, T, k=0, p=1.0, cap=0):
+    b = lambda x, dt: np.broadcast_to(np.asarray(x, dt), (B,)).copy()
+    return {"temperature": b(T, np.float32), "top_k": b(k, np.int32), "top_p": b(p, np.float32),
+            "max_new_tokens": b(cap, np.int32)}
+
+
+def _rp(prm):
+    return sv.make_row_params(len(prm["temperature"]), prm["temperature"], prm["top_k"], prm["top_p"],
+                              prm["max_new_tokens"])
+
+
+def _draw(v, draft_dev, prm, seed, step=0, pos0=0, out=None):
+    o = v.sample_draft(draft_dev, _rp(prm), seed, step, pos0, out=out)
+    torch.cuda.synchronize()
+    return o
+
+
+def _check_draft(o, draft_f32, prm, seed, step=0, pos0=0, max_tol=0.02):
+    n = draft_f32.shape[1]
+    sl = slice(pos0, pos0 + n)
+    rep = compare_draft(o["tokens"][:, sl], o["stats"][:, sl], o["flags"][:, sl], draft_f32,
+                        prm["temperature"], seed, step, pos0)
+    print(rep.summary())
+    rep.assert_ok(max_tol)
+    return rep
+
+
+def test_draft_tiny_rows_chi2(gpu):
+    """Tiny draft rows (V=32, fp32, T=1), 20,000 broadcast rows: parity with
+    the oracle and, per position, the draws follow softmax(z) (chi-square)."""
+    w = synth.tiny()
+    R = 20000
+    d = w.draft.expand(R, -1, -1)
+    prm = _prm(R, 1.0)
+    with sv.Verifier(R, 4, 32) as v:
+        o = _draw(v, w.draft.cuda().expand(R, -1, -1), prm, 0xD1A)
+    _check_draft(o, d.numpy(), prm, 0xD1A)
+    toks = o["tokens"].cpu().numpy()
+    for i in range(4):
+        P = torch.softmax(torch.from_numpy(w.draft_f32()[0, i].astype(np.float64)), 0).numpy()
+        counts = np.bincount(toks[:, i], minlength=32)
+        keep = P * R >= 5
+        obs, exp = counts[keep], P[keep] * R
+        if (~keep).any():
+            obs = np.append(obs, counts[~keep].sum())
+            exp = np.append(exp, P[~keep].sum() * R)
+        assert stats.chisquare(obs, exp * obs.sum() / exp.sum()).pvalue > 1e-3, i
+
+
+def test_draft_serving_batch_full_size(gpu):
+    """B=64, 5 positions, V=128256, bf16, T=0.7: one call for all positions,
+    then one position per call into the same outputs: identical."""
+    w = synth.serving_batch()
+    prm = _prm(w.B, w.temperature)
+    dd = w.draft.cuda()
+    with sv.Verifier(w.B, w.gamma, w.V) as v:
+        o = _draw(v, dd, prm, w.seed, step=3)
+        _check_draft(o, w.draft_f32(), prm, w.seed, step=3)
+        o2 = {"tokens": torch.full((w.B, w.gamma), -7, dtype=torch.int32, device=gpu),
+              "stats": torch.zeros(w.B, w.gamma, 2, device=gpu),
+              "flags": torch.full((w.B, w.gamma), -7, dtype=torch.int32, device=gpu)}
+        for i in range(w.gamma):
+            _draw(v, dd[:, i:i + 1], prm, w.seed, step=3, pos0=i, out=o2)
+    for k in ("tokens", "stats", "flags"):
+        assert torch.equal(o[k], o2[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,n,aligned", [(1, 2, True), (7, 3, True), (8193, 2, True),
+                                         (16385, 4, False), (40000, 3, False), (300, 31, True)])
+def test_draft_greedy_ragged(gpu, dtype, V, n, aligned):
+    """Even rows T=0.9, odd rows greedy; ragged vocabularies (a partial last
+    chunk, a partial 16-byte group), rows that do not start 16-byte aligned,
+    and n up to the largest gamma."""
+    rng = np.random.default_rng(V * 3 + n)
+    B = 6
+    _, d = synth.make_logits(rng, B, n, V + 1, 2.0, 0.7, boost_count=min(20, V))
+    dt = torch.from_numpy(d)
+    if dtype == "bf16":
+        dt = dt.to(torch.bfloat16)
+    dv = dt.cuda()
+    dv = dv[:, :, :V] if aligned else dv[:, :, 1:]          # unaligned rows start one entry in
+    df = (dt[:, :, :V] if aligned else dt[:, :, 1:]).float().numpy()
+    T = np.where(np.arange(B) % 2 == 0, 0.9, 0.0)
+    prm = _prm(B, T)
+    with sv.Verifier(B, max(n, 1), V) as v:
+        o = _draw(v, dv, prm, 4321 + V)
+    _check_draft(o, df, prm, 4321 + V, max_tol=0.2)
+
+
+def test_draft_rows_without_a_draw(gpu):
+    """NaN, +inf and all -inf rows give -1 and NONFINITE_ROW (greedy rows
+    too); top-k / top-p rows give -1 and UNSUPPORTED; other rows draw."""
+    rng = np.random.default_rng(8)
+    B, n, V = 8, 2, 9000
+    d = rng.standard_normal((B, n, V)).astype(np.float32)
+    d[0, 1, 17] = np.nan
+    d[1, 0, 4] = np.inf
+    d[2, 1] = -np.inf
+    d[3, 0, 5] = np.nan                                     # greedy row
+    T = np.array([1, 1, 1, 0, 1, 1, 0.8, 1.2], np.float32)
+    k = np.array([0, 0, 0, 0, 5, 0, 0, 0], np.int32)
+    p = np.array([1, 1, 1, 1, 1, 0.9, 1, 1], np.float32)
+    prm = {"temperature": T, "top_k": k, "top_p": p, "max_new_tokens": np.zeros(B, np.int32)}
+    with sv.Verifier(B, n, V) as v:
+        o = _draw(v, torch.from_numpy(d).cuda(), prm, 5)
+    tok, fl = o["tokens"].cpu().numpy(), o["flags"].cpu().numpy()
+    st = o["stats"].cpu().numpy()
+    for (b, i) in [(0, 1), (1, 0), (2, 1), (3, 0)]:
+        assert tok[b, i] == -1 and fl[b, i] == sv.FLAG_NONFINITE_ROW and np.isnan(st[b, i]).all()
+    for b in (4, 5):
+        assert (tok[b] == -1).all() and (fl[b] == sv.FLAG_UNSUPPORTED).all() and np.isnan(st[b]).all()
+    # every other row against the oracle (same row indices, so same uniforms)
+    rep = compare_draft(o["tokens"], o["stats"], o["flags"], d, T, 5, skip_rows=(4, 5))
+    print(rep.summary())
+    rep.assert_ok(0.2)
+
+
+def _verify_both(v, w_t, w_d, tokens, stats_, prm, seed, step=0):
+    rp = _rp(prm)
+    tok = torch.from_numpy(np.ascontiguousarray(tokens, np.int32)).cuda() if isinstance(tokens, np.ndarray) \
+        else tokens
+    a = v.verify_sample(w_t, w_d, tok, rp, seed, step, diag=True)
+    b = v.verify_sample_qstats(w_t, w_d, stats_, tok, rp, seed, step, diag=True)
+    torch.cuda.synchronize()
+    for key in ("num_accepted", "out_tokens", "num_emitted", "row_flags"):
+        assert torch.equal(a[key], b[key]), key
+    for key in ("p_at_draft", "q_at_draft", "residual_sum"):
+        x, y = a[key].cpu().numpy(), b[key].cpu().numpy()
+        assert np.array_equal(x, y, equal_nan=True), key
+    return b
+
+
+def test_qstats_verify_serving_batch_bitwise(gpu):
+    """The drafter's draws and statistics from the sampler, then both verify
+    entry points: bit-identical outputs, and parity with the oracle."""
+    w = synth.serving_batch()
+    prm = _prm(w.B, w.temperature)
+    t, d = w.target.cuda(), w.draft.cuda()
+    with sv.Verifier(w.B, w.gamma, w.V) as v:
+        for step in range(2):
+            o = _draw(v, d, prm, w.seed + 1, step)
+            out = _verify_both(v, t, d, o["tokens"], o["stats"], prm, w.seed, step)
+            toks = o["tokens"].cpu().numpy()
+            orc = oracle.verify_sample(w.target_f32(), w.draft_f32(), toks, w.temperature, 0, 1.0, 0,
+                                       w.seed, step, keep_weights=True)
+            rep = compare(out, orc, toks, w.target_f32(), w.draft_f32(), prm)
+            print(rep.summary())
+            rep.assert_ok()
+
+
+def test_qstats_verify_greedy_truncated_mixed(gpu):
+    """Rows of every mode in one call (handle with truncation): greedy rows
+    and truncated rows ignore the statistics (truncated rows' draft tokens
+    come from the oracle's truncated draw; their statistics are NaN)."""
+    rng = np.random.default_rng(41)
+    B, gamma, V = 24, 4, 50000
+    t, d = synth.make_logits(rng, B, gamma, V, 3.0, 1.0, boost_count=20)
+    tt, dd = torch.from_numpy(t).to(torch.bfloat16), torch.from_numpy(d).to(torch.bfloat16)
+    mode = np.arange(B) % 3                                  # 0 sample, 1 greedy, 2 truncated
+    T = np.where(mode == 1, 0.0, 0.8).astype(np.float32)
+    k = np.where(mode == 2, 40, 0).astype(np.int32)
+    p = np.where(mode == 2, 0.9, 1.0).astype(np.float32)
+    cap = rng.integers(0, 6, B).astype(np.int32)
+    prm = {"temperature": T, "top_k": k, "top_p": p, "max_new_tokens": cap}
+    with sv.Verifier(B, gamma, V, max_top_k=64) as v:
+        o = _draw(v, dd.cuda(), prm, 77)
+        toks = o["tokens"].cpu().numpy()
+        df = dd.float().numpy()
+        tr = mode == 2
+        toks[tr] = oracle.sample_draft_tokens(df[tr], 0.8, 40, 0.9, 78)
+        out = _verify_both(v, tt.cuda(), dd.cuda(), toks, o["stats"], prm, 79)
+    orc = oracle.verify_sample(tt.float().numpy(), df, toks, T, k, p, cap, 79, keep_weights=True)
+    rep = compare(out, orc, toks, tt.float().numpy(), df, prm)
+    print(rep.summary())
+    rep.assert_ok(0.1)
+
+
+def test_qstats_non_finite_statistics_mark_the_row(gpu):
+    """A NaN statistic, a zero sum or a max of -inf makes the row emit
+    nothing with NONFINITE_ROW; the other rows are unaffected."""
+    w = synth.serving_batch(B=8, V=20000)
+    prm = _prm(w.B, w.temperature)
+    t, d = w.target.cuda(), w.draft.cuda()
+    with sv.Verifier(w.B, w.gamma, w.V) as v:
+        o = _draw(v, d, prm, 3)
+        st = o["stats"].clone()
+        st[1, 0, 1] = float("nan")
+        st[2, 0, 1] = 0.0
+        st[3, 0, 0] = float("-inf")
+        rp = _rp(prm)
+        good = v.verify_sample(t, d, o["tokens"], rp, 9)
+        bad = v.verify_sample_qstats(t, d, st, o["tokens"], rp, 9)
+        torch.cuda.synchronize()
+    fl = bad["row_flags"].cpu().numpy()
+    em = bad["num_emitted"].cpu().numpy()
+    for b in (1, 2, 3):
+        assert fl[b] & sv.FLAG_NONFINITE_ROW and em[b] == 0
+    keep = [0, 4, 5, 6, 7]
+    for key in ("num_accepted", "out_tokens", "num_emitted", "row_flags"):
+        assert torch.equal(good[key][keep], bad[key][keep]), key

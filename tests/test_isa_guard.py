@@ -1,4 +1,4 @@
-"""Static guard on the gfx950 code of the verify kernels (CPU only).
+"""Static guard on the gfx950 code of the verify and draft-sampler kernels (CPU only).
 
 A cross-lane read ``v_readlane_b32 sD, vS, sIdx`` returns lane sIdx of vS
 whatever EXEC holds.  When the compiler spills vS and reloads it inside a
@@ -89,8 +89,10 @@ def test_checker_finds_the_fault_pattern():
 
 @pytest.mark.skipif(shutil.which(specv_build.hipcc()) is None and not os.path.exists(specv_build.hipcc()),
                     reason="hipcc not available")
-def test_no_dynamic_lane_read_of_a_spill_reload(tmp_path):
-    src = os.path.join(os.path.dirname(specv_build.__file__), "csrc", "specv_kernels.hip")
+@pytest.mark.parametrize("source,kernel", [("specv_kernels.hip", "k_verify"),
+                                           ("specv_draft.hip", "k_sample_draft")])
+def test_no_dynamic_lane_read_of_a_spill_reload(tmp_path, source, kernel):
+    src = os.path.join(os.path.dirname(specv_build.__file__), "csrc", source)
     out = tmp_path / "kernels.s"
     flags = [f for f in specv_build.FLAGS if f not in ("-shared", "-fPIC")]
     cmd = [specv_build.hipcc(), *flags, "-I", specv_build.INCLUDE, "-I", os.path.dirname(src),
@@ -98,5 +100,5 @@ def test_no_dynamic_lane_read_of_a_spill_reload(tmp_path):
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=str(tmp_path))
     assert r.returncode == 0, r.stderr[-2000:]
     asm = out.read_text()
-    assert "k_verify" in asm
+    assert kernel in asm
     assert stale_lane_reads(asm) == []
