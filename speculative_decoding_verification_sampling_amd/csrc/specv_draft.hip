@@ -16,8 +16,11 @@
 //      them into the row's (m, s), and turns them into chunk masses
 //      s_c * exp2((m_c - m) * scale) whose prefix sums locate the chunk
 //      holding u * W; every workgroup of the row computes the same thing;
-//   3. the workgroup owning that chunk finds the token in its registers with
-//      a block prefix sum and writes the token and the row's (m, s).
+//   3. the workgroup owning that chunk finds the token in its registers and
+//      writes the token and the row's (m, s).  Its in-chunk running sums (in
+//      the chunk's own exp2 units) are computed by every workgroup while the
+//      statistics are in flight, so that after the hand-off the owner only
+//      compares the target with its groups' ranges.
 // One hand-off per row, and the row is read once.  The chunk statistics and
 // their merge are the verify kernel's, so the (m, s) written here equal the
 // normalisers the verify step computes from the same row.
@@ -115,10 +118,65 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
         }
     }
 
-    // 2. the row's statistics and the chunk holding u * W (wave 0)
+    // 2. (sampled rows) while the other chunks' statistics are on their way:
+    //    this chunk's weights exp2((z - m_c) * scale) in token order, as
+    //    group sums gw[j] with their starting running sums gstart[j] (group
+    //    (j, tid) follows every (j', *) with j' < j and every (j, tid') with
+    //    tid' < tid), and the last entry with weight
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int NG = kPerThread / G;
+    __shared__ float gtot[NG][kWaves];
+    __shared__ int lastW[kWaves], sTok;
+    float gw[NG], gstart[NG], nms = 0.f;
+    if (!greedy) {
+        const float mc = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+        nms = mc == -kInf ? 0.f : -mc * scale;
+        int lastpos = -1;
+        float incl[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            float sj = 0.f;
+            int lastin = -1;
+#pragma unroll
+            for (int e = 0; e < G; ++e) {
+                const float x = fast_exp2(fmaf(r.elem(j * G + e), scale, nms));
+                sj += x;
+                if (x > 0.f) lastin = e;
+            }
+            gw[j] = sj;
+            if (lastin >= 0) lastpos = (j * kBlock + tid) * G + lastin;
+            incl[j] = wave_scan_incl(sj);
+            if (lane == kWave - 1) gtot[j][wave] = incl[j];
+        }
+        lastpos = wave_max_int(lastpos);
+        if (lane == 0) lastW[wave] = lastpos;
+        if (tid == 0) sTok = 0x7fffffff;
+        __syncthreads();
+        float gbase = 0.f;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            float before = 0.f, tot = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2) {
+                const float g = gtot[j][w2];
+                if (w2 < wave) before += g;
+                tot += g;
+            }
+            gstart[j] = gbase + before + (incl[j] - gw[j]);
+            gbase += tot;
+        }
+    }
+
+    // 3. the row's statistics and the chunk holding u * W (wave 0)
     __shared__ int sChosen, sDone;
-    __shared__ float sBase, sTarget, sM, sS;
+    __shared__ float sLocal, sM, sS;
     if (wave == 0) {
+        // the uniform does not depend on the statistics: drawn before the wait
+        float u = 0.f;
+        if (!greedy) {
+            u = uniform24(a.seed, b, pos, PURPOSE_DRAFT, a.step);
+            asm volatile("" : "+v"(u));
+        }
         float m = -kInf;
         unsigned second = 0;
         bool ok = true;
@@ -126,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
         const bool late = __ballot(!ok) != 0;
         int chosen = -1, tok = -1;
         unsigned flags = 0;
-        float M = nan, S = nan, base = 0.f, target = 0.f;
+        float M = nan, S = nan, local = 0.f;
         if (greedy) {
             int arg = lane < a.C ? (int)second : 0x7fffffff;
             const bool isnan_m = lane < a.C && __builtin_isnan(m);
@@ -144,17 +202,21 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
             } else {
                 M = Mr;
                 S = Sr;
+                // chunk masses s_c * exp2((m_c - M) * scale) and their prefix sums
                 const float wc = m > -kInf ? s * fast_exp2((m - M) * scale) : 0.f;
                 const float incl = wave_scan_incl(wc);
                 const float W = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), kWave - 1));
-                target = uniform24(a.seed, b, pos, PURPOSE_DRAFT, a.step) * W;
+                const float target = u * W;
                 const unsigned long long hit = __ballot(wc > 0.f && incl > target);
                 const unsigned long long any = __ballot(wc > 0.f);
                 // rounding: without a hit, the last chunk with mass
                 chosen = hit ? __builtin_ctzll(hit) : (any ? 63 - __builtin_clzll(any) : -1);
                 const float before = __int_as_float(
                     __builtin_amdgcn_readlane(__float_as_int(incl), chosen > 0 ? chosen - 1 : 0));
-                base = chosen > 0 ? before : 0.f;
+                const float mch = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), chosen > 0 ? chosen : 0));
+                // u * W - (mass of the earlier chunks), in the chosen chunk's own
+                // units exp2((z - m_c) * scale)
+                local = (target - (chosen > 0 ? before : 0.f)) * fast_exp2((M - mch) * scale);
             }
         }
         if (late) {
@@ -165,8 +227,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
         if (lane == 0) {
             sChosen = chosen;
             sDone = chosen < 0;
-            sBase = base;
-            sTarget = target;
+            sLocal = local;
             sM = M;
             sS = S;
             // rows with nothing left to draw (greedy, bad, late) are written by
@@ -177,25 +238,37 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
     __syncthreads();
     if (sDone || sChosen != c) return;
 
-    // 3. the owner of the chunk finds the token
-    constexpr int G = BF16 ? 8 : 4;
-    constexpr int NG = kPerThread / G;
-    const float M = sM;
-    float w[kPerThread], gw[NG];
+    // 4. the owner of the chunk: the group whose running-sum range holds the
+    //    target claims it and scans its entries (the first whose running sum
+    //    exceeds the target, else, rounding, the group's last entry with
+    //    weight); the lowest claimed token wins; with no claim (rounding),
+    //    the chunk's last entry with weight
+    const float tloc = sLocal;
+    int claim = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-        float s = 0.f;
+        if (claim == 0x7fffffff && gw[j] > 0.f && tloc >= gstart[j] && tloc < gstart[j] + gw[j]) {
+            float run = gstart[j];
+            int first = -1, lastin = -1;
 #pragma unroll
-        for (int e = 0; e < G; ++e) {
-            w[j * G + e] = fast_exp2(__fmul_rn(r.elem(j * G + e) - M, scale));
-            s += w[j * G + e];
+            for (int e = 0; e < G; ++e) {
+                const float x = fast_exp2(fmaf(r.elem(j * G + e), scale, nms));
+                run += x;
+                if (x > 0.f) {
+                    lastin = e;
+                    if (first < 0 && run > tloc) first = e;
+                }
+            }
+            claim = (j * kBlock + tid) * G + (first >= 0 ? first : lastin);
         }
-        gw[j] = s;
     }
-    const int t = chunk_inverse_cdf<BF16>(w, gw, sBase, sTarget);
+    if (claim != 0x7fffffff) atomicMin(&sTok, claim);
+    __syncthreads();
     if (tid == 0) {
+        int t = sTok;
+        if (t == 0x7fffffff) t = max(max(lastW[0], lastW[1]), max(lastW[2], lastW[3]));
         if (t < 0) write_draft(a, o, -1, nan, nan, SPECV_FLAG_NONFINITE_ROW);
-        else write_draft(a, o, c * kChunk + t, M, sS, 0u);
+        else write_draft(a, o, c * kChunk + t, sM, sS, 0u);
     }
 }
 
