@@ -44,8 +44,9 @@ removed.  No draft logits exist.
 The drafter's side: ``sample_draft_tokens`` draws d_i ~ q_i (the processed
 draft distribution, inverse CDF with the uniform of purpose DRAFT), and
 ``draft_row_stats`` gives the statistics a drafter that sampled q_i can hand
-to the verifier, m = max z and s = sum exp((z - m) / T), from which
-q_i(v) = exp((z_v - m) / T) / s on an untruncated row.
+to the verifier: over the kept set, m = max z, s = sum exp((z - m) / T) and
+the threshold t = min z (-inf without truncation), from which
+q_i(v) = [z_v >= t] exp((z_v - m) / T) / s.
 
 Pins (``tests/test_oracle_*.py``): the worked example of 11.1.3, exact
 enumeration over all 2^24 uniforms on small rows, the 11.1.3 identities,
@@ -364,27 +365,36 @@ def verify_greedy(target, tokens, max_new_tokens=0, eos_id=-1):
     return _finish(results, B, gamma)
 
 
-def draft_row_stats(draft, temperature):
-    """Statistics of each draft row, as a drafter that samples q_i can hand
-    them to the verifier: m = the largest logit and s = sum_v exp((z_v - m)/T),
-    so that q_i(v) = exp((z_v - m)/T) / s for an untruncated row (the
-    temperature division of the tutorial's section 3.3).  Rows with
-    temperature 0, or with NaN / +inf / no finite logit, get NaN for both.
-    Returns float64 [B, gamma, 2]."""
+def draft_row_stats(draft, temperature, top_k=0, top_p=1.0):
+    """Statistics of each processed draft row, as a drafter that samples q_i
+    can hand them to the verifier: with K the kept set (every finite token
+    when no truncation is on; the top-k / top-p set otherwise),
+    m = max_{v in K} z_v (the row maximum), s = sum_{v in K} exp((z_v - m)/T)
+    and the threshold t = min_{v in K} z_v (-inf when top-k and top-p are
+    both off), so that q_i(v) = [z_v >= t] exp((z_v - m)/T) / s (the
+    temperature division of the tutorial's section 3.3; q is the truncated
+    distribution actually sampled, "11.1 核心原理" 11.1.2).  Rows with
+    temperature 0, or with NaN / +inf / no finite logit, get NaN.
+    Returns float64 [B, gamma, 3] = (m, s, t)."""
     draft = np.asarray(draft, np.float64)
     B, gamma, V = draft.shape
     T = _broadcast(temperature, B, np.float64)
-    out = np.full((B, gamma, 2), np.nan)
+    K = _broadcast(top_k, B, np.int64)
+    Pp = _broadcast(top_p, B, np.float64)
+    out = np.full((B, gamma, 3), np.nan)
     for b in range(B):
         if T[b] == 0.0:
             continue
+        truncated = (0 < K[b] < V) or Pp[b] < 1.0
         for i in range(gamma):
-            z = draft[b, i]
-            if np.isnan(z).any() or np.isposinf(z).any() or not np.isfinite(z).any():
+            Q = process_row(draft[b, i], T[b], K[b], Pp[b])
+            if Q.nonfinite:
                 continue
+            z = draft[b, i][Q.kept]
             m = z.max()
             out[b, i, 0] = m
             out[b, i, 1] = np.exp((z - m) / T[b]).sum()
+            out[b, i, 2] = z.min() if truncated else -np.inf
     return out
 
 

@@ -10,7 +10,9 @@ What fixes them, independently of the oracle's own code:
   11.1.2: q is the distribution actually sampled);
 * greedy drafts equal ``torch.argmax`` (first maximal index);
 * the statistics: m is the row maximum and m / T + log s equals
-  ``torch.logsumexp(z / T)``, so exp((z - m) / T) / s is q;
+  ``torch.logsumexp(z / T)``, so exp((z - m) / T) / s is q; with top-k /
+  top-p, [z >= t] exp((z - m) / T) / s equals ``torch.softmax`` over a
+  brute-force kept set (the definitions written out with full sorts);
 * a row with NaN / +inf or nothing finite gives token -1 and NaN statistics;
 * drawing one column at a time with its position equals drawing them all.
 
@@ -100,6 +102,7 @@ def _lse_check(d, T, st):
     lse = torch.logsumexp(z / T, -1).numpy()
     assert np.array_equal(st[..., 0], m)
     assert np.allclose(st[..., 0] / T + np.log(st[..., 1]), lse, rtol=0, atol=1e-12)
+    assert np.all(st[..., 2] == -np.inf)
 
 
 @pytest.mark.parametrize("T", [1.0, 0.7, 2.5])
@@ -133,7 +136,7 @@ def test_bad_rows_and_greedy_rows():
     st = oracle.draft_row_stats(d, T)
     assert toks[0, 1] == -1 and toks[1, 0] == -1 and toks[2, 1] == -1
     assert np.isnan(st[0, 1]).all() and np.isnan(st[1, 0]).all() and np.isnan(st[2, 1]).all()
-    assert toks[0, 0] >= 0 and np.isfinite(st[0, 0]).all()
+    assert toks[0, 0] >= 0 and np.isfinite(st[0, 0, :2]).all() and st[0, 0, 2] == -np.inf
     assert np.isnan(st[3]).all()                    # greedy rows: no statistics
     assert toks[3].tolist() == d[3].argmax(-1).tolist()
     g = oracle.sample_draft_tokens(d[1:2], 0.0, 0, 1.0, seed=4)
@@ -151,3 +154,49 @@ def test_column_at_a_time_equals_all_at_once(monkeypatch):
     wrong = [oracle.sample_draft_tokens(d[:, i:i + 1], 0.9, 0, 1.0, seed=77, step=5)[:, 0]
              for i in range(4)]
     assert not all(np.array_equal(wrong[i], full[:, i]) for i in range(4))
+
+
+def _brute_kept(z, T, k, top_p):
+    """Kept set from the definitions: top-k by counting larger values (ties
+    kept), then the highest level whose value-ordered mass reaches top_p."""
+    V = len(z)
+    keep = np.array([(z > z[v]).sum() < k for v in range(V)]) if 0 < k < V else np.ones(V, bool)
+    if top_p < 1.0:
+        x = z / T
+        e = np.where(keep, np.exp(x - x[keep].max()), 0.0)
+        pi = e / e.sum()
+        best = min(z[keep])
+        for lv in sorted(set(z[keep].tolist())):
+            if pi[keep & (z >= lv)].sum() >= top_p:
+                best = lv
+        keep = keep & (z >= best)
+    return keep
+
+
+@pytest.mark.parametrize("k,top_p", [(5, 1.0), (0, 0.8), (12, 0.9), (40, 0.5)])
+def test_row_stats_truncated_brute_force(k, top_p):
+    rng = np.random.default_rng(k + int(top_p * 100))
+    d = np.round(rng.standard_normal((3, 2, 60)) * 8) / 4          # coarse values: ties
+    T = 0.8
+    st = oracle.draft_row_stats(d, T, k, top_p)
+    for b in range(3):
+        for i in range(2):
+            z = d[b, i]
+            keep = _brute_kept(z, T, k, top_p)
+            q_bf = torch.softmax(torch.tensor(np.where(keep, z / T, -np.inf)), 0).numpy()
+            m, s, t = st[b, i]
+            q = np.where(z >= t, np.exp((z - m) / T), 0.0) / s
+            assert np.allclose(q, q_bf, rtol=1e-12, atol=1e-300)
+            assert t == z[keep].min() and m == z.max()
+
+
+def test_row_stats_truncated_negative_control(monkeypatch):
+    """Statistics that keep the whole row under top-k fail the pin."""
+    d = np.round(np.random.default_rng(9).standard_normal((1, 1, 40)) * 8) / 4
+    st = oracle.draft_row_stats(d, 0.8, 0, 1.0)                     # untruncated
+    z = d[0, 0]
+    keep = _brute_kept(z, 0.8, 5, 1.0)
+    q_bf = torch.softmax(torch.tensor(np.where(keep, z / 0.8, -np.inf)), 0).numpy()
+    m, s, t = st[0, 0]
+    q = np.where(z >= t, np.exp((z - m) / 0.8), 0.0) / s
+    assert not np.allclose(q, q_bf, rtol=1e-12, atol=1e-300)
