@@ -190,8 +190,7 @@ def main():
     drawn = None
     if drafted:
         drawn = {"tokens": torch.full((B, gamma), -1, dtype=torch.int32, device=dev),
-                 "stats": torch.zeros(B, gamma, 2, dtype=torch.float32, device=dev),
-                 "flags": torch.zeros(B, gamma, dtype=torch.int32, device=dev)}
+                 "stats": torch.zeros(B, gamma, 4, dtype=torch.float32, device=dev)}
 
     def call(k, step):
         t, d, cols = sets[k % len(sets)]

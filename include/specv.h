@@ -118,6 +118,22 @@ typedef struct {
     int32_t max_new_tokens; /* >= 1: at most this many tokens emitted; <= 0: no cap      */
 } specv_row_params;
 
+/* Statistics of one processed draft row, written by specv_sample_draft and
+ * read by specv_verify_sample_qstats (16 bytes).  With K the row's kept set
+ * (every finite token without truncation; the top-k / top-p set otherwise):
+ *   max        m = max_{v in K} z_v (the row maximum)
+ *   sum        s = sum_{v in K} exp((z_v - m) / T), float32
+ *   threshold  K = {v : z_v >= threshold}; -inf without truncation
+ *   flags      SPECV_FLAG_* found while drawing (see specv_sample_draft)
+ * so that q(v) = [z_v >= threshold] * exp((z_v - m) / T) / s.  max, sum and
+ * threshold are NaN for greedy rows and rows without a draw. */
+typedef struct {
+    float max;
+    float sum;
+    float threshold;
+    int32_t flags;
+} specv_draft_stats;
+
 /* Optional diagnostic outputs (device pointers, each may be NULL). */
 typedef struct {
     float* p_at_draft;    /* [B, gamma]: p_i(d_i) for every accept test run, NaN otherwise */
@@ -175,57 +191,58 @@ SPECV_API specv_status specv_verify_point_mass(specv_handle h, void* stream,
 /* Draft-side sampler: draws d_i ~ q_i for positions pos0 .. pos0+n_pos-1 of
  * B rows in one pass over the draft logits, and returns each row's
  * statistics for specv_verify_sample_qstats.  q_i is the draft distribution
- * after the row's temperature ("11.1 核心原理" 11.1.2: the proposal is the
- * distribution actually sampled; the "投机解码 Speculative Decoding"
- * tutorial, section 3.3, for the temperature); the draw is the inverse CDF at
- * the Philox uniform of purpose 0 with counter (b, pos0 + i, 0, step):
- * ascending token order, the first token whose running mass exceeds u * W.
- * A drafter that produces one position at a time calls this once per
- * position (n_pos = 1, pos0 = the position).
+ * after the row's temperature, top-k and top-p ("11.1 核心原理" 11.1.2: the
+ * proposal is the distribution actually sampled; the "投机解码 Speculative
+ * Decoding" tutorial, section 3.3, for the temperature); the draw is the
+ * inverse CDF at the Philox uniform of purpose 0 with counter
+ * (b, pos0 + i, 0, step): ascending token order, the first token whose
+ * running mass exceeds u * W.  A drafter that produces one position at a
+ * time calls this once per position (n_pos = 1, pos0 = the position).
  *   draft_logits    [B, n_pos, V] of dtype; row (b, i) is position pos0 + i
  *                   and starts at draft + b*d_stride_b + i*d_stride_pos
  *   row_params      specv_row_params [B] (max_new_tokens is not used)
  *   out_tokens      int32 [B, out_stride]: entry (b, pos0 + i) gets d_i, or -1
- *                   for a row that defines no draw (below)
- *   out_stats       float [B, out_stride, 2] or NULL: entry (b, pos0 + i) gets
- *                   (m, s), m = max_v z_v and s = sum_v exp((z_v - m) / T) in
- *                   float32, so that q_i(v) = exp((z_v - m) / T) / s; NaN for
- *                   greedy and undrawn rows
- *   out_flags       int32 [B, out_stride] or NULL: SPECV_FLAG_NONFINITE_ROW
- *                   (NaN / +inf or no finite logit: token -1),
- *                   SPECV_FLAG_UNSUPPORTED (top-k or top-p on: this sampler
- *                   draws untruncated and greedy rows only; token -1),
- *                   SPECV_FLAG_INTERNAL (a bounded wait expired), else 0
+ *                   for a row without a draw (below)
+ *   out_stats       specv_draft_stats [B, out_stride] or NULL: entry
+ *                   (b, pos0 + i) gets the row's statistics and flags:
+ *                   SPECV_FLAG_NONFINITE_ROW (NaN / +inf or no finite logit),
+ *                   SPECV_FLAG_CAND_OVERFLOW (truncation candidates exceeded
+ *                   the workspace), SPECV_FLAG_UNSUPPORTED (top-k / top-p on a
+ *                   handle without truncation workspace, or top_k above its
+ *                   max_top_k), SPECV_FLAG_INTERNAL (a bounded wait expired):
+ *                   these rows get token -1; SPECV_FLAG_TOPP_NEAR (the top-p
+ *                   decision was within 1e-5 of top_p) is informational
  * Rows with temperature 0 take the draft argmax (lowest index on ties).
  * Other entries of the outputs are left as they are.  0 <= pos0,
  * pos0 + n_pos <= out_stride, n_pos <= max(max_gamma, 1), B <= max_batch,
- * V <= max_vocab (SPECV_E_SHAPE / SPECV_E_CAPACITY); n_pos == 0 or B == 0 is
- * a no-op.  Calls on a handle, sampler or verify, must not overlap. */
+ * V <= max_vocab (SPECV_E_SHAPE / SPECV_E_CAPACITY); out_stats 16-byte
+ * aligned; n_pos == 0 or B == 0 is a no-op.  Calls on a handle, sampler or
+ * verify, must not overlap. */
 SPECV_API specv_status specv_sample_draft(specv_handle h, void* stream,
                                  const void* draft_logits, int64_t d_stride_b, int64_t d_stride_pos,
                                  specv_dtype dtype, int B, int n_pos, int V, int pos0,
                                  const specv_row_params* row_params, uint64_t seed, uint32_t step,
-                                 int32_t* out_tokens, float* out_stats, int32_t* out_flags,
+                                 int32_t* out_tokens, specv_draft_stats* out_stats,
                                  int64_t out_stride);
 
 /* Stochastic verification reusing the drafter's row statistics: the round of
- * specv_verify_sample, with draft_stats [B, s_stride_b, 2] (float32; entry
- * (b, i) for position i, as specv_sample_draft writes them) standing for the
- * normalisers of the untruncated sampling rows' draft distributions:
- * q_i(v) = exp((z_v - m) / T) / s.  Such rows read no draft row for their
- * accept tests (only the entry at d_i); the draft row where the round stops
- * is read for the correction draw.  The statistics must come from the same
- * draft logits and temperatures as this call's; a NaN, a zero s or an m of
- * -inf marks the row non-finite.  Greedy and truncated rows ignore the
- * statistics (truncated rows reduce their draft rows as specv_verify_sample
- * does).  With statistics from specv_sample_draft the outputs equal
+ * specv_verify_sample, with draft_stats [B, s_stride_b] (entry (b, i) for
+ * position i, as specv_sample_draft writes them) standing for the draft
+ * distributions' normalisers and, for truncated rows, their kept sets.  No
+ * draft row is streamed: the accept tests load q's entry at d_i, and the
+ * draft row where the round stops is read for the correction draw (its
+ * kept-list entries only, for truncated rows).  The statistics must come from
+ * the same draft logits and row parameters as this call's; a row whose
+ * statistics are marked non-finite (or are NaN, a zero sum, a max of -inf)
+ * emits nothing with SPECV_FLAG_NONFINITE_ROW.  Greedy rows ignore them.
+ * With statistics from specv_sample_draft the outputs equal
  * specv_verify_sample's bit for bit.  s_stride_b >= gamma; draft_stats
- * 8-byte aligned.  Other arguments, layouts, ownership and errors as
+ * 16-byte aligned.  Other arguments, layouts, ownership and errors as
  * specv_verify_sample. */
 SPECV_API specv_status specv_verify_sample_qstats(specv_handle h, void* stream,
                                  const void* target_logits, int64_t t_stride_b, int64_t t_stride_pos,
                                  const void* draft_logits, int64_t d_stride_b, int64_t d_stride_pos,
-                                 const float* draft_stats, int64_t s_stride_b,
+                                 const specv_draft_stats* draft_stats, int64_t s_stride_b,
                                  specv_dtype dtype, int B, int gamma, int V,
                                  const int32_t* draft_tokens, const specv_row_params* row_params,
                                  uint64_t seed, uint32_t step, int32_t eos_id,

@@ -131,7 +131,7 @@ def load_library():
         vp, i64, i64,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         vp, u64, u32,
-        vp, vp, vp, i64]
+        vp, vp, i64]
     lib.specv_sample_draft.restype = ctypes.c_int
     lib.specv_verify_greedy.argtypes = [
         vp, vp,
@@ -259,8 +259,9 @@ class Verifier:
     def verify_sample_qstats(self, target, draft, draft_stats, tokens, row_params, seed, step=0,
                              eos_id=-1, out=None, diag=False):
         """Stochastic verification reusing the drafter's row statistics:
-        draft_stats float32 [B, >= gamma, 2] (max, sum) per draft row, as
-        ``sample_draft`` returns them.  Otherwise as verify_sample."""
+        draft_stats float32 [B, >= gamma, 4] records (max, sum, threshold,
+        flags as int32 bits) per draft row, as ``sample_draft`` returns them.
+        Otherwise as verify_sample."""
         return self._verify_two_model(target, draft, draft_stats, tokens, row_params, seed, step,
                                       eos_id, out, diag)
 
@@ -300,8 +301,8 @@ class Verifier:
             return o
         if (draft_stats.dtype != torch.float32 or not draft_stats.is_cuda or draft_stats.dim() != 3
                 or draft_stats.shape[0] != B or draft_stats.shape[1] < gamma
-                or draft_stats.shape[2] != 2 or not draft_stats.is_contiguous()):
-            raise SpecvError("draft_stats must be a contiguous float32 [B, >= gamma, 2] device tensor")
+                or draft_stats.shape[2] != 4 or not draft_stats.is_contiguous()):
+            raise SpecvError("draft_stats must be a contiguous float32 [B, >= gamma, 4] device tensor")
         st = load_library().specv_verify_sample_qstats(
             self._h, self._stream(), *drows, _ptr(draft_stats), draft_stats.shape[1], *common)
         _check(st, "specv_verify_sample_qstats")
@@ -310,33 +311,34 @@ class Verifier:
     def sample_draft(self, draft, row_params, seed, step=0, pos0=0, width=None, out=None):
         """Draft-side sampler: d_i ~ q_i for positions pos0 .. pos0 + n - 1
         of the round, from draft logits [B, n, V] (float32 or bfloat16), with
-        each row's statistics (max, sum) for verify_sample_qstats.  Returns
-        {"tokens": int32 [B, width], "stats": float32 [B, width, 2],
-        "flags": int32 [B, width]} (``width`` defaults to pos0 + n); pass
-        ``out`` (such a dict) to fill columns of existing tensors, e.g. one
-        position per call.  Asynchronous on the current stream."""
+        each row's statistics for verify_sample_qstats.  Returns
+        {"tokens": int32 [B, width], "stats": float32 [B, width, 4],
+        "flags": int32 [B, width]}: stats holds (max, sum, threshold, flags
+        bits) records and "flags" is a view of their last field.  ``width``
+        defaults to pos0 + n; pass ``out`` (such a dict) to fill columns of
+        existing tensors, e.g. one position per call.  Asynchronous on the
+        current stream."""
         B, n, V = draft.shape
         dsb, dsp = _rows(draft, "draft", None)
         if row_params.dtype != torch.int32 or not row_params.is_contiguous() or row_params.shape != (B, 4):
             raise SpecvError("row_params must be a contiguous int32 [B, 4] device tensor")
         if out is None:
             w = pos0 + n if width is None else int(width)
+            st = torch.full((B, w, 4), float("nan"), dtype=torch.float32, device=draft.device)
+            st.view(torch.int32)[..., 3] = 0
             out = {"tokens": torch.full((B, w), -1, dtype=torch.int32, device=draft.device),
-                   "stats": torch.full((B, w, 2), float("nan"), dtype=torch.float32, device=draft.device),
-                   "flags": torch.zeros(B, w, dtype=torch.int32, device=draft.device)}
-        tok, sts, fl = out["tokens"], out.get("stats"), out.get("flags")
+                   "stats": st, "flags": st.view(torch.int32)[..., 3]}
+        tok, sts = out["tokens"], out.get("stats")
         w = tok.shape[1]
         if tok.dtype != torch.int32 or not tok.is_contiguous() or tok.shape[0] != B:
             raise SpecvError("tokens output must be a contiguous int32 [B, width] tensor")
         if sts is not None and (sts.dtype != torch.float32 or not sts.is_contiguous()
-                                or tuple(sts.shape) != (B, w, 2)):
-            raise SpecvError("stats output must be a contiguous float32 [B, width, 2] tensor")
-        if fl is not None and (fl.dtype != torch.int32 or not fl.is_contiguous() or tuple(fl.shape) != (B, w)):
-            raise SpecvError("flags output must be a contiguous int32 [B, width] tensor")
+                                or tuple(sts.shape) != (B, w, 4)):
+            raise SpecvError("stats output must be a contiguous float32 [B, width, 4] tensor")
         st = load_library().specv_sample_draft(
             self._h, self._stream(), _ptr(draft), dsb, dsp, _dtype_code(draft), B, n, V, int(pos0),
             _ptr(row_params), int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF,
-            _ptr(tok), _ptr(sts), _ptr(fl), w)
+            _ptr(tok), _ptr(sts), w)
         _check(st, "specv_sample_draft")
         return out
 

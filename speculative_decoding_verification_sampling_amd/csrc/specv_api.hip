@@ -29,7 +29,6 @@ struct specv_ctx {
     int prof_calls = 0;
     double ms_kernel = 0.0;
     unsigned epoch = 0;             // call number; the kernel tags published decisions with it
-    unsigned draft_epoch = 0;       // draft sampler call number (its own tagged words)
 };
 
 namespace {
@@ -79,7 +78,6 @@ void free_ws(specv::Workspace& ws) {
     if (ws.cand_meta) (void)hipFree(ws.cand_meta);
     if (ws.trow) (void)hipFree(ws.trow);
     if (ws.kept) (void)hipFree(ws.kept);
-    if (ws.dstats) (void)hipFree(ws.dstats);
     ws = specv::Workspace{};
 }
 
@@ -125,14 +123,6 @@ specv::Args base_args(specv_handle h, int B, int gamma, int V) {
     return a;
 }
 
-size_t draft_stats_words(const specv_ctx* h) {
-    return (size_t)h->cfg.max_batch * std::max(h->cfg.max_gamma, 1) * h->max_chunks * 2;
-}
-
-hipError_t clear_draft_ws(specv_ctx* h, hipStream_t stream) {
-    return hipMemsetAsync(h->ws.dstats, 0, draft_stats_words(h) * sizeof(unsigned long long), stream);
-}
-
 // Zero the epoch-tagged records and the arrival counters (handle creation,
 // and the rare epoch wrap).  Fresh allocations may
 // hold another handle's words with the same epoch numbers, so every tagged
@@ -151,23 +141,33 @@ hipError_t clear_ws(specv_ctx* h, hipStream_t stream) {
     if (e == hipSuccess) e = hipMemsetAsync(ws.ctr, 0, 2 * groups * specv::kSlot * sizeof(unsigned), stream);
     if (e == hipSuccess)
         e = hipMemsetAsync(ws.status, 0, 2 * rows * specv::kSlot * sizeof(unsigned), stream);
-    if (e == hipSuccess) e = clear_draft_ws(h, stream);
     return e;
 }
 
+// The epoch tag of the next call, clearing every tagged record first when
+// the tags would repeat.  Verify calls advance the epoch by 1: a verify call
+// clears the counters and status words of the other parity for the next
+// one, so consecutive verify calls must alternate parity.  Sampler calls
+// touch no counters or status words and advance it by 2, keeping the parity
+// the next verify call expects; they share the tagged chunk statistics with
+// verify calls, so every call's tag is distinct.
+bool next_epoch(specv_handle h, hipStream_t s, unsigned step, unsigned* out) {
+    unsigned next = h->epoch + step;
+    if (next >= 0x7fffffffu) {
+        if (clear_ws(h, s) != hipSuccess) return false;
+        next = step;
+    }
+    *out = next;
+    return true;
+}
+
 // One launch of the verify kernel with the next epoch tag.  The epoch
-// advances only when the launch succeeded: a call clears the counters and
-// status words of the other parity for the next call, so the next call must
-// use the other parity exactly when this one ran.
+// advances only when the launch succeeded.
 specv_status launch(specv_handle h, specv::Args& a, bool bf16, bool vec, void* stream) {
     if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    unsigned next = h->epoch + 1;
-    if (next >= 0x7fffffffu) {
-        // epoch tags would repeat: start again from cleared records
-        if (clear_ws(h, s) != hipSuccess) return SPECV_E_HIP;
-        next = 1;
-    }
+    unsigned next;
+    if (!next_epoch(h, s, 1, &next)) return SPECV_E_HIP;
     a.epoch = next;
     if (specv::launch_verify(a, bf16, vec, s, next_events(h)) != hipSuccess) return SPECV_E_HIP;
     h->epoch = next;
@@ -221,8 +221,7 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
               alloc(&ws.rowrec, (size_t)cfg->max_batch * specv::kRowWords) == hipSuccess &&
               alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks * 2) == hipSuccess &&
               alloc(&ws.ctr, 2 * groups * specv::kSlot) == hipSuccess &&
-              alloc(&ws.status, (size_t)2 * cfg->max_batch * (specv::kSlot / 2)) == hipSuccess &&
-              alloc(&ws.dstats, draft_stats_words(h)) == hipSuccess;
+              alloc(&ws.status, (size_t)2 * cfg->max_batch * (specv::kSlot / 2)) == hipSuccess;
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
@@ -286,7 +285,8 @@ namespace {
 // 2 draft logits plus the drafter's row statistics (specv_verify_sample_qstats).
 specv_status verify_sampling(specv_handle h, void* stream, const void* target_logits,
                              int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
-                             int64_t d_stride_b, int64_t d_stride_pos, const float* draft_stats,
+                             int64_t d_stride_b, int64_t d_stride_pos,
+                             const specv_draft_stats* draft_stats,
                              int64_t s_stride_b, specv_dtype dtype, int B, int gamma, int V,
                              const int32_t* draft_tokens, const specv_row_params* row_params,
                              uint64_t seed, uint32_t step, int32_t eos_id, int32_t* out_num_accepted,
@@ -307,7 +307,7 @@ specv_status verify_sampling(specv_handle h, void* stream, const void* target_lo
     if (prop == 2 && gamma > 0) {
         if (!draft_stats) return SPECV_E_NULL;
         if (s_stride_b < gamma) return SPECV_E_SHAPE;
-        if (!aligned(draft_stats, 8)) return SPECV_E_ALIGN;
+        if (!aligned(draft_stats, 16)) return SPECV_E_ALIGN;
     }
     if (!aligned(row_params, 16)) return SPECV_E_ALIGN;
     if (diag && ((diag->p_at_draft && !aligned(diag->p_at_draft, 4)) ||
@@ -365,7 +365,7 @@ specv_status specv_verify_sample(specv_handle h, void* stream, const void* targe
 specv_status specv_verify_sample_qstats(specv_handle h, void* stream, const void* target_logits,
                                         int64_t t_stride_b, int64_t t_stride_pos,
                                         const void* draft_logits, int64_t d_stride_b,
-                                        int64_t d_stride_pos, const float* draft_stats,
+                                        int64_t d_stride_pos, const specv_draft_stats* draft_stats,
                                         int64_t s_stride_b, specv_dtype dtype, int B, int gamma, int V,
                                         const int32_t* draft_tokens,
                                         const specv_row_params* row_params, uint64_t seed,
@@ -393,8 +393,8 @@ specv_status specv_verify_point_mass(specv_handle h, void* stream, const void* t
 specv_status specv_sample_draft(specv_handle h, void* stream, const void* draft_logits,
                                 int64_t d_stride_b, int64_t d_stride_pos, specv_dtype dtype, int B,
                                 int n_pos, int V, int pos0, const specv_row_params* row_params,
-                                uint64_t seed, uint32_t step, int32_t* out_tokens, float* out_stats,
-                                int32_t* out_flags, int64_t out_stride) {
+                                uint64_t seed, uint32_t step, int32_t* out_tokens,
+                                specv_draft_stats* out_stats, int64_t out_stride) {
     if (!h) return SPECV_E_NULL;
     if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
     if (B < 0 || n_pos < 0 || V < 1 || pos0 < 0 || d_stride_b < 0 || d_stride_pos < 0)
@@ -406,7 +406,7 @@ specv_status specv_sample_draft(specv_handle h, void* stream, const void* draft_
     if (!draft_logits || !row_params || !out_tokens) return SPECV_E_NULL;
     const size_t es = dtype == SPECV_BF16 ? 2 : 4;
     if (!aligned(draft_logits, es) || !aligned(row_params, 16) || !aligned(out_tokens, 4) ||
-        (out_stats && !aligned(out_stats, 8)) || (out_flags && !aligned(out_flags, 4)))
+        (out_stats && !aligned(out_stats, 16)))
         return SPECV_E_ALIGN;
     if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -425,18 +425,17 @@ specv_status specv_sample_draft(specv_handle h, void* stream, const void* draft_
     a.step = step;
     a.out_tok = out_tokens;
     a.out_stats = out_stats;
-    a.out_flags = out_flags;
-    a.stats = h->ws.dstats;
-    unsigned next = h->draft_epoch + 1;
-    if (next >= 0x7fffffffu) {
-        if (clear_draft_ws(h, s) != hipSuccess) return SPECV_E_HIP;
-        next = 1;
-    }
+    a.ws = h->ws;
+    a.cand_cap = h->cand_cap;
+    a.kept_cap = h->kept_cap;
+    a.max_top_k = h->cfg.max_top_k;
+    unsigned next;
+    if (!next_epoch(h, s, 2, &next)) return SPECV_E_HIP;
     a.epoch = next;
     const bool vec = rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es);
     if (specv::launch_sample_draft(a, dtype == SPECV_BF16, vec, s, next_events(h)) != hipSuccess)
         return SPECV_E_HIP;
-    h->draft_epoch = next;
+    h->epoch = next;
     return SPECV_OK;
 }
 

@@ -1,29 +1,35 @@
 // libspecv draft-side sampler for gfx950: d_i ~ q_i in one pass over the
 // draft logits, plus the row statistics the verifier can reuse.
 //
-// q_i is the draft model's distribution after its temperature ("11.1 核心原理"
-// 11.1.2: the proposal is the distribution actually sampled; the tutorial's
-// section 3.3 divides the logits by the temperature).  The draw is the
-// inverse CDF of q_i at a Philox uniform of purpose 0 (DRAFT): tokens in
-// ascending index order, the first whose running mass exceeds u * W.
+// q_i is the draft model's distribution after its temperature, top-k and
+// top-p ("11.1 核心原理" 11.1.2: the proposal is the distribution actually
+// sampled; the tutorial's section 3.3 divides the logits by the
+// temperature).  The draw is the inverse CDF of q_i at a Philox uniform of
+// purpose 0 (DRAFT): tokens in ascending index order, the first whose
+// running mass exceeds u * W.
 //
 // Workgroup (i, b, c), position-major, one per 8192-entry chunk of draft row
 // (b, i):
 //   1. reads its chunk once (16-byte loads) and reduces it to (max, sum of
 //      exp2((z - max) * log2(e) / T)), or (max, lowest argmax) for greedy
-//      rows, published as two epoch-tagged words;
-//   2. wave 0 reads every chunk's words of the row (lane c: chunk c), merges
-//      them into the row's (m, s), and turns them into chunk masses
-//      s_c * exp2((m_c - m) * scale) whose prefix sums locate the chunk
-//      holding u * W; every workgroup of the row computes the same thing;
+//      rows, published as two epoch-tagged words; truncated rows also keep
+//      their top-k candidates (published before the words);
+//   2. untruncated rows: wave 0 reads every chunk's words of the row (lane
+//      c: chunk c), merges them into the row's (m, s), and turns them into
+//      chunk masses s_c * exp2((m_c - m) * scale) whose prefix sums locate
+//      the chunk holding u * W; every workgroup of the row computes the same
+//      thing;
 //   3. the workgroup owning that chunk finds the token in its registers and
-//      writes the token and the row's (m, s).  Its in-chunk running sums (in
-//      the chunk's own exp2 units) are computed by every workgroup while the
-//      statistics are in flight, so that after the hand-off the owner only
-//      compares the target with its groups' ranges.
-// One hand-off per row, and the row is read once.  The chunk statistics and
-// their merge are the verify kernel's, so the (m, s) written here equal the
-// normalisers the verify step computes from the same row.
+//      writes the token and the row's statistics.  Its in-chunk running sums
+//      (in the chunk's own exp2 units) are computed by every workgroup while
+//      the statistics are in flight, so that after the hand-off the owner
+//      only compares the target with its groups' ranges;
+//   2'. truncated rows: chunk 0's workgroup waits for every chunk, merges the
+//      candidates into the row's kept list (the verify kernel's row merge:
+//      top-k threshold, then top-p) and draws from the kept list.
+// One hand-off per row, and the row is read once.  The chunk statistics, the
+// row merge and their order are the verify kernel's, so the statistics
+// written here equal what the verify step computes from the same row.
 //
 // Waits: a row's C workgroups have consecutive IDs and each waits only for
 // its own row.  Workgroups are dispatched in increasing ID order within each
@@ -38,22 +44,95 @@
 
 #include "specv_device.hpp"
 #include "specv_internal.hpp"
+#include "specv_rows.hpp"
 
 namespace specv {
 namespace {
 
 __device__ inline void write_draft(const DraftArgs& a, long long o, int tok, float m, float s,
-                                   unsigned flags) {
+                                   float thr, unsigned flags) {
     a.out_tok[o] = tok;
     if (a.out_stats) {
-        a.out_stats[o * 2] = m;
-        a.out_stats[o * 2 + 1] = s;
+        specv_draft_stats st;
+        st.max = m;
+        st.sum = s;
+        st.threshold = thr;
+        st.flags = (int)flags;
+        a.out_stats[o] = st;
     }
-    if (a.out_flags) a.out_flags[o] = (int)flags;
 }
 
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
+// The verify kernel's argument view of a sampler call, for the shared
+// workspace indexing and truncation steps: draft row (b, i) is side 1 of
+// pair (b, i), with n positions per batch row.
+__device__ inline Args verify_view(const DraftArgs& a) {
+    Args v{};
+    v.drf = a.drf;
+    v.d_sb = a.d_sb;
+    v.d_sp = a.d_sp;
+    v.B = a.B;
+    v.V = a.V;
+    v.C = a.C;
+    v.P = a.n;
+    v.cand_cap = a.cand_cap;
+    v.kept_cap = a.kept_cap;
+    v.max_top_k = a.max_top_k;
+    v.epoch = a.epoch;
+    v.ws = a.ws;
+    return v;
+}
+
+// Truncated draft row (b, i) after every chunk published its candidates and
+// statistics (chunk 0's workgroup, whole workgroup): the kept list by the
+// verify kernel's row merge, then the inverse CDF over the kept tokens in
+// ascending index order.
+template <bool BF16>
+__device__ void draw_truncated(const DraftArgs& a, const Args& va, int b, int i, long long o,
+                               const Plan& pl, float u, TruncScratch& sc) {
+    const int tid = threadIdx.x;
+    const float nan = __builtin_nanf("");
+    const TruncRow tr = row_merge<BF16>(va, b, i, 1, pl, sc);
+    if (tr.bad || (tr.flags & SPECV_FLAG_CAND_OVERFLOW) || tr.n_kept <= 0) {
+        if (tid == 0)
+            write_draft(a, o, -1, nan, nan, nan,
+                        tr.flags | ((tr.bad || (tr.n_kept <= 0 && !(tr.flags & SPECV_FLAG_CAND_OVERFLOW)))
+                                        ? SPECV_FLAG_NONFINITE_ROW : 0u));
+        return;
+    }
+    // row_merge leaves the kept list in sc.v / sc.idx (value descending)
+    __shared__ int sTok, sLast;
+    const int n = tr.n_kept;
+    const int n2 = pow2_at_least(n);
+    for (int j = tid; j < n2; j += kBlock) {
+        sc.w[j] = j < n ? fast_exp2(__fmul_rn(sc.v[j] - tr.zmax, pl.scale)) : 0.f;
+        if (j >= n) sc.idx[j] = 0x7fffffff;
+    }
+    if (tid == 0) {
+        sTok = 0x7fffffff;
+        sLast = -1;
+    }
+    __syncthreads();
+    bitonic_sort(sc.w, sc.idx, n2, by_index);       // weights in token order
+    for (int j = tid; j < n; j += kBlock) sc.v[j] = sc.w[j];
+    __syncthreads();
+    block_inclusive_scan(sc.v, n, sc.red);          // running sums
+    const float target = u * sc.v[n - 1];
+    for (int j = tid; j < n; j += kBlock) {
+        if (sc.w[j] > 0.f) {
+            if (sc.v[j] > target) atomicMin(&sTok, j);
+            atomicMax(&sLast, j);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const int j = sTok != 0x7fffffff ? sTok : sLast;     // rounding: last with weight
+        if (j < 0) write_draft(a, o, -1, nan, nan, nan, tr.flags | SPECV_FLAG_NONFINITE_ROW);
+        else write_draft(a, o, sc.idx[j], tr.zmax, tr.S, tr.tstar, tr.flags);
+    }
+}
+
+template <bool BF16, bool VEC, bool TRUNC>
+__device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int per = a.B * a.C;
     const int i = blockIdx.x / per;
@@ -63,14 +142,17 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
     const float nan = __builtin_nanf("");
     const specv_row_params rp = a.params[b];
     const bool greedy = !(rp.temperature > 0.f);
-    const bool trunc = !greedy && ((rp.top_k > 0 && rp.top_k < a.V) || rp.top_p < 1.f);
+    const bool topk_on = rp.top_k > 0 && rp.top_k < a.V;
+    const bool trunc = !greedy && (topk_on || rp.top_p < 1.f);
     const int pos = a.pos0 + i;
     const long long o = (long long)b * a.out_stride + pos;
-    if (trunc) {
-        if (c == 0 && tid == 0) write_draft(a, o, -1, nan, nan, SPECV_FLAG_UNSUPPORTED);
+    if (trunc && (!TRUNC || a.cand_cap == 0 || (topk_on && rp.top_k > a.max_top_k))) {
+        // the handle reserved no room for these candidates
+        if (c == 0 && tid == 0) write_draft(a, o, -1, nan, nan, nan, SPECV_FLAG_UNSUPPORTED);
         return;
     }
     const float scale = greedy ? 0.f : kLog2e / rp.temperature;
+    const Args va = verify_view(a);
     const void* row = row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i);
     const int v0 = c * kChunk;
     const int len = min(kChunk, a.V - v0);
@@ -79,8 +161,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
     r.finish(row, v0, len);
 
     // 1. chunk statistics, merged across the four waves as the verify's
-    //    streaming units merge them
-    unsigned long long* words = a.stats + ((long long)i * a.B + b) * a.C * 2;
+    //    streaming units merge them (side 1 of pair (b, i) of the workspace)
     __shared__ float sm[kWaves], ss[kWaves];
     __shared__ int si[kWaves];
     __shared__ unsigned sb[kWaves];
@@ -100,7 +181,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
                 merge_arg(best, bi, sm[w], si[w]);
                 bad |= sb[w];
             }
-            publish_stats(words + c * 2, bad ? nan : best, (unsigned)bi, a.epoch);
+            publish_stats(stats_words(va, b, i, 1, c), bad ? nan : best, (unsigned)bi, a.epoch);
         }
     } else {
         float m, s;
@@ -109,12 +190,54 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
             sm[wave] = m;
             ss[wave] = s;
         }
+        if constexpr (TRUNC) {
+            if (trunc) {
+                // the chunk's top-k candidates, complete before its statistics
+                // are published (the statistics words tell the merge they are in)
+                Plan pl{};
+                pl.keff = topk_on ? rp.top_k : a.max_top_k;
+                float x[kPerThread];
+                r.get(x);
+                chunk_candidates<BF16>(va, side_row(va, b, i, 1), c, pl.keff, x, *sc);
+                wait_stores();
+            }
+        }
         __syncthreads();
         if (tid == 0) {
             m = sm[0];
             s = ss[0];
             for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[w], ss[w], scale);
-            publish_stats(words + c * 2, m, __float_as_uint(s), a.epoch);
+            publish_stats(stats_words(va, b, i, 1, c), m, __float_as_uint(s), a.epoch);
+        }
+    }
+    if constexpr (TRUNC) {
+        if (trunc) {
+            // 2'. chunk 0's workgroup merges the row and draws
+            if (c != 0) return;
+            __shared__ int sLate;
+            if (wave == 0) {
+                float m = -kInf;
+                unsigned second = 0;
+                bool ok = true;
+                if (lane < a.C) ok = published_stats(stats_words(va, b, i, 1, lane), a.epoch, m, second);
+                const bool late = __ballot(!ok) != 0;
+                if (lane == 0) sLate = late;
+            }
+            __syncthreads();
+            if (sLate) {
+                if (tid == 0) write_draft(a, o, -1, nan, nan, nan, SPECV_FLAG_INTERNAL);
+                return;
+            }
+            Plan pl{};
+            pl.mode = MODE_TRUNC;
+            pl.scale = scale;
+            pl.top_k = rp.top_k;
+            pl.top_p = rp.top_p;
+            pl.kmode = topk_on ? 1 : 0;
+            pl.keff = topk_on ? rp.top_k : a.max_top_k;
+            const float u = uniform24(a.seed, b, pos, PURPOSE_DRAFT, a.step);
+            draw_truncated<BF16>(a, va, b, i, o, pl, u, *sc);
+            return;
         }
     }
 
@@ -180,7 +303,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
         float m = -kInf;
         unsigned second = 0;
         bool ok = true;
-        if (lane < a.C) ok = published_stats(words + lane * 2, a.epoch, m, second);
+        if (lane < a.C) ok = published_stats(stats_words(va, b, i, 1, lane), a.epoch, m, second);
         const bool late = __ballot(!ok) != 0;
         int chosen = -1, tok = -1;
         unsigned flags = 0;
@@ -232,7 +355,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
             sS = S;
             // rows with nothing left to draw (greedy, bad, late) are written by
             // chunk 0's workgroup
-            if (chosen < 0 && c == 0) write_draft(a, o, tok, nan, nan, flags);
+            if (chosen < 0 && c == 0) write_draft(a, o, tok, nan, nan, nan, flags);
         }
     }
     __syncthreads();
@@ -267,9 +390,21 @@ __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
     if (tid == 0) {
         int t = sTok;
         if (t == 0x7fffffff) t = max(max(lastW[0], lastW[1]), max(lastW[2], lastW[3]));
-        if (t < 0) write_draft(a, o, -1, nan, nan, SPECV_FLAG_NONFINITE_ROW);
-        else write_draft(a, o, c * kChunk + t, sM, sS, 0u);
+        if (t < 0) write_draft(a, o, -1, nan, nan, nan, SPECV_FLAG_NONFINITE_ROW);
+        else write_draft(a, o, c * kChunk + t, sM, sS, -kInf, 0u);
     }
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
+    sample_draft_block<BF16, VEC, false>(a, nullptr);
+}
+
+// With the truncation path (handles created with max_top_k > 0) and its LDS.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_sample_draft_trunc(DraftArgs a) {
+    __shared__ TruncScratch sc;
+    sample_draft_block<BF16, VEC, true>(a, &sc);
 }
 
 }  // namespace
@@ -278,8 +413,13 @@ hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStrea
                                hipEvent_t* ev) {
     const long long blocks = (long long)a.n * a.B * a.C;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    void (*fn)(DraftArgs) = bf16 ? (vec ? k_sample_draft<true, true> : k_sample_draft<true, false>)
-                                 : (vec ? k_sample_draft<false, true> : k_sample_draft<false, false>);
+    void (*fn)(DraftArgs);
+    if (a.cand_cap > 0)
+        fn = bf16 ? (vec ? k_sample_draft_trunc<true, true> : k_sample_draft_trunc<true, false>)
+                  : (vec ? k_sample_draft_trunc<false, true> : k_sample_draft_trunc<false, false>);
+    else
+        fn = bf16 ? (vec ? k_sample_draft<true, true> : k_sample_draft<true, false>)
+                  : (vec ? k_sample_draft<false, true> : k_sample_draft<false, false>);
     hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev ? ev[0] : nullptr,
                           ev ? ev[1] : nullptr, 0, a);
     return hipGetLastError();

@@ -91,8 +91,6 @@ struct Workspace {
                                 // count -1 when the chunk's candidates overflowed
     TruncRow* trow;             // [max_batch * max_pos * 2]
     Cand* kept;                 // [max_batch * max_pos * 2 * kept_cap]
-    unsigned long long* dstats; // [max_batch * max(max_gamma, 1) * max_chunks][2]: the draft
-                                // sampler's chunk statistics (its own epochs)
 };
 
 struct Args {
@@ -108,7 +106,7 @@ struct Args {
                                   // q_i is the point mass on d_i and no draft logits are read;
                                   // 2 (specv_verify_sample_qstats) draft logits plus the
                                   // drafter's row statistics
-    const float* qstats;          // prop 2: [B][qs_sb][2] (max, sum) of draft row (b, i)
+    const specv_draft_stats* qstats;  // prop 2: [B][qs_sb] statistics of draft row (b, i)
     long long qs_sb;
     int cand_cap;                 // candidates per (row, chunk); 0: no truncation
     int kept_cap;                 // kept-set entries per row: min(kKeptCap, max_vocab)
@@ -142,11 +140,13 @@ struct DraftArgs {
     const specv_row_params* params;
     unsigned long long seed;
     unsigned step;
-    unsigned epoch;               // per-handle sampler call number (never 0)
+    unsigned epoch;               // the handle's call number (shared with verify calls)
     int* out_tok;                 // [B][out_stride]
-    float* out_stats;             // [B][out_stride][2] or nullptr
-    int* out_flags;               // [B][out_stride] or nullptr
-    unsigned long long* stats;    // [n * B][C][2] epoch-tagged chunk statistics
+    specv_draft_stats* out_stats; // [B][out_stride] or nullptr
+    Workspace ws;                 // the handle's: chunk statistics and, for truncated rows,
+                                  // candidates and kept lists of draft row (b, i) = side 1 of
+                                  // pair (b, i) with n positions per batch row
+    int cand_cap, kept_cap, max_top_k;
 };
 
 hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStream_t stream,

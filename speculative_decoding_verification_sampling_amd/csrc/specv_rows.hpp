@@ -1,0 +1,759 @@
+// Row-level device code shared by the verify and draft-sampler kernels:
+// per-row plans (mode, caps, temperature scale), workspace indexing, output
+// helpers, and the truncation steps (top-k candidates per chunk, the
+// row-level top-k / top-p merge into a kept list, draws from a kept list).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "specv_device.hpp"
+#include "specv_internal.hpp"
+
+namespace specv {
+namespace {
+
+enum Mode { MODE_SAMPLE = 0, MODE_GREEDY = 1, MODE_TRUNC = 2, MODE_SKIP = 3 };
+// What stands for the proposal q (a template parameter, so that each kind
+// is a kernel of its own):
+//   kPropLogits: draft logits rows, reduced by the stream like the target's;
+//   kPropPoint:  q_i is the point mass on d_i, no draft rows exist;
+//   kPropStats:  draft logits rows plus the drafter's row statistics (max,
+//                sum, kept-set threshold: specv_draft_stats), so the stream
+//                reads no draft row: the accept test loads q's entry at d_i,
+//                and only the row where the round stops is read, for the
+//                correction draw (its kept-list entries, for truncated rows).
+constexpr int kPropLogits = 0, kPropPoint = 1, kPropStats = 2;
+enum Kind { KIND_NONE = 0, KIND_RESIDUAL = 1, KIND_BONUS = 2 };
+// outcome of one pair (low byte of PW_STATE)
+enum Outcome { OUT_ACC = 1, OUT_REJ = 2, OUT_BAD = 3, OUT_BONUS = 4 };
+
+// ---------------------------------------------------------------- row plan
+// What one batch row needs, from its parameters and draft tokens alone.
+struct Plan {
+    int mode;
+    int cap;        // tokens the round may emit: max_new_tokens and the first EOS
+    int nt;         // positions whose target row the round may consult: min(cap, gamma + 1)
+    int ntest;      // accept tests the round may run: min(cap, gamma)
+    float scale;    // log2(e) / T
+    int top_k;
+    float top_p;
+    int keff;       // truncated rows: candidates wanted per chunk (top_k, or the handle's
+                    // max_top_k for top-p alone)
+    int kmode;      // truncated rows: 1 when top-k is on (normaliser over the top-k set)
+    unsigned flags;
+    int tok;        // lane i < gamma: draft token d_i
+};
+
+// Computed by every wave on its own: lane i loads d_i, so the parameters and
+// all the tokens arrive in one memory round trip.
+__device__ inline Plan make_plan(const Args& a, int b) {
+    const int lane = threadIdx.x % kWave;
+    Plan p;
+    float T = 0.f;
+    int k = 0;
+    float tp = 1.f;
+    int cap = 0;
+    if (a.params) {
+        const specv_row_params rp = a.params[b];
+        T = rp.temperature;
+        k = rp.top_k;
+        tp = rp.top_p;
+        cap = rp.max_new_tokens;
+    } else if (a.caps) {
+        cap = a.caps[b];
+    }
+    const int d = lane < a.gamma ? a.tokens[(long long)b * a.gamma + lane] : 0;
+    p.tok = d;
+    // emission ends after max_new_tokens tokens and after an emitted EOS; an
+    // EOS among the drafts therefore caps the round at its position + 1
+    int ce = cap >= 1 ? cap : 0x7fffffff;
+    const unsigned long long oor = __ballot(lane < a.gamma && (d < 0 || d >= a.V));
+    const unsigned long long eos = __ballot(lane < a.gamma && d == a.eos);
+    p.flags = oor ? SPECV_FLAG_TOKEN_OOR : 0u;
+    if (eos) ce = min(ce, __builtin_ctzll(eos) + 1);
+    p.cap = ce;
+    p.top_k = k;
+    p.top_p = tp;
+    const bool greedy = a.greedy_all || !(T > 0.f);
+    const bool topk_on = k > 0 && k < a.V;
+    const bool topp_on = tp < 1.f;
+    if (p.flags & SPECV_FLAG_TOKEN_OOR) {
+        p.mode = MODE_SKIP;
+    } else if (greedy) {
+        p.mode = MODE_GREEDY;
+    } else if (topk_on || topp_on) {
+        if (a.cand_cap == 0 || (topk_on && k > a.max_top_k)) {
+            p.mode = MODE_SKIP;               // the handle reserved no room for these candidates
+            p.flags |= SPECV_FLAG_UNSUPPORTED;
+        } else {
+            p.mode = MODE_TRUNC;
+        }
+    } else {
+        p.mode = MODE_SAMPLE;
+    }
+    p.scale = greedy ? 0.f : kLog2e / T;
+    p.kmode = topk_on ? 1 : 0;
+    p.keff = topk_on ? k : a.max_top_k;
+    p.nt = min(ce, a.gamma + 1);
+    p.ntest = min(ce, a.gamma);
+    return p;
+}
+
+
+// ---------------------------------------------------------------- workspace
+__device__ inline long long pair_id(const Args& a, int b, int k) { return (long long)b * a.P + k; }
+
+// Draft token d_k of row b, by a load from the same (uniform) address in
+// every lane.  Never a cross-lane read of the plan's lane-distributed
+// tokens: in code that only some lanes execute, the compiler may reload a
+// spilled register for the active lanes alone, and a read of another lane
+// then returns garbage.
+__device__ inline int draft_token(const Args& a, int b, int k) {
+    return a.tokens[(long long)b * a.gamma + k];
+}
+__device__ inline long long side_row(const Args& a, int b, int k, int side) {
+    return pair_id(a, b, k) * 2 + side;
+}
+__device__ inline long long part_index(const Args& a, int b, int k, int side, int c) {
+    return side_row(a, b, k, side) * a.C + c;
+}
+
+// A chunk's statistics move as two epoch-tagged words: (max, sum) for
+// sampling and truncated rows, the sum NaN when the chunk held NaN / +inf;
+// (max, argmax) for greedy rows, the max NaN when the chunk held NaN / +inf.
+// Readers poll until both tags are this call's, so the writer never waits
+// for its stores to complete.
+__device__ inline unsigned long long* stats_words(const Args& a, int b, int k, int side, int c) {
+    return a.ws.stats + part_index(a, b, k, side, c) * 2;
+}
+
+// Diagnostics of one row by one wave: lane i holds p_i(d_i), q_i(d_i).
+__device__ inline void write_diag_wave(const Args& a, int b, int tested, float p, float q) {
+    const int i = threadIdx.x % kWave;
+    if (i < a.gamma) {
+        const bool t = i < tested;
+        if (a.p_at) a.p_at[(long long)b * a.gamma + i] = t ? p : __builtin_nanf("");
+        if (a.q_at) a.q_at[(long long)b * a.gamma + i] = t ? q : __builtin_nanf("");
+    }
+}
+
+// Final outputs of one row by one wave (lane i holds d_i in ``tok``): the
+// first nemit drafts, then ``sampled`` (if >= 0), -1 padding.
+__device__ inline void write_outputs_wave(const Args& a, int b, int nemit, int nacc, unsigned flags,
+                                          bool dead, int sampled, float wres, int tok) {
+    const int lane = threadIdx.x % kWave;
+    const int g1 = a.gamma + 1;
+    if (dead) {
+        nemit = 0;
+        nacc = 0;
+        sampled = -1;
+    }
+    if (lane < g1) {
+        int t = -1;
+        if (lane < nemit) t = tok;
+        else if (lane == nemit && sampled >= 0) t = sampled;
+        a.out_tok[(long long)b * g1 + lane] = t;
+    }
+    if (lane == 0) {
+        a.out_emit[b] = nemit + (sampled >= 0 ? 1 : 0);
+        a.out_acc[b] = nacc;
+        if (a.out_flags) a.out_flags[b] = (int)flags;
+        if (a.wres) a.wres[b] = wres;
+    }
+}
+
+// ---------------------------------------------------------------- truncation
+// Top-k / top-p rows ("11.1 核心原理" 11.1.2: p and q are the distributions
+// after truncation; q is the truncated proposal actually sampled).
+//   per chunk:   each thread keeps its top-j finite values (j = ceil(2k / 256)
+//                <= 8); the k-th largest of those 256 j values, L, has at
+//                least k chunk entries >= L, so every finite entry >= L is a
+//                superset of the chunk's top k (typically ~k entries);
+//   per row:     (the workgroup deciding the position) the row's top-k
+//                threshold is >= every chunk's L, so only candidates >= max L
+//                are gathered (at most 2048); they are sorted (value desc,
+//                index asc), the k-th entry is the top-k threshold (ties
+//                kept), and the prefix is scanned for top-p: the first level
+//                whose cumulative mass reaches top_p ends the kept set (ties
+//                at a level all kept);
+//   per batch row: the accept tests use the kept sets, and the correction /
+//                bonus sample is drawn from the (short) kept list of the
+//                sampled row, tokens in ascending index order.
+
+__device__ inline bool finite_logit(float x) { return x > -kInf && x <= 3.402823466e38f; }
+
+__device__ inline void publish_cand(Cand* p, float v, int idx) {
+    const unsigned long long w =
+        (unsigned long long)__float_as_uint(v) | ((unsigned long long)(unsigned)idx << 32);
+    publish(reinterpret_cast<unsigned long long*>(p), w);
+}
+
+__device__ inline Cand published_cand(const Cand* p) {
+    const unsigned long long w = published(reinterpret_cast<const unsigned long long*>(p));
+    Cand c;
+    c.v = __uint_as_float((unsigned)w);
+    c.idx = (int)(unsigned)(w >> 32);
+    return c;
+}
+
+__device__ inline int pow2_at_least(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+// (value desc, index asc)
+__device__ inline bool by_value(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+// index asc
+__device__ inline bool by_index(float, int ia, float, int ib) { return ia < ib; }
+
+// Block-wide bitonic sort of v / idx [0, n), n a power of two <= kKeptCap,
+// so that entry x comes before entry y when prec(x, y).  Entries must be
+// visible to the block (caller synchronised); result visible on return.
+template <typename Prec>
+__device__ void bitonic_sort(float* v, int* idx, int n, Prec prec) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += kBlock) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const float va = v[i], vb = v[ixj];
+                    const int ia = idx[i], ib = idx[ixj];
+                    const bool sw = (i & k) == 0 ? prec(vb, ib, va, ia) : prec(va, ia, vb, ib);
+                    if (sw) {
+                        v[i] = vb;
+                        v[ixj] = va;
+                        idx[i] = ib;
+                        idx[ixj] = ia;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Block-wide exclusive scan of one int per thread; returns this thread's
+// offset and writes the total to *total (both visible to all threads).
+__device__ inline int block_excl_scan(int x, int* scratch /* kWaves + 1 */, int* total) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int incl = wave_scan_incl(x);
+    if (lane == kWave - 1) scratch[wave] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) base += scratch[w];
+        tot += scratch[w];
+    }
+    *total = tot;
+    __syncthreads();
+    return base + incl - x;
+}
+
+// In-place inclusive prefix sum of w[0, n), n <= kKeptCap: eight consecutive
+// entries per thread in order, then across threads.
+__device__ void block_inclusive_scan(float* w, int n, float* red) {
+    constexpr int per = kKeptCap / kBlock;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int base = threadIdx.x * per;
+    float loc[per];
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+        run += base + j < n ? w[base + j] : 0.f;
+        loc[j] = run;
+    }
+    const float incl = wave_scan_incl(run);
+    if (lane == kWave - 1) red[wave] = incl;
+    __syncthreads();
+    float wbase = 0.f;
+    for (int w2 = 0; w2 < wave; ++w2) wbase += red[w2];
+    const float excl = wbase + incl - run;
+#pragma unroll
+    for (int j = 0; j < per; ++j)
+        if (base + j < n) w[base + j] = excl + loc[j];
+    __syncthreads();
+}
+
+__device__ inline long long cand_base(const Args& a, long long rowid, int c) {
+    return (rowid * a.C + c) * a.cand_cap;
+}
+
+// Order-preserving key of a raw logit (larger value -> larger key).  bf16
+// values are fp32 patterns with zero low halves, so their keys fit 16 bits.
+template <bool BF16>
+__device__ inline unsigned order_key(float x) {
+    unsigned u = __float_as_uint(x);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return BF16 ? (u >> 16) : u;
+}
+
+// Candidate f of a row (flat index over its chunks, offsets in sc.off).
+__device__ inline Cand row_candidate(const Args& a, long long rowid, const unsigned* off, int f) {
+    int lo = 0, hi = a.C - 1;                  // chunk c with off[c] <= f < off[c + 1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int)off[mid] <= f) lo = mid;
+        else hi = mid - 1;
+    }
+    return published_cand(a.ws.cand + cand_base(a, rowid, lo) + (f - (int)off[lo]));
+}
+
+// Radix select (8-bit digits from the top) of the K-th largest order key
+// among the row's candidates with value >= L, read from global memory.
+template <bool BF16>
+__device__ unsigned select_kth_key(const Args& a, long long rowid, int total, float L, int K,
+                                   TruncScratch& sc) {
+    constexpr int KB = BF16 ? 16 : 32;
+    const int tid = threadIdx.x;
+    __shared__ unsigned sPrefix, sDigit;
+    __shared__ int sRemaining, sAbove;
+    if (tid == 0) {
+        sPrefix = 0;
+        sRemaining = K;
+    }
+    for (int pass = 0; pass < KB / 8; ++pass) {
+        const int shift = KB - 8 * (pass + 1);
+        sc.hist[tid] = 0;                      // kBlock == 256 bins
+        __syncthreads();
+        const unsigned prefix = sPrefix;
+        const unsigned hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8)) & (BF16 ? 0xFFFFu : 0xFFFFFFFFu);
+        for (int f0 = 0; f0 < total; f0 += 4 * kBlock) {
+            Cand cv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = f0 + q * kBlock + tid;
+                cv[q] = f < total ? row_candidate(a, rowid, sc.off, f) : Cand{-kInf, 0};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (cv[q].v >= L && finite_logit(cv[q].v)) {
+                    const unsigned key = order_key<BF16>(cv[q].v);
+                    if ((key & hi_mask) == prefix) atomicAdd(&sc.hist[(key >> shift) & 255u], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        // bin t holds hist[t]; entries in bins >= t: total - (entries in bins < t)
+        const int h = (int)sc.hist[tid];
+        int binned;
+        const int below = block_excl_scan(h, sc.misc, &binned);
+        const int ge = binned - below;
+        const int need = sRemaining;
+        if (ge >= need && ge - h < need) {
+            sDigit = (unsigned)tid;
+            sAbove = ge - h;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            sPrefix |= sDigit << shift;
+            sRemaining -= sAbove;
+        }
+        __syncthreads();
+    }
+    return sPrefix;
+}
+
+// Candidates of one chunk (whole workgroup): every finite entry >= L.
+template <bool BF16>
+__device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff,
+                                 const float (&x)[kPerThread], TruncScratch& sc) {
+    const int tid = threadIdx.x;
+    // twice as many per-thread tops as needed keeps L close to the k-th value
+    const int jj = min(8, (2 * keff + kBlock - 1) / kBlock);
+    float tp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tp[j] = -kInf;                // this thread's top 8, desc
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        float v = x[k];
+        if (!(finite_logit(v) && v > tp[7])) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {                       // insertion, larger values first
+            if (v > tp[j]) {
+                const float s = tp[j];
+                tp[j] = v;
+                v = s;
+            }
+        }
+    }
+    const int n = kBlock * jj;
+    const int n2 = pow2_at_least(n);
+    __syncthreads();                                        // sc may still be read
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < jj) {
+            sc.v[tid * jj + j] = tp[j];
+            sc.idx[tid * jj + j] = 0;
+        }
+    for (int i = n + tid; i < n2; i += kBlock) {
+        sc.v[i] = -kInf;
+        sc.idx[i] = 0;
+    }
+    __syncthreads();
+    bitonic_sort(sc.v, sc.idx, n2, by_value);
+    const float L = sc.v[keff - 1];        // keff <= 256 * jj / 2 <= n2
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) cnt += finite_logit(x[k]) && x[k] >= L;
+    int total;
+    const int off = block_excl_scan(cnt, sc.misc, &total);
+    if (total <= a.cand_cap) {
+        Cand* dst = a.ws.cand + cand_base(a, rowid, c);
+        int o = off;
+        const int v0 = c * kChunk;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k)
+            if (finite_logit(x[k]) && x[k] >= L) publish_cand(dst + o++, x[k], v0 + chunk_index<BF16>(k));
+    }
+    if (tid == 0)
+        publish_cand(a.ws.cand_meta + rowid * a.C + c, L, total <= a.cand_cap ? total : -1);
+}
+
+// Row-level truncation (whole workgroup) of logits row (b, k, side), once
+// every chunk's candidates are published.  Publishes the kept list and the
+// row's TruncRow, and returns the TruncRow to every thread; when the row
+// keeps n_kept > 0 entries, sc.v / sc.idx [0, n_kept) also hold the kept
+// list (value descending, index ascending) on return.
+template <bool BF16>
+__device__ TruncRow row_merge(const Args& a, int b, int k, int side, const Plan& pl,
+                              TruncScratch& sc) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const long long rowid = side_row(a, b, k, side);
+    __shared__ float sL, sM, sS, sZ1;
+    __shared__ unsigned sBad, sFlags;
+    __shared__ int sTotal, sN, sJ, sLevelStart;
+    __shared__ TruncRow sOut;
+    unsigned* off = sc.off;                // chunk offsets [0, C]
+    __syncthreads();                       // shared state may still be read
+    if (tid == 0) {
+        sBad = 0;
+        sFlags = 0;
+        sN = 0;
+        sJ = 0x7fffffff;
+        sLevelStart = 0x7fffffff;
+        sOut.zmax = -kInf;
+        sOut.tstar = kInf;
+        sOut.S = 0.f;
+        sOut.n_kept = 0;
+        sOut.flags = 0;
+        sOut.bad = 0;
+    }
+    // chunk bounds and counts (lane c holds chunk c; C <= 64), and the row
+    // statistics (for top-p alone)
+    if (wave == 0) {
+        float L = -kInf;
+        int cnt = 0;
+        bool ovf = false;
+        if (lane < a.C) {
+            const Cand m = published_cand(a.ws.cand_meta + rowid * a.C + lane);
+            L = m.v;
+            ovf = m.idx < 0;
+            cnt = ovf ? 0 : m.idx;
+        }
+        L = wave_max(L);
+        const int incl = wave_scan_incl(cnt);
+        if (lane < a.C) off[lane] = (unsigned)(incl - cnt);
+        if (lane == a.C - 1) {
+            off[a.C] = (unsigned)incl;
+            sTotal = incl;
+        }
+        const unsigned long long any_ovf = __ballot(ovf);
+        if (lane == 0) {
+            sL = L;
+            if (any_ovf) sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+        }
+    } else if (wave == 1) {
+        float m = -kInf, s = 0.f;
+        if (lane < a.C) {
+            unsigned sw = 0;
+            (void)published_stats(stats_words(a, b, k, side, lane), a.epoch, m, sw);
+            s = __uint_as_float(sw);
+        }
+        wave_merge_ms(m, s, pl.scale);
+        if (lane == 0) {
+            sM = m;
+            sS = s;
+            if (__builtin_isnan(s) || m == -kInf) sBad = 1;
+        }
+    }
+    __syncthreads();
+    // gather the candidates >= max L into LDS
+    const float L = sL;
+    const int total = sTotal;
+    auto gather = [&](unsigned min_key) {
+        for (int f0 = 0; f0 < total; f0 += 4 * kBlock) {
+            Cand cv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = f0 + q * kBlock + tid;
+                cv[q] = f < total ? row_candidate(a, rowid, off, f) : Cand{-kInf, 0};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (cv[q].v >= L && finite_logit(cv[q].v) && order_key<BF16>(cv[q].v) >= min_key) {
+                    const int pos = atomicAdd(&sN, 1);
+                    if (pos < kKeptCap) {
+                        sc.v[pos] = cv[q].v;
+                        sc.idx[pos] = cv[q].idx;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    };
+    gather(0u);
+    if (sN > kKeptCap) {
+        // too many candidates above the chunk bounds: select the exact top-k
+        // key over them in global memory, then keep only entries >= it
+        const int K = min(pl.keff, sN);
+        const unsigned kkey = select_kth_key<BF16>(a, rowid, total, L, K, sc);
+        if (tid == 0) sN = 0;
+        __syncthreads();
+        gather(kkey);
+    }
+    const int n1 = sN;
+    if (n1 > kKeptCap && tid == 0) sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+    __syncthreads();
+    TruncRow* tr = &a.ws.trow[rowid];
+    if ((sFlags & SPECV_FLAG_CAND_OVERFLOW) || sBad || n1 == 0) {
+        if (tid == 0) {
+            sOut.bad = (sBad || n1 == 0) ? 1u : 0u;
+            sOut.flags = sFlags;
+            sOut.n_kept = 0;
+            publish(&tr->bad, sOut.bad);
+            publish(&tr->flags, sFlags);
+            publish(&tr->n_kept, 0);
+        }
+        __syncthreads();
+        return sOut;
+    }
+    // sort the gathered entries: value desc, index asc
+    const int n2 = pow2_at_least(n1);
+    for (int i = n1 + tid; i < n2; i += kBlock) {
+        sc.v[i] = -kInf;
+        sc.idx[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    bitonic_sort(sc.v, sc.idx, n2, by_value);
+    // top-k: the K-th largest (with multiplicity) ends the kept prefix; all
+    // entries equal to it are kept
+    const int K = min(pl.keff, n1);
+    const float tk = sc.v[K - 1];
+    // count of entries >= tk (a prefix of the sorted list)
+    int cnt = 0;
+    for (int i = tid; i < n1; i += kBlock) cnt += sc.v[i] >= tk;
+    int nk1;
+    (void)block_excl_scan(cnt, sc.misc, &nk1);
+    const float zmax = sc.v[0];
+    const float scale = pl.scale;
+    for (int i = tid; i < nk1; i += kBlock) sc.w[i] = fast_exp2(__fmul_rn(sc.v[i] - zmax, scale));
+    __syncthreads();
+    block_inclusive_scan(sc.w, nk1, sc.red);
+    if (tid == 0) {
+        // normaliser of the top-k-renormalised softmax: the kept top-k set, or
+        // the whole row when top-k is off
+        sZ1 = pl.kmode ? sc.w[nk1 - 1] : sS * fast_exp2(__fmul_rn(sM - zmax, scale));
+    }
+    __syncthreads();
+    const float Z1 = sZ1;
+    int jstar = nk1 - 1;
+    if (pl.top_p < 1.f) {
+        // first level end whose cumulative mass reaches top_p
+        for (int i = tid; i < nk1; i += kBlock) {
+            const bool level_end = i == nk1 - 1 || sc.v[i + 1] != sc.v[i];
+            if (level_end && sc.w[i] / Z1 >= pl.top_p) atomicMin(&sJ, i);
+        }
+        __syncthreads();
+        if (sJ == 0x7fffffff) {
+            if (!pl.kmode) {
+                // top-p alone: the candidates hold less than top_p of the mass
+                if (tid == 0) {
+                    sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+                    sOut.bad = 0;
+                    sOut.flags = sFlags;
+                    sOut.n_kept = 0;
+                    publish(&tr->bad, 0u);
+                    publish(&tr->flags, sFlags);
+                    publish(&tr->n_kept, 0);
+                }
+                __syncthreads();
+                return sOut;
+            }
+            jstar = nk1 - 1;                // rounding: keep the whole top-k set
+        } else {
+            jstar = sJ;
+        }
+        const float tv = sc.v[jstar];
+        for (int i = tid; i <= jstar; i += kBlock)
+            if (sc.v[i] == tv) atomicMin(&sLevelStart, i);
+        __syncthreads();
+        if (tid == 0) {
+            const float cum = sc.w[jstar] / Z1;
+            const int ls = sLevelStart;
+            const float prev = ls > 0 ? sc.w[ls - 1] / Z1 : 0.f;
+            if (fabsf(cum - pl.top_p) < 1e-5f || (ls > 0 && fabsf(prev - pl.top_p) < 1e-5f))
+                sFlags |= SPECV_FLAG_TOPP_NEAR;
+        }
+    }
+    const int nkept = jstar + 1;
+    Cand* kept = a.ws.kept + rowid * a.kept_cap;
+    for (int i = tid; i < nkept; i += kBlock) publish_cand(kept + i, sc.v[i], sc.idx[i]);
+    __syncthreads();
+    if (tid == 0) {
+        sOut.zmax = zmax;
+        sOut.tstar = sc.v[jstar];
+        sOut.S = sc.w[jstar];
+        sOut.n_kept = nkept;
+        sOut.flags = sFlags;
+        sOut.bad = 0;
+        publish(&tr->zmax, zmax);
+        publish(&tr->tstar, sc.v[jstar]);
+        publish(&tr->S, sc.w[jstar]);
+        publish(&tr->n_kept, nkept);
+        publish(&tr->flags, sFlags);
+        publish(&tr->bad, 0u);
+    }
+    __syncthreads();
+    return sOut;
+}
+
+__device__ inline bool trow_dead(const TruncRow& t) {
+    return t.bad != 0 || (t.flags & SPECV_FLAG_CAND_OVERFLOW) || t.n_kept == 0;
+}
+
+// Probability of raw logit z under a truncated row: membership in the kept
+// set is decided on the raw value (z >= tstar).
+__device__ inline float trunc_prob(const TruncRow& t, float z, float scale) {
+    if (!(finite_logit(z) && z >= t.tstar)) return 0.f;
+    return fast_exp2(__fmul_rn(z - t.zmax, scale)) / t.S;
+}
+
+// A draft row's truncation from the drafter's statistics (specv_draft_stats):
+// kept set {z >= threshold}, max, and the kept set's sum; flags as the
+// drafter found them.  A row the drafter marked non-finite is bad; one with
+// candidates that overflowed keeps nothing.
+__device__ inline TruncRow stats_trow(const specv_draft_stats& st) {
+    TruncRow t{};
+    const unsigned fl = (unsigned)st.flags;
+    t.zmax = st.max;
+    t.tstar = st.threshold;
+    t.S = st.sum;
+    t.flags = fl & (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
+    const bool valid = st.sum > 0.f && finite_logit(st.max) && !__builtin_isnan(st.threshold);
+    t.bad = (fl & SPECV_FLAG_NONFINITE_ROW) || (!valid && !(fl & SPECV_FLAG_CAND_OVERFLOW)) ? 1u : 0u;
+    t.n_kept = valid && !t.bad && !(fl & SPECV_FLAG_CAND_OVERFLOW) ? 1 : 0;
+    return t;
+}
+
+__device__ inline TruncRow published_trow(const TruncRow* p) {
+    TruncRow t;
+    t.zmax = published(&p->zmax);
+    t.tstar = published(&p->tstar);
+    t.S = published(&p->S);
+    t.n_kept = published(&p->n_kept);
+    t.flags = published(&p->flags);
+    t.bad = published(&p->bad);
+    return t;
+}
+
+// Correction / bonus sample of a truncated row (whole workgroup) at position
+// pos: weights over the kept set of p_pos (zero weight elsewhere), tokens in
+// ascending index order, first running sum > u * W.  Returns the token (-1 if
+// no weight anywhere) to every thread; *wres gets W of a correction, and
+// *fallback is set when the correction mass vanished and p was used.
+template <bool BF16, int PROP>
+__device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, const Plan& pl,
+                            TruncScratch& sc, float* wres, bool* fallback) {
+    const int tid = threadIdx.x;
+    __shared__ TruncRow tT, tQ;
+    __shared__ float sWsum;
+    __shared__ int sTok, sLastPos, sFb;
+    const float scale = pl.scale;
+    constexpr bool pm = PROP == kPropPoint;  // q = the point mass on d_pos
+    __syncthreads();
+    if (tid == 0) {
+        tT = published_trow(&a.ws.trow[side_row(a, b, pos, 0)]);
+        if (res && !pm)
+            tQ = PROP == kPropStats ? stats_trow(a.qstats[(long long)b * a.qs_sb + pos])
+                                    : published_trow(&a.ws.trow[side_row(a, b, pos, 1)]);
+        sTok = 0x7fffffff;
+        sLastPos = -1;
+        sFb = 0;
+    }
+    __syncthreads();
+    const int n = tT.n_kept;
+    if (n <= 0) return -1;                  // (a dead row is never sampled)
+    const Cand* kept = a.ws.kept + side_row(a, b, pos, 0) * a.kept_cap;
+    const int dpm = res && pm ? draft_token(a, b, pos) : -1;
+    const void* qrow = res && !pm ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+    // sc.v = weight, sc.idx = token, sc.w = p (fallback weight)
+    float part = 0.f;
+    for (int i = tid; i < n; i += kBlock) {
+        const Cand cv = published_cand(kept + i);
+        const float p = __fmul_rn(fast_exp2(__fmul_rn(cv.v - tT.zmax, scale)), 1.f / tT.S);
+        float w = p;
+        if (res) {
+            float q;
+            if (pm) {
+                q = cv.idx == dpm ? 1.f : 0.f;
+            } else {
+                const float zq = load_elem<BF16>(qrow, cv.idx);
+                q = (finite_logit(zq) && zq >= tQ.tstar)
+                        ? __fmul_rn(fast_exp2(__fmul_rn(zq - tQ.zmax, scale)), 1.f / tQ.S)
+                        : 0.f;
+            }
+            w = fmaxf(__fsub_rn(p, q), 0.f);
+        }
+        sc.v[i] = w;
+        sc.w[i] = p;
+        sc.idx[i] = cv.idx;
+        part += w;
+    }
+    part = wave_sum(part);
+    if (tid % kWave == 0) sc.red[tid / kWave] = part;
+    __syncthreads();
+    if (tid == 0) {
+        float W = 0.f;
+        for (int w2 = 0; w2 < kWaves; ++w2) W += sc.red[w2];
+        sWsum = W;
+        sFb = res && (!(W > 0.f) || !__builtin_isfinite(W));
+    }
+    __syncthreads();
+    *wres = res ? sWsum : 0.f;
+    *fallback = sFb != 0;
+    if (sFb) {
+        // the correction mass vanished: sample from p at that position
+        for (int i = tid; i < n; i += kBlock) sc.v[i] = sc.w[i];
+    }
+    // tokens in ascending index order, then the first running sum > u * W
+    const int n2 = pow2_at_least(n);
+    for (int i = n + tid; i < n2; i += kBlock) {
+        sc.v[i] = 0.f;
+        sc.idx[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    bitonic_sort(sc.v, sc.idx, n2, by_index);
+    for (int i = tid; i < n; i += kBlock) sc.w[i] = sc.v[i];
+    __syncthreads();
+    block_inclusive_scan(sc.w, n, sc.red);
+    const float target = u * sc.w[n - 1];
+    for (int i = tid; i < n; i += kBlock) {
+        if (sc.v[i] > 0.f) {
+            if (sc.w[i] > target) atomicMin(&sTok, i);
+            atomicMax(&sLastPos, i);
+        }
+    }
+    __syncthreads();
+    const int j = sTok != 0x7fffffff ? sTok : sLastPos;     // clamp: last positive weight
+    const int tok = j >= 0 ? sc.idx[j] : -1;
+    __syncthreads();
+    return tok;
+}
+
+}  // namespace
+}  // namespace specv

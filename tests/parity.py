@@ -168,38 +168,52 @@ def _check_values(rep, b, gpu, orc, eo, greedy):
             rep.w_floor_only += 1
 
 
-def compare_draft(gpu_tok, gpu_stats, gpu_flags, draft_f32, temperature, seed, step=0, pos0=0,
-                  report=None, skip_rows=()):
+def compare_draft(gpu_tok, gpu_stats, draft_f32, temperature, seed, step=0, pos0=0,
+                  top_k=0, top_p=1.0, report=None, skip_rows=()):
     """Compare the draft sampler's outputs for positions pos0 .. pos0+n-1
-    (arrays already sliced to those columns) with the oracle's draw and row
-    statistics.  Tokens: identical, or (sampled rows) inside the CDF window;
-    greedy tokens bit-exact; m exact; s within REL_TOL; flags exact.  Batch
-    rows in ``skip_rows`` are not compared."""
+    (arrays already sliced to those columns; gpu_stats float32 [B, n, 4]
+    records (max, sum, threshold, flags bits)) with the oracle's draw and row
+    statistics.  Tokens: identical, or (sampled rows) inside the CDF window,
+    or (truncated rows) a top-p decision the oracle marked near; greedy
+    tokens bit-exact; max and threshold exact; sum within REL_TOL; flags:
+    NONFINITE_ROW exactly where the oracle has no draw, TOPP_NEAR allowed.
+    Batch rows in ``skip_rows`` are not compared."""
     rep = report or Report()
     d = np.asarray(draft_f32)
     B, n, V = d.shape
     T = np.broadcast_to(np.asarray(temperature, np.float64), (B,))
-    o_tok = oracle.sample_draft_tokens(d, T, 0, 1.0, seed, step, pos0)
-    o_st = oracle.draft_row_stats(d, T)
-    g_tok, g_st, g_fl = _np(gpu_tok), _np(gpu_stats), _np(gpu_flags)
+    K = np.broadcast_to(np.asarray(top_k, np.int64), (B,))
+    Pp = np.broadcast_to(np.asarray(top_p, np.float64), (B,))
+    o_tok = oracle.sample_draft_tokens(d, T, K, Pp, seed, step, pos0)
+    o_st = oracle.draft_row_stats(d, T, K, Pp)
+    g_tok, g_st = _np(gpu_tok), _np(gpu_stats)
+    g_fl = np.ascontiguousarray(g_st).view(np.int32)[..., 3]
     for b in range(B):
         if b in skip_rows:
             continue
         for i in range(n):
             rep.rows += 1
             t, o = int(g_tok[b, i]), int(o_tok[b, i])
+            fl = int(g_fl[b, i]) & ~oracle.FLAG_TOPP_NEAR
             want_flag = oracle.FLAG_NONFINITE_ROW if o < 0 else 0
-            if int(g_fl[b, i]) != want_flag:
+            if fl != want_flag:
                 rep.fail(b, f"pos {pos0 + i}: flags {int(g_fl[b, i])} want {want_flag}")
                 continue
+            truncated = T[b] > 0 and o >= 0 and ((0 < K[b] < V) or Pp[b] < 1.0)
+            Q = oracle.process_row(d[b, i], T[b], K[b], Pp[b]) if truncated else None
+            if Q is not None and Q.topp_near:
+                # the kept set may legitimately differ between float32 and float64
+                rep.tolerated["topp_near"] += 1
+                continue
             if T[b] > 0 and o >= 0:
-                m, s = float(g_st[b, i, 0]), float(g_st[b, i, 1])
+                m, s, th = (float(x) for x in g_st[b, i, :3])
+                om, os_, ot = o_st[b, i]
                 rep.value_checks += 1
-                if m != o_st[b, i, 0] or not abs(s - o_st[b, i, 1]) <= REL_TOL * o_st[b, i, 1]:
-                    rep.fail(b, f"pos {pos0 + i}: stats ({m}, {s}) oracle {tuple(o_st[b, i])}")
+                if m != om or th != ot or not abs(s - os_) <= REL_TOL * os_:
+                    rep.fail(b, f"pos {pos0 + i}: stats ({m}, {s}, {th}) oracle ({om}, {os_}, {ot})")
                     continue
-            elif not np.isnan(g_st[b, i]).all():
-                rep.fail(b, f"pos {pos0 + i}: stats {g_st[b, i]} written for a greedy / undrawn row")
+            elif not np.isnan(g_st[b, i, :3]).all():
+                rep.fail(b, f"pos {pos0 + i}: stats {g_st[b, i, :3]} written for a greedy / undrawn row")
                 continue
             if t == o:
                 rep.exact += 1
@@ -207,7 +221,7 @@ def compare_draft(gpu_tok, gpu_stats, gpu_flags, draft_f32, temperature, seed, s
             if T[b] == 0 or o < 0:
                 rep.fail(b, f"pos {pos0 + i}: token {t} oracle {o}")
                 continue
-            q = oracle.process_row(d[b, i], T[b]).probs
+            q = (Q if Q is not None else oracle.process_row(d[b, i], T[b], K[b], Pp[b])).probs
             if not (0 <= t < V) or q[t] <= 0:
                 rep.fail(b, f"pos {pos0 + i}: token {t} has no draft mass")
                 continue

@@ -68,7 +68,7 @@ def test_verify_rejects_null_handle(lib):
                                         None, None, 0, 0, -1, None, None, None, None, None)
     assert rc == 1
     rc = lib.specv_sample_draft(None, None, None, 0, 0, 1, 1, 1, 1, 0, None, 0, 0,
-                                None, None, None, 1)
+                                None, None, 1)
     assert rc == 1
     assert lib.specv_destroy(None) == 0
 
@@ -83,3 +83,35 @@ def test_row_params_layout():
     assert a[:, 1].tolist() == [0, 50, 5]
     assert np.allclose(a[:, 2].view(np.float32), [1.0, 0.9, 0.5])
     assert a[:, 3].tolist() == [0, 3, 9]
+
+
+def test_struct_layouts_match_the_binding(tmp_path):
+    """The records the binding builds or reads as tensors: specv_row_params
+    (4 x 4 bytes: float, int32, float, int32) and specv_draft_stats (float
+    max, sum, threshold, int32 flags), compiled from the public header."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "specv.h"\n'
+        'int main(void) {\n'
+        '  printf("%zu %zu %zu %zu %zu\\n", sizeof(specv_row_params), offsetof(specv_row_params, top_k),\n'
+        '         offsetof(specv_row_params, top_p), offsetof(specv_row_params, max_new_tokens), 0ul);\n'
+        '  printf("%zu %zu %zu %zu\\n", sizeof(specv_draft_stats), offsetof(specv_draft_stats, sum),\n'
+        '         offsetof(specv_draft_stats, threshold), offsetof(specv_draft_stats, flags));\n'
+        '  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([gcc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    assert lines[0].split()[:4] == ["16", "4", "8", "12"]
+    assert lines[1].split() == ["16", "4", "8", "12"]
+
+
+def test_binding_exposes_every_entry_point():
+    for m in ("verify_sample", "verify_sample_qstats", "verify_point_mass", "verify_greedy",
+              "sample_draft", "set_profiling", "profile", "close"):
+        assert callable(getattr(sv.Verifier, m, None)), m

@@ -48,11 +48,11 @@ def _draw(v, draft_dev, prm, seed, step=0, pos0=0, out=None):
     return o
 
 
-def _check_draft(o, draft_f32, prm, seed, step=0, pos0=0, max_tol=0.02):
+def _check_draft(o, draft_f32, prm, seed, step=0, pos0=0, max_tol=0.02, skip_rows=()):
     n = draft_f32.shape[1]
     sl = slice(pos0, pos0 + n)
-    rep = compare_draft(o["tokens"][:, sl], o["stats"][:, sl], o["flags"][:, sl], draft_f32,
-                        prm["temperature"], seed, step, pos0)
+    rep = compare_draft(o["tokens"][:, sl], o["stats"][:, sl], draft_f32, prm["temperature"], seed,
+                        step, pos0, prm["top_k"], prm["top_p"], skip_rows=skip_rows)
     print(rep.summary())
     rep.assert_ok(max_tol)
     return rep
@@ -90,12 +90,11 @@ def test_draft_serving_batch_full_size(gpu):
         o = _draw(v, dd, prm, w.seed, step=3)
         _check_draft(o, w.draft_f32(), prm, w.seed, step=3)
         o2 = {"tokens": torch.full((w.B, w.gamma), -7, dtype=torch.int32, device=gpu),
-              "stats": torch.zeros(w.B, w.gamma, 2, device=gpu),
-              "flags": torch.full((w.B, w.gamma), -7, dtype=torch.int32, device=gpu)}
+              "stats": torch.zeros(w.B, w.gamma, 4, device=gpu)}
         for i in range(w.gamma):
             _draw(v, dd[:, i:i + 1], prm, w.seed, step=3, pos0=i, out=o2)
-    for k in ("tokens", "stats", "flags"):
-        assert torch.equal(o[k], o2[k]), k
+    assert torch.equal(o["tokens"], o2["tokens"])
+    assert torch.equal(o["stats"].view(torch.int32), o2["stats"].view(torch.int32))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -123,7 +122,8 @@ def test_draft_greedy_ragged(gpu, dtype, V, n, aligned):
 
 def test_draft_rows_without_a_draw(gpu):
     """NaN, +inf and all -inf rows give -1 and NONFINITE_ROW (greedy rows
-    too); top-k / top-p rows give -1 and UNSUPPORTED; other rows draw."""
+    too); top-k / top-p rows give -1 and UNSUPPORTED on a handle without
+    truncation workspace, and draw on one with it; other rows draw."""
     rng = np.random.default_rng(8)
     B, n, V = 8, 2, 9000
     d = rng.standard_normal((B, n, V)).astype(np.float32)
@@ -138,15 +138,54 @@ def test_draft_rows_without_a_draw(gpu):
     with sv.Verifier(B, n, V) as v:
         o = _draw(v, torch.from_numpy(d).cuda(), prm, 5)
     tok, fl = o["tokens"].cpu().numpy(), o["flags"].cpu().numpy()
-    st = o["stats"].cpu().numpy()
+    st = o["stats"].cpu().numpy()[..., :3]
     for (b, i) in [(0, 1), (1, 0), (2, 1), (3, 0)]:
         assert tok[b, i] == -1 and fl[b, i] == sv.FLAG_NONFINITE_ROW and np.isnan(st[b, i]).all()
     for b in (4, 5):
         assert (tok[b] == -1).all() and (fl[b] == sv.FLAG_UNSUPPORTED).all() and np.isnan(st[b]).all()
     # every other row against the oracle (same row indices, so same uniforms)
-    rep = compare_draft(o["tokens"], o["stats"], o["flags"], d, T, 5, skip_rows=(4, 5))
-    print(rep.summary())
-    rep.assert_ok(0.2)
+    _check_draft(o, d, prm, 5, max_tol=0.2, skip_rows=(4, 5))
+    # with truncation workspace the top-k row draws too; top-p alone on this
+    # flat row needs far more than max_top_k candidates per chunk, so that
+    # row is flagged CAND_OVERFLOW and gets no token
+    with sv.Verifier(B, n, V, max_top_k=16) as v:
+        o = _draw(v, torch.from_numpy(d).cuda(), prm, 5)
+    _check_draft(o, d, prm, 5, max_tol=0.2, skip_rows=(5,))
+    assert (o["tokens"][5] == -1).all() and (o["flags"][5] == sv.FLAG_CAND_OVERFLOW).all()
+
+
+def test_draft_truncated_full_size(gpu):
+    """B=32, 5 positions, V=152064, bf16, T=0.7, top-k 50, top-p 0.9: the
+    kept set by the verify kernel's row merge, the draw over it."""
+    w = synth.truncated()
+    prm = _prm(w.B, w.temperature, w.top_k, w.top_p)
+    with sv.Verifier(w.B, w.gamma, w.V, max_top_k=64) as v:
+        o = _draw(v, w.draft.cuda(), prm, 0x7A, step=2)
+    _check_draft(o, w.draft_f32(), prm, 0x7A, step=2, max_tol=0.05)
+    th = o["stats"][..., 2].cpu().numpy()
+    assert np.isfinite(th).all()                    # truncated rows carry their threshold
+
+
+@pytest.mark.parametrize("k,p", [(5, 1.0), (0, 0.8), (12, 0.9)])
+def test_draft_truncated_tiny_chi2(gpu, k, p):
+    """V=32 rows, 20,000 broadcast copies: the draws follow the truncated q."""
+    w = synth.tiny()
+    R = 20000
+    prm = _prm(R, 1.0, k, p)
+    with sv.Verifier(R, 4, 32, max_top_k=16) as v:
+        o = _draw(v, w.draft.cuda().expand(R, -1, -1), prm, 0xD1B + k)
+    _check_draft(o, w.draft.expand(R, -1, -1).numpy(), prm, 0xD1B + k)
+    toks = o["tokens"].cpu().numpy()
+    for i in range(4):
+        q = oracle.process_row(w.draft_f32()[0, i], 1.0, k, p).probs
+        counts = np.bincount(toks[:, i], minlength=32)
+        assert counts[q == 0].sum() == 0
+        keep = q * R >= 5
+        obs, exp = counts[keep], q[keep] * R
+        if (~keep & (q > 0)).any():
+            obs = np.append(obs, counts[~keep & (q > 0)].sum())
+            exp = np.append(exp, q[~keep & (q > 0)].sum() * R)
+        assert stats.chisquare(obs, exp * obs.sum() / exp.sum()).pvalue > 1e-3, i
 
 
 def _verify_both(v, w_t, w_d, tokens, stats_, prm, seed, step=0):
@@ -184,8 +223,7 @@ def test_qstats_verify_serving_batch_bitwise(gpu):
 
 def test_qstats_verify_greedy_truncated_mixed(gpu):
     """Rows of every mode in one call (handle with truncation): greedy rows
-    and truncated rows ignore the statistics (truncated rows' draft tokens
-    come from the oracle's truncated draw; their statistics are NaN)."""
+    ignore the statistics; truncated rows take their kept sets from them."""
     rng = np.random.default_rng(41)
     B, gamma, V = 24, 4, 50000
     t, d = synth.make_logits(rng, B, gamma, V, 3.0, 1.0, boost_count=20)
@@ -200,13 +238,29 @@ def test_qstats_verify_greedy_truncated_mixed(gpu):
         o = _draw(v, dd.cuda(), prm, 77)
         toks = o["tokens"].cpu().numpy()
         df = dd.float().numpy()
-        tr = mode == 2
-        toks[tr] = oracle.sample_draft_tokens(df[tr], 0.8, 40, 0.9, 78)
+        assert (toks >= 0).all()
         out = _verify_both(v, tt.cuda(), dd.cuda(), toks, o["stats"], prm, 79)
     orc = oracle.verify_sample(tt.float().numpy(), df, toks, T, k, p, cap, 79, keep_weights=True)
     rep = compare(out, orc, toks, tt.float().numpy(), df, prm)
     print(rep.summary())
     rep.assert_ok(0.1)
+
+
+def test_qstats_verify_truncated_full_size_bitwise(gpu):
+    """The truncated workload (V=152064, top-k 50, top-p 0.9) through the
+    sampler and both verify entry points: bit-identical, and oracle parity."""
+    w = synth.truncated()
+    prm = _prm(w.B, w.temperature, w.top_k, w.top_p)
+    t, d = w.target.cuda(), w.draft.cuda()
+    with sv.Verifier(w.B, w.gamma, w.V, max_top_k=64) as v:
+        o = _draw(v, d, prm, 0x7B)
+        out = _verify_both(v, t, d, o["tokens"], o["stats"], prm, w.seed)
+    toks = o["tokens"].cpu().numpy()
+    orc = oracle.verify_sample(w.target_f32(), w.draft_f32(), toks, w.temperature, w.top_k,
+                               w.top_p, 0, w.seed, keep_weights=True)
+    rep = compare(out, orc, toks, w.target_f32(), w.draft_f32(), prm)
+    print(rep.summary())
+    rep.assert_ok(0.05)
 
 
 def test_qstats_non_finite_statistics_mark_the_row(gpu):
