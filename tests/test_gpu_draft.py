@@ -263,6 +263,34 @@ def test_qstats_verify_truncated_full_size_bitwise(gpu):
     rep.assert_ok(0.05)
 
 
+def test_qstats_verify_mixed_full_size_with_eos(gpu):
+    """The mixed workload (B=256, gamma=8, V=128256: even rows T=1, odd rows
+    greedy, caps 1..9) with an EOS id that some draws hit: the sampler's
+    draws and records, both verify entry points bit-identical, oracle parity."""
+    w = synth.mixed()
+    prm = _prm(w.B, w.temperature, 0, 1.0, w.max_new_tokens)
+    t, d = w.target.cuda(), w.draft.cuda()
+    with sv.Verifier(w.B, w.gamma, w.V) as v:
+        o = _draw(v, d, prm, 0x3C)
+        toks = o["tokens"].cpu().numpy()
+        eos = int(toks[0, 3])
+        out = _verify_both(v, t, d, o["tokens"], o["stats"], prm, w.seed, step=1)
+        rp = _rp(prm)
+        a = v.verify_sample(t, d, o["tokens"], rp, w.seed, 1, eos)
+        b = v.verify_sample_qstats(t, d, o["stats"], o["tokens"], rp, w.seed, 1, eos)
+        torch.cuda.synchronize()
+    for key in ("num_accepted", "out_tokens", "num_emitted", "row_flags"):
+        assert torch.equal(a[key], b[key]), key
+    _check_draft(o, w.draft_f32(), prm, 0x3C)
+    orc = oracle.verify_sample(w.target_f32(), w.draft_f32(), toks, w.temperature, 0, 1.0,
+                               w.max_new_tokens, w.seed, 1, eos, keep_weights=True)
+    rep = compare(b, orc, toks, w.target_f32(), w.draft_f32(), prm)
+    print(rep.summary())
+    rep.assert_ok(0.05)
+    em = b["num_emitted"].cpu().numpy()
+    assert (em <= w.max_new_tokens).all()
+
+
 def test_qstats_non_finite_statistics_mark_the_row(gpu):
     """A NaN statistic, a zero sum or a max of -inf makes the row emit
     nothing with NONFINITE_ROW; the other rows are unaffected."""
