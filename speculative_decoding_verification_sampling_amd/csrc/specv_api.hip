@@ -467,7 +467,6 @@ specv_status specv_verify_greedy(specv_handle h, void* stream, const void* targe
     a.out_flags = out_row_flags;
     const bool vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es);
     return launch(h, a, dtype == SPECV_BF16, vec, stream);
-    return SPECV_OK;
 }
 
 }  // extern "C"
