@@ -78,9 +78,15 @@ def sampler_bytes(B, V, es):
 
 
 def kernel_source_hash():
+    """Hash of the device-code sources (every file under csrc/ except the
+    host-side C ABI), so that counter figures are dropped once a kernel
+    changes."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
-        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
+    d = os.path.dirname(KERNEL_SRC)
+    for name in sorted(os.listdir(d)):
+        if name == "specv_api.hip" or not name.endswith((".hip", ".hpp")):
+            continue
+        with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 

@@ -314,3 +314,52 @@ def test_qstats_non_finite_statistics_mark_the_row(gpu):
     keep = [0, 4, 5, 6, 7]
     for key in ("num_accepted", "out_tokens", "num_emitted", "row_flags"):
         assert torch.equal(good[key][keep], bad[key][keep]), key
+
+
+def test_sampler_argument_errors_and_offsets(gpu):
+    """Status codes of specv_sample_draft / specv_verify_sample_qstats for
+    bad arguments (through the C ABI directly), no-op calls, and a call
+    that fills two middle columns of a wider output."""
+    import ctypes
+    lib = sv.load_library()
+    B, n, V = 4, 2, 300
+    d = torch.randn(B, 5, V, device="cuda")
+    rp = _rp(_prm(B, 0.9))
+    tok = torch.full((B, 5), -7, dtype=torch.int32, device="cuda")
+    st = torch.zeros(B, 5, 4, device="cuda")
+    with sv.Verifier(B, 5, V) as v:
+        h = v._h
+        call = lambda **kw: lib.specv_sample_draft(
+            h, None, ctypes.c_void_p(kw.get("d", d).data_ptr()), d.stride(0), d.stride(1), 0,
+            kw.get("B", B), kw.get("n", n), kw.get("V", V), kw.get("pos0", 0),
+            ctypes.c_void_p(rp.data_ptr()), 1, 0, ctypes.c_void_p(tok.data_ptr()),
+            ctypes.c_void_p(kw.get("st", st.data_ptr())), kw.get("stride", 5))
+        assert call(stride=1) == 2                                   # pos0 + n > out_stride
+        assert call(pos0=4) == 2
+        assert call(n=6, stride=10) == 5                             # n above max(max_gamma, 1)
+        assert call(B=5) == 5                                        # B above max_batch
+        assert call(V=301) == 5                                      # V above max_vocab
+        assert call(st=st.data_ptr() + 8) == 4                       # records 16-byte aligned
+        assert call(n=0) == 0 and call(B=0) == 0                     # no-ops
+        torch.cuda.synchronize()
+        assert (tok == -7).all()
+        # columns 2 and 3 of a width-5 output, positions 2 and 3 of the round
+        o = {"tokens": tok, "stats": st}
+        v.sample_draft(d[:, 2:4], rp, 1, 0, pos0=2, out=o)
+        torch.cuda.synchronize()
+        assert (tok[:, [0, 1, 4]] == -7).all() and (tok[:, 2:4] >= 0).all()
+        ref = v.sample_draft(d, rp, 1, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(ref["tokens"][:, 2:4], tok[:, 2:4])
+        assert torch.equal(ref["stats"][:, 2:4].view(torch.int32), st[:, 2:4].view(torch.int32))
+        # the statistics verify: a short stride and misaligned records are refused
+        t = torch.randn(B, 3, V, device="cuda")
+        toks = ref["tokens"][:, :2].contiguous()
+        outs = [torch.zeros(B * 3, dtype=torch.int32, device="cuda") for _ in range(3)]
+        ptr = lambda x: ctypes.c_void_p(x.data_ptr())
+        args = lambda sp, ss: (h, None, ptr(t), t.stride(0), t.stride(1), ptr(d), d.stride(0),
+                               d.stride(1), ctypes.c_void_p(sp), ss, 0, B, 2, V, ptr(toks), ptr(rp),
+                               1, 0, -1, ptr(outs[0]), ptr(outs[1]), ptr(outs[2]), None, None)
+        assert lib.specv_verify_sample_qstats(*args(ref["stats"].data_ptr(), 1)) == 2
+        assert lib.specv_verify_sample_qstats(*args(ref["stats"].data_ptr() + 4, 5)) == 4
+        assert lib.specv_verify_sample_qstats(*args(0, 5)) == 1
