@@ -39,7 +39,10 @@
  * Ownership: the caller owns every input and output buffer.  A handle owns a
  * device workspace allocated once by specv_create and freed by
  * specv_destroy; verify calls allocate nothing.  One handle serves one stream
- * at a time (calls on a handle must not overlap).
+ * at a time (calls on a handle must not overlap).  Each call takes a fresh
+ * tag for the records its workgroups exchange, chosen on the host when the
+ * call is made, so a call captured into a HIP graph must not be replayed:
+ * replays would reuse the tag and could read the previous replay's records.
  *
  * Errors: every argument error is reported synchronously, before anything is
  * enqueued, as a non-zero specv_status.  Calls are otherwise asynchronous on
