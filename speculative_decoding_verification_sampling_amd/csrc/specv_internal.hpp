@@ -69,8 +69,10 @@ struct PairRec {
 // position draws the correction / bonus token, the row's flags so far, and
 // that position's normalisers.  Epoch-tagged words like PairRec.
 enum RowWord {
-    RW_REC = 0,           // kind | (position << 3) | (flags << 8)
+    RW_REC = 0,           // kind | (position << 3)
     RW_MT, RW_INVT, RW_MQ, RW_INVQ,
+    RW_FLAGS,             // the row's flags from the consulted positions (published once
+                          // they are gathered, possibly after the words above)
     kRowWords = 8
 };
 

@@ -128,7 +128,22 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
     const int nacc = r.how == H_STOP || r.how == H_CAPPED ? r.n : a.gamma;
     __shared__ int fKind, fDead, fAt;
     __shared__ unsigned fFlags;
+    unsigned long long* rowrec = a.ws.rowrec + (long long)b * kRowWords;
     if (wave == 0) {
+        // A sampling row whose round ends at this position hands its draw to
+        // its sampling workgroups at once: the kind, the position and this
+        // pair's normalisers do not depend on the other positions' records,
+        // which only add flags (RW_FLAGS, published once gathered).
+        const int at = r.how == H_STOP ? r.n : a.gamma;
+        const bool early = pl.mode == MODE_SAMPLE && at == k &&
+                           ((r.how == H_STOP && (own.state & 0xffu) == OUT_REJ) || r.how == H_BONUS);
+        if (early) {
+            const unsigned rec = (unsigned)(r.how == H_STOP ? KIND_RESIDUAL : KIND_BONUS) | ((unsigned)at << 3);
+            const unsigned v = lane == RW_MT ? __float_as_uint(own.mt) : lane == RW_INVT ? __float_as_uint(own.invt)
+                             : lane == RW_MQ ? __float_as_uint(own.mq) : lane == RW_INVQ ? __float_as_uint(own.invq)
+                             : rec;
+            if (lane <= RW_INVQ) put_tagged(&rowrec[lane], v, a.epoch);
+        }
         unsigned long long w[kPairWords];
 #pragma unroll
         for (int i = 0; i < kPairWords; ++i) w[i] = 0;
@@ -170,7 +185,6 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
         // the record of the position that ended the round, read from its lane
         // here, with every lane active (a cross-lane read inside a branch that
         // only some lanes take can see registers the branch never restored)
-        const int at = r.how == H_STOP ? r.n : a.gamma;
         const unsigned s_at = __builtin_amdgcn_readlane(rs, at);
         const int a_at = __builtin_amdgcn_readlane((int)(unsigned)w[PW_ARG], at);
         const unsigned mt_at = __builtin_amdgcn_readlane((unsigned)w[PW_MT], at);
@@ -193,12 +207,13 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
         const bool samp = pl.mode == MODE_SAMPLE && kind != KIND_NONE;
         if (kind == KIND_NONE) write_outputs_wave(a, b, nacc, nacc, flags, dead, sampled, 0.f, pl.tok);
         if (pl.mode == MODE_SAMPLE) {
-            // the row record: lane i < kRowWords writes word i
-            const unsigned rec = (unsigned)(samp ? kind : KIND_NONE) | ((unsigned)(samp ? at : 0) << 3) |
-                                 ((flags & 0xffu) << 8);
+            // the row record (lane i writes word i), unless handed over above,
+            // and the row's flags
+            const unsigned rec = (unsigned)(samp ? kind : KIND_NONE) | ((unsigned)(samp ? at : 0) << 3);
             const unsigned v = lane == RW_MT ? mt_at : lane == RW_INVT ? invt_at
-                             : lane == RW_MQ ? mq_at : lane == RW_INVQ ? invq_at : rec;
-            if (lane <= RW_INVQ) put_tagged(&a.ws.rowrec[(long long)b * kRowWords + lane], v, a.epoch);
+                             : lane == RW_MQ ? mq_at : lane == RW_INVQ ? invq_at
+                             : lane == RW_FLAGS ? (flags & 0xffu) : rec;
+            if ((lane <= RW_INVQ && !early) || lane == RW_FLAGS) put_tagged(&rowrec[lane], v, a.epoch);
         }
         if (lane == 0) {
             fKind = kind;
@@ -434,10 +449,11 @@ struct Weights {
 // registers: each publishes its chunk's weight sum and p mass, reads all of
 // them, and the workgroup whose chunk holds u * W scans it (tokens in
 // ascending order, first running sum > u * W) and writes the outputs.
-// ``flags_in``: the row's flags so far.  Whole workgroup.
+// The row's flags (RW_FLAGS of the row record) are read with the chunk sums.
+// Whole workgroup.
 template <bool BF16, bool VEC, int PROP>
 __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan& pl, Weights wt,
-                                 unsigned flags_in, const ChunkRegs<BF16, VEC>& rt,
+                                 const ChunkRegs<BF16, VEC>& rt,
                                  const ChunkRegs<BF16, VEC>& rd) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     constexpr int G = BF16 ? 8 : 4;
@@ -501,15 +517,18 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         }
         unsigned long long* base = a.ws.wsum + (long long)b * a.C * 2;
         if (lane < 2) put_tagged(base + c * 2 + lane, __float_as_uint(lane == 0 ? wc : pc), a.epoch);
+        const unsigned long long* rflags = a.ws.rowrec + (long long)b * kRowWords + RW_FLAGS;
         bool done = false;
-        unsigned long long w0 = 0, w1 = 0;
+        unsigned long long w0 = 0, w1 = 0, wf = 0;
 #pragma unroll 1
         for (int spin = 0; spin < kSpinLimit; ++spin) {
             if (lane < a.C) {
                 w0 = published(base + lane * 2);
                 w1 = published(base + lane * 2 + 1);
             }
-            const bool mine = lane >= a.C || (tag_is(w0, a.epoch) && tag_is(w1, a.epoch));
+            if (lane == 0) wf = published(rflags);
+            const bool mine = (lane >= a.C || (tag_is(w0, a.epoch) && tag_is(w1, a.epoch))) &&
+                              (lane != 0 || tag_is(wf, a.epoch));
             if (__ballot(mine) == ~0ull) {
                 done = true;
                 break;
@@ -518,7 +537,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         }
         float vw = lane < a.C ? __uint_as_float((unsigned)w0) : 0.f;
         const float vp = lane < a.C ? __uint_as_float((unsigned)w1) : 0.f;
-        unsigned flags = flags_in;
+        unsigned flags = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)wf) & 0xffu;
         int res = wt.residual;
         float W = wave_sum(vw);
         const float wres = res ? W : 0.f;
@@ -739,7 +758,7 @@ __device__ void sample_item(const Args& a, int b, int c) {
     wt.mq = __uint_as_float(sRec[RW_MQ]);
     wt.invq = __uint_as_float(sRec[RW_INVQ]);
     wt.st = pl.scale;
-    sample_from_regs<BF16, VEC, PROP>(a, b, k, c, pl, wt, (rec >> 8) & 0xffu, rt, rd);
+    sample_from_regs<BF16, VEC, PROP>(a, b, k, c, pl, wt, rt, rd);
 }
 
 // ---------------------------------------------------------------- k_verify
