@@ -1,7 +1,7 @@
 """Throughput of the speculative-sampling verify step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu-baseline]
-                    [--workload serving|point-mass|drafted]
+                    [--workload serving|point-mass|drafted|truncated|mixed]
 
 Workload: the serving batch, B=64 rows, gamma=5 drafts, V=128256 bfloat16
 logits (target [64, 6, 128256], draft [64, 5, 128256]), T=0.7, synthetic
@@ -15,6 +15,12 @@ memory-side cache cannot serve a call from the previous one.
 drafts (the argmax of the draft logits, standing in for n-gram /
 prompt-lookup proposals) through ``specv_verify_point_mass``, which reads no
 draft logits.
+
+``--workload truncated`` (B=32, gamma=5, V=152064, bf16, T=0.7, top-k 50 and
+top-p 0.9 on both distributions, draft tokens drawn by ``specv_sample_draft``
+from the truncated draft distribution) and ``--workload mixed`` (B=256,
+gamma=8, V=128256, bf16, even rows T=1, odd rows greedy, per-row caps 1..9)
+run the other synthetic configurations through ``specv_verify_sample``.
 
 ``--workload drafted`` runs the drafter's side too: a step is gamma calls of
 ``specv_sample_draft`` (one per position, as an autoregressive drafter
@@ -41,6 +47,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "verified rows/sec + achieved HBM GB/s (% peak), V=128256 γ=5 B=64 bf16"
 METRIC_POINT_MASS = ("verified rows/sec + achieved HBM GB/s (% peak), point-mass drafts, "
                      "V=128256 γ=5 B=64 bf16")
+METRIC_TRUNCATED = ("verified rows/sec + achieved HBM GB/s (% peak), top-k 50 top-p 0.9, "
+                    "V=152064 γ=5 B=32 bf16")
+METRIC_MIXED = ("verified rows/sec + achieved HBM GB/s (% peak), half greedy rows, caps 1..9, "
+                "V=128256 γ=8 B=256 bf16")
 METRIC_DRAFTED = ("verified rows/sec + achieved HBM GB/s (% peak), drafter-sampled proposals "
                   "with row statistics, V=128256 γ=5 B=64 bf16")
 PEAK_HBM_GBPS = 8000.0
@@ -51,6 +61,8 @@ TRAFFIC_FILES = {
     ("point-mass", "k_verify"): os.path.join(ROOT, "profiles", "traffic_k_verify_point_mass.json"),
     ("drafted", "k_verify"): os.path.join(ROOT, "profiles", "traffic_k_verify_drafted.json"),
     ("drafted", "k_sample_draft"): os.path.join(ROOT, "profiles", "traffic_k_sample_draft_drafted.json"),
+    ("truncated", "k_verify"): os.path.join(ROOT, "profiles", "traffic_k_verify_truncated.json"),
+    ("mixed", "k_verify"): os.path.join(ROOT, "profiles", "traffic_k_verify_mixed.json"),
 }
 
 
@@ -68,7 +80,7 @@ def algorithmic_bytes(B, gamma, V, es, caps, eos_cut, greedy, point_mass=False, 
         if qstats:
             nd = min(nd, 1)
         total += (nt + nd) * V * es
-    return total
+    return int(total)
 
 
 def sampler_bytes(B, V, es):
@@ -142,7 +154,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("serving", "point-mass", "drafted"), default="serving")
+    ap.add_argument("--workload", choices=("serving", "point-mass", "drafted", "truncated", "mixed"),
+                    default="serving")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run --steps device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -176,11 +189,18 @@ def main():
 
     point_mass = args.workload == "point-mass"
     drafted = args.workload == "drafted"
-    w = synth.serving_batch()
+    truncated = args.workload == "truncated"
+    w = {"truncated": synth.truncated, "mixed": synth.mixed}.get(args.workload, synth.serving_batch)()
     B, gamma, V = w.B, w.gamma, w.V
+    max_top_k = 64 if truncated else 0
     # deterministic drafts stand in for n-gram / prompt-lookup proposals
     tok_np = (w.draft.to(torch.float32).numpy().argmax(-1).astype(np.int32) if point_mass
               else w.tokens)
+    if truncated:
+        # proposals from the truncated draft distribution, drawn on the device
+        with sv.Verifier(B, gamma, V, max_top_k=max_top_k) as vd:
+            rp = sv.make_row_params(B, w.temperature, w.top_k, w.top_p, w.max_new_tokens, dev)
+            tok_np = vd.sample_draft(w.draft.to(dev), rp, w.seed + 1)["tokens"].cpu().numpy()
     sets = []
     for _ in range(max(1, args.sets)):
         t = w.target.to(dev)
@@ -191,7 +211,7 @@ def main():
     tokens = torch.from_numpy(tok_np).to(dev)
     params = sv.make_row_params(B, w.temperature, w.top_k, w.top_p, w.max_new_tokens, dev)
     out = None
-    v = sv.Verifier(B, gamma, V)
+    v = sv.Verifier(B, gamma, V, max_top_k=max_top_k)
     vs = sv.Verifier(B, gamma, V) if drafted else None      # the drafter's handle, timed apart
     drawn = None
     if drafted:
@@ -277,14 +297,22 @@ def main():
 
     rows_per_s = B / (ms_step * 1e-3)
     if point_mass:
-        desc = "deterministic drafts (argmax of target + noise 1.5), no draft logits"
+        desc = "serving batch, deterministic drafts (argmax of target + noise 1.5), no draft logits"
     elif drafted:
-        desc = ("draft noise 1.5, drafts drawn on the device one position per call with the rows' "
-                "statistics, verified with those statistics")
+        desc = ("serving batch, draft noise 1.5, drafts drawn on the device one position per call "
+                "with the rows' statistics, verified with those statistics")
+    elif truncated:
+        desc = ("truncated batch, T=0.7, top-k 50, top-p 0.9 on target and draft, draft noise 1.5, "
+                "drafts drawn on the device from the truncated draft distribution")
+    elif args.workload == "mixed":
+        desc = ("mixed batch, even rows T=1 and odd rows greedy, per-row draft noise U[0.3, 4], "
+                "caps U{1..9}")
     else:
-        desc = "draft noise 1.5"
+        desc = "serving batch, T=0.7, draft noise 1.5"
+    metric = {"point-mass": METRIC_POINT_MASS, "drafted": METRIC_DRAFTED, "truncated": METRIC_TRUNCATED,
+              "mixed": METRIC_MIXED}.get(args.workload, METRIC)
     line = {
-        "metric": METRIC_POINT_MASS if point_mass else (METRIC_DRAFTED if drafted else METRIC),
+        "metric": metric,
         "value": rows_per_s,
         "unit": "verified rows/s",
         "n_gpus": 1,
@@ -296,8 +324,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"serving batch B={B} gamma={gamma} V={V} bf16 T=0.7, "
-                               f"20 boosted tokens, {desc}",
+        "config": {"workload": f"B={B} gamma={gamma} V={V} bf16, 20 boosted tokens, {desc}",
                    "B": B, "gamma": gamma, "V": V, "rotated_input_sets": len(sets)},
         "emitted_tokens_per_s": tokens_per_call / (ms_step * 1e-3),
         "step_hbm_gbps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,

@@ -194,11 +194,8 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScra
             if (trunc) {
                 // the chunk's top-k candidates, complete before its statistics
                 // are published (the statistics words tell the merge they are in)
-                Plan pl{};
-                pl.keff = topk_on ? rp.top_k : a.max_top_k;
-                float x[kPerThread];
-                r.get(x);
-                chunk_candidates<BF16>(va, side_row(va, b, i, 1), c, pl.keff, x, *sc);
+                chunk_candidates<BF16>(va, side_row(va, b, i, 1), c, topk_on ? rp.top_k : a.max_top_k, r,
+                                       *sc);
                 wait_stores();
             }
         }

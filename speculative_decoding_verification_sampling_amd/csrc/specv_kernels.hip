@@ -685,11 +685,7 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
                 ss[side][wave] = s;
             }
             if constexpr (TRUNC) {
-                if (trunc) {
-                    float x[kPerThread];
-                    r.get(x);
-                    chunk_candidates<BF16>(a, side_row(a, b, k, side), c, pl.keff, x, *sc);
-                }
+                if (trunc) chunk_candidates<BF16>(a, side_row(a, b, k, side), c, pl.keff, r, *sc);
             }
         }
         __syncthreads();

@@ -358,19 +358,31 @@ __device__ unsigned select_kth_key(const Args& a, long long rowid, int total, fl
     return sPrefix;
 }
 
-// Candidates of one chunk (whole workgroup): every finite entry >= L.
-template <bool BF16>
-__device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff,
-                                 const float (&x)[kPerThread], TruncScratch& sc) {
+// Value whose order key is ``key`` (the inverse of order_key for keys of
+// float32 values); for a key with its low bits cleared, the smallest value
+// of that key range.
+__device__ inline float key_value(unsigned key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Candidates of one chunk (whole workgroup) held in registers: every finite
+// entry >= L, where L is a lower bound of the chunk's keff-th largest entry:
+// each thread keeps its top jj = ceil(2 keff / 256) <= 8 finite entries, so
+// at least keff chunk entries are >= the keff-th largest of those 256 jj
+// values; that value is found by a radix select (two 8-bit digits) over the
+// top 16 bits of the values' order keys, which for float32 rounds it down to
+// the start of its key range (still a lower bound).
+template <bool BF16, typename Regs>
+__device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff, const Regs& r,
+                                 TruncScratch& sc) {
     const int tid = threadIdx.x;
-    // twice as many per-thread tops as needed keeps L close to the k-th value
     const int jj = min(8, (2 * keff + kBlock - 1) / kBlock);
     float tp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) tp[j] = -kInf;                // this thread's top 8, desc
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-        float v = x[k];
+        float v = r.elem(k);
         if (!(finite_logit(v) && v > tp[7])) continue;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {                       // insertion, larger values first
@@ -381,25 +393,53 @@ __device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff
             }
         }
     }
-    const int n = kBlock * jj;
-    const int n2 = pow2_at_least(n);
-    __syncthreads();                                        // sc may still be read
+    // radix select of the keff-th largest 16-bit key among the jj tops
+    __shared__ unsigned sSel, sNeed;
+    __shared__ int sFound;
+    if (tid == 0) {
+        sSel = 0;
+        sNeed = (unsigned)keff;
+        sFound = 1;
+    }
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        __syncthreads();                                    // sc may still be read; sSel set
+        sc.hist[tid] = 0;                                   // kBlock == 256 bins
+        __syncthreads();
+        // read before any thread updates them below (after the scan's barriers)
+        const unsigned sel = sSel;
+        const int need = (int)sNeed;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < jj) {
-            sc.v[tid * jj + j] = tp[j];
-            sc.idx[tid * jj + j] = 0;
+        for (int j = 0; j < 8; ++j) {
+            if (j < jj && finite_logit(tp[j])) {
+                const unsigned k16 = order_key<false>(tp[j]) >> 16;
+                if (pass == 0) atomicAdd(&sc.hist[k16 >> 8], 1u);
+                else if ((k16 >> 8) == sel) atomicAdd(&sc.hist[k16 & 255u], 1u);
+            }
         }
-    for (int i = n + tid; i < n2; i += kBlock) {
-        sc.v[i] = -kInf;
-        sc.idx[i] = 0;
+        __syncthreads();
+        // bin t holds hist[t]; entries in bins >= t: all - (entries in bins < t)
+        const int h = (int)sc.hist[tid];
+        int all;
+        const int below = block_excl_scan(h, sc.misc, &all);
+        const int ge = all - below;
+        if (all < need) {
+            if (tid == 0) sFound = 0;                       // fewer finite tops than keff
+        } else if (ge >= need && ge - h < need) {
+            // this bin holds the need-th largest: shared by exactly one thread
+            if (pass == 0) {
+                sSel = (unsigned)tid;
+                sNeed = (unsigned)(need - (ge - h));
+            } else {
+                sSel = (sSel << 8) | (unsigned)tid;
+            }
+        }
     }
     __syncthreads();
-    bitonic_sort(sc.v, sc.idx, n2, by_value);
-    const float L = sc.v[keff - 1];        // keff <= 256 * jj / 2 <= n2
+    const float L = sFound ? key_value(sSel << 16) : -kInf;
     int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) cnt += finite_logit(x[k]) && x[k] >= L;
+    for (int k = 0; k < kPerThread; ++k) cnt += finite_logit(r.elem(k)) && r.elem(k) >= L;
     int total;
     const int off = block_excl_scan(cnt, sc.misc, &total);
     if (total <= a.cand_cap) {
@@ -407,8 +447,10 @@ __device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff
         int o = off;
         const int v0 = c * kChunk;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k)
-            if (finite_logit(x[k]) && x[k] >= L) publish_cand(dst + o++, x[k], v0 + chunk_index<BF16>(k));
+        for (int k = 0; k < kPerThread; ++k) {
+            const float x = r.elem(k);
+            if (finite_logit(x) && x >= L) publish_cand(dst + o++, x, v0 + chunk_index<BF16>(k));
+        }
     }
     if (tid == 0)
         publish_cand(a.ws.cand_meta + rowid * a.C + c, L, total <= a.cand_cap ? total : -1);
