@@ -102,24 +102,18 @@ __device__ void draw_truncated(const DraftArgs& a, const Args& va, int b, int i,
     // row_merge leaves the kept list in sc.v / sc.idx (value descending)
     __shared__ int sTok, sLast;
     const int n = tr.n_kept;
-    const int n2 = pow2_at_least(n);
-    for (int j = tid; j < n2; j += kBlock) {
-        sc.w[j] = j < n ? fast_exp2(__fmul_rn(sc.v[j] - tr.zmax, pl.scale)) : 0.f;
-        if (j >= n) sc.idx[j] = 0x7fffffff;
-    }
+    for (int j = tid; j < n; j += kBlock) sc.w[j] = fast_exp2(__fmul_rn(sc.v[j] - tr.zmax, pl.scale));
     if (tid == 0) {
         sTok = 0x7fffffff;
         sLast = -1;
     }
     __syncthreads();
-    bitonic_sort(sc.w, sc.idx, n2, by_index);       // weights in token order
-    for (int j = tid; j < n; j += kBlock) sc.v[j] = sc.w[j];
-    __syncthreads();
-    block_inclusive_scan(sc.v, n, sc.red);          // running sums
-    const float target = u * sc.v[n - 1];
+    rank_sort(sc.w, sc.idx, n, sc.v, sc.idx2, by_index);   // weights in token order
+    block_inclusive_scan(sc.v, sc.w, n, sc.red);            // running sums
+    const float target = u * sc.w[n - 1];
     for (int j = tid; j < n; j += kBlock) {
-        if (sc.w[j] > 0.f) {
-            if (sc.v[j] > target) atomicMin(&sTok, j);
+        if (sc.v[j] > 0.f) {
+            if (sc.w[j] > target) atomicMin(&sTok, j);
             atomicMax(&sLast, j);
         }
     }
@@ -127,7 +121,7 @@ __device__ void draw_truncated(const DraftArgs& a, const Args& va, int b, int i,
     if (tid == 0) {
         const int j = sTok != 0x7fffffff ? sTok : sLast;     // rounding: last with weight
         if (j < 0) write_draft(a, o, -1, nan, nan, nan, tr.flags | SPECV_FLAG_NONFINITE_ROW);
-        else write_draft(a, o, sc.idx[j], tr.zmax, tr.S, tr.tstar, tr.flags);
+        else write_draft(a, o, sc.idx2[j], tr.zmax, tr.S, tr.tstar, tr.flags);
     }
 }
 

@@ -43,6 +43,7 @@ struct TruncScratch {
     float v[kKeptCap];
     int idx[kKeptCap];
     float w[kKeptCap];
+    int idx2[kKeptCap];
     unsigned hist[256];
     unsigned off[kMaxChunks + 1];
     float red[kBlock / 64];

@@ -173,11 +173,12 @@ __device__ inline void write_outputs_wave(const Args& a, int b, int nemit, int n
 //                superset of the chunk's top k (typically ~k entries);
 //   per row:     (the workgroup deciding the position) the row's top-k
 //                threshold is >= every chunk's L, so only candidates >= max L
-//                are gathered (at most 2048); they are sorted (value desc,
-//                index asc), the k-th entry is the top-k threshold (ties
-//                kept), and the prefix is scanned for top-p: the first level
-//                whose cumulative mass reaches top_p ends the kept set (ties
-//                at a level all kept);
+//                are gathered (at most 2048); a radix select finds the k-th
+//                largest of them, the top-k threshold (ties kept); the
+//                entries at or above it are sorted (value desc, index asc)
+//                and scanned for top-p: the first level whose cumulative
+//                mass reaches top_p ends the kept set (ties at a level all
+//                kept);
 //   per batch row: the accept tests use the kept sets, and the correction /
 //                bonus sample is drawn from the (short) kept list of the
 //                sampled row, tokens in ascending index order.
@@ -198,12 +199,6 @@ __device__ inline Cand published_cand(const Cand* p) {
     return c;
 }
 
-__device__ inline int pow2_at_least(int n) {
-    int p = 1;
-    while (p < n) p <<= 1;
-    return p;
-}
-
 // (value desc, index asc)
 __device__ inline bool by_value(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
@@ -211,30 +206,39 @@ __device__ inline bool by_value(float va, int ia, float vb, int ib) {
 // index asc
 __device__ inline bool by_index(float, int ia, float, int ib) { return ia < ib; }
 
-// Block-wide bitonic sort of v / idx [0, n), n a power of two <= kKeptCap,
-// so that entry x comes before entry y when prec(x, y).  Entries must be
-// visible to the block (caller synchronised); result visible on return.
+// Block-wide rank sort of (iv, ii) [0, n) into (ov, oi): entry x lands at
+// the number of entries y with prec(y, x), so prec must order the entries
+// strictly (by_value with distinct indices, by_index with distinct indices).
+// One pass of n comparisons per entry and a single barrier: for the short
+// lists here (the kept sets) it beats a bitonic network, whose log^2 n
+// barrier-separated stages dominate the row merge.  The inputs must be
+// visible to the block and must not alias the outputs; the result is
+// visible on return.
 template <typename Prec>
-__device__ void bitonic_sort(float* v, int* idx, int n, Prec prec) {
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += kBlock) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const float va = v[i], vb = v[ixj];
-                    const int ia = idx[i], ib = idx[ixj];
-                    const bool sw = (i & k) == 0 ? prec(vb, ib, va, ia) : prec(va, ia, vb, ib);
-                    if (sw) {
-                        v[i] = vb;
-                        v[ixj] = va;
-                        idx[i] = ib;
-                        idx[ixj] = ia;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+__device__ void rank_sort(const float* iv, const int* ii, int n, float* ov, int* oi, Prec prec) {
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const float vi = iv[i];
+        const int xi = ii[i];
+        int r = 0;
+#pragma unroll 4
+        for (int j = 0; j < n; ++j) r += prec(iv[j], ii[j], vi, xi) ? 1 : 0;
+        ov[r] = vi;
+        oi[r] = xi;
     }
+    __syncthreads();
+}
+
+// Slot of this lane's entry in an LDS list whose length is *count (one
+// atomic per wave), or -1 when the lane keeps nothing.
+__device__ inline int wave_reserve(bool keep, int* count) {
+    const unsigned long long m = __ballot(keep);
+    if (m == 0) return -1;
+    const int lead = __ffsll((long long)m) - 1;
+    int base = 0;
+    if ((int)(threadIdx.x % kWave) == lead) base = atomicAdd(count, __popcll(m));
+    base = __shfl(base, lead, kWave);
+    const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    return keep ? base + below : -1;
 }
 
 // Block-wide exclusive scan of one int per thread; returns this thread's
@@ -254,9 +258,10 @@ __device__ inline int block_excl_scan(int x, int* scratch /* kWaves + 1 */, int*
     return base + incl - x;
 }
 
-// In-place inclusive prefix sum of w[0, n), n <= kKeptCap: eight consecutive
-// entries per thread in order, then across threads.
-__device__ void block_inclusive_scan(float* w, int n, float* red) {
+// Inclusive prefix sum of in[0, n) into out[0, n) (in == out allowed),
+// n <= kKeptCap: eight consecutive entries per thread in order, then across
+// threads.
+__device__ void block_inclusive_scan(const float* in, float* w, int n, float* red) {
     constexpr int per = kKeptCap / kBlock;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int base = threadIdx.x * per;
@@ -264,7 +269,7 @@ __device__ void block_inclusive_scan(float* w, int n, float* red) {
     float run = 0.f;
 #pragma unroll
     for (int j = 0; j < per; ++j) {
-        run += base + j < n ? w[base + j] : 0.f;
+        run += base + j < n ? in[base + j] : 0.f;
         loc[j] = run;
     }
     const float incl = wave_scan_incl(run);
@@ -363,6 +368,58 @@ __device__ unsigned select_kth_key(const Args& a, long long rowid, int total, fl
 // of that key range.
 __device__ inline float key_value(unsigned key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Value whose order key (order_key<BF16>, so bf16 keys are 16 bits) is key.
+template <bool BF16>
+__device__ inline float value_of_key(unsigned key) {
+    if (BF16) {
+        const unsigned k32 = key << 16;
+        return __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7fffffffu) : (~k32 & 0xffff0000u));
+    }
+    return key_value(key);
+}
+
+// Order key of the K-th largest (with multiplicity) of the finite values
+// v[0, n) in LDS, 1 <= K <= n: a radix select over 8-bit digits from the top
+// (two passes for bf16 keys, four for float32).  v must be visible to the
+// block; the result is returned to every thread.
+template <bool BF16>
+__device__ unsigned lds_select_kth(const float* v, int n, int K, TruncScratch& sc) {
+    constexpr int KB = BF16 ? 16 : 32;
+    const int tid = threadIdx.x;
+    __shared__ unsigned sSel;
+    __shared__ int sNeed;
+    if (tid == 0) {
+        sSel = 0;
+        sNeed = K;
+    }
+#pragma unroll 1
+    for (int pass = 0; pass < KB / 8; ++pass) {
+        const int shift = KB - 8 * (pass + 1);
+        __syncthreads();                                    // sSel / sNeed set, hist free
+        sc.hist[tid] = 0;                                   // kBlock == 256 bins
+        __syncthreads();
+        // read before any thread updates them below (after the scan's barriers)
+        const unsigned sel = sSel;
+        const int need = sNeed;
+        for (int i = tid; i < n; i += kBlock) {
+            const unsigned key = order_key<BF16>(v[i]);
+            if (pass == 0 || (key >> (shift + 8)) == sel) atomicAdd(&sc.hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        // bin t holds hist[t]; entries in bins >= t: all - (entries in bins < t)
+        const int h = (int)sc.hist[tid];
+        int all;
+        const int below = block_excl_scan(h, sc.misc, &all);
+        const int ge = all - below;
+        if (ge >= need && ge - h < need) {                  // exactly one thread
+            sSel = (sel << 8) | (unsigned)tid;
+            sNeed = need - (ge - h);
+        }
+    }
+    __syncthreads();
+    return sSel;
 }
 
 // Candidates of one chunk (whole workgroup) held in registers: every finite
@@ -537,12 +594,12 @@ __device__ TruncRow row_merge(const Args& a, int b, int k, int side, const Plan&
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (cv[q].v >= L && finite_logit(cv[q].v) && order_key<BF16>(cv[q].v) >= min_key) {
-                    const int pos = atomicAdd(&sN, 1);
-                    if (pos < kKeptCap) {
-                        sc.v[pos] = cv[q].v;
-                        sc.idx[pos] = cv[q].idx;
-                    }
+                const bool keep =
+                    cv[q].v >= L && finite_logit(cv[q].v) && order_key<BF16>(cv[q].v) >= min_key;
+                const int pos = wave_reserve(keep, &sN);
+                if (pos >= 0 && pos < kKeptCap) {
+                    sc.v[pos] = cv[q].v;
+                    sc.idx[pos] = cv[q].idx;
                 }
             }
         }
@@ -574,28 +631,29 @@ __device__ TruncRow row_merge(const Args& a, int b, int k, int side, const Plan&
         __syncthreads();
         return sOut;
     }
-    // sort the gathered entries: value desc, index asc
-    const int n2 = pow2_at_least(n1);
-    for (int i = n1 + tid; i < n2; i += kBlock) {
-        sc.v[i] = -kInf;
-        sc.idx[i] = 0x7fffffff;
-    }
-    __syncthreads();
-    bitonic_sort(sc.v, sc.idx, n2, by_value);
-    // top-k: the K-th largest (with multiplicity) ends the kept prefix; all
-    // entries equal to it are kept
+    // top-k: the K-th largest value (with multiplicity) ends the kept set,
+    // and every entry equal to it is kept; those entries are moved to
+    // (w, idx2), then sorted into (v, idx): value desc, index asc
     const int K = min(pl.keff, n1);
-    const float tk = sc.v[K - 1];
-    // count of entries >= tk (a prefix of the sorted list)
+    const float tk = K < n1 ? value_of_key<BF16>(lds_select_kth<BF16>(sc.v, n1, K, sc)) : -kInf;
     int cnt = 0;
     for (int i = tid; i < n1; i += kBlock) cnt += sc.v[i] >= tk;
     int nk1;
-    (void)block_excl_scan(cnt, sc.misc, &nk1);
+    int o = block_excl_scan(cnt, sc.misc, &nk1);
+    for (int i = tid; i < n1; i += kBlock) {
+        if (sc.v[i] >= tk) {
+            sc.w[o] = sc.v[i];
+            sc.idx2[o] = sc.idx[i];
+            ++o;
+        }
+    }
+    __syncthreads();
+    rank_sort(sc.w, sc.idx2, nk1, sc.v, sc.idx, by_value);
     const float zmax = sc.v[0];
     const float scale = pl.scale;
     for (int i = tid; i < nk1; i += kBlock) sc.w[i] = fast_exp2(__fmul_rn(sc.v[i] - zmax, scale));
     __syncthreads();
-    block_inclusive_scan(sc.w, nk1, sc.red);
+    block_inclusive_scan(sc.w, sc.w, nk1, sc.red);
     if (tid == 0) {
         // normaliser of the top-k-renormalised softmax: the kept top-k set, or
         // the whole row when top-k is off
@@ -772,27 +830,21 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
         // the correction mass vanished: sample from p at that position
         for (int i = tid; i < n; i += kBlock) sc.v[i] = sc.w[i];
     }
-    // tokens in ascending index order, then the first running sum > u * W
-    const int n2 = pow2_at_least(n);
-    for (int i = n + tid; i < n2; i += kBlock) {
-        sc.v[i] = 0.f;
-        sc.idx[i] = 0x7fffffff;
-    }
     __syncthreads();
-    bitonic_sort(sc.v, sc.idx, n2, by_index);
-    for (int i = tid; i < n; i += kBlock) sc.w[i] = sc.v[i];
-    __syncthreads();
-    block_inclusive_scan(sc.w, n, sc.red);
-    const float target = u * sc.w[n - 1];
+    // weights in ascending token order into (w, idx2), running sums into v,
+    // then the first running sum > u * W
+    rank_sort(sc.v, sc.idx, n, sc.w, sc.idx2, by_index);
+    block_inclusive_scan(sc.w, sc.v, n, sc.red);
+    const float target = u * sc.v[n - 1];
     for (int i = tid; i < n; i += kBlock) {
-        if (sc.v[i] > 0.f) {
-            if (sc.w[i] > target) atomicMin(&sTok, i);
+        if (sc.w[i] > 0.f) {
+            if (sc.v[i] > target) atomicMin(&sTok, i);
             atomicMax(&sLastPos, i);
         }
     }
     __syncthreads();
     const int j = sTok != 0x7fffffff ? sTok : sLastPos;     // clamp: last positive weight
-    const int tok = j >= 0 ? sc.idx[j] : -1;
+    const int tok = j >= 0 ? sc.idx2[j] : -1;
     __syncthreads();
     return tok;
 }
