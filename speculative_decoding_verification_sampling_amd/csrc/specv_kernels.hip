@@ -118,7 +118,7 @@ struct PairVals {
 // truncated rows draw their token here from the kept lists, and sampling rows
 // hand the draw to their sampling workgroups through the row record.
 template <bool BF16, bool TRUNC, int PROP>
-__device__ void finish_row(const Args& a, int b, int k, const PairVals& own, const Plan& pl,
+__device__ __forceinline__ void finish_row(const Args& a, int b, int k, const PairVals& own, const Plan& pl,
                            unsigned long long st, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const Res r = resolve(st, pl, a.gamma);
@@ -254,7 +254,7 @@ __device__ void finish_row(const Args& a, int b, int k, const PairVals& own, con
 // so its stores need not complete first, except for truncated rows, whose
 // kept lists and TruncRows are read untagged.
 template <bool BF16, bool TRUNC, int PROP>
-__device__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncScratch* sc) {
+__device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const Plan& pl, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
@@ -613,7 +613,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
 constexpr int kSkipFrom = SPECV_SKIP_FROM;
 
 template <bool BF16, bool VEC, bool TRUNC, int PROP>
-__device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc) {
+__device__ __forceinline__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const unsigned par = a.epoch & 1u;
     const bool check = k >= kSkipFrom;
@@ -674,10 +674,9 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
                           a.epoch);
         }
     } else {
-#pragma unroll
-        for (int side = 0; side < 2; ++side) {
-            if (side == 1 && !two) break;
-            const ChunkRegs<BF16, VEC>& r = side == 0 ? rt : rd;
+        // one call per side on its own registers (selecting between rt and
+        // rd by reference would put both in private memory)
+        auto side_stats = [&](int side, const ChunkRegs<BF16, VEC>& r) {
             float m, s;
             wave_chunk_ms(r, scale, m, s);
             if (lane == 0) {
@@ -687,7 +686,9 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
             if constexpr (TRUNC) {
                 if (trunc) chunk_candidates<BF16>(a, side_row(a, b, k, side), c, pl.keff, r, *sc);
             }
-        }
+        };
+        side_stats(0, rt);
+        if (two) side_stats(1, rd);
         __syncthreads();
         if (tid == 0) {
             for (int side = 0; side < (two ? 2 : 1); ++side) {
@@ -707,7 +708,7 @@ __device__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc
 // stopped at, or of the bonus row, and takes part in the sample.  Rows of
 // other modes never need one.
 template <bool BF16, bool VEC, int PROP>
-__device__ void sample_item(const Args& a, int b, int c) {
+__device__ __forceinline__ void sample_item(const Args& a, int b, int c) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const Plan pl = make_plan(a, b);
     if (pl.mode != MODE_SAMPLE) return;

@@ -519,7 +519,7 @@ __device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff
 // keeps n_kept > 0 entries, sc.v / sc.idx [0, n_kept) also hold the kept
 // list (value descending, index ascending) on return.
 template <bool BF16>
-__device__ TruncRow row_merge(const Args& a, int b, int k, int side, const Plan& pl,
+__device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int side, const Plan& pl,
                               TruncScratch& sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const long long rowid = side_row(a, b, k, side);
