@@ -139,6 +139,22 @@ __device__ inline int chunk_index(int k) {
     return ((k / G) * kBlock + (int)threadIdx.x) * G + (k % G);
 }
 
+// w[i] for a per-lane index i, by a tree of selects over the register array
+// (indexing it directly would put the array in private memory).
+template <int N>
+__device__ inline unsigned pick_word(const unsigned (&w)[N], int i) {
+    unsigned t[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) t[j] = w[j];
+#pragma unroll
+    for (int s = 1; s < N; s <<= 1) {
+        const bool hi = (i & s) != 0;
+#pragma unroll
+        for (int j = 0; j + s < N; j += 2 * s) t[j] = hi ? t[j + s] : t[j];
+    }
+    return t[0];
+}
+
 // One chunk of one logits row held in registers, in chunk_index's layout;
 // entries past the row's end read as -inf.
 //   VEC:  packed 16-byte groups (bfloat16: 8 entries, float32: 4); every
@@ -209,6 +225,23 @@ struct ChunkRegs<BF16, true> {
             return __uint_as_float(e == 0 ? g.x : e == 1 ? g.y : e == 2 ? g.z : g.w);
         }
     }
+    // entry i for a per-lane i
+    __device__ inline float elem_dyn(int i) const {
+        unsigned w[4 * NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            w[4 * j] = q[j].x;
+            w[4 * j + 1] = q[j].y;
+            w[4 * j + 2] = q[j].z;
+            w[4 * j + 3] = q[j].w;
+        }
+        if constexpr (BF16) {
+            const unsigned x = pick_word(w, i >> 1);
+            return (i & 1) ? bf16_hi(x) : bf16_lo(x);
+        } else {
+            return __uint_as_float(pick_word(w, i));
+        }
+    }
 };
 
 template <bool BF16>
@@ -234,6 +267,12 @@ struct ChunkRegs<BF16, false> {
         for (int k = 0; k < kPerThread; ++k) y[k] = x[k];
     }
     __device__ inline float elem(int i) const { return x[i]; }
+    __device__ inline float elem_dyn(int i) const {
+        unsigned w[kPerThread];
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) w[k] = __float_as_uint(x[k]);
+        return __uint_as_float(pick_word(w, i));
+    }
 };
 
 // Merge (m, s) statistics: s is relative to m in units of exp2(. * scale).

@@ -683,12 +683,14 @@ __device__ __forceinline__ void stream_unit(const Args& a, int k, int b, int c, 
                 sm[side][wave] = m;
                 ss[side][wave] = s;
             }
-            if constexpr (TRUNC) {
-                if (trunc) chunk_candidates<BF16>(a, side_row(a, b, k, side), c, pl.keff, r, *sc);
-            }
         };
         side_stats(0, rt);
         if (two) side_stats(1, rd);
+        if constexpr (TRUNC) {
+            if (trunc)
+                chunk_candidates_pair<BF16>(a, side_row(a, b, k, 0), side_row(a, b, k, 1), two, c, pl.keff,
+                                            rt, rd, *sc);
+        }
         __syncthreads();
         if (tid == 0) {
             for (int side = 0; side < (two ? 2 : 1); ++side) {

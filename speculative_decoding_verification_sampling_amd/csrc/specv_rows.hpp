@@ -199,21 +199,26 @@ __device__ inline Cand published_cand(const Cand* p) {
     return c;
 }
 
-// (value desc, index asc)
-__device__ inline bool by_value(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
-}
-// index asc
-__device__ inline bool by_index(float, int ia, float, int ib) { return ia < ib; }
+// Orders for rank_sort, without short-circuit evaluation (a branch there
+// would wait on each LDS load in turn).
+struct ByValue {      // value desc, index asc
+    __device__ bool operator()(float va, int ia, float vb, int ib) const {
+        return (va > vb) | ((va == vb) & (ia < ib));
+    }
+};
+struct ByIndex {      // index asc
+    __device__ bool operator()(float, int ia, float, int ib) const { return ia < ib; }
+};
 
 // Block-wide rank sort of (iv, ii) [0, n) into (ov, oi): entry x lands at
 // the number of entries y with prec(y, x), so prec must order the entries
-// strictly (by_value with distinct indices, by_index with distinct indices).
-// One pass of n comparisons per entry and a single barrier: for the short
-// lists here (the kept sets) it beats a bitonic network, whose log^2 n
-// barrier-separated stages dominate the row merge.  The inputs must be
-// visible to the block and must not alias the outputs; the result is
-// visible on return.
+// strictly (ByValue or ByIndex, with distinct indices).  One pass of n
+// comparisons per entry and a single barrier: for the short lists here (the
+// kept sets) it beats a bitonic network, whose log^2 n barrier-separated
+// stages dominate the row merge.  The inputs are kKeptCap-entry, 16-byte
+// aligned LDS arrays (read four entries at a time, up to n rounded up to a
+// multiple of four), visible to the block and not aliasing the outputs;
+// the result is visible on return.
 template <typename Prec>
 __device__ void rank_sort(const float* iv, const int* ii, int n, float* ov, int* oi, Prec prec) {
     for (int i = threadIdx.x; i < n; i += kBlock) {
@@ -221,7 +226,14 @@ __device__ void rank_sort(const float* iv, const int* ii, int n, float* ov, int*
         const int xi = ii[i];
         int r = 0;
 #pragma unroll 4
-        for (int j = 0; j < n; ++j) r += prec(iv[j], ii[j], vi, xi) ? 1 : 0;
+        for (int j = 0; j < n; j += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(iv + j);
+            const int4 i4 = *reinterpret_cast<const int4*>(ii + j);
+            r += (int)prec(v4.x, i4.x, vi, xi);
+            r += (int)((j + 1 < n) & prec(v4.y, i4.y, vi, xi));
+            r += (int)((j + 2 < n) & prec(v4.z, i4.z, vi, xi));
+            r += (int)((j + 3 < n) & prec(v4.w, i4.w, vi, xi));
+        }
         ov[r] = vi;
         oi[r] = xi;
     }
@@ -422,95 +434,171 @@ __device__ unsigned lds_select_kth(const float* v, int n, int K, TruncScratch& s
     return sSel;
 }
 
-// Candidates of one chunk (whole workgroup) held in registers: every finite
-// entry >= L, where L is a lower bound of the chunk's keff-th largest entry:
-// each thread keeps its top jj = ceil(2 keff / 256) <= 8 finite entries, so
-// at least keff chunk entries are >= the keff-th largest of those 256 jj
-// values; that value is found by a radix select (two 8-bit digits) over the
-// top 16 bits of the values' order keys, which for float32 rounds it down to
-// the start of its key range (still a lower bound).
-template <bool BF16, typename Regs>
-__device__ void chunk_candidates(const Args& a, long long rowid, int c, int keff, const Regs& r,
-                                 TruncScratch& sc) {
-    const int tid = threadIdx.x;
-    const int jj = min(8, (2 * keff + kBlock - 1) / kBlock);
+// Wave 0 of the workgroup: the bin t of the 256-bin histogram h (bins in
+// ascending key order) that holds the need-th largest entry: *sel = t and
+// *rest = need - (entries in the bins above t); *found = 0 when h holds
+// fewer than need entries.  h must be visible to the wave.
+__device__ inline void wave_find_bin(const unsigned* h, int need, unsigned* sel, int* rest,
+                                     int* found) {
+    const int lane = threadIdx.x % kWave;
+    const uint4 v = *reinterpret_cast<const uint4*>(h + 4 * lane);
+    const int cs[4] = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    const int own = cs[0] + cs[1] + cs[2] + cs[3];
+    const int incl = wave_scan_incl(own);
+    const int total = __shfl(incl, kWave - 1, kWave);
+    if (lane == 0 && total < need) *found = 0;
+    int ge = total - (incl - own);                          // entries in bins >= 4 * lane
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (ge >= need && ge - cs[e] < need) {              // exactly one lane and bin
+            *sel = (unsigned)(4 * lane + e);
+            *rest = need - (ge - cs[e]);
+        }
+        ge -= cs[e];
+    }
+}
+
+// This thread's top jj (<= 8) finite entries of a chunk as 16-bit order keys,
+// largest first (0: none).
+template <typename Regs>
+__device__ __forceinline__ void thread_top_keys(const Regs& r, int jj, unsigned (&k16)[8]) {
     float tp[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tp[j] = -kInf;                // this thread's top 8, desc
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        float v = r.elem(k);
-        if (!(finite_logit(v) && v > tp[7])) continue;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {                       // insertion, larger values first
-            if (v > tp[j]) {
-                const float s = tp[j];
-                tp[j] = v;
-                v = s;
-            }
-        }
-    }
-    // radix select of the keff-th largest 16-bit key among the jj tops
-    __shared__ unsigned sSel, sNeed;
-    __shared__ int sFound;
-    if (tid == 0) {
-        sSel = 0;
-        sNeed = (unsigned)keff;
-        sFound = 1;
-    }
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-        __syncthreads();                                    // sc may still be read; sSel set
-        sc.hist[tid] = 0;                                   // kBlock == 256 bins
-        __syncthreads();
-        // read before any thread updates them below (after the scan's barriers)
-        const unsigned sel = sSel;
-        const int need = (int)sNeed;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j < jj && finite_logit(tp[j])) {
-                const unsigned k16 = order_key<false>(tp[j]) >> 16;
-                if (pass == 0) atomicAdd(&sc.hist[k16 >> 8], 1u);
-                else if ((k16 >> 8) == sel) atomicAdd(&sc.hist[k16 & 255u], 1u);
-            }
-        }
-        __syncthreads();
-        // bin t holds hist[t]; entries in bins >= t: all - (entries in bins < t)
-        const int h = (int)sc.hist[tid];
-        int all;
-        const int below = block_excl_scan(h, sc.misc, &all);
-        const int ge = all - below;
-        if (all < need) {
-            if (tid == 0) sFound = 0;                       // fewer finite tops than keff
-        } else if (ge >= need && ge - h < need) {
-            // this bin holds the need-th largest: shared by exactly one thread
-            if (pass == 0) {
-                sSel = (unsigned)tid;
-                sNeed = (unsigned)(need - (ge - h));
-            } else {
-                sSel = (sSel << 8) | (unsigned)tid;
-            }
-        }
-    }
-    __syncthreads();
-    const float L = sFound ? key_value(sSel << 16) : -kInf;
-    int cnt = 0;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) cnt += finite_logit(r.elem(k)) && r.elem(k) >= L;
-    int total;
-    const int off = block_excl_scan(cnt, sc.misc, &total);
-    if (total <= a.cand_cap) {
-        Cand* dst = a.ws.cand + cand_base(a, rowid, c);
-        int o = off;
-        const int v0 = c * kChunk;
+    for (int j = 0; j < 8; ++j) tp[j] = -kInf;
+    if (jj == 1) {                                          // top_k <= 128: the maximum
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
-            const float x = r.elem(k);
-            if (finite_logit(x) && x >= L) publish_cand(dst + o++, x, v0 + chunk_index<BF16>(k));
+            const float v = r.elem(k);
+            if (finite_logit(v)) tp[0] = fmaxf(tp[0], v);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            float v = r.elem(k);
+            if (!(finite_logit(v) && v > tp[7])) continue;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {                   // insertion, larger values first
+                if (v > tp[j]) {
+                    const float t = tp[j];
+                    tp[j] = v;
+                    v = t;
+                }
+            }
         }
     }
-    if (tid == 0)
-        publish_cand(a.ws.cand_meta + rowid * a.C + c, L, total <= a.cand_cap ? total : -1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k16[j] = j < jj && finite_logit(tp[j]) ? order_key<false>(tp[j]) >> 16 : 0u;
+}
+
+// Publishes this thread's entries of a chunk that are finite and >= L into
+// dst (slots by a wave prefix sum and one LDS atomic per wave on *count; the
+// order within the list is immaterial); slots past cap are only counted.
+template <bool BF16, typename Regs>
+__device__ __forceinline__ void emit_candidates(const Regs& r, float L, Cand* dst, int cap, int v0,
+                                                int* count) {
+    const int lane = threadIdx.x % kWave;
+    unsigned kept = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const float x = r.elem(k);
+        kept |= (finite_logit(x) && x >= L) ? (1u << k) : 0u;
+    }
+    const int cnt = __popc(kept);
+    const int incl = wave_scan_incl(cnt);
+    int base = 0;
+    if (lane == kWave - 1) base = atomicAdd(count, incl);
+    base = __shfl(base, kWave - 1, kWave);
+    int o = base + incl - cnt;
+    while (kept) {
+        const int k = __ffs(kept) - 1;
+        kept &= kept - 1;
+        if (o < cap) publish_cand(dst + o, r.elem_dyn(k), v0 + chunk_index<BF16>(k));
+        ++o;
+    }
+}
+
+// Candidates of one chunk (whole workgroup) held in registers, for one row or
+// for two at once (a unit's target and draft rows share the barriers): every
+// finite entry >= L, where L is a lower bound of the chunk's keff-th largest
+// entry: each thread keeps its top jj = ceil(2 keff / 256) <= 8 finite
+// entries, so at least keff chunk entries are >= the keff-th largest of those
+// 256 jj values; that value is found by a radix select (two 8-bit digits,
+// each from an LDS histogram whose bin one wave finds) over the top 16 bits
+// of the values' order keys, which for float32 rounds it down to the start of
+// its key range (still a lower bound).  Row 1 (r1) is used only when two.
+template <bool BF16, typename Regs>
+__device__ __forceinline__ void chunk_candidates_pair(const Args& a, long long row0, long long row1, bool two, int c,
+                                      int keff, const Regs& r0, const Regs& r1, TruncScratch& sc) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int jj = min(8, (2 * keff + kBlock - 1) / kBlock);
+    unsigned ka[8], kb[8];
+    thread_top_keys(r0, jj, ka);
+    if (two) {
+        thread_top_keys(r1, jj, kb);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kb[j] = 0u;
+    }
+    // first digit: histograms h0a / h0b; second digit: h1a / h1b
+    unsigned* h0a = sc.hist;                                // kBlock == 256 bins each
+    unsigned* h1a = reinterpret_cast<unsigned*>(sc.idx2);
+    unsigned* h0b = h1a + 256;
+    unsigned* h1b = h1a + 512;
+    __shared__ unsigned sSel[2];
+    __shared__ int sRest[2], sFound[2], sCount[2];
+    __syncthreads();                                        // sc may still be read
+    h0a[tid] = 0;
+    h1a[tid] = 0;
+    h0b[tid] = 0;
+    h1b[tid] = 0;
+    if (tid < 2) {
+        sFound[tid] = 1;
+        sCount[tid] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (ka[j]) atomicAdd(&h0a[ka[j] >> 8], 1u);
+        if (kb[j]) atomicAdd(&h0b[kb[j] >> 8], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) wave_find_bin(h0a, keff, &sSel[0], &sRest[0], &sFound[0]);
+    else if (wave == 1 && two) wave_find_bin(h0b, keff, &sSel[1], &sRest[1], &sFound[1]);
+    __syncthreads();
+    // read before waves 0 / 1 update them below (after the next barrier)
+    const unsigned da = sSel[0], db = sSel[1];
+    const int na = sRest[0], nb = sRest[1];
+    const bool fa = sFound[0] != 0;                         // else fewer finite tops than keff
+    const bool fb = two && sFound[1] != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (fa && ka[j] && (ka[j] >> 8) == da) atomicAdd(&h1a[ka[j] & 255u], 1u);
+        if (fb && kb[j] && (kb[j] >> 8) == db) atomicAdd(&h1b[kb[j] & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0 && fa) wave_find_bin(h1a, na, &sSel[0], &sRest[0], &sFound[0]);
+    else if (wave == 1 && fb) wave_find_bin(h1b, nb, &sSel[1], &sRest[1], &sFound[1]);
+    __syncthreads();
+    const float La = fa ? key_value(((da << 8) | sSel[0]) << 16) : -kInf;
+    const float Lb = fb ? key_value(((db << 8) | sSel[1]) << 16) : -kInf;
+    const int v0 = c * kChunk;
+    emit_candidates<BF16>(r0, La, a.ws.cand + cand_base(a, row0, c), a.cand_cap, v0, &sCount[0]);
+    if (two) emit_candidates<BF16>(r1, Lb, a.ws.cand + cand_base(a, row1, c), a.cand_cap, v0, &sCount[1]);
+    __syncthreads();
+    if (tid == 0) {
+        const int total = sCount[0];
+        publish_cand(a.ws.cand_meta + row0 * a.C + c, La, total <= a.cand_cap ? total : -1);
+    } else if (two && tid == kWave) {
+        const int total = sCount[1];
+        publish_cand(a.ws.cand_meta + row1 * a.C + c, Lb, total <= a.cand_cap ? total : -1);
+    }
+}
+
+// One row's candidates of one chunk (see chunk_candidates_pair).
+template <bool BF16, typename Regs>
+__device__ inline void chunk_candidates(const Args& a, long long rowid, int c, int keff, const Regs& r,
+                                        TruncScratch& sc) {
+    chunk_candidates_pair<BF16>(a, rowid, rowid, false, c, keff, r, r, sc);
 }
 
 // Row-level truncation (whole workgroup) of logits row (b, k, side), once
@@ -648,7 +736,7 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         }
     }
     __syncthreads();
-    rank_sort(sc.w, sc.idx2, nk1, sc.v, sc.idx, by_value);
+    rank_sort(sc.w, sc.idx2, nk1, sc.v, sc.idx, ByValue{});
     const float zmax = sc.v[0];
     const float scale = pl.scale;
     for (int i = tid; i < nk1; i += kBlock) sc.w[i] = fast_exp2(__fmul_rn(sc.v[i] - zmax, scale));
@@ -833,7 +921,7 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     __syncthreads();
     // weights in ascending token order into (w, idx2), running sums into v,
     // then the first running sum > u * W
-    rank_sort(sc.v, sc.idx, n, sc.w, sc.idx2, by_index);
+    rank_sort(sc.v, sc.idx, n, sc.w, sc.idx2, ByIndex{});
     block_inclusive_scan(sc.w, sc.v, n, sc.red);
     const float target = u * sc.v[n - 1];
     for (int i = tid; i < n; i += kBlock) {
