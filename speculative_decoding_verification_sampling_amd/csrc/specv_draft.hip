@@ -108,7 +108,7 @@ __device__ void draw_truncated(const DraftArgs& a, const Args& va, int b, int i,
         sLast = -1;
     }
     __syncthreads();
-    rank_sort(sc.w, sc.idx, n, sc.v, sc.idx2, ByIndex{});   // weights in token order
+    rank_sort(sc.w, sc.idx, n, sc.v, sc.idx2, ByIndex{}, reinterpret_cast<int*>(sc.hist));   // weights in token order
     block_inclusive_scan(sc.v, sc.w, n, sc.red);            // running sums
     const float target = u * sc.w[n - 1];
     for (int j = tid; j < n; j += kBlock) {

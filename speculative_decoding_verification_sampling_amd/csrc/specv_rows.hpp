@@ -212,28 +212,59 @@ struct ByIndex {      // index asc
 
 // Block-wide rank sort of (iv, ii) [0, n) into (ov, oi): entry x lands at
 // the number of entries y with prec(y, x), so prec must order the entries
-// strictly (ByValue or ByIndex, with distinct indices).  One pass of n
-// comparisons per entry and a single barrier: for the short lists here (the
-// kept sets) it beats a bitonic network, whose log^2 n barrier-separated
-// stages dominate the row merge.  The inputs are kKeptCap-entry, 16-byte
-// aligned LDS arrays (read four entries at a time, up to n rounded up to a
-// multiple of four), visible to the block and not aliasing the outputs;
-// the result is visible on return.
+// strictly (ByValue or ByIndex, with distinct indices).  n comparisons per
+// entry, split over the waves for short lists (partial ranks summed through
+// part, kBlock ints of LDS): for the kept sets here it beats a bitonic
+// network, whose log^2 n barrier-separated stages dominate the row merge.
+// The inputs are kKeptCap-entry, 16-byte aligned LDS arrays (read four
+// entries at a time, up to n rounded up to a multiple of four), visible to
+// the block and not aliasing the outputs; the result is visible on return.
 template <typename Prec>
-__device__ void rank_sort(const float* iv, const int* ii, int n, float* ov, int* oi, Prec prec) {
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        const float vi = iv[i];
-        const int xi = ii[i];
-        int r = 0;
+__device__ void rank_sort(const float* iv, const int* ii, int n, float* ov, int* oi, Prec prec,
+                          int* part) {
+    const int J = n <= kWave ? 4 : (n <= 2 * kWave ? 2 : 1);     // comparison ranges per entry
+    if (J == 1) {
+        for (int i = threadIdx.x; i < n; i += kBlock) {
+            const float vi = iv[i];
+            const int xi = ii[i];
+            int r = 0;
 #pragma unroll 4
-        for (int j = 0; j < n; j += 4) {
+            for (int j = 0; j < n; j += 4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(iv + j);
+                const int4 i4 = *reinterpret_cast<const int4*>(ii + j);
+                r += (int)prec(v4.x, i4.x, vi, xi);
+                r += (int)((j + 1 < n) & prec(v4.y, i4.y, vi, xi));
+                r += (int)((j + 2 < n) & prec(v4.z, i4.z, vi, xi));
+                r += (int)((j + 3 < n) & prec(v4.w, i4.w, vi, xi));
+            }
+            ov[r] = vi;
+            oi[r] = xi;
+        }
+        __syncthreads();
+        return;
+    }
+    const int width = kBlock / J;                           // entries per range group
+    const int i = (int)threadIdx.x % width, g = (int)threadIdx.x / width;
+    const int len = (n + 4 * J - 1) / (4 * J) * 4;          // comparisons per range
+    const int j0 = g * len, j1 = min(n, j0 + len);
+    float vi = 0.f;
+    int xi = 0, r = 0;
+    if (i < n) {
+        vi = iv[i];
+        xi = ii[i];
+        for (int j = j0; j < j1; j += 4) {
             const float4 v4 = *reinterpret_cast<const float4*>(iv + j);
             const int4 i4 = *reinterpret_cast<const int4*>(ii + j);
             r += (int)prec(v4.x, i4.x, vi, xi);
-            r += (int)((j + 1 < n) & prec(v4.y, i4.y, vi, xi));
-            r += (int)((j + 2 < n) & prec(v4.z, i4.z, vi, xi));
-            r += (int)((j + 3 < n) & prec(v4.w, i4.w, vi, xi));
+            r += (int)((j + 1 < j1) & prec(v4.y, i4.y, vi, xi));
+            r += (int)((j + 2 < j1) & prec(v4.z, i4.z, vi, xi));
+            r += (int)((j + 3 < j1) & prec(v4.w, i4.w, vi, xi));
         }
+    }
+    part[threadIdx.x] = r;
+    __syncthreads();
+    if (g == 0 && i < n) {
+        for (int h = 1; h < J; ++h) r += part[h * width + i];
         ov[r] = vi;
         oi[r] = xi;
     }
@@ -392,48 +423,6 @@ __device__ inline float value_of_key(unsigned key) {
     return key_value(key);
 }
 
-// Order key of the K-th largest (with multiplicity) of the finite values
-// v[0, n) in LDS, 1 <= K <= n: a radix select over 8-bit digits from the top
-// (two passes for bf16 keys, four for float32).  v must be visible to the
-// block; the result is returned to every thread.
-template <bool BF16>
-__device__ unsigned lds_select_kth(const float* v, int n, int K, TruncScratch& sc) {
-    constexpr int KB = BF16 ? 16 : 32;
-    const int tid = threadIdx.x;
-    __shared__ unsigned sSel;
-    __shared__ int sNeed;
-    if (tid == 0) {
-        sSel = 0;
-        sNeed = K;
-    }
-#pragma unroll 1
-    for (int pass = 0; pass < KB / 8; ++pass) {
-        const int shift = KB - 8 * (pass + 1);
-        __syncthreads();                                    // sSel / sNeed set, hist free
-        sc.hist[tid] = 0;                                   // kBlock == 256 bins
-        __syncthreads();
-        // read before any thread updates them below (after the scan's barriers)
-        const unsigned sel = sSel;
-        const int need = sNeed;
-        for (int i = tid; i < n; i += kBlock) {
-            const unsigned key = order_key<BF16>(v[i]);
-            if (pass == 0 || (key >> (shift + 8)) == sel) atomicAdd(&sc.hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        // bin t holds hist[t]; entries in bins >= t: all - (entries in bins < t)
-        const int h = (int)sc.hist[tid];
-        int all;
-        const int below = block_excl_scan(h, sc.misc, &all);
-        const int ge = all - below;
-        if (ge >= need && ge - h < need) {                  // exactly one thread
-            sSel = (sel << 8) | (unsigned)tid;
-            sNeed = need - (ge - h);
-        }
-    }
-    __syncthreads();
-    return sSel;
-}
-
 // Wave 0 of the workgroup: the bin t of the 256-bin histogram h (bins in
 // ascending key order) that holds the need-th largest entry: *sel = t and
 // *rest = need - (entries in the bins above t); *found = 0 when h holds
@@ -456,6 +445,43 @@ __device__ inline void wave_find_bin(const unsigned* h, int need, unsigned* sel,
         }
         ge -= cs[e];
     }
+}
+
+// Order key of the K-th largest (with multiplicity) of the finite values
+// v[0, n) in LDS, 1 <= K <= n: a radix select over 8-bit digits from the top
+// (two passes for bf16 keys, four for float32), one histogram per digit in
+// sc.idx2, each bin found by wave 0.  v must be visible to the block; the
+// result is returned to every thread.
+template <bool BF16>
+__device__ unsigned lds_select_kth(const float* v, int n, int K, TruncScratch& sc) {
+    constexpr int NP = BF16 ? 2 : 4;
+    constexpr int KB = 8 * NP;
+    const int tid = threadIdx.x, wave = tid / kWave;
+    unsigned* h = reinterpret_cast<unsigned*>(sc.idx2);
+    __shared__ unsigned sSel;
+    __shared__ int sRest, sFound;
+    __syncthreads();                                        // sc.idx2 may still be read
+#pragma unroll
+    for (int p = 0; p < NP; ++p) h[p * 256 + tid] = 0;      // kBlock == 256 bins
+    __syncthreads();
+    unsigned prefix = 0;
+    int need = K;
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int shift = KB - 8 * (pass + 1);
+        unsigned* hp = h + 256 * pass;
+        for (int i = tid; i < n; i += kBlock) {
+            const unsigned key = order_key<BF16>(v[i]);
+            if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&hp[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) wave_find_bin(hp, need, &sSel, &sRest, &sFound);
+        __syncthreads();
+        // read before wave 0 updates them (after the next pass's barrier)
+        prefix = (prefix << 8) | sSel;
+        need = sRest;
+    }
+    return prefix;
 }
 
 // This thread's top jj (<= 8) finite entries of a chunk as 16-bit order keys,
@@ -613,9 +639,30 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
     const long long rowid = side_row(a, b, k, side);
     __shared__ float sL, sM, sS, sZ1;
     __shared__ unsigned sBad, sFlags;
-    __shared__ int sTotal, sN, sJ, sLevelStart;
+    __shared__ int sTotal, sN, sJ, sLevelStart, sMaxCnt;
     __shared__ TruncRow sOut;
     unsigned* off = sc.off;                // chunk offsets [0, C]
+    // slots [0, S) of every chunk's list are read before the lists' lengths
+    // are known, in the same memory round trip (S about 1.5 keff, which
+    // covers the usual list of a little over keff; longer lists are finished
+    // afterwards); slot p is (chunk p / S, entry p % S)
+    const int S = min(a.cand_cap, max(64, (3 * pl.keff / 2 + 15) & ~15));
+    const int nspec = a.C * S;
+    const float invS = 1.f / (float)S;
+    const Cand* cbase = a.ws.cand + cand_base(a, rowid, 0);
+    auto slot_chunk = [&](int p) {          // p / S, exact for p < 2^24
+        int c = (int)((float)p * invS);
+        c -= c * S > p;
+        c += (c + 1) * S <= p;
+        return c;
+    };
+    auto spec_load = [&](int p) {
+        const int c = slot_chunk(p);
+        return p < nspec ? published_cand(cbase + (long long)c * a.cand_cap + (p - c * S)) : Cand{-kInf, 0};
+    };
+    Cand cv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cv[q] = spec_load(q * kBlock + tid);
     __syncthreads();                       // shared state may still be read
     if (tid == 0) {
         sBad = 0;
@@ -649,6 +696,8 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
             off[a.C] = (unsigned)incl;
             sTotal = incl;
         }
+        const int mc = wave_max_int(cnt);
+        if (lane == 0) sMaxCnt = mc;
         const unsigned long long any_ovf = __ballot(ovf);
         if (lane == 0) {
             sL = L;
@@ -672,28 +721,56 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
     // gather the candidates >= max L into LDS
     const float L = sL;
     const int total = sTotal;
-    auto gather = [&](unsigned min_key) {
+    auto take = [&](const Cand& x, bool listed, unsigned min_key) {
+        const bool keep = listed && x.v >= L && finite_logit(x.v) && order_key<BF16>(x.v) >= min_key;
+        const int pos = wave_reserve(keep, &sN);
+        if (pos >= 0 && pos < kKeptCap) {
+            sc.v[pos] = x.v;
+            sc.idx[pos] = x.idx;
+        }
+    };
+    for (int p0 = 0;;) {                   // the speculative slots, 8 per thread a round
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int p = p0 + q * kBlock + tid;
+            const int c = min(slot_chunk(p), a.C - 1);
+            take(cv[q], p < nspec && p - c * S < (int)(off[c + 1] - off[c]), 0u);
+        }
+        p0 += 8 * kBlock;
+        if (p0 >= nspec) break;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cv[q] = spec_load(p0 + q * kBlock + tid);
+    }
+    // all of a row's candidates from slot ``from`` of each list on
+    auto gather = [&](unsigned min_key, int from) {
         for (int f0 = 0; f0 < total; f0 += 4 * kBlock) {
-            Cand cv[4];
+            Cand cw[4];
+            bool in[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int f = f0 + q * kBlock + tid;
-                cv[q] = f < total ? row_candidate(a, rowid, off, f) : Cand{-kInf, 0};
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bool keep =
-                    cv[q].v >= L && finite_logit(cv[q].v) && order_key<BF16>(cv[q].v) >= min_key;
-                const int pos = wave_reserve(keep, &sN);
-                if (pos >= 0 && pos < kKeptCap) {
-                    sc.v[pos] = cv[q].v;
-                    sc.idx[pos] = cv[q].idx;
+                in[q] = false;
+                cw[q] = Cand{-kInf, 0};
+                if (f < total) {
+                    int lo = 0, hi = a.C - 1;  // chunk c with off[c] <= f < off[c + 1]
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if ((int)off[mid] <= f) lo = mid;
+                        else hi = mid - 1;
+                    }
+                    if (f - (int)off[lo] >= from) {
+                        in[q] = true;
+                        cw[q] = published_cand(a.ws.cand + cand_base(a, rowid, lo) + (f - (int)off[lo]));
+                    }
                 }
             }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) take(cw[q], in[q], min_key);
         }
         __syncthreads();
     };
-    gather(0u);
+    if (sMaxCnt > S) gather(0u, S);        // lists longer than the slots read
+    else __syncthreads();
     if (sN > kKeptCap) {
         // too many candidates above the chunk bounds: select the exact top-k
         // key over them in global memory, then keep only entries >= it
@@ -701,7 +778,7 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         const unsigned kkey = select_kth_key<BF16>(a, rowid, total, L, K, sc);
         if (tid == 0) sN = 0;
         __syncthreads();
-        gather(kkey);
+        gather(kkey, 0);
     }
     const int n1 = sN;
     if (n1 > kKeptCap && tid == 0) sFlags |= SPECV_FLAG_CAND_OVERFLOW;
@@ -736,7 +813,7 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         }
     }
     __syncthreads();
-    rank_sort(sc.w, sc.idx2, nk1, sc.v, sc.idx, ByValue{});
+    rank_sort(sc.w, sc.idx2, nk1, sc.v, sc.idx, ByValue{}, reinterpret_cast<int*>(sc.hist));
     const float zmax = sc.v[0];
     const float scale = pl.scale;
     for (int i = tid; i < nk1; i += kBlock) sc.w[i] = fast_exp2(__fmul_rn(sc.v[i] - zmax, scale));
@@ -921,7 +998,7 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     __syncthreads();
     // weights in ascending token order into (w, idx2), running sums into v,
     // then the first running sum > u * W
-    rank_sort(sc.v, sc.idx, n, sc.w, sc.idx2, ByIndex{});
+    rank_sort(sc.v, sc.idx, n, sc.w, sc.idx2, ByIndex{}, reinterpret_cast<int*>(sc.hist));
     block_inclusive_scan(sc.w, sc.v, n, sc.red);
     const float target = u * sc.v[n - 1];
     for (int i = tid; i < n; i += kBlock) {
