@@ -1,13 +1,17 @@
-"""Static guard on the gfx950 code of the verify and draft-sampler kernels (CPU only).
+"""Static guards on the gfx950 code of the verify and draft-sampler kernels (CPU only).
 
-A cross-lane read ``v_readlane_b32 sD, vS, sIdx`` returns lane sIdx of vS
-whatever EXEC holds.  When the compiler spills vS and reloads it inside a
-branch that only some lanes take, the reload (``scratch_load``) writes the
-active lanes alone, and a read of another lane returns stale data.  An index
-taken from such a read once sent a load out of bounds.  The kernels now read
-such values with uniform loads; this test compiles them to assembly and fails
-if any dynamically indexed ``v_readlane`` reads a VGPR whose last definition
-(in program order) is a scratch reload.
+1. A cross-lane read ``v_readlane_b32 sD, vS, sIdx`` returns lane sIdx of vS
+   whatever EXEC holds.  When the compiler spills vS and reloads it inside a
+   branch that only some lanes take, the reload (``scratch_load``) writes the
+   active lanes alone, and a read of another lane returns stale data.  An
+   index taken from such a read once sent a load out of bounds.  The kernels
+   now read such values with uniform loads; the test fails if any dynamically
+   indexed ``v_readlane`` reads a VGPR whose last definition (in program
+   order) is a scratch reload.
+2. No kernel uses private memory or makes a call.  When the compiler keeps a
+   large step out of line, it copies the whole argument block to private
+   memory and reads every field from there.  On the truncation kernels that
+   cost a third of their time.
 """
 
 import os
@@ -87,18 +91,47 @@ def test_checker_finds_the_fault_pattern():
     assert stale_lane_reads(asm) == [("kern", "v_readlane_b32 s20, v88, s3")]
 
 
-@pytest.mark.skipif(shutil.which(specv_build.hipcc()) is None and not os.path.exists(specv_build.hipcc()),
-                    reason="hipcc not available")
-@pytest.mark.parametrize("source,kernel", [("specv_kernels.hip", "k_verify"),
-                                           ("specv_draft.hip", "k_sample_draft")])
-def test_no_dynamic_lane_read_of_a_spill_reload(tmp_path, source, kernel):
+@pytest.fixture(scope="module", params=[("specv_kernels.hip", "k_verify"),
+                                        ("specv_draft.hip", "k_sample_draft")])
+def compiled(request, tmp_path_factory):
+    """(kernel name stem, gfx950 assembly) of one source."""
+    if shutil.which(specv_build.hipcc()) is None and not os.path.exists(specv_build.hipcc()):
+        pytest.skip("hipcc not available")
+    source, kernel = request.param
     src = os.path.join(os.path.dirname(specv_build.__file__), "csrc", source)
-    out = tmp_path / "kernels.s"
+    tmp = tmp_path_factory.mktemp("isa")
+    out = tmp / "kernels.s"
     flags = [f for f in specv_build.FLAGS if f not in ("-shared", "-fPIC")]
     cmd = [specv_build.hipcc(), *flags, "-I", specv_build.INCLUDE, "-I", os.path.dirname(src),
            "--offload-device-only", "-S", src, "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True, cwd=str(tmp_path))
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=str(tmp))
     assert r.returncode == 0, r.stderr[-2000:]
     asm = out.read_text()
     assert kernel in asm
+    return kernel, asm
+
+
+def test_no_dynamic_lane_read_of_a_spill_reload(compiled):
+    _, asm = compiled
     assert stale_lane_reads(asm) == []
+
+
+def private_use(asm):
+    """(kernel, private bytes per lane) of kernels with private memory, and
+    the number of call instructions."""
+    sizes = re.findall(r"\.name:\s+(\S+)\s*\n\s+\.private_segment_fixed_size:\s+(\d+)", asm)
+    return [(n, int(v)) for n, v in sizes if int(v) > 0], len(re.findall(r"\bs_swappc_b64\b", asm))
+
+
+def test_private_use_checker():
+    asm = ("    .name:           kern_a\n    .private_segment_fixed_size: 0\n"
+           "    .name:           kern_b\n    .private_segment_fixed_size: 368\n"
+           "\ts_swappc_b64 s[30:31], s[0:1]\n")
+    assert private_use(asm) == ([("kern_b", 368)], 1)
+
+
+def test_kernels_use_no_private_memory_and_make_no_calls(compiled):
+    kernel, asm = compiled
+    pairs = re.findall(r"\.name:\s+\S+\s*\n\s+\.private_segment_fixed_size:", asm)
+    assert len(pairs) >= 4, "kernel metadata not found"
+    assert private_use(asm) == ([], 0)
