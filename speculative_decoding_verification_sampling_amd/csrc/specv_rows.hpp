@@ -813,6 +813,91 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         }
     }
     __syncthreads();
+    if (nk1 <= kWave) {
+        // the usual short list (top-k of a few dozen): one wave sorts, scans
+        // and cuts it with cross-lane operations, lane i holding entry i
+        if (wave == 0) {
+            const bool in = lane < nk1;
+            const float vi = in ? sc.w[lane] : -kInf;
+            const int xi = in ? sc.idx2[lane] : 0x7fffffff;
+            int r = lane;                               // lanes past the list keep their place
+            if (in) r = 0;
+            for (int j = 0; j < nk1; ++j) {             // rank: value desc, index asc
+                const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vi), j));
+                const int xj = __builtin_amdgcn_readlane(xi, j);
+                r += (int)(in & ByValue{}(vj, xj, vi, xi));
+            }
+            const float v = __int_as_float(__builtin_amdgcn_ds_permute(r * 4, __float_as_int(vi)));
+            const int x = __builtin_amdgcn_ds_permute(r * 4, xi);
+            const float zmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+            const float scale = pl.scale;
+            const float w = in ? fast_exp2(__fmul_rn(v - zmax, scale)) : 0.f;
+            const float cum = wave_scan_incl(w);
+            const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), nk1 - 1));
+            // normaliser of the top-k-renormalised softmax: the kept top-k
+            // set, or the whole row when top-k is off
+            const float Z1 = pl.kmode ? last : sS * fast_exp2(__fmul_rn(sM - zmax, scale));
+            unsigned flags = sFlags;
+            int jstar = nk1 - 1;
+            bool none = false;
+            if (pl.top_p < 1.f) {
+                // first level end whose cumulative mass reaches top_p
+                const float vnext = __shfl(v, lane + 1 < kWave ? lane + 1 : lane, kWave);
+                const bool level_end = in && (lane == nk1 - 1 || vnext != v);
+                const unsigned long long hit = __ballot(level_end && cum / Z1 >= pl.top_p);
+                if (hit) jstar = __ffsll((long long)hit) - 1;
+                else none = !pl.kmode;                  // top-p alone: candidates short of top_p
+                if (!none) {
+                    const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), jstar));
+                    const unsigned long long lvl = __ballot(in && lane <= jstar && v == tv);
+                    const int ls = __ffsll((long long)lvl) - 1;
+                    const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), jstar)) / Z1;
+                    const float pv = ls > 0
+                        ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), ls > 0 ? ls - 1 : 0)) / Z1
+                        : 0.f;
+                    if (fabsf(cj - pl.top_p) < 1e-5f || (ls > 0 && fabsf(pv - pl.top_p) < 1e-5f))
+                        flags |= SPECV_FLAG_TOPP_NEAR;
+                }
+            }
+            if (none) {
+                flags |= SPECV_FLAG_CAND_OVERFLOW;
+                if (lane == 0) {
+                    sOut.bad = 0;
+                    sOut.flags = flags;
+                    sOut.n_kept = 0;
+                    publish(&tr->bad, 0u);
+                    publish(&tr->flags, flags);
+                    publish(&tr->n_kept, 0);
+                }
+            } else {
+                const int nkept = jstar + 1;
+                const float tstar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), jstar));
+                const float S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), jstar));
+                Cand* kept = a.ws.kept + rowid * a.kept_cap;
+                if (lane < nkept) {
+                    publish_cand(kept + lane, v, x);
+                    sc.v[lane] = v;                     // the kept list, for the caller
+                    sc.idx[lane] = x;
+                }
+                if (lane == 0) {
+                    sOut.zmax = zmax;
+                    sOut.tstar = tstar;
+                    sOut.S = S;
+                    sOut.n_kept = nkept;
+                    sOut.flags = flags;
+                    sOut.bad = 0;
+                    publish(&tr->zmax, zmax);
+                    publish(&tr->tstar, tstar);
+                    publish(&tr->S, S);
+                    publish(&tr->n_kept, nkept);
+                    publish(&tr->flags, flags);
+                    publish(&tr->bad, 0u);
+                }
+            }
+        }
+        __syncthreads();
+        return sOut;
+    }
     rank_sort(sc.w, sc.idx2, nk1, sc.v, sc.idx, ByValue{}, reinterpret_cast<int*>(sc.hist));
     const float zmax = sc.v[0];
     const float scale = pl.scale;
@@ -956,6 +1041,60 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     const Cand* kept = a.ws.kept + side_row(a, b, pos, 0) * a.kept_cap;
     const int dpm = res && pm ? draft_token(a, b, pos) : -1;
     const void* qrow = res && !pm ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+    if (n <= kWave) {
+        // a short kept list: one wave weighs, orders by token, scans and
+        // picks, lane i holding entry i
+        if (tid < kWave) {
+            const int lane = tid;
+            const bool in = lane < n;
+            float p = 0.f, w = 0.f;
+            int x = 0x7fffffff;
+            if (in) {
+                const Cand cv = published_cand(kept + lane);
+                x = cv.idx;
+                p = __fmul_rn(fast_exp2(__fmul_rn(cv.v - tT.zmax, scale)), 1.f / tT.S);
+                w = p;
+                if (res) {
+                    float q;
+                    if (pm) {
+                        q = cv.idx == dpm ? 1.f : 0.f;
+                    } else {
+                        const float zq = load_elem<BF16>(qrow, cv.idx);
+                        q = (finite_logit(zq) && zq >= tQ.tstar)
+                                ? __fmul_rn(fast_exp2(__fmul_rn(zq - tQ.zmax, scale)), 1.f / tQ.S)
+                                : 0.f;
+                    }
+                    w = fmaxf(__fsub_rn(p, q), 0.f);
+                }
+            }
+            const float W = wave_sum(w);
+            const bool fb = res && (!(W > 0.f) || !__builtin_isfinite(W));
+            if (fb) w = p;                          // the correction mass vanished: p
+            int r = lane;                           // lanes past the list keep their place
+            if (in) r = 0;
+            for (int j = 0; j < n; ++j) r += (int)(in & (__builtin_amdgcn_readlane(x, j) < x));
+            const float ws = __int_as_float(__builtin_amdgcn_ds_permute(r * 4, __float_as_int(w)));
+            const int xs = __builtin_amdgcn_ds_permute(r * 4, x);
+            const float cum = wave_scan_incl(ws);
+            const float target = u * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), n - 1));
+            const unsigned long long pos = __ballot(lane < n && ws > 0.f);
+            const unsigned long long hit = __ballot(lane < n && ws > 0.f && cum > target);
+            // the first running sum > u W; clamp: the last positive weight
+            const int j = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll(pos) : -1);
+            const int tok = j >= 0 ? __builtin_amdgcn_readlane(xs, j) : -1;
+            if (lane == 0) {
+                sTok = tok;
+                sWsum = W;
+                sFb = fb ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        *wres = res ? sWsum : 0.f;
+        *fallback = sFb != 0;
+        const int tok = sTok;
+        __syncthreads();
+        return tok;
+    }
     // sc.v = weight, sc.idx = token, sc.w = p (fallback weight)
     float part = 0.f;
     for (int i = tid; i < n; i += kBlock) {
