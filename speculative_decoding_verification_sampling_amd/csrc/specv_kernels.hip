@@ -274,9 +274,18 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
     const int d = test ? draft_token(a, b, k) : 0;
     if (trunc) {
         if constexpr (TRUNC) {
-            const TruncRow t0 = row_merge<BF16>(a, b, k, 0, pl, *sc);
-            TruncRow t1 = t0;
-            if (two) t1 = row_merge<BF16>(a, b, k, 1, pl, *sc);
+            // both rows in lockstep when they take the usual path, else one
+            // after the other
+            __shared__ TruncRow dPair[2];
+            TruncRow t0, t1;
+            if (two && row_merge_pair<BF16>(a, b, k, pl, *sc, dPair)) {
+                t0 = dPair[0];
+                t1 = dPair[1];
+            } else {
+                t0 = row_merge<BF16>(a, b, k, 0, pl, *sc);
+                t1 = t0;
+                if (two) t1 = row_merge<BF16>(a, b, k, 1, pl, *sc);
+            }
             if (tid == 0) {
                 dT[0] = t0;
                 dT[1] = qs && qside ? stats_trow(a.qstats[(long long)b * a.qs_sb + k]) : t1;

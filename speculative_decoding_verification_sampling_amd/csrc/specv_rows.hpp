@@ -627,6 +627,289 @@ __device__ inline void chunk_candidates(const Args& a, long long rowid, int c, i
     chunk_candidates_pair<BF16>(a, rowid, rowid, false, c, keff, r, r, sc);
 }
 
+// One wave (lane i holding entry i): the kept set of a row from its
+// candidates at or above the top-k threshold, (cw, cx)[0, n) with
+// 1 <= n <= 64, with cross-lane operations and no block barriers: rank
+// (value desc, index asc) by lane reads, order by ds_permute, DPP scan, cut
+// at top-p by ballots.  Publishes the kept list and the row's TruncRow,
+// leaves the sorted kept list in (kv, kx)[0, n_kept) and the TruncRow in
+// *out (lane 0).  rowM / rowS: the whole row's statistics (for top-p alone);
+// flags: flags found so far.
+__device__ __forceinline__ void short_merge_wave(const Args& a, long long rowid, const Plan& pl,
+                                                 const float* cw, const int* cx, int n, float rowM,
+                                                 float rowS, unsigned flags, float* kv, int* kx,
+                                                 TruncRow* out) {
+    const int lane = threadIdx.x % kWave;
+    TruncRow* tr = &a.ws.trow[rowid];
+    const bool in = lane < n;
+    const float vi = in ? cw[lane] : -kInf;
+    const int xi = in ? cx[lane] : 0x7fffffff;
+    int r = lane;                                   // lanes past the list keep their place
+    if (in) r = 0;
+    for (int j = 0; j < n; ++j) {                   // rank: value desc, index asc
+        const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vi), j));
+        const int xj = __builtin_amdgcn_readlane(xi, j);
+        r += (int)(in & ByValue{}(vj, xj, vi, xi));
+    }
+    const float v = __int_as_float(__builtin_amdgcn_ds_permute(r * 4, __float_as_int(vi)));
+    const int x = __builtin_amdgcn_ds_permute(r * 4, xi);
+    const float zmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+    const float scale = pl.scale;
+    const float w = in ? fast_exp2(__fmul_rn(v - zmax, scale)) : 0.f;
+    const float cum = wave_scan_incl(w);
+    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), n - 1));
+    // normaliser of the top-k-renormalised softmax: the kept top-k set, or
+    // the whole row when top-k is off
+    const float Z1 = pl.kmode ? last : rowS * fast_exp2(__fmul_rn(rowM - zmax, scale));
+    int jstar = n - 1;
+    bool none = false;
+    if (pl.top_p < 1.f) {
+        // first level end whose cumulative mass reaches top_p
+        const float vnext = __shfl(v, lane + 1 < kWave ? lane + 1 : lane, kWave);
+        const bool level_end = in && (lane == n - 1 || vnext != v);
+        const unsigned long long hit = __ballot(level_end && cum / Z1 >= pl.top_p);
+        if (hit) jstar = __ffsll((long long)hit) - 1;
+        else none = !pl.kmode;                      // top-p alone: candidates short of top_p
+        if (!none) {
+            const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), jstar));
+            const unsigned long long lvl = __ballot(in && lane <= jstar && v == tv);
+            const int ls = __ffsll((long long)lvl) - 1;
+            const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), jstar)) / Z1;
+            const float pv =
+                ls > 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), ls > 0 ? ls - 1 : 0)) / Z1
+                       : 0.f;
+            if (fabsf(cj - pl.top_p) < 1e-5f || (ls > 0 && fabsf(pv - pl.top_p) < 1e-5f))
+                flags |= SPECV_FLAG_TOPP_NEAR;
+        }
+    }
+    if (none) {
+        flags |= SPECV_FLAG_CAND_OVERFLOW;
+        if (lane == 0) {
+            TruncRow o{};
+            o.zmax = -kInf;
+            o.tstar = kInf;
+            o.flags = flags;
+            *out = o;
+            publish(&tr->bad, 0u);
+            publish(&tr->flags, flags);
+            publish(&tr->n_kept, 0);
+        }
+        return;
+    }
+    const int nkept = jstar + 1;
+    const float tstar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), jstar));
+    const float S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), jstar));
+    Cand* kept = a.ws.kept + rowid * a.kept_cap;
+    if (lane < nkept) {
+        publish_cand(kept + lane, v, x);
+        kv[lane] = v;
+        kx[lane] = x;
+    }
+    if (lane == 0) {
+        TruncRow o{};
+        o.zmax = zmax;
+        o.tstar = tstar;
+        o.S = S;
+        o.n_kept = nkept;
+        o.flags = flags;
+        o.bad = 0;
+        *out = o;
+        publish(&tr->zmax, zmax);
+        publish(&tr->tstar, tstar);
+        publish(&tr->S, S);
+        publish(&tr->n_kept, nkept);
+        publish(&tr->flags, flags);
+        publish(&tr->bad, 0u);
+    }
+}
+
+// Both rows of pair (b, k), target (side 0) and draft (side 1), merged in
+// lockstep: every step of row_merge for the two rows shares the barriers,
+// and the one-wave kept-set steps run on waves 0 and 1 at once.  Only the
+// usual case is taken (top-k <= 64, no candidate overflow, every list within
+// its first S slots, at most kKeptCap / 2 gathered and 64 kept per row);
+// otherwise it returns false having published nothing, and the caller merges
+// the rows one at a time.  On true, out[0] / out[1] hold the rows'
+// TruncRows (as row_merge returns them) for every thread.
+template <bool BF16>
+__device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, const Plan& pl,
+                                               TruncScratch& sc, TruncRow* out) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    if (pl.keff > kWave) return false;
+    constexpr int kHalf = kKeptCap / 2;
+    const long long row0 = side_row(a, b, k, 0), row1 = side_row(a, b, k, 1);
+    __shared__ float pL[2], pM[2], pS[2];
+    __shared__ int pN[2], pMaxCnt[2], pTotal[2];
+    __shared__ unsigned pBad;
+    __shared__ unsigned pOff[2][kMaxChunks + 1];
+    __shared__ TruncRow pOut[2];
+    // slots [0, S) of both rows' chunk lists, read with the lists' lengths
+    const int S = min(a.cand_cap, max(64, (3 * pl.keff / 2 + 15) & ~15));
+    const int nspec = a.C * S;
+    const float invS = 1.f / (float)S;
+    auto slot_chunk = [&](int p) {          // p / S, exact for p < 2^24
+        int c = (int)((float)p * invS);
+        c -= c * S > p;
+        c += (c + 1) * S <= p;
+        return c;
+    };
+    auto spec_load = [&](int p) {           // p over both rows: side p / nspec
+        const int side = p >= nspec ? 1 : 0;
+        const int ps = p - side * nspec;
+        const int c = slot_chunk(ps);
+        const Cand* base = a.ws.cand + cand_base(a, side ? row1 : row0, c);
+        return p < 2 * nspec ? published_cand(base + (ps - c * S)) : Cand{-kInf, 0};
+    };
+    constexpr int NQ = 12;                  // slots per thread a round
+    Cand cv[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) cv[q] = spec_load(q * kBlock + tid);
+    if (tid == 0) {                         // (one call per workgroup)
+        pBad = 0;
+        pN[0] = pN[1] = 0;
+    }
+    __syncthreads();
+    // lengths and bounds (waves 0, 2) and row statistics (waves 1, 3)
+    {
+        const int side = wave >> 1;
+        const long long rowid = side ? row1 : row0;
+        if ((wave & 1) == 0) {
+            float L = -kInf;
+            int cnt = 0;
+            bool ovf = false;
+            if (lane < a.C) {
+                const Cand m = published_cand(a.ws.cand_meta + rowid * a.C + lane);
+                L = m.v;
+                ovf = m.idx < 0;
+                cnt = ovf ? 0 : m.idx;
+            }
+            L = wave_max(L);
+            const int incl = wave_scan_incl(cnt);
+            if (lane < a.C) pOff[side][lane] = (unsigned)(incl - cnt);
+            if (lane == a.C - 1) {
+                pOff[side][a.C] = (unsigned)incl;
+                pTotal[side] = incl;
+            }
+            const int mc = wave_max_int(cnt);
+            const unsigned long long any_ovf = __ballot(ovf);
+            if (lane == 0) {
+                pL[side] = L;
+                pMaxCnt[side] = mc;
+                if (any_ovf) atomicOr(&pBad, 1u);
+            }
+        } else {
+            float m = -kInf, sm = 0.f;
+            if (lane < a.C) {
+                unsigned sw = 0;
+                (void)published_stats(stats_words(a, b, k, side, lane), a.epoch, m, sw);
+                sm = __uint_as_float(sw);
+            }
+            wave_merge_ms(m, sm, pl.scale);
+            if (lane == 0) {
+                pM[side] = m;
+                pS[side] = sm;
+                if (__builtin_isnan(sm) || m == -kInf) atomicOr(&pBad, 1u);
+            }
+        }
+    }
+    __syncthreads();
+    if (pBad || pMaxCnt[0] > S || pMaxCnt[1] > S) return false;
+    // gather both rows' candidates >= their max L into the halves of (v, idx)
+    for (int p0 = 0;;) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int p = p0 + q * kBlock + tid;
+            const int side = p >= nspec ? 1 : 0;
+            const int ps = p - side * nspec;
+            const int c = min(slot_chunk(ps), a.C - 1);
+            const bool listed = p < 2 * nspec && ps - c * S < (int)(pOff[side][c + 1] - pOff[side][c]);
+            const bool keep = listed && cv[q].v >= pL[side] && finite_logit(cv[q].v);
+            // one reservation per side, so that every lane takes part in both
+            const int pos0 = wave_reserve(keep && side == 0, &pN[0]);
+            const int pos1 = wave_reserve(keep && side == 1, &pN[1]);
+            const int pos = side ? pos1 : pos0;
+            if (pos >= 0 && pos < kHalf) {
+                sc.v[side * kHalf + pos] = cv[q].v;
+                sc.idx[side * kHalf + pos] = cv[q].idx;
+            }
+        }
+        p0 += NQ * kBlock;
+        if (p0 >= 2 * nspec) break;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) cv[q] = spec_load(p0 + q * kBlock + tid);
+    }
+    __syncthreads();
+    const int n[2] = {pN[0], pN[1]};
+    if (n[0] == 0 || n[1] == 0 || n[0] > kHalf || n[1] > kHalf) return false;
+    // the top-k threshold of each row: radix select over 8-bit digits, both
+    // rows per pass (histograms in idx2: row r, digit d at (r * NP + d) * 256)
+    constexpr int NP = BF16 ? 2 : 4;
+    constexpr int KB = 8 * NP;
+    unsigned* h = reinterpret_cast<unsigned*>(sc.idx2);
+    __shared__ unsigned pSel[2];
+    __shared__ int pRest[2], pFound[2];
+#pragma unroll
+    for (int d = 0; d < 2 * NP; ++d) h[d * 256 + tid] = 0;
+    __syncthreads();
+    unsigned prefix[2] = {0u, 0u};
+    int need[2] = {min(pl.keff, n[0]), min(pl.keff, n[1])};
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int shift = KB - 8 * (pass + 1);
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            unsigned* hp = h + (side * NP + pass) * 256;
+            for (int i = tid; i < n[side]; i += kBlock) {
+                const unsigned key = order_key<BF16>(sc.v[side * kHalf + i]);
+                if (pass == 0 || (key >> (shift + 8)) == prefix[side]) atomicAdd(&hp[(key >> shift) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        if (wave < 2)
+            wave_find_bin(h + (wave * NP + pass) * 256, wave ? need[1] : need[0], &pSel[wave], &pRest[wave],
+                          &pFound[wave]);
+        __syncthreads();
+        // read before waves 0 / 1 update them (after the next pass's barrier)
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            prefix[side] = (prefix[side] << 8) | pSel[side];
+            need[side] = pRest[side];
+        }
+    }
+    const float tk[2] = {value_of_key<BF16>(prefix[0]), value_of_key<BF16>(prefix[1])};
+    // the entries at or above each threshold, into the halves of (w, idx2);
+    // both counts scanned at once (row 1's in the high 16 bits)
+    int cnt = 0;
+#pragma unroll
+    for (int side = 0; side < 2; ++side)
+        for (int i = tid; i < n[side]; i += kBlock) cnt += (sc.v[side * kHalf + i] >= tk[side]) << (16 * side);
+    int tot;
+    const int o = block_excl_scan(cnt, sc.misc, &tot);
+    const int nk[2] = {tot & 0xffff, tot >> 16};
+    if (nk[0] > kWave || nk[1] > kWave) return false;
+    int oo[2] = {o & 0xffff, o >> 16};
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+        for (int i = tid; i < n[side]; i += kBlock) {
+            const float x = sc.v[side * kHalf + i];
+            if (x >= tk[side]) {
+                sc.w[side * kHalf + oo[side]] = x;
+                sc.idx2[side * kHalf + oo[side]] = sc.idx[side * kHalf + i];
+                ++oo[side];
+            }
+        }
+    }
+    __syncthreads();
+    if (wave < 2)
+        short_merge_wave(a, wave ? row1 : row0, pl, sc.w + wave * kHalf, sc.idx2 + wave * kHalf, wave ? nk[1] : nk[0],
+                         pM[wave], pS[wave], 0u, sc.v + wave * kHalf, sc.idx + wave * kHalf, &pOut[wave]);
+    __syncthreads();
+    out[0] = pOut[0];
+    out[1] = pOut[1];
+    __syncthreads();
+    return true;
+}
+
 // Row-level truncation (whole workgroup) of logits row (b, k, side), once
 // every chunk's candidates are published.  Publishes the kept list and the
 // row's TruncRow, and returns the TruncRow to every thread; when the row
@@ -814,87 +1097,8 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
     }
     __syncthreads();
     if (nk1 <= kWave) {
-        // the usual short list (top-k of a few dozen): one wave sorts, scans
-        // and cuts it with cross-lane operations, lane i holding entry i
-        if (wave == 0) {
-            const bool in = lane < nk1;
-            const float vi = in ? sc.w[lane] : -kInf;
-            const int xi = in ? sc.idx2[lane] : 0x7fffffff;
-            int r = lane;                               // lanes past the list keep their place
-            if (in) r = 0;
-            for (int j = 0; j < nk1; ++j) {             // rank: value desc, index asc
-                const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vi), j));
-                const int xj = __builtin_amdgcn_readlane(xi, j);
-                r += (int)(in & ByValue{}(vj, xj, vi, xi));
-            }
-            const float v = __int_as_float(__builtin_amdgcn_ds_permute(r * 4, __float_as_int(vi)));
-            const int x = __builtin_amdgcn_ds_permute(r * 4, xi);
-            const float zmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
-            const float scale = pl.scale;
-            const float w = in ? fast_exp2(__fmul_rn(v - zmax, scale)) : 0.f;
-            const float cum = wave_scan_incl(w);
-            const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), nk1 - 1));
-            // normaliser of the top-k-renormalised softmax: the kept top-k
-            // set, or the whole row when top-k is off
-            const float Z1 = pl.kmode ? last : sS * fast_exp2(__fmul_rn(sM - zmax, scale));
-            unsigned flags = sFlags;
-            int jstar = nk1 - 1;
-            bool none = false;
-            if (pl.top_p < 1.f) {
-                // first level end whose cumulative mass reaches top_p
-                const float vnext = __shfl(v, lane + 1 < kWave ? lane + 1 : lane, kWave);
-                const bool level_end = in && (lane == nk1 - 1 || vnext != v);
-                const unsigned long long hit = __ballot(level_end && cum / Z1 >= pl.top_p);
-                if (hit) jstar = __ffsll((long long)hit) - 1;
-                else none = !pl.kmode;                  // top-p alone: candidates short of top_p
-                if (!none) {
-                    const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), jstar));
-                    const unsigned long long lvl = __ballot(in && lane <= jstar && v == tv);
-                    const int ls = __ffsll((long long)lvl) - 1;
-                    const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), jstar)) / Z1;
-                    const float pv = ls > 0
-                        ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), ls > 0 ? ls - 1 : 0)) / Z1
-                        : 0.f;
-                    if (fabsf(cj - pl.top_p) < 1e-5f || (ls > 0 && fabsf(pv - pl.top_p) < 1e-5f))
-                        flags |= SPECV_FLAG_TOPP_NEAR;
-                }
-            }
-            if (none) {
-                flags |= SPECV_FLAG_CAND_OVERFLOW;
-                if (lane == 0) {
-                    sOut.bad = 0;
-                    sOut.flags = flags;
-                    sOut.n_kept = 0;
-                    publish(&tr->bad, 0u);
-                    publish(&tr->flags, flags);
-                    publish(&tr->n_kept, 0);
-                }
-            } else {
-                const int nkept = jstar + 1;
-                const float tstar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), jstar));
-                const float S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), jstar));
-                Cand* kept = a.ws.kept + rowid * a.kept_cap;
-                if (lane < nkept) {
-                    publish_cand(kept + lane, v, x);
-                    sc.v[lane] = v;                     // the kept list, for the caller
-                    sc.idx[lane] = x;
-                }
-                if (lane == 0) {
-                    sOut.zmax = zmax;
-                    sOut.tstar = tstar;
-                    sOut.S = S;
-                    sOut.n_kept = nkept;
-                    sOut.flags = flags;
-                    sOut.bad = 0;
-                    publish(&tr->zmax, zmax);
-                    publish(&tr->tstar, tstar);
-                    publish(&tr->S, S);
-                    publish(&tr->n_kept, nkept);
-                    publish(&tr->flags, flags);
-                    publish(&tr->bad, 0u);
-                }
-            }
-        }
+        // the usual short list (top-k of a few dozen): one wave
+        if (wave == 0) short_merge_wave(a, rowid, pl, sc.w, sc.idx2, nk1, sM, sS, sFlags, sc.v, sc.idx, &sOut);
         __syncthreads();
         return sOut;
     }
