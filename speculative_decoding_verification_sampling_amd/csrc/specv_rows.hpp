@@ -178,7 +178,9 @@ __device__ inline void write_outputs_wave(const Args& a, int b, int nemit, int n
 //                entries at or above it are sorted (value desc, index asc)
 //                and scanned for top-p: the first level whose cumulative
 //                mass reaches top_p ends the kept set (ties at a level all
-//                kept);
+//                kept); a pair's target and draft rows go through these steps
+//                in lockstep when both take the usual path, and a list of at
+//                most 64 entries is sorted, scanned and cut by one wave;
 //   per batch row: the accept tests use the kept sets, and the correction /
 //                bonus sample is drawn from the (short) kept list of the
 //                sampled row, tokens in ascending index order.
