@@ -612,6 +612,9 @@ __device__ __forceinline__ void chunk_candidates_pair(const Args& a, long long r
     const int v0 = c * kChunk;
     emit_candidates<BF16>(r0, La, a.ws.cand + cand_base(a, row0, c), a.cand_cap, v0, &sCount[0]);
     if (two) emit_candidates<BF16>(r1, Lb, a.ws.cand + cand_base(a, row1, c), a.cand_cap, v0, &sCount[1]);
+    // a barrier does not wait for other waves' stores: each wave completes
+    // its own, so that the lists are out before the unit's arrival is counted
+    wait_stores();
     __syncthreads();
     if (tid == 0) {
         const int total = sCount[0];
@@ -707,6 +710,7 @@ __device__ __forceinline__ void short_merge_wave(const Args& a, long long rowid,
         kv[lane] = v;
         kx[lane] = x;
     }
+    wait_stores();                                  // out before the decision is published
     if (lane == 0) {
         TruncRow o{};
         o.zmax = zmax;
@@ -1159,6 +1163,7 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
     const int nkept = jstar + 1;
     Cand* kept = a.ws.kept + rowid * a.kept_cap;
     for (int i = tid; i < nkept; i += kBlock) publish_cand(kept + i, sc.v[i], sc.idx[i]);
+    wait_stores();                         // every wave's entries out before the decision
     __syncthreads();
     if (tid == 0) {
         sOut.zmax = zmax;
