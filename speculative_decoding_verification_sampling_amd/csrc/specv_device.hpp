@@ -440,10 +440,12 @@ __device__ inline bool published_stats(const unsigned long long* w, unsigned epo
 //   wave_chunk_argmax: max and lowest index of the max (v0 + chunk index), and
 //                      whether an entry is NaN or +inf.
 template <typename Regs>
-__device__ __forceinline__ void wave_chunk_ms(const Regs& r, float scale, float& m, float& s) {
+__device__ __forceinline__ void wave_chunk_ms(const Regs& r, float scale, float& m, float& s,
+                                              float* thread_max = nullptr) {
     float cm = -kInf;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) cm = fmaxf(cm, r.elem(i));
+    if (thread_max) *thread_max = cm;           // this thread's maximum (NaN ignored)
     const float nms = cm == -kInf ? 0.f : -cm * scale;
     s = 0.f;
 #pragma unroll

@@ -685,20 +685,21 @@ __device__ __forceinline__ void stream_unit(const Args& a, int k, int b, int c, 
     } else {
         // one call per side on its own registers (selecting between rt and
         // rd by reference would put both in private memory)
-        auto side_stats = [&](int side, const ChunkRegs<BF16, VEC>& r) {
+        auto side_stats = [&](int side, const ChunkRegs<BF16, VEC>& r, float& tmax) {
             float m, s;
-            wave_chunk_ms(r, scale, m, s);
+            wave_chunk_ms(r, scale, m, s, &tmax);
             if (lane == 0) {
                 sm[side][wave] = m;
                 ss[side][wave] = s;
             }
         };
-        side_stats(0, rt);
-        if (two) side_stats(1, rd);
+        float tmax0 = -kInf, tmax1 = -kInf;     // the threads' maxima, the top-k tops when k <= 128
+        side_stats(0, rt, tmax0);
+        if (two) side_stats(1, rd, tmax1);
         if constexpr (TRUNC) {
             if (trunc)
                 chunk_candidates_pair<BF16>(a, side_row(a, b, k, 0), side_row(a, b, k, 1), two, c, pl.keff,
-                                            rt, rd, *sc);
+                                            rt, rd, *sc, true, tmax0, tmax1);
         }
         __syncthreads();
         if (tid == 0) {

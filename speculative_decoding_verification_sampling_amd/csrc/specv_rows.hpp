@@ -554,18 +554,29 @@ __device__ __forceinline__ void emit_candidates(const Regs& r, float L, Cand* ds
 // each from an LDS histogram whose bin one wave finds) over the top 16 bits
 // of the values' order keys, which for float32 rounds it down to the start of
 // its key range (still a lower bound).  Row 1 (r1) is used only when two.
+// max0 / max1: the threads' maxima from the statistics pass when given
+// (have_max), used as the tops when jj = 1 (a non-finite maximum means no
+// finite top, or a row the merge rejects as bad).
 template <bool BF16, typename Regs>
 __device__ __forceinline__ void chunk_candidates_pair(const Args& a, long long row0, long long row1, bool two, int c,
-                                      int keff, const Regs& r0, const Regs& r1, TruncScratch& sc) {
+                                      int keff, const Regs& r0, const Regs& r1, TruncScratch& sc,
+                                      bool have_max = false, float max0 = 0.f, float max1 = 0.f) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int jj = min(8, (2 * keff + kBlock - 1) / kBlock);
     unsigned ka[8], kb[8];
-    thread_top_keys(r0, jj, ka);
-    if (two) {
-        thread_top_keys(r1, jj, kb);
-    } else {
+    if (have_max && jj == 1) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kb[j] = 0u;
+        for (int j = 0; j < 8; ++j) ka[j] = kb[j] = 0u;
+        ka[0] = finite_logit(max0) ? order_key<false>(max0) >> 16 : 0u;
+        if (two) kb[0] = finite_logit(max1) ? order_key<false>(max1) >> 16 : 0u;
+    } else {
+        thread_top_keys(r0, jj, ka);
+        if (two) {
+            thread_top_keys(r1, jj, kb);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kb[j] = 0u;
+        }
     }
     // first digit: histograms h0a / h0b; second digit: h1a / h1b
     unsigned* h0a = sc.hist;                                // kBlock == 256 bins each
