@@ -274,6 +274,27 @@ SPECV_API specv_status specv_verify_greedy(specv_handle h, void* stream,
 SPECV_API specv_status specv_set_profiling(specv_handle h, int enable);
 SPECV_API specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms_kernel);
 
+/* The per-call kernel durations behind specv_get_profile: waits for the
+ * recorded events, then copies the first min(max_samples, recorded) of the
+ * per-call milliseconds since the last reset (at most 65536 are kept) to the
+ * host array ms_out and their number to *n_out.  Does not reset.  Errors:
+ * SPECV_E_NULL (h or n_out NULL, or ms_out NULL with max_samples > 0),
+ * SPECV_E_HIP. */
+SPECV_API specv_status specv_get_profile_samples(specv_handle h, int max_samples, float* ms_out,
+                                                 int* n_out);
+
+/* Measurement aid, no part of the verify step: one streaming read of the
+ * device buffer buf (bytes, a multiple of 16, 16-byte aligned) by ``grid``
+ * workgroups of 16-byte loads, the load shape of the verify kernels; each
+ * workgroup writes the XOR of what it read to sink[blockIdx] (device,
+ * uint32 [grid]) so that the read cannot be elided.  Timing it gives the
+ * device's one-pass read rate, the ceiling the verify kernels are compared
+ * with.  Asynchronous on ``stream``; allocates nothing.  Errors: SPECV_E_NULL,
+ * SPECV_E_SHAPE (bytes < 16 or not a multiple of 16, grid < 1),
+ * SPECV_E_ALIGN, SPECV_E_HIP. */
+SPECV_API specv_status specv_read_ceiling(void* stream, const void* buf, int64_t bytes, int grid,
+                                          uint32_t* sink);
+
 /* Free the workspace and the handle.  Waits for the device first.  NULL is
  * accepted. */
 SPECV_API specv_status specv_destroy(specv_handle h);

@@ -54,7 +54,12 @@ E[N] against the closed form of the ICML summary and the tutorial's printed
 E(4), E(8) at alpha = 0.7, chi-square tests of the emitted distribution, and
 the greedy path against ``torch.argmax``; the drafter's draw by exact
 enumeration against ``torch.softmax``, its statistics against
-``torch.logsumexp``.
+``torch.logsumexp``; ``cdf_interval`` against brute force on exact dyadic
+grids (the interval of t is exactly the set of uniforms for which
+``inverse_cdf`` returns t), and the reported residual sum against the
+reject mass of 11.1.3 (0.2 on the worked example; 1 - sum min(p, q) at the
+stopping position, with p and q from ``torch.softmax``)
+(``tests/test_oracle_interval_residual.py``).
 """
 
 import numpy as np
@@ -135,7 +140,7 @@ def _sample_row(b, trow, drow, toks, T, k, p, cap, eos_id, seed, step, keep_weig
     p_at = np.full(gamma, np.nan)
     q_at = np.full(gamma, np.nan)
     W_out = 0.0
-    ev = {"accept_tests": [], "sample": None}
+    ev = {"accept_tests": [], "sample": None, "topp_near": []}
     for i in range(gamma):
         if len(emitted) >= cap:
             return emitted, n_acc, flags, p_at, q_at, W_out, ev
@@ -145,6 +150,7 @@ def _sample_row(b, trow, drow, toks, T, k, p, cap, eos_id, seed, step, keep_weig
             return [], 0, flags | FLAG_NONFINITE_ROW, p_at, q_at, 0.0, ev
         if P.topp_near or Q.topp_near:
             flags |= FLAG_TOPP_NEAR
+            ev["topp_near"].append(i)
         d = int(toks[i])
         pd, qd = P.probs[d], Q.probs[d]
         p_at[i], q_at[i] = pd, qd
@@ -179,6 +185,7 @@ def _sample_row(b, trow, drow, toks, T, k, p, cap, eos_id, seed, step, keep_weig
         return [], 0, flags | FLAG_NONFINITE_ROW, p_at, q_at, 0.0, ev
     if P.topp_near:
         flags |= FLAG_TOPP_NEAR
+        ev["topp_near"].append(gamma)
     u3 = float(uniform(seed, b, gamma, PURPOSE_BONUS, step))
     t = inverse_cdf(P.probs, u3)
     ev["sample"] = {"kind": "bonus", "pos": gamma, "u": u3, "W": float(P.probs.sum()),
@@ -197,7 +204,7 @@ def _point_mass_row(b, trow, toks, T, k, p, cap, eos_id, seed, step, keep_weight
     p_at = np.full(gamma, np.nan)
     q_at = np.full(gamma, np.nan)
     W_out = 0.0
-    ev = {"accept_tests": [], "sample": None}
+    ev = {"accept_tests": [], "sample": None, "topp_near": []}
     for i in range(gamma):
         if len(emitted) >= cap:
             return emitted, n_acc, flags, p_at, q_at, W_out, ev
@@ -206,6 +213,7 @@ def _point_mass_row(b, trow, toks, T, k, p, cap, eos_id, seed, step, keep_weight
             return [], 0, flags | FLAG_NONFINITE_ROW, p_at, q_at, 0.0, ev
         if P.topp_near:
             flags |= FLAG_TOPP_NEAR
+            ev["topp_near"].append(i)
         d = int(toks[i])
         delta = np.zeros_like(P.probs)
         delta[d] = 1.0                        # q_i: all mass on the proposed token
@@ -239,6 +247,7 @@ def _point_mass_row(b, trow, toks, T, k, p, cap, eos_id, seed, step, keep_weight
         return [], 0, flags | FLAG_NONFINITE_ROW, p_at, q_at, 0.0, ev
     if P.topp_near:
         flags |= FLAG_TOPP_NEAR
+        ev["topp_near"].append(gamma)
     u3 = float(uniform(seed, b, gamma, PURPOSE_BONUS, step))
     t = inverse_cdf(P.probs, u3)
     ev["sample"] = {"kind": "bonus", "pos": gamma, "u": u3, "W": float(P.probs.sum()),
@@ -301,12 +310,12 @@ def verify_sample(target, draft, tokens, temperature, top_k, top_p, max_new_toke
         toks = tokens[b]
         if ((toks < 0) | (toks >= V)).any():
             results.append(([], 0, FLAG_TOKEN_OOR, np.full(gamma, np.nan),
-                            np.full(gamma, np.nan), 0.0, {"accept_tests": [], "sample": None}))
+                            np.full(gamma, np.nan), 0.0, {"accept_tests": [], "sample": None, "topp_near": []}))
             continue
         if T[b] == 0.0:
             em, na, fl = _greedy_row(target[b], toks, caps[b], eos_id)
             results.append((em, na, fl, np.full(gamma, np.nan), np.full(gamma, np.nan), 0.0,
-                            {"accept_tests": [], "sample": None}))
+                            {"accept_tests": [], "sample": None, "topp_near": []}))
             continue
         results.append(_sample_row(b, target[b], draft[b], toks, T[b], K[b], Pp[b], caps[b],
                                    eos_id, seed, step, keep_weights))
@@ -333,12 +342,12 @@ def verify_point_mass(target, tokens, temperature, top_k, top_p, max_new_tokens,
         toks = tokens[b]
         if ((toks < 0) | (toks >= V)).any():
             results.append(([], 0, FLAG_TOKEN_OOR, np.full(gamma, np.nan),
-                            np.full(gamma, np.nan), 0.0, {"accept_tests": [], "sample": None}))
+                            np.full(gamma, np.nan), 0.0, {"accept_tests": [], "sample": None, "topp_near": []}))
             continue
         if T[b] == 0.0:
             em, na, fl = _greedy_row(target[b], toks, caps[b], eos_id)
             results.append((em, na, fl, np.full(gamma, np.nan), np.full(gamma, np.nan), 0.0,
-                            {"accept_tests": [], "sample": None}))
+                            {"accept_tests": [], "sample": None, "topp_near": []}))
             continue
         results.append(_point_mass_row(b, target[b], toks, T[b], K[b], Pp[b], caps[b], eos_id,
                                        seed, step, keep_weights))
@@ -361,7 +370,7 @@ def verify_greedy(target, tokens, max_new_tokens=0, eos_id=-1):
         else:
             em, na, fl = _greedy_row(target[b], toks, caps[b], eos_id)
         results.append((em, na, fl, np.full(gamma, np.nan), np.full(gamma, np.nan), 0.0,
-                        {"accept_tests": [], "sample": None}))
+                        {"accept_tests": [], "sample": None, "topp_near": []}))
     return _finish(results, B, gamma)
 
 

@@ -34,6 +34,7 @@ __all__ = [
     "FLAG_UNSUPPORTED",
     "FLAG_INTERNAL",
     "EXPORTED_SYMBOLS",
+    "read_ceiling",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,7 +54,7 @@ SPECV_BF16 = 1
 EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_point_mass",
                     "specv_verify_sample_qstats", "specv_sample_draft", "specv_verify_greedy",
                     "specv_destroy", "specv_status_string", "specv_set_profiling",
-                    "specv_get_profile")
+                    "specv_get_profile", "specv_get_profile_samples", "specv_read_ceiling")
 
 
 class SpecvError(RuntimeError):
@@ -145,6 +146,11 @@ def load_library():
     lib.specv_get_profile.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                       ctypes.POINTER(ctypes.c_double)]
     lib.specv_get_profile.restype = ctypes.c_int
+    lib.specv_get_profile_samples.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                                              ctypes.POINTER(ctypes.c_int)]
+    lib.specv_get_profile_samples.restype = ctypes.c_int
+    lib.specv_read_ceiling.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    lib.specv_read_ceiling.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -192,6 +198,18 @@ def _rows(t, name, lead):
     return t.stride(0), t.stride(1)
 
 
+def read_ceiling(buf, grid, sink):
+    """One streaming read of the device tensor ``buf`` (its bytes, a multiple
+    of 16) by ``grid`` workgroups on the current stream (measurement aid);
+    ``sink`` is an int32 device tensor of at least ``grid`` entries."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_cuda or not buf.is_contiguous() or sink.numel() < grid or sink.dtype != torch.int32:
+        raise SpecvError("read_ceiling needs a contiguous device buffer and an int32 sink of grid entries")
+    st = load_library().specv_read_ceiling(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
+                                           _ptr(buf), nbytes, int(grid), _ptr(sink))
+    _check(st, "specv_read_ceiling")
+
+
 class Verifier:
     """A libspecv handle: owns the device workspace for calls up to the given
     maxima.  Calls run on the current torch stream of the handle's device."""
@@ -236,6 +254,15 @@ class Verifier:
                                                 ctypes.byref(ms)),
                "specv_get_profile")
         return n.value, ms.value
+
+    def profile_samples(self, max_samples=1 << 16):
+        """Per-call kernel milliseconds recorded since the last reset (numpy
+        float32); waits for the recorded events, does not reset."""
+        buf = (ctypes.c_float * max_samples)()
+        n = ctypes.c_int()
+        _check(load_library().specv_get_profile_samples(self._h, max_samples, buf, ctypes.byref(n)),
+               "specv_get_profile_samples")
+        return np.frombuffer(buf, dtype=np.float32, count=n.value).copy()
 
     def _stream(self):
         return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)

@@ -28,11 +28,13 @@ struct specv_ctx {
     size_t ev_next = 0;
     int prof_calls = 0;
     double ms_kernel = 0.0;
+    std::vector<float> samples;     // per-call kernel milliseconds since the last reset
     unsigned epoch = 0;             // call number; the kernel tags published decisions with it
 };
 
 namespace {
 constexpr size_t kProfRing = 512;
+constexpr size_t kMaxSamples = 1 << 16;
 
 hipError_t drain_slot(specv_ctx* h, size_t slot) {
     if (!h->ev_live[slot]) return hipSuccess;
@@ -44,6 +46,7 @@ hipError_t drain_slot(specv_ctx* h, size_t slot) {
     if (err != hipSuccess) return err;
     h->ms_kernel += ms;
     h->prof_calls += 1;
+    if (h->samples.size() < kMaxSamples) h->samples.push_back(ms);
     h->ev_live[slot] = 0;
     return hipSuccess;
 }
@@ -261,7 +264,29 @@ specv_status specv_get_profile(specv_handle h, int reset, int* calls, double* ms
     if (reset) {
         h->prof_calls = 0;
         h->ms_kernel = 0.0;
+        h->samples.clear();
     }
+    return SPECV_OK;
+}
+
+specv_status specv_get_profile_samples(specv_handle h, int max_samples, float* ms_out, int* n_out) {
+    if (!h || !n_out || (max_samples > 0 && !ms_out)) return SPECV_E_NULL;
+    for (size_t s = 0; s < h->ev_live.size(); ++s)
+        if (drain_slot(h, s) != hipSuccess) return SPECV_E_HIP;
+    const int n = (int)std::min<size_t>(h->samples.size(), (size_t)std::max(max_samples, 0));
+    for (int i = 0; i < n; ++i) ms_out[i] = h->samples[i];
+    *n_out = n;
+    return SPECV_OK;
+}
+
+specv_status specv_read_ceiling(void* stream, const void* buf, int64_t bytes, int grid, uint32_t* sink) {
+    if (!buf || !sink) return SPECV_E_NULL;
+    if (bytes < 16 || (bytes % 16) != 0 || grid < 1) return SPECV_E_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0 || (reinterpret_cast<uintptr_t>(sink) % 4) != 0)
+        return SPECV_E_ALIGN;
+    if (specv::launch_read_ceiling(buf, bytes / 16, grid, sink, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return SPECV_E_HIP;
     return SPECV_OK;
 }
 

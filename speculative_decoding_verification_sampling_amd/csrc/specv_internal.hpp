@@ -164,4 +164,9 @@ hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStrea
 // and end.
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev);
 
+// A plain streaming read of n16 16-byte words (measurement aid): ``grid``
+// workgroups, each folding its share into one word of sink[grid].
+hipError_t launch_read_ceiling(const void* buf, long long n16, int grid, unsigned* sink,
+                               hipStream_t stream);
+
 }  // namespace specv

@@ -131,6 +131,22 @@ def llama_vocab(sigma_d, seed=1002):
                     _store(d, "f32"), tokens, T, k, p, cap, seed=0x5EED0002 + int(seed))
 
 
+def llama_vocab_rounds(sigma_d, rounds=1000, seed=1012):
+    """The Llama-style workload with fresh logits every round: ``rounds``
+    independent rows (B = rounds, gamma=4, V=32000, float32), each drawn as
+    ``llama_vocab`` draws its one row (N(0, 3^2) + 20 boosted tokens, draft
+    noise sigma_d), with draft tokens from the stand-in sampler; T=1.  The
+    data seed depends on sigma_d, so the three noise levels see different
+    rows."""
+    rng = np.random.default_rng(seed * 1000 + int(round(sigma_d * 10)))
+    t, d = make_logits(rng, rounds, 4, 32000, 3.0, sigma_d, BOOST_COUNT)
+    T, k, p, cap = _params(rounds, 1.0)
+    tokens = gumbel_max_tokens(rng, d, T)
+    return Workload(f"llama-rounds{rounds}-V32000-g4-f32-sd{sigma_d}", rounds, 4, 32000, "f32",
+                    _store(t, "f32"), _store(d, "f32"), tokens, T, k, p, cap,
+                    seed=0x5EED0012 + int(round(sigma_d * 10)))
+
+
 def serving_batch(seed=1003, B=64, gamma=5, V=128256):
     """B=64, gamma=5, V=128256, bfloat16; N(0, 3^2) + boost, draft noise
     N(0, 1.5^2); T=0.7; no truncation."""
@@ -173,6 +189,7 @@ def mixed(seed=1005, B=256, gamma=8, V=128256):
 WORKLOADS = {
     "tiny": tiny,
     "llama_vocab": llama_vocab,
+    "llama_vocab_rounds": llama_vocab_rounds,
     "serving_batch": serving_batch,
     "truncated": truncated,
     "mixed": mixed,

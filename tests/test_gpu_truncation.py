@@ -53,8 +53,8 @@ def run_trunc(target, draft, prm, seed, max_top_k=1024, tokens=None, step=0, eos
     return out, orc, tokens, tf, df
 
 
-def check(out, orc, tokens, tf, df, prm, max_tol=0.05):
-    rep = compare(out, orc, tokens, tf, df, prm)
+def check(out, orc, tokens, tf, df, prm, max_tol=0.05, workload=None):
+    rep = compare(out, orc, tokens, tf, df, prm, workload=workload)
     print(rep.summary())
     rep.assert_ok(max_tol)
     return rep
@@ -64,7 +64,8 @@ def test_truncated_workload_full_size(gpu):
     w = synth.truncated()
     prm = _prm(w.B, w.temperature, w.top_k, w.top_p)
     out, orc, toks, tf, df = run_trunc(w.target, w.draft, prm, w.seed, max_top_k=64)
-    rep = check(out, orc, toks, tf, df, prm)
+    rep = check(out, orc, toks, tf, df, prm,
+                workload="config 4: truncated B=32 gamma=5 V=152064 bf16 T=0.7 top-k 50 top-p 0.9")
     assert rep.value_checks > w.B
     f = out["row_flags"].cpu().numpy()
     assert not (f & (sv.FLAG_CAND_OVERFLOW | sv.FLAG_UNSUPPORTED)).any()
