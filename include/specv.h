@@ -171,6 +171,40 @@ SPECV_API specv_status specv_verify_sample(specv_handle h, void* stream,
                                  int32_t* out_num_emitted, int32_t* out_row_flags,
                                  const specv_diag* diag);
 
+/* specv_verify_sample for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  No handle: the records the verify kernels exchange live in
+ * one static device array of SPECV_NOALLOC_SCRATCH_BYTES per device (held
+ * by each device the library runs on until the process ends), laid out for
+ * B <= SPECV_NOALLOC_MAX_BATCH, gamma <= SPECV_NOALLOC_MAX_GAMMA and
+ * V <= SPECV_NOALLOC_MAX_VOCAB; larger calls are rejected with
+ * SPECV_E_CAPACITY before anything is enqueued.  Nothing is allocated by
+ * this call or any other.  The array has no truncation candidates, so rows
+ * with top-k / top-p are flagged SPECV_FLAG_UNSUPPORTED and emit nothing.
+ *   device          HIP device ordinal the call runs on (the calling
+ *                   thread's current device is restored on return); stream
+ *                   must belong to it.  SPECV_E_PARAM if out of range.
+ * Other arguments, layouts, outputs and errors as specv_verify_sample; the
+ * outputs equal specv_verify_sample's on the same inputs.  The first call
+ * on a device clears its array with a kernel on ``stream``.  Every call on
+ * a device shares that device's array: calls that overlap on one device
+ * (on other streams, or from host threads without stream order between
+ * them) race, and their outputs are undefined.  As with a handle, a call
+ * captured into a HIP graph must not be replayed. */
+#define SPECV_NOALLOC_MAX_BATCH 256
+#define SPECV_NOALLOC_MAX_GAMMA 15
+#define SPECV_NOALLOC_MAX_VOCAB 262144
+#define SPECV_NOALLOC_SCRATCH_BYTES 6832128
+SPECV_API specv_status specv_verify_sample_noalloc(int device, void* stream,
+                                 const void* target_logits, int64_t t_stride_b, int64_t t_stride_pos,
+                                 const void* draft_logits, int64_t d_stride_b, int64_t d_stride_pos,
+                                 specv_dtype dtype, int B, int gamma, int V,
+                                 const int32_t* draft_tokens, const specv_row_params* row_params,
+                                 uint64_t seed, uint32_t step, int32_t eos_id,
+                                 int32_t* out_num_accepted, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, int32_t* out_row_flags,
+                                 const specv_diag* diag);
+
 /* Stochastic verification against deterministic drafts: n-gram or
  * prompt-lookup proposals ("投机解码 Speculative Decoding" tutorial, sections
  * 2.1 and 4.2; the ICML summary's remark that the approximation model may be

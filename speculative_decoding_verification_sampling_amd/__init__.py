@@ -35,6 +35,7 @@ __all__ = [
     "FLAG_INTERNAL",
     "EXPORTED_SYMBOLS",
     "read_ceiling",
+    "verify_sample_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,7 +55,8 @@ SPECV_BF16 = 1
 EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_point_mass",
                     "specv_verify_sample_qstats", "specv_sample_draft", "specv_verify_greedy",
                     "specv_destroy", "specv_status_string", "specv_set_profiling",
-                    "specv_get_profile", "specv_get_profile_samples", "specv_read_ceiling")
+                    "specv_get_profile", "specv_get_profile_samples", "specv_read_ceiling",
+                    "specv_verify_sample_noalloc")
 
 
 class SpecvError(RuntimeError):
@@ -151,6 +153,8 @@ def load_library():
     lib.specv_get_profile_samples.restype = ctypes.c_int
     lib.specv_read_ceiling.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     lib.specv_read_ceiling.restype = ctypes.c_int
+    lib.specv_verify_sample_noalloc.argtypes = [ctypes.c_int] + lib.specv_verify_sample.argtypes[1:]
+    lib.specv_verify_sample_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -196,6 +200,51 @@ def _rows(t, name, lead):
     if t.shape[2] > 1 and t.stride(2) != 1:
         raise SpecvError(f"{name} must be contiguous along the vocabulary")
     return t.stride(0), t.stride(1)
+
+
+def verify_sample_noalloc(target, draft, tokens, row_params, seed, step=0, eos_id=-1, out=None,
+                          diag=False):
+    """specv_verify_sample_noalloc: Verifier.verify_sample without a handle,
+    for callers that cannot allocate device memory (the library's static
+    per-device scratch array; B <= 256, gamma <= 15, V <= 262144, no
+    truncated rows).  Runs on the current torch device and stream.  The
+    output tensors are allocated here unless ``out`` (and, with ``diag``,
+    its diagnostics) are given."""
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    tsb, tsp = _rows(target, "target", None)
+    dsb = dsp = 0
+    if gamma > 0:
+        dsb, dsp = _rows(draft, "draft", B)
+        if draft.shape[1] != gamma or draft.shape[2] != V or draft.dtype != target.dtype:
+            raise SpecvError("draft must be [B, gamma, V] with the target's dtype")
+    for t, n in ((tokens, "tokens"), (row_params, "row_params")):
+        if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+            raise SpecvError(f"{n} must be a contiguous int32 device tensor")
+    if tokens.shape != (B, gamma) or row_params.shape != (B, 4):
+        raise SpecvError("tokens must be [B, gamma] and row_params [B, 4]")
+    dev = target.device
+    if out is None:
+        z = dict(dtype=torch.int32, device=dev)
+        out = {"num_accepted": torch.empty(B, **z), "out_tokens": torch.empty(B, gamma + 1, **z),
+               "num_emitted": torch.empty(B, **z), "row_flags": torch.empty(B, **z)}
+    d = None
+    if diag:
+        for key, shape in (("p_at_draft", (B, gamma)), ("q_at_draft", (B, gamma)), ("residual_sum", (B,))):
+            if key not in out:
+                out[key] = torch.empty(*shape, dtype=torch.float32, device=dev)
+        d = _Diag(out["p_at_draft"].data_ptr(), out["q_at_draft"].data_ptr(),
+                  out["residual_sum"].data_ptr())
+    st = load_library().specv_verify_sample_noalloc(
+        dev.index if dev.index is not None else torch.cuda.current_device(),
+        ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream),
+        _ptr(target), tsb, tsp, _ptr(draft if gamma > 0 else None), dsb, dsp,
+        _dtype_code(target), B, gamma, V, _ptr(tokens), _ptr(row_params),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFF, int(eos_id),
+        _ptr(out["num_accepted"]), _ptr(out["out_tokens"]), _ptr(out["num_emitted"]),
+        _ptr(out.get("row_flags")), ctypes.byref(d) if d is not None else None)
+    _check(st, "specv_verify_sample_noalloc")
+    return out
 
 
 def read_ceiling(buf, grid, sink):

@@ -86,17 +86,16 @@ void free_ws(specv::Workspace& ws) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Validation shared by both entry points.
-specv_status check_common(specv_handle h, const void* target, int64_t t_sb, int64_t t_sp,
+// Validation shared by the verify entry points, against the sizes a
+// workspace was laid out for.
+specv_status check_common(const specv::Limits& lim, const void* target, int64_t t_sb, int64_t t_sp,
                           specv_dtype dtype, int B, int gamma, int V, const int32_t* tokens,
                           int32_t* out_acc, int32_t* out_tok, int32_t* out_emit,
                           int32_t* out_flags) {
-    if (!h) return SPECV_E_NULL;
     if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
     if (B < 0 || gamma < 0 || gamma > SPECV_MAX_GAMMA || V < 1) return SPECV_E_SHAPE;
     if (t_sb < 0 || t_sp < 0) return SPECV_E_SHAPE;
-    if (B > h->cfg.max_batch || gamma > h->cfg.max_gamma || V > h->cfg.max_vocab)
-        return SPECV_E_CAPACITY;
+    if (B > lim.max_batch || gamma > lim.max_gamma || V > lim.max_vocab) return SPECV_E_CAPACITY;
     if (B == 0) return SPECV_OK;
     if (!target || !out_acc || !out_tok || !out_emit) return SPECV_E_NULL;
     if (gamma > 0 && !tokens) return SPECV_E_NULL;
@@ -108,21 +107,31 @@ specv_status check_common(specv_handle h, const void* target, int64_t t_sb, int6
     return SPECV_OK;
 }
 
+specv::Limits handle_limits(specv_handle h) {
+    specv::Limits l;
+    l.max_batch = h->cfg.max_batch;
+    l.max_gamma = h->cfg.max_gamma;
+    l.max_vocab = h->cfg.max_vocab;
+    l.max_top_k = h->cfg.max_top_k;
+    l.cand_cap = h->cand_cap;
+    l.kept_cap = h->kept_cap;
+    return l;
+}
+
 bool rows_vec_aligned(const void* base, int64_t sb, int64_t sp, size_t es) {
     return aligned(base, 16) && ((sb * (int64_t)es) % 16) == 0 && ((sp * (int64_t)es) % 16) == 0;
 }
 
-specv::Args base_args(specv_handle h, int B, int gamma, int V) {
+specv::Args base_args(const specv::Limits& lim, int B, int gamma, int V) {
     specv::Args a{};
     a.B = B;
     a.gamma = gamma;
     a.V = V;
     a.C = (V + specv::kChunk - 1) / specv::kChunk;
     a.P = gamma + 1;
-    a.ws = h->ws;
-    a.cand_cap = h->cand_cap;
-    a.kept_cap = h->kept_cap;
-    a.max_top_k = h->cfg.max_top_k;
+    a.cand_cap = lim.cand_cap;
+    a.kept_cap = lim.kept_cap;
+    a.max_top_k = lim.max_top_k;
     return a;
 }
 
@@ -303,12 +312,12 @@ specv_status specv_destroy(specv_handle h) {
 
 }  // extern "C"
 
-namespace {
+namespace specv {
 
 // Stochastic verification.  prop: 0 draft logits (specv_verify_sample);
 // 1 no draft logits, q_i is the point mass on d_i (specv_verify_point_mass);
 // 2 draft logits plus the drafter's row statistics (specv_verify_sample_qstats).
-specv_status verify_sampling(specv_handle h, void* stream, const void* target_logits,
+specv_status verify_sampling_args(const specv::Limits& lim, const void* target_logits,
                              int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
                              int64_t d_stride_b, int64_t d_stride_pos,
                              const specv_draft_stats* draft_stats,
@@ -316,9 +325,9 @@ specv_status verify_sampling(specv_handle h, void* stream, const void* target_lo
                              const int32_t* draft_tokens, const specv_row_params* row_params,
                              uint64_t seed, uint32_t step, int32_t eos_id, int32_t* out_num_accepted,
                              int32_t* out_tokens, int32_t* out_num_emitted, int32_t* out_row_flags,
-                             const specv_diag* diag, int prop) {
+                             const specv_diag* diag, int prop, specv::Args* out, bool* out_vec) {
     const bool point_mass = prop == 1;
-    specv_status st = check_common(h, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
+    specv_status st = check_common(lim, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
                                    draft_tokens, out_num_accepted, out_tokens, out_num_emitted,
                                    out_row_flags);
     if (st != SPECV_OK || B == 0) return st;
@@ -340,7 +349,7 @@ specv_status verify_sampling(specv_handle h, void* stream, const void* target_lo
                  (diag->residual_sum && !aligned(diag->residual_sum, 4))))
         return SPECV_E_ALIGN;
 
-    specv::Args a = base_args(h, B, gamma, V);
+    specv::Args a = base_args(lim, B, gamma, V);
     a.tgt = target_logits;
     a.t_sb = t_stride_b;
     a.t_sp = t_stride_pos;
@@ -364,8 +373,34 @@ specv_status verify_sampling(specv_handle h, void* stream, const void* target_lo
     a.p_at = diag ? diag->p_at_draft : nullptr;
     a.q_at = diag ? diag->q_at_draft : nullptr;
     a.wres = diag ? diag->residual_sum : nullptr;
-    const bool vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es) &&
-                     (point_mass || gamma == 0 || rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es));
+    *out_vec = rows_vec_aligned(target_logits, t_stride_b, t_stride_pos, es) &&
+               (point_mass || gamma == 0 || rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es));
+    *out = a;
+    return SPECV_OK;
+}
+
+}  // namespace specv
+
+namespace {
+
+specv_status verify_sampling(specv_handle h, void* stream, const void* target_logits,
+                             int64_t t_stride_b, int64_t t_stride_pos, const void* draft_logits,
+                             int64_t d_stride_b, int64_t d_stride_pos,
+                             const specv_draft_stats* draft_stats,
+                             int64_t s_stride_b, specv_dtype dtype, int B, int gamma, int V,
+                             const int32_t* draft_tokens, const specv_row_params* row_params,
+                             uint64_t seed, uint32_t step, int32_t eos_id, int32_t* out_num_accepted,
+                             int32_t* out_tokens, int32_t* out_num_emitted, int32_t* out_row_flags,
+                             const specv_diag* diag, int prop) {
+    if (!h) return SPECV_E_NULL;
+    specv::Args a;
+    bool vec = false;
+    const specv_status st = verify_sampling_args(
+        handle_limits(h), target_logits, t_stride_b, t_stride_pos, draft_logits, d_stride_b, d_stride_pos,
+        draft_stats, s_stride_b, dtype, B, gamma, V, draft_tokens, row_params, seed, step, eos_id,
+        out_num_accepted, out_tokens, out_num_emitted, out_row_flags, diag, prop, &a, &vec);
+    if (st != SPECV_OK || B == 0) return st;
+    a.ws = h->ws;
     return launch(h, a, dtype == SPECV_BF16, vec, stream);
 }
 
@@ -470,13 +505,16 @@ specv_status specv_verify_greedy(specv_handle h, void* stream, const void* targe
                                  const int32_t* max_new_tokens, int32_t eos_id,
                                  int32_t* out_num_accepted, int32_t* out_tokens,
                                  int32_t* out_num_emitted, int32_t* out_row_flags) {
-    specv_status st = check_common(h, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
+    if (!h) return SPECV_E_NULL;
+    const specv::Limits lim = handle_limits(h);
+    specv_status st = check_common(lim, target_logits, t_stride_b, t_stride_pos, dtype, B, gamma, V,
                                    draft_tokens, out_num_accepted, out_tokens, out_num_emitted,
                                    out_row_flags);
     if (st != SPECV_OK || B == 0) return st;
     if (max_new_tokens && !aligned(max_new_tokens, 4)) return SPECV_E_ALIGN;
     const size_t es = dtype == SPECV_BF16 ? 2 : 4;
-    specv::Args a = base_args(h, B, gamma, V);
+    specv::Args a = base_args(lim, B, gamma, V);
+    a.ws = h->ws;
     a.tgt = target_logits;
     a.t_sb = t_stride_b;
     a.t_sp = t_stride_pos;

@@ -164,6 +164,29 @@ hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStrea
 // and end.
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev);
 
+// The sizes a workspace is laid out for, and its truncation capacity.
+struct Limits {
+    int max_batch, max_gamma, max_vocab, max_top_k;
+    int cand_cap;                 // candidates per (row, chunk); 0: no truncation workspace
+    int kept_cap;
+};
+
+// Checks the arguments of a stochastic verify call against ``lim`` (prop:
+// kPropLogits draft logits, kPropPoint point-mass drafts, kPropStats the
+// drafter's statistics) and packs them into *out, all but the workspace and
+// the epoch; *out_vec tells whether every row start allows 16-byte loads.
+// Returns the status the entry point reports; with B == 0 there is nothing
+// to launch.
+specv_status verify_sampling_args(const Limits& lim, const void* target_logits, int64_t t_stride_b,
+                                  int64_t t_stride_pos, const void* draft_logits, int64_t d_stride_b,
+                                  int64_t d_stride_pos, const specv_draft_stats* draft_stats,
+                                  int64_t s_stride_b, specv_dtype dtype, int B, int gamma, int V,
+                                  const int32_t* draft_tokens, const specv_row_params* row_params,
+                                  uint64_t seed, uint32_t step, int32_t eos_id,
+                                  int32_t* out_num_accepted, int32_t* out_tokens,
+                                  int32_t* out_num_emitted, int32_t* out_row_flags,
+                                  const specv_diag* diag, int prop, Args* out, bool* out_vec);
+
 // A plain streaming read of n16 16-byte words (measurement aid): ``grid``
 // workgroups, each folding its share into one word of sink[grid].
 hipError_t launch_read_ceiling(const void* buf, long long n16, int grid, unsigned* sink,
