@@ -86,12 +86,15 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype;
 #define SPECV_FLAG_Q_ZERO             (1 << 2) /* an accept test met d_i outside q_i's support
                                                   (accepted iff p_i(d_i) > 0)                       */
 #define SPECV_FLAG_RESIDUAL_FALLBACK  (1 << 3) /* residual mass 0 / not finite: sampled from p_i    */
-#define SPECV_FLAG_CAND_OVERFLOW      (1 << 4) /* truncation candidates exceeded the workspace:
-                                                  the row emits nothing                             */
+#define SPECV_FLAG_CAND_OVERFLOW      (1 << 4) /* reserved; never set: rows whose truncation the
+                                                  candidate lists cannot settle (ties beyond the
+                                                  lists, top-p alone on flat rows, top_k above
+                                                  max_top_k) are truncated exactly over the
+                                                  whole row                                         */
 #define SPECV_FLAG_TOPP_NEAR          (1 << 5) /* a top-p cumulative mass was within 1e-5 of top_p  */
-#define SPECV_FLAG_UNSUPPORTED        (1 << 6) /* truncation the handle cannot run: top_p < 1
-                                                  without 0 < top_k < V, or top_k above the
-                                                  handle's max_top_k: the row emits nothing         */
+#define SPECV_FLAG_UNSUPPORTED        (1 << 6) /* a top-k / top-p row on a handle (or entry point)
+                                                  without truncation workspace (max_top_k == 0):
+                                                  the row emits nothing                             */
 
 #define SPECV_FLAG_INTERNAL           (1 << 7) /* the sampling phase timed out waiting for the row's
                                                   decision (a launch without co-residency): the
@@ -106,9 +109,13 @@ typedef struct {
     int max_batch;   /* largest B of any call                                     */
     int max_gamma;   /* largest gamma (0 .. SPECV_MAX_GAMMA)                      */
     int max_vocab;   /* largest V (at most SPECV_MAX_VOCAB)                       */
-    int max_top_k;   /* largest top_k of truncated rows (0 .. SPECV_MAX_TOP_K);
-                        0 reserves no candidate workspace: truncated rows are then
-                        flagged SPECV_FLAG_UNSUPPORTED                            */
+    int max_top_k;   /* candidates kept per 8192-entry chunk of truncated rows
+                        (0 .. SPECV_MAX_TOP_K): rows with top_k <= max_top_k (and
+                        top-p rows whose kept set the candidates hold) take the
+                        candidate path; others, a larger top_k included, are
+                        truncated exactly over the whole row (slower); 0 reserves
+                        no candidate workspace: truncated rows are then flagged
+                        SPECV_FLAG_UNSUPPORTED                                    */
 } specv_config;
 
 /* Per-row sampling parameters, device array [B] (16 bytes each). */
@@ -243,10 +250,9 @@ SPECV_API specv_status specv_verify_point_mass(specv_handle h, void* stream,
  *   out_stats       specv_draft_stats [B, out_stride] or NULL: entry
  *                   (b, pos0 + i) gets the row's statistics and flags:
  *                   SPECV_FLAG_NONFINITE_ROW (NaN / +inf or no finite logit),
- *                   SPECV_FLAG_CAND_OVERFLOW (truncation candidates exceeded
- *                   the workspace), SPECV_FLAG_UNSUPPORTED (top-k / top-p on a
- *                   handle without truncation workspace, or top_k above its
- *                   max_top_k), SPECV_FLAG_INTERNAL (a bounded wait expired):
+ *                   SPECV_FLAG_UNSUPPORTED (top-k / top-p on a handle without
+ *                   truncation workspace), SPECV_FLAG_INTERNAL (a bounded
+ *                   wait expired):
  *                   these rows get token -1; SPECV_FLAG_TOPP_NEAR (the top-p
  *                   decision was within 1e-5 of top_p) is informational
  * Rows with temperature 0 take the draft argmax (lowest index on ties).

@@ -87,16 +87,25 @@ __device__ inline Args verify_view(const DraftArgs& a) {
 // verify kernel's row merge, then the inverse CDF over the kept tokens in
 // ascending index order.
 template <bool BF16>
-__device__ void draw_truncated(const DraftArgs& a, const Args& va, int b, int i, long long o,
+__device__ __forceinline__ void draw_truncated(const DraftArgs& a, const Args& va, int b, int i, long long o,
                                const Plan& pl, float u, TruncScratch& sc) {
     const int tid = threadIdx.x;
     const float nan = __builtin_nanf("");
-    const TruncRow tr = row_merge<BF16>(va, b, i, 1, pl, sc);
-    if (tr.bad || (tr.flags & SPECV_FLAG_CAND_OVERFLOW) || tr.n_kept <= 0) {
-        if (tid == 0)
-            write_draft(a, o, -1, nan, nan, nan,
-                        tr.flags | ((tr.bad || (tr.n_kept <= 0 && !(tr.flags & SPECV_FLAG_CAND_OVERFLOW)))
-                                        ? SPECV_FLAG_NONFINITE_ROW : 0u));
+    const TruncRow tr = row_settle<BF16>(va, b, i, 1, pl, row_merge<BF16>(va, b, i, 1, pl, sc), sc);
+    if (tr.bad || tr.n_kept == 0) {
+        if (tid == 0) write_draft(a, o, -1, nan, nan, nan, tr.flags | SPECV_FLAG_NONFINITE_ROW);
+        return;
+    }
+    if (tr.n_kept == kThresholdForm) {
+        // kept set {z >= tstar} without a list: a scan of the row
+        float W;
+        bool fb;
+        const int tok = threshold_draw<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i), tr, nullptr, tr, -1, false,
+                                             a.V, pl.scale, u, sc, &W, &fb);
+        if (tid == 0) {
+            if (tok < 0) write_draft(a, o, -1, nan, nan, nan, tr.flags | SPECV_FLAG_NONFINITE_ROW);
+            else write_draft(a, o, tok, tr.zmax, tr.S, tr.tstar, tr.flags);
+        }
         return;
     }
     // row_merge leaves the kept list in sc.v / sc.idx (value descending)
@@ -140,8 +149,8 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScra
     const bool trunc = !greedy && (topk_on || rp.top_p < 1.f);
     const int pos = a.pos0 + i;
     const long long o = (long long)b * a.out_stride + pos;
-    if (trunc && (!TRUNC || a.cand_cap == 0 || (topk_on && rp.top_k > a.max_top_k))) {
-        // the handle reserved no room for these candidates
+    if (trunc && (!TRUNC || a.cand_cap == 0)) {
+        // the handle reserved no room for candidates
         if (c == 0 && tid == 0) write_draft(a, o, -1, nan, nan, nan, SPECV_FLAG_UNSUPPORTED);
         return;
     }
@@ -188,7 +197,7 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScra
             if (trunc) {
                 // the chunk's top-k candidates, complete before its statistics
                 // are published (the statistics words tell the merge they are in)
-                chunk_candidates<BF16>(va, side_row(va, b, i, 1), c, topk_on ? rp.top_k : a.max_top_k, r,
+                chunk_candidates<BF16>(va, side_row(va, b, i, 1), c, topk_on ? min(rp.top_k, a.max_top_k) : a.max_top_k, r,
                                        *sc);
                 wait_stores();
             }
@@ -225,7 +234,7 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScra
             pl.top_k = rp.top_k;
             pl.top_p = rp.top_p;
             pl.kmode = topk_on ? 1 : 0;
-            pl.keff = topk_on ? rp.top_k : a.max_top_k;
+            pl.keff = topk_on ? min(rp.top_k, a.max_top_k) : a.max_top_k;
             const float u = uniform24(a.seed, b, pos, PURPOSE_DRAFT, a.step);
             draw_truncated<BF16>(a, va, b, i, o, pl, u, *sc);
             return;

@@ -39,7 +39,7 @@ struct TruncRow {
 };
 
 // LDS scratch of the truncation steps (one per workgroup, reused).
-struct TruncScratch {
+struct alignas(16) TruncScratch {   // 8-byte LDS atomics on v and w
     float v[kKeptCap];
     int idx[kKeptCap];
     float w[kKeptCap];

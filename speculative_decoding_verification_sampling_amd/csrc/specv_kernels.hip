@@ -286,6 +286,15 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
                 t1 = t0;
                 if (two) t1 = row_merge<BF16>(a, b, k, 1, pl, *sc);
             }
+            // rows the candidates could not settle: the exact truncation,
+            // from one call site
+#pragma unroll 1
+            for (int side = 0; side < (two ? 2 : 1); ++side) {
+                const TruncRow t = row_settle<BF16>(a, b, k, side, pl, side ? t1 : t0, *sc);
+                if (side) t1 = t;
+                else t0 = t;
+            }
+            if (!two) t1 = t0;
             if (tid == 0) {
                 dT[0] = t0;
                 dT[1] = qs && qside ? stats_trow(a.qstats[(long long)b * a.qs_sb + k]) : t1;
@@ -366,7 +375,7 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
         } else if (trunc) {
             const TruncRow& t0 = dT[0];
             const TruncRow& t1 = dT[1];
-            flags = (t0.flags | (qside ? t1.flags : 0u)) & (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
+            flags = (t0.flags | (qside ? t1.flags : 0u)) & SPECV_FLAG_TOPP_NEAR;
             if (t0.bad || (qside && t1.bad)) flags |= SPECV_FLAG_NONFINITE_ROW;
             if (trow_dead(t0) || (qside && trow_dead(t1))) {
                 outcome = OUT_BAD;

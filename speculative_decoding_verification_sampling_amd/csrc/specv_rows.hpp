@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "specv_device.hpp"
@@ -40,7 +41,8 @@ struct Plan {
     int top_k;
     float top_p;
     int keff;       // truncated rows: candidates wanted per chunk (top_k, or the handle's
-                    // max_top_k for top-p alone)
+                    // max_top_k for top-p alone or a larger top_k, whose rows are
+                    // truncated exactly)
     int kmode;      // truncated rows: 1 when top-k is on (normaliser over the top-k set)
     unsigned flags;
     int tok;        // lane i < gamma: draft token d_i
@@ -84,8 +86,8 @@ __device__ inline Plan make_plan(const Args& a, int b) {
     } else if (greedy) {
         p.mode = MODE_GREEDY;
     } else if (topk_on || topp_on) {
-        if (a.cand_cap == 0 || (topk_on && k > a.max_top_k)) {
-            p.mode = MODE_SKIP;               // the handle reserved no room for these candidates
+        if (a.cand_cap == 0) {
+            p.mode = MODE_SKIP;               // the handle reserved no room for candidates
             p.flags |= SPECV_FLAG_UNSUPPORTED;
         } else {
             p.mode = MODE_TRUNC;
@@ -95,7 +97,7 @@ __device__ inline Plan make_plan(const Args& a, int b) {
     }
     p.scale = greedy ? 0.f : kLog2e / T;
     p.kmode = topk_on ? 1 : 0;
-    p.keff = topk_on ? k : a.max_top_k;
+    p.keff = topk_on ? min(k, a.max_top_k) : a.max_top_k;
     p.nt = min(ce, a.gamma + 1);
     p.ntest = min(ce, a.gamma);
     return p;
@@ -643,13 +645,382 @@ __device__ inline void chunk_candidates(const Args& a, long long rowid, int c, i
     chunk_candidates_pair<BF16>(a, rowid, rowid, false, c, keff, r, r, sc);
 }
 
+// ---------------------------------------------------------------- exact truncation
+// The slow path, for rows whose truncation the candidate lists cannot
+// settle: heavy ties at the top-k threshold (a chunk's candidates overflow
+// their slots), top-p without top-k on a flat row (the kept set needs more
+// entries than the candidates hold), top_k above the handle's max_top_k.
+// The top-k threshold (the k-th largest finite value, ties kept) and the
+// top-p threshold (the largest value t whose set {z >= t} holds at least
+// top_p of the top-k-renormalised mass) come from radix descents over the
+// order keys of the whole row, which the deciding workgroup reads from
+// global memory: one pass per 8-bit digit (two for bfloat16 keys, four for
+// float32), each a 256-bin histogram of the entries still in range.  Counts
+// are integers and masses exp2((z - max) * log2(e) / T) are summed in 2^-40
+// fixed point, so every sum is exact and independent of the order of
+// accumulation.  The row is then kept in threshold form: the kept set
+// {z >= tstar} without a list (TruncRow::n_kept == kThresholdForm), its
+// normaliser from the same sums; draws from such a row scan the row itself
+// (threshold_draw).
+constexpr int kThresholdForm = -1;          // TruncRow::n_kept: kept set {z >= tstar}, no list
+constexpr int kNeedsExact = -2;             // short_merge_wave: the candidates cannot settle the row
+constexpr float kMassUnit = 1099511627776.0f;   // 2^40
+constexpr double kInvMassUnit = 1.0 / 1099511627776.0;
+
+__device__ inline unsigned long long mass_fixed(float w) {
+    return (unsigned long long)(w * kMassUnit);
+}
+
+__device__ inline unsigned long long wave_sum_u64(unsigned long long x) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
+__device__ inline unsigned long long wave_scan_incl_u64(unsigned long long x) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Sum over the workgroup (every thread gets it).
+__device__ inline unsigned long long block_sum_u64(unsigned long long x) {
+    __shared__ unsigned long long red[kWaves];
+    x = wave_sum_u64(x);
+    __syncthreads();
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
+    __syncthreads();
+    unsigned long long t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += red[w];
+    __syncthreads();
+    return t;
+}
+
+// Calls f(z) for every entry of a logits row of length V: coalesced loads
+// (thread t reads entries t, t + 256, ...), eight in flight per thread.
+template <bool BF16, typename F>
+__device__ __forceinline__ void for_row(const void* row, int V, F f) {
+    for (int v0 = 0; v0 < V; v0 += 8 * kBlock) {
+        float z[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int v = v0 + j * kBlock + (int)threadIdx.x;
+            z[j] = v < V ? load_elem<BF16>(row, v) : -kInf;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f(z[j]);
+    }
+}
+
+// Radix descent over the finite entries of ``row`` with order key >= kmin,
+// each of weight 1 (scale == 0) or of fixed-point mass
+// exp2((z - zmax) * scale): the largest key t such that the entries with
+// key >= t weigh at least ``need`` (with frac > 0, need = ceil(frac * total
+// weight), at least 1).  Returns false, t = kmin, when the total is below
+// need.  *above gets the weight of the entries with key > t, *atleast that
+// of key >= t, *total the total.  Whole workgroup; the histograms live in
+// sc.v (one per wave) and sc.w.
+template <bool BF16>
+__device__ __forceinline__ bool row_descent(const void* row, int V, unsigned kmin, float zmax, float scale,
+                            unsigned long long need, double frac, TruncScratch& sc, unsigned* t,
+                            unsigned long long* above, unsigned long long* atleast,
+                            unsigned long long* total) {
+    constexpr int NP = BF16 ? 2 : 4;
+    constexpr int KB = 8 * NP;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const bool weighted = scale != 0.f;
+    unsigned long long* hist = reinterpret_cast<unsigned long long*>(sc.v);   // [kWaves][256]
+    unsigned long long* tot = reinterpret_cast<unsigned long long*>(sc.w);    // [256]
+    __shared__ unsigned dPrefix;
+    __shared__ unsigned long long dAbove, dNeed, dTotal, dAtLeast;
+    __shared__ int dFound;
+    __syncthreads();                                         // sc may still be read
+    if (tid == 0) {
+        dPrefix = 0;
+        dAbove = 0;
+        dAtLeast = 0;
+        dTotal = 0;
+        dNeed = need;
+        dFound = 1;
+    }
+    for (int pass = 0; pass < NP; ++pass) {
+        const int shift = KB - 8 * (pass + 1);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) hist[w * 256 + tid] = 0ull;           // kBlock == 256 bins
+        __syncthreads();
+        const unsigned prefix = dPrefix;
+        for_row<BF16>(row, V, [&](float z) {
+            const unsigned key = order_key<BF16>(z);
+            const bool in = finite_logit(z) && key >= kmin && (pass == 0 || (key >> (shift + 8)) == prefix);
+            const unsigned bin = (key >> shift) & 255u;
+            const unsigned long long wt = in ? (weighted ? mass_fixed(fast_exp2(__fmul_rn(z - zmax, scale))) : 1ull)
+                                             : 0ull;
+            // a flat row sends a whole wave to one bin: one atomic for it
+            const unsigned long long ins = __ballot(in);
+            if (ins == 0) return;
+            const unsigned b0 = (unsigned)__shfl((int)bin, __ffsll((long long)ins) - 1, kWave);
+            if (__ballot(in && bin != b0) == 0) {
+                const unsigned long long s = wave_sum_u64(wt);
+                if (lane == 0) atomicAdd(&hist[wave * 256 + b0], s);
+            } else if (in) {
+                atomicAdd(&hist[wave * 256 + bin], wt);
+            }
+        });
+        __syncthreads();
+        unsigned long long h = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) h += hist[w * 256 + tid];
+        tot[tid] = h;
+        __syncthreads();
+        if (tid == 0) {
+            if (pass == 0) {
+                unsigned long long all = 0;
+                for (int d = 0; d < 256; ++d) all += tot[d];
+                dTotal = all;
+                if (frac > 0.0) {
+                    const double n = ceil(frac * (double)all);
+                    dNeed = n < 1.0 ? 1ull : (unsigned long long)n;
+                }
+                if (all < dNeed) dFound = 0;
+            }
+            if (dFound) {
+                unsigned long long run = dAbove;
+                unsigned sel = 0;
+                for (int d = 255; d >= 0; --d) {
+                    if (run + tot[d] >= dNeed) {
+                        sel = (unsigned)d;
+                        break;
+                    }
+                    run += tot[d];
+                }
+                dAbove = run;
+                dPrefix = (prefix << 8) | sel;
+                dAtLeast = run + tot[sel];
+            }
+        }
+        __syncthreads();
+        if (!dFound) break;
+    }
+    const bool found = dFound != 0;
+    *t = found ? dPrefix : kmin;
+    *above = dAbove;
+    *atleast = dAtLeast;
+    *total = dTotal;
+    __syncthreads();
+    return found;
+}
+
+// Fixed-point mass of the finite entries of ``row`` with key >= kmin.
+template <bool BF16>
+__device__ __forceinline__ unsigned long long row_mass(const void* row, int V, unsigned kmin, float zmax, float scale) {
+    unsigned long long part = 0;
+    for_row<BF16>(row, V, [&](float z) {
+        if (finite_logit(z) && order_key<BF16>(z) >= kmin) part += mass_fixed(fast_exp2(__fmul_rn(z - zmax, scale)));
+    });
+    return block_sum_u64(part);
+}
+
+// The exact truncation of logits row (b, k, side) (whole workgroup), given
+// the row's maximum: published as the row's TruncRow in threshold form and
+// returned to every thread.  ``flags`` (flags found so far) gains TOPP_NEAR
+// when the cumulative mass at the chosen level or the level above lies
+// within 1e-5 of top_p.
+template <bool BF16>
+__device__ __forceinline__ TruncRow row_truncate_exact(const Args& a, int b, int k, int side, const Plan& pl, float zmax,
+                                       unsigned flags, TruncScratch& sc) {
+    const void* row = side ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k) : row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k);
+    TruncRow* tr = &a.ws.trow[side_row(a, b, k, side)];
+    unsigned long long above, atleast, total;
+    // the top-k threshold: the k-th largest finite value with multiplicity;
+    // with fewer finite entries than k every finite entry stays (key 0)
+    unsigned kkey = 0;
+    if (pl.kmode) {
+        unsigned t;
+        if (row_descent<BF16>(row, a.V, 0u, zmax, 0.f, (unsigned long long)pl.top_k, 0.0, sc, &t, &above, &atleast,
+                              &total))
+            kkey = t;
+    }
+    unsigned key = kkey;
+    unsigned long long S2;
+    if (pl.top_p < 1.f) {
+        // the largest t with mass(key >= t) >= ceil(top_p * mass(key >= kkey))
+        row_descent<BF16>(row, a.V, kkey, zmax, pl.scale, 1ull, (double)pl.top_p, sc, &key, &above, &S2, &total);
+        const double cj = (double)S2 / (double)total, pv = (double)above / (double)total;
+        if (fabs(cj - (double)pl.top_p) < 1e-5 || (above > 0 && fabs(pv - (double)pl.top_p) < 1e-5))
+            flags |= SPECV_FLAG_TOPP_NEAR;
+    } else {
+        S2 = row_mass<BF16>(row, a.V, kkey, zmax, pl.scale);
+    }
+    __shared__ TruncRow xOut;
+    if (threadIdx.x == 0) {
+        TruncRow o{};
+        o.zmax = zmax;
+        // key 0: every finite value is kept
+        o.tstar = key ? value_of_key<BF16>(key) : -3.402823466e38f;
+        o.S = (float)((double)S2 * kInvMassUnit);
+        o.n_kept = kThresholdForm;
+        o.flags = flags;
+        o.bad = S2 == 0 ? 1u : 0u;
+        xOut = o;
+        publish(&tr->zmax, o.zmax);
+        publish(&tr->tstar, o.tstar);
+        publish(&tr->S, o.S);
+        publish(&tr->n_kept, o.n_kept);
+        publish(&tr->flags, o.flags);
+        publish(&tr->bad, o.bad);
+    }
+    __syncthreads();
+    const TruncRow out = xOut;
+    __syncthreads();
+    return out;
+}
+
+// Inverse-CDF draw (whole workgroup) over a whole row of length V in
+// ascending token order: weight w(v) = p(v), p from row ``prow`` truncated
+// as tP (kept set {z >= tP.tstar}); with ``res``, w(v) = max(p(v) - q(v), 0)
+// with q from row ``qrow`` truncated as tQ, or the point mass on token dpm
+// when qrow is null.  The token is the first whose running weight exceeds
+// u * W; weights are summed in 2^-40 fixed point over tiles of 256 entries
+// (a tile per wave at a time, lane i holding entries 4i .. 4i + 3).  When
+// the residual weighs nothing the draw falls back to p (*fallback).  *W
+// gets the total weight drawn from (before the fallback).  Returns -1 when
+// nothing weighs anything.
+template <bool BF16>
+__device__ __forceinline__ int threshold_draw(const void* prow, const TruncRow& tP, const void* qrow, const TruncRow& tQ, int dpm,
+                              bool res, int V, float scale, float u, TruncScratch& sc, float* W, bool* fallback) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    constexpr int kTile = 4 * kWave;
+    const int ntiles = (V + kTile - 1) / kTile;             // <= 2048 (V <= 524288)
+    // tile sums [ntiles] over sc.v and sc.idx (adjacent, 16 KB together)
+    static_assert(offsetof(TruncScratch, idx) == offsetof(TruncScratch, v) + sizeof(float) * kKeptCap &&
+                      2 * kKeptCap * sizeof(float) >= kMaxChunks * kChunk / (4 * kWave) * sizeof(unsigned long long),
+                  "tile sums do not fit sc.v and sc.idx");
+    unsigned long long* tsum = reinterpret_cast<unsigned long long*>(sc.v);
+    const float invP = 1.f / tP.S, invQ = 1.f / tQ.S;
+    auto weight = [&](int v, bool resid) -> unsigned long long {
+        if (v >= V) return 0ull;
+        const float z = load_elem<BF16>(prow, v);
+        const float p = (finite_logit(z) && z >= tP.tstar) ? __fmul_rn(fast_exp2(__fmul_rn(z - tP.zmax, scale)), invP)
+                                                           : 0.f;
+        if (!resid) return mass_fixed(p);
+        float q;
+        if (qrow) {
+            const float zq = load_elem<BF16>(qrow, v);
+            q = (finite_logit(zq) && zq >= tQ.tstar) ? __fmul_rn(fast_exp2(__fmul_rn(zq - tQ.zmax, scale)), invQ)
+                                                     : 0.f;
+        } else {
+            q = v == dpm ? 1.f : 0.f;
+        }
+        return mass_fixed(fmaxf(__fsub_rn(p, q), 0.f));
+    };
+    __shared__ unsigned long long xSeg[kBlock / kWave + 1];
+    __shared__ int xTile;
+    __shared__ unsigned long long xBase;
+    __shared__ int xTok;
+    auto tile_sums = [&](bool resid) {
+        __syncthreads();
+        for (int t0 = wave; t0 < ntiles; t0 += 2 * kWaves) {
+            unsigned long long s[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int t = t0 + q * kWaves;
+                s[q] = 0;
+                if (t < ntiles) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[q] += weight(t * kTile + 4 * lane + e, resid);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int t = t0 + q * kWaves;
+                const unsigned long long ts = wave_sum_u64(s[q]);
+                if (t < ntiles && lane == 0) tsum[t] = ts;
+            }
+        }
+        __syncthreads();
+        unsigned long long part = 0;
+        for (int t = tid; t < ntiles; t += kBlock) part += tsum[t];
+        return block_sum_u64(part);
+    };
+    unsigned long long Wf = tile_sums(res);
+    *W = (float)((double)Wf * kInvMassUnit);
+    const bool fb = res && Wf == 0;
+    *fallback = fb;
+    if (fb) Wf = tile_sums(false);
+    if (Wf == 0) return -1;
+    const bool resid = res && !fb;
+    // the target: floor(u * W), u = m * 2^-24 (exact in two parts)
+    const unsigned long long m = (unsigned long long)(u * 16777216.f);
+    const unsigned long long target = (Wf >> 24) * m + (((Wf & 0xffffffull) * m) >> 24);
+    // the tile holding the first running sum > target: thread t scans its
+    // contiguous run of tiles after a block scan of the runs' sums
+    const int per = (ntiles + kBlock - 1) / kBlock;
+    const int t0 = tid * per, t1 = min(ntiles, t0 + per);
+    unsigned long long run = 0;
+    for (int t = t0; t < t1; ++t) run += tsum[t];
+    const unsigned long long incl = wave_scan_incl_u64(run);
+    if (lane == kWave - 1) xSeg[wave] = incl;
+    if (tid == 0) xTile = -1;
+    __syncthreads();
+    unsigned long long before = incl - run;
+    for (int w = 0; w < wave; ++w) before += xSeg[w];
+    if (before <= target && target < before + run) {
+        unsigned long long acc = before;
+        for (int t = t0; t < t1; ++t) {
+            if (target < acc + tsum[t]) {
+                xTile = t;
+                xBase = acc;
+                break;
+            }
+            acc += tsum[t];
+        }
+    }
+    __syncthreads();
+    const int tile = xTile;                   // found, as target < W (a miss draws nothing)
+    if (tile < 0) {
+        if (tid == 0) xTok = -1;
+    } else if (wave == 0) {
+        unsigned long long e[4], ls = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            e[j] = weight(tile * kTile + 4 * lane + j, resid);
+            ls += e[j];
+        }
+        unsigned long long acc = xBase + wave_scan_incl_u64(ls) - ls;
+        int hit = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc += e[j];
+            if (hit == 0x7fffffff && e[j] > 0 && acc > target) hit = tile * kTile + 4 * lane + j;
+        }
+        const unsigned long long any = __ballot(hit != 0x7fffffff);
+        if (any) {
+            const int first = __ffsll((long long)any) - 1;
+            const int tok = __shfl(hit, first, kWave);
+            if (lane == 0) xTok = tok;
+        } else if (lane == 0) {
+            xTok = -1;
+        }
+    }
+    __syncthreads();
+    const int tok = xTok;
+    __syncthreads();
+    return tok;
+}
+
 // One wave (lane i holding entry i): the kept set of a row from its
 // candidates at or above the top-k threshold, (cw, cx)[0, n) with
 // 1 <= n <= 64, with cross-lane operations and no block barriers: rank
 // (value desc, index asc) by lane reads, order by ds_permute, DPP scan, cut
 // at top-p by ballots.  Publishes the kept list and the row's TruncRow,
 // leaves the sorted kept list in (kv, kx)[0, n_kept) and the TruncRow in
-// *out (lane 0).  rowM / rowS: the whole row's statistics (for top-p alone);
+// *out (lane 0); when the candidates cannot settle the row (top-p alone,
+// short of top_p) it publishes nothing and *out has n_kept == kNeedsExact.  rowM / rowS: the whole row's statistics (for top-p alone);
 // flags: flags found so far.
 __device__ __forceinline__ void short_merge_wave(const Args& a, long long rowid, const Plan& pl,
                                                  const float* cw, const int* cx, int n, float rowM,
@@ -699,16 +1070,15 @@ __device__ __forceinline__ void short_merge_wave(const Args& a, long long rowid,
         }
     }
     if (none) {
-        flags |= SPECV_FLAG_CAND_OVERFLOW;
+        // top-p alone and the candidates hold less than top_p: nothing is
+        // published; the caller takes the exact truncation
         if (lane == 0) {
             TruncRow o{};
             o.zmax = -kInf;
             o.tstar = kInf;
             o.flags = flags;
+            o.n_kept = kNeedsExact;
             *out = o;
-            publish(&tr->bad, 0u);
-            publish(&tr->flags, flags);
-            publish(&tr->n_kept, 0);
         }
         return;
     }
@@ -747,12 +1117,13 @@ __device__ __forceinline__ void short_merge_wave(const Args& a, long long rowid,
 // its first S slots, at most kKeptCap / 2 gathered and 64 kept per row);
 // otherwise it returns false having published nothing, and the caller merges
 // the rows one at a time.  On true, out[0] / out[1] hold the rows'
-// TruncRows (as row_merge returns them) for every thread.
+// TruncRows (as row_merge returns them, a row marked kNeedsExact included)
+// for every thread.
 template <bool BF16>
 __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, const Plan& pl,
                                                TruncScratch& sc, TruncRow* out) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    if (pl.keff > kWave) return false;
+    if (pl.keff > kWave || (pl.kmode && pl.top_k > pl.keff)) return false;
     constexpr int kHalf = kKeptCap / 2;
     const long long row0 = side_row(a, b, k, 0), row1 = side_row(a, b, k, 1);
     __shared__ float pL[2], pM[2], pS[2];
@@ -921,6 +1292,14 @@ __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, cons
         short_merge_wave(a, wave ? row1 : row0, pl, sc.w + wave * kHalf, sc.idx2 + wave * kHalf, wave ? nk[1] : nk[0],
                          pM[wave], pS[wave], 0u, sc.v + wave * kHalf, sc.idx + wave * kHalf, &pOut[wave]);
     __syncthreads();
+    if (tid == 0) {
+        // top-p alone short of top_p among a row's candidates: that row is
+        // marked for the exact truncation, with its maximum
+#pragma unroll
+        for (int side = 0; side < 2; ++side)
+            if (pOut[side].n_kept == kNeedsExact) pOut[side].zmax = pM[side];
+    }
+    __syncthreads();
     out[0] = pOut[0];
     out[1] = pOut[1];
     __syncthreads();
@@ -931,14 +1310,16 @@ __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, cons
 // every chunk's candidates are published.  Publishes the kept list and the
 // row's TruncRow, and returns the TruncRow to every thread; when the row
 // keeps n_kept > 0 entries, sc.v / sc.idx [0, n_kept) also hold the kept
-// list (value descending, index ascending) on return.
+// list (value descending, index ascending) on return.  A row the candidates
+// cannot settle is returned unpublished with n_kept == kNeedsExact, its
+// maximum in zmax and its flags so far: row_settle finishes it.
 template <bool BF16>
 __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int side, const Plan& pl,
                               TruncScratch& sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const long long rowid = side_row(a, b, k, side);
     __shared__ float sL, sM, sS, sZ1;
-    __shared__ unsigned sBad, sFlags;
+    __shared__ unsigned sBad, sFlags, sExact;
     __shared__ int sTotal, sN, sJ, sLevelStart, sMaxCnt;
     __shared__ TruncRow sOut;
     unsigned* off = sc.off;                // chunk offsets [0, C]
@@ -967,6 +1348,7 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
     if (tid == 0) {
         sBad = 0;
         sFlags = 0;
+        sExact = 0;
         sN = 0;
         sJ = 0x7fffffff;
         sLevelStart = 0x7fffffff;
@@ -1001,7 +1383,7 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         const unsigned long long any_ovf = __ballot(ovf);
         if (lane == 0) {
             sL = L;
-            if (any_ovf) sFlags |= SPECV_FLAG_CAND_OVERFLOW;
+            if (any_ovf) sExact = 1;           // a chunk's list overflowed: heavy ties
         }
     } else if (wave == 1) {
         float m = -kInf, s = 0.f;
@@ -1018,6 +1400,31 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         }
     }
     __syncthreads();
+    TruncRow* tr = &a.ws.trow[rowid];
+    auto publish_bad = [&]() {
+        if (tid == 0) {
+            sOut.bad = 1;
+            sOut.n_kept = 0;
+            publish(&tr->bad, 1u);
+            publish(&tr->flags, 0u);
+            publish(&tr->n_kept, 0);
+        }
+        __syncthreads();
+        return sOut;
+    };
+    // a row the candidate lists cannot settle: nothing published; the
+    // caller takes the exact truncation (row_settle)
+    auto needs_exact = [&](float zmax, unsigned flags) {
+        TruncRow o{};
+        o.zmax = zmax;
+        o.tstar = kInf;
+        o.flags = flags;
+        o.n_kept = kNeedsExact;
+        return o;
+    };
+    if (sBad) return publish_bad();
+    // top_k beyond the candidates, or a list that overflowed: exactly
+    if ((pl.kmode && pl.top_k > pl.keff) || sExact) return needs_exact(sM, 0u);
     // gather the candidates >= max L into LDS
     const float L = sL;
     const int total = sTotal;
@@ -1081,21 +1488,9 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         gather(kkey, 0);
     }
     const int n1 = sN;
-    if (n1 > kKeptCap && tid == 0) sFlags |= SPECV_FLAG_CAND_OVERFLOW;
-    __syncthreads();
-    TruncRow* tr = &a.ws.trow[rowid];
-    if ((sFlags & SPECV_FLAG_CAND_OVERFLOW) || sBad || n1 == 0) {
-        if (tid == 0) {
-            sOut.bad = (sBad || n1 == 0) ? 1u : 0u;
-            sOut.flags = sFlags;
-            sOut.n_kept = 0;
-            publish(&tr->bad, sOut.bad);
-            publish(&tr->flags, sFlags);
-            publish(&tr->n_kept, 0);
-        }
-        __syncthreads();
-        return sOut;
-    }
+    // more candidates above the top-k key than LDS holds (ties): exactly
+    if (n1 > kKeptCap) return needs_exact(sM, 0u);
+    if (n1 == 0) return publish_bad();
     // top-k: the K-th largest value (with multiplicity) ends the kept set,
     // and every entry equal to it is kept; those entries are moved to
     // (w, idx2), then sorted into (v, idx): value desc, index asc
@@ -1117,6 +1512,7 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         // the usual short list (top-k of a few dozen): one wave
         if (wave == 0) short_merge_wave(a, rowid, pl, sc.w, sc.idx2, nk1, sM, sS, sFlags, sc.v, sc.idx, &sOut);
         __syncthreads();
+        if (sOut.n_kept == kNeedsExact) return needs_exact(sM, sOut.flags);
         return sOut;
     }
     rank_sort(sc.w, sc.idx2, nk1, sc.v, sc.idx, ByValue{}, reinterpret_cast<int*>(sc.hist));
@@ -1141,20 +1537,8 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
         }
         __syncthreads();
         if (sJ == 0x7fffffff) {
-            if (!pl.kmode) {
-                // top-p alone: the candidates hold less than top_p of the mass
-                if (tid == 0) {
-                    sFlags |= SPECV_FLAG_CAND_OVERFLOW;
-                    sOut.bad = 0;
-                    sOut.flags = sFlags;
-                    sOut.n_kept = 0;
-                    publish(&tr->bad, 0u);
-                    publish(&tr->flags, sFlags);
-                    publish(&tr->n_kept, 0);
-                }
-                __syncthreads();
-                return sOut;
-            }
+            // top-p alone: the candidates hold less than top_p of the mass
+            if (!pl.kmode) return needs_exact(sM, sFlags);
             jstar = nk1 - 1;                // rounding: keep the whole top-k set
         } else {
             jstar = sJ;
@@ -1194,8 +1578,19 @@ __device__ __forceinline__ TruncRow row_merge(const Args& a, int b, int k, int s
     return sOut;
 }
 
+// A row that row_merge / row_merge_pair marked kNeedsExact gets the exact
+// whole-row truncation (published, returned to every thread); any other row
+// is returned as it is.  Each kernel calls this from one place, so that the
+// slow path is inlined once.
+template <bool BF16>
+__device__ __forceinline__ TruncRow row_settle(const Args& a, int b, int k, int side, const Plan& pl,
+                                               const TruncRow& t, TruncScratch& sc) {
+    if (t.n_kept != kNeedsExact) return t;
+    return row_truncate_exact<BF16>(a, b, k, side, pl, t.zmax, t.flags, sc);
+}
+
 __device__ inline bool trow_dead(const TruncRow& t) {
-    return t.bad != 0 || (t.flags & SPECV_FLAG_CAND_OVERFLOW) || t.n_kept == 0;
+    return t.bad != 0 || t.n_kept == 0;
 }
 
 // Probability of raw logit z under a truncated row: membership in the kept
@@ -1206,19 +1601,19 @@ __device__ inline float trunc_prob(const TruncRow& t, float z, float scale) {
 }
 
 // A draft row's truncation from the drafter's statistics (specv_draft_stats):
-// kept set {z >= threshold}, max, and the kept set's sum; flags as the
-// drafter found them.  A row the drafter marked non-finite is bad; one with
-// candidates that overflowed keeps nothing.
+// kept set {z >= threshold}, max, and the kept set's sum (threshold form);
+// flags as the drafter found them.  A row the drafter marked non-finite, or
+// whose statistics are not valid, is bad.
 __device__ inline TruncRow stats_trow(const specv_draft_stats& st) {
     TruncRow t{};
     const unsigned fl = (unsigned)st.flags;
     t.zmax = st.max;
     t.tstar = st.threshold;
     t.S = st.sum;
-    t.flags = fl & (SPECV_FLAG_TOPP_NEAR | SPECV_FLAG_CAND_OVERFLOW);
+    t.flags = fl & SPECV_FLAG_TOPP_NEAR;
     const bool valid = st.sum > 0.f && finite_logit(st.max) && !__builtin_isnan(st.threshold);
-    t.bad = (fl & SPECV_FLAG_NONFINITE_ROW) || (!valid && !(fl & SPECV_FLAG_CAND_OVERFLOW)) ? 1u : 0u;
-    t.n_kept = valid && !t.bad && !(fl & SPECV_FLAG_CAND_OVERFLOW) ? 1 : 0;
+    t.bad = (fl & SPECV_FLAG_NONFINITE_ROW) || !valid ? 1u : 0u;
+    t.n_kept = t.bad ? 0 : kThresholdForm;
     return t;
 }
 
@@ -1259,10 +1654,19 @@ __device__ int trunc_sample(const Args& a, int b, int pos, bool res, float u, co
     }
     __syncthreads();
     const int n = tT.n_kept;
-    if (n <= 0) return -1;                  // (a dead row is never sampled)
-    const Cand* kept = a.ws.kept + side_row(a, b, pos, 0) * a.kept_cap;
     const int dpm = res && pm ? draft_token(a, b, pos) : -1;
     const void* qrow = res && !pm ? row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, pos) : nullptr;
+    if (n == kThresholdForm) {
+        // kept set {z >= tstar} without a list: a scan of the row
+        const TruncRow t = tT, q = tQ;
+        float W;
+        const int tok = threshold_draw<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, pos), t, qrow, q, dpm, res, a.V,
+                                             scale, u, sc, &W, fallback);
+        *wres = res ? W : 0.f;
+        return tok;
+    }
+    if (n <= 0) return -1;                  // (a dead row is never sampled)
+    const Cand* kept = a.ws.kept + side_row(a, b, pos, 0) * a.kept_cap;
     if (n <= kWave) {
         // a short kept list: one wave weighs, orders by token, scans and
         // picks, lane i holding entry i

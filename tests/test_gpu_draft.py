@@ -6,8 +6,9 @@ statistics (``specv_verify_sample_qstats``) with ``specv_verify_sample``
 Covered: the tiny workload over 20,000 rows with a chi-square test of the
 draws, the serving batch at full size (all positions in one call, and one
 position per call), greedy rows, ragged vocabularies and unaligned rows,
-gamma at its maximum, rows that define no draw, truncated rows (flagged, and
-verified from their draft rows), and statistics that mark a row non-finite.
+gamma at its maximum, rows that define no draw, truncated rows (including
+rows only the exact whole-row truncation settles, verified from their draft
+rows), and statistics that mark a row non-finite.
 """
 
 import numpy as np
@@ -145,13 +146,41 @@ def test_draft_rows_without_a_draw(gpu):
         assert (tok[b] == -1).all() and (fl[b] == sv.FLAG_UNSUPPORTED).all() and np.isnan(st[b]).all()
     # every other row against the oracle (same row indices, so same uniforms)
     _check_draft(o, d, prm, 5, max_tol=0.2, skip_rows=(4, 5))
-    # with truncation workspace the top-k row draws too; top-p alone on this
-    # flat row needs far more than max_top_k candidates per chunk, so that
-    # row is flagged CAND_OVERFLOW and gets no token
+    # with truncation workspace the top-k row draws too, and so does top-p
+    # alone on this flat row, whose kept set needs far more than max_top_k
+    # candidates per chunk (the exact whole-row truncation)
     with sv.Verifier(B, n, V, max_top_k=16) as v:
         o = _draw(v, torch.from_numpy(d).cuda(), prm, 5)
-    _check_draft(o, d, prm, 5, max_tol=0.2, skip_rows=(5,))
-    assert (o["tokens"][5] == -1).all() and (o["flags"][5] == sv.FLAG_CAND_OVERFLOW).all()
+    _check_draft(o, d, prm, 5, max_tol=0.2)
+    assert (o["tokens"][5] >= 0).all() and not (o["flags"][5] & sv.FLAG_CAND_OVERFLOW).any()
+
+
+@pytest.mark.parametrize("k,p", [(0, 0.9), (0, 0.95), (50, 1.0), (300, 0.9)])
+def test_draft_exact_truncation_full_vocab(gpu, k, p):
+    """V=152064 bf16 draft rows the candidates cannot settle: flat rows
+    (sigma 0.1) with top-p alone, a constant row, a 3000-way tie at the
+    top-k threshold, top_k above max_top_k (64); draws and statistics match
+    the oracle, and verification from those statistics matches the
+    verification that re-reads the draft rows, bit for bit."""
+    rng = np.random.default_rng(900 + k + int(100 * p))
+    B, n, V = 6, 3, 152064
+    d = (rng.standard_normal((B, n, V)) * 0.1).astype(np.float32)
+    d[0] = 0.25
+    ids = rng.choice(V, size=3030, replace=False)
+    d[1, :, ids[:30]] = 3.0
+    d[1, :, ids[30:]] = 2.0
+    dt = torch.from_numpy(d).to(torch.bfloat16)
+    df = dt.float().numpy()
+    prm = _prm(B, 1.0, k, p)
+    with sv.Verifier(B, n, V, max_top_k=64) as v:
+        o = _draw(v, dt.cuda(), prm, 0xE7 + k)
+        _check_draft(o, df, prm, 0xE7 + k, max_tol=0.2)
+        fl = o["flags"].cpu().numpy()
+        assert (o["tokens"].cpu().numpy() >= 0).all()
+        assert not (fl & (sv.FLAG_CAND_OVERFLOW | sv.FLAG_UNSUPPORTED)).any()
+        t = (df[:, :1] + 0.05 * rng.standard_normal((B, n + 1, V))).astype(np.float32)
+        tt = torch.from_numpy(t).to(torch.bfloat16).cuda()
+        _verify_both(v, tt, dt.cuda(), o["tokens"], o["stats"], prm, 0xE8 + k)
 
 
 def test_draft_truncated_full_size(gpu):

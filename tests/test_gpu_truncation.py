@@ -5,8 +5,9 @@ The truncated workload: B=32, gamma=5, V=152064, bf16, T=0.7, top-k=50 and
 top-p=0.9 on target and draft alike, draft tokens drawn from the truncated
 draft distribution (Philox purpose DRAFT, by the oracle's sampler).  Plus
 top-k alone, top-p alone, k=1, ties at the threshold, top_p=0, ragged float32
-vocabularies, and the documented limits (candidate overflow, a handle
-without truncation workspace).
+vocabularies; rows the candidate lists cannot settle (top-p alone on flat
+rows, ties beyond every buffer, top_k above max_top_k), which take the exact
+whole-row truncation; and a handle without truncation workspace.
 """
 
 import numpy as np
@@ -119,22 +120,93 @@ def test_truncation_with_caps_eos_and_greedy_rows(gpu):
         check(out, orc, toks2, tf2, df2, prm, max_tol=0.1)
 
 
-def test_top_p_alone_beyond_candidates_is_flagged(gpu):
-    """Top-p without top-k on a flat distribution needs more tokens than the
-    handle's max_top_k candidates: the row is flagged CAND_OVERFLOW and emits
-    nothing (a documented limit), instead of a wrong sample."""
-    rng = np.random.default_rng(2)
-    B, gamma, V = 4, 2, 30000
-    t = (rng.standard_normal((B, gamma + 1, V)) * 0.1).astype(np.float32)
-    d = (t[:, :gamma] + 0.05 * rng.standard_normal((B, gamma, V))).astype(np.float32)
-    toks = d.argmax(-1).astype(np.int32)
-    with sv.Verifier(B, gamma, V, max_top_k=64) as v:
-        out = v.verify_sample(torch.from_numpy(t).cuda(), torch.from_numpy(d).cuda(),
-                              torch.from_numpy(toks).cuda(), sv.make_row_params(B, 1.0, 0, 0.9), 3)
-        torch.cuda.synchronize()
+def _no_overflow(out):
     f = out["row_flags"].cpu().numpy()
-    assert (f & sv.FLAG_CAND_OVERFLOW).all()
-    assert (out["num_emitted"].cpu().numpy() == 0).all()
+    assert not (f & (sv.FLAG_CAND_OVERFLOW | sv.FLAG_UNSUPPORTED)).any()
+
+
+@pytest.mark.parametrize("top_p", [0.9, 0.95])
+def test_top_p_alone_flat_rows_full_vocab(gpu, top_p):
+    """Top-p without top-k on flat rows (sigma 0.1, V=152064, bf16, T=1): the
+    kept set holds most of the vocabulary, far more than the candidates, and
+    comes from the exact whole-row truncation; parity with the oracle."""
+    rng = np.random.default_rng(int(top_p * 1000))
+    B, gamma, V = 8, 3, 152064
+    t, d = synth.make_logits(rng, B, gamma, V, 0.1, 0.05)
+    tt, dd = torch.from_numpy(t).to(torch.bfloat16), torch.from_numpy(d).to(torch.bfloat16)
+    prm = _prm(B, 1.0, 0, top_p)
+    out, orc, toks, tf, df = run_trunc(tt, dd, prm, 0xF1A7, max_top_k=64)
+    rep = check(out, orc, toks, tf, df, prm, max_tol=0.1,
+                workload=f"top-p {top_p} alone, flat rows sigma 0.1, B=8 gamma=3 V=152064 bf16")
+    assert rep.value_checks > 0
+    _no_overflow(out)
+
+
+def _tied_rows(rng, B, gamma, V):
+    """Rows whose top-k threshold sits in a huge tie: b % 3 == 0 constant rows
+    (every chunk's candidate list overflows), b % 3 == 1 thirty entries at 3
+    and 3000 at 2 over N(0, 0.3) (more tied candidates than LDS holds),
+    b % 3 == 2 ordinary rows; draft rows the target's with a few entries
+    moved, so that the accept tests see p != q."""
+    t = (rng.standard_normal((B, gamma + 1, V)) * 0.3).astype(np.float32)
+    for b in range(B):
+        for i in range(gamma + 1):
+            if b % 3 == 0:
+                t[b, i] = 0.5
+            elif b % 3 == 1:
+                ids = rng.choice(V, size=3030, replace=False)
+                t[b, i, ids[:30]] = 3.0
+                t[b, i, ids[30:]] = 2.0
+            else:
+                t[b, i, rng.choice(V, size=20, replace=False)] += 4.0
+    d = t[:, :gamma].copy()
+    for b in range(B):
+        for i in range(gamma):
+            d[b, i, rng.choice(V, size=200, replace=False)] += 1.0
+    return t, d
+
+
+@pytest.mark.parametrize("k,p", [(50, 1.0), (50, 0.8), (0, 0.5)])
+def test_heavy_ties_full_vocab(gpu, k, p):
+    """Ties at the threshold beyond every candidate buffer (V=152064, bf16):
+    constant rows, a 3000-way tie, ordinary rows in one batch."""
+    rng = np.random.default_rng(17 + k)
+    B, gamma, V = 6, 2, 152064
+    t, d = _tied_rows(rng, B, gamma, V)
+    tt, dd = torch.from_numpy(t).to(torch.bfloat16), torch.from_numpy(d).to(torch.bfloat16)
+    prm = _prm(B, 1.0, k, p)
+    out, orc, toks, tf, df = run_trunc(tt, dd, prm, 0x71E5 + k, max_top_k=64)
+    check(out, orc, toks, tf, df, prm, max_tol=0.2,
+          workload=f"heavy ties top-k {k} top-p {p}, B=6 gamma=2 V=152064 bf16")
+    _no_overflow(out)
+
+
+@pytest.mark.parametrize("k,p", [(100, 1.0), (2000, 0.9), (5000, 1.0), (17, 0.95)])
+def test_top_k_beyond_max_top_k(gpu, k, p):
+    """top_k above the handle's max_top_k (16): the rows are truncated
+    exactly over the whole row instead of being refused."""
+    rng = np.random.default_rng(300 + k)
+    B, gamma, V = 8, 3, 40000
+    t, d = synth.make_logits(rng, B, gamma, V, 2.0, 0.5, boost_count=20)
+    tt, dd = torch.from_numpy(t).to(torch.bfloat16), torch.from_numpy(d).to(torch.bfloat16)
+    prm = _prm(B, 0.8, k, p)
+    out, orc, toks, tf, df = run_trunc(tt, dd, prm, 0xB16 + k, max_top_k=16)
+    check(out, orc, toks, tf, df, prm, max_tol=0.2,
+          workload=f"top-k {k} > max_top_k 16, top-p {p}, B=8 gamma=3 V=40000 bf16")
+    _no_overflow(out)
+
+
+def test_exact_truncation_f32_rows(gpu):
+    """The exact truncation on float32 keys (four radix passes): top-p alone on
+    flat rows and a constant row, ragged V."""
+    rng = np.random.default_rng(404)
+    B, gamma, V = 6, 2, 50001
+    t, d = synth.make_logits(rng, B, gamma, V, 0.2, 0.1)
+    t[0] = 1.25
+    prm = _prm(B, 0.9, 0, 0.9)
+    out, orc, toks, tf, df = run_trunc(torch.from_numpy(t), torch.from_numpy(d), prm, 0xF32, max_top_k=32)
+    check(out, orc, toks, tf, df, prm, max_tol=0.2)
+    _no_overflow(out)
 
 
 def test_handle_without_truncation_workspace(gpu):
