@@ -39,10 +39,16 @@
  * Ownership: the caller owns every input and output buffer.  A handle owns a
  * device workspace allocated once by specv_create and freed by
  * specv_destroy; verify calls allocate nothing.  One handle serves one stream
- * at a time (calls on a handle must not overlap).  Each call takes a fresh
- * tag for the records its workgroups exchange, chosen on the host when the
- * call is made, so a call captured into a HIP graph must not be replayed:
- * replays would reuse the tag and could read the previous replay's records.
+ * at a time (calls on a handle must not overlap).  Calls enqueue one kernel
+ * and nothing else (no memset, no host synchronisation), and may be captured
+ * into a HIP graph and replayed.  The records a launch's workgroups exchange
+ * are tagged with a call number: an eager call takes it from the handle (on
+ * the host); a call made while its stream is being captured launches a
+ * kernel that takes it on the device and advances it there (one closing
+ * workgroup per launch), so every replay gets its own.  The two kinds keep
+ * separate records in the handle and may be mixed freely.  A replay repeats
+ * the captured arguments, seed and step included, and so draws the same
+ * uniforms as the captured call on the same inputs.
  *
  * Errors: every argument error is reported synchronously, before anything is
  * enqueued, as a non-zero specv_status.  Calls are otherwise asynchronous on
@@ -196,12 +202,15 @@ SPECV_API specv_status specv_verify_sample(specv_handle h, void* stream,
  * on a device clears its array with a kernel on ``stream``.  Every call on
  * a device shares that device's array: calls that overlap on one device
  * (on other streams, or from host threads without stream order between
- * them) race, and their outputs are undefined.  As with a handle, a call
- * captured into a HIP graph must not be replayed. */
+ * them) race, and their outputs are undefined.  Every call takes its call
+ * number on the device (the array keeps no host state), so a call may be
+ * captured into a HIP graph and replayed; when the captured call is the
+ * device's first, the graph also holds the clearing kernel, and every
+ * replay clears the array first (correct, only slower). */
 #define SPECV_NOALLOC_MAX_BATCH 256
 #define SPECV_NOALLOC_MAX_GAMMA 15
 #define SPECV_NOALLOC_MAX_VOCAB 262144
-#define SPECV_NOALLOC_SCRATCH_BYTES 6832128
+#define SPECV_NOALLOC_SCRATCH_BYTES 11567872
 SPECV_API specv_status specv_verify_sample_noalloc(int device, void* stream,
                                  const void* target_logits, int64_t t_stride_b, int64_t t_stride_pos,
                                  const void* draft_logits, int64_t d_stride_b, int64_t d_stride_pos,

@@ -19,7 +19,16 @@ struct specv_ctx {
     int max_chunks;
     int cand_cap;      // candidates per (row, chunk); 0 without truncation support
     int kept_cap;      // kept-set entries per row
+    // The exchange records, in two forms.  Eager calls use ``ws``: the host
+    // numbers them (``epoch``), tagged records in one set, counters and
+    // status words in two sets by parity.  Calls made while the stream is
+    // being captured into a graph use ``ws_dev``: the launch takes its number
+    // on the device (every replay a new one), all records in two sets.  The
+    // truncation storage (written before it is read within each launch) is
+    // shared.
     specv::Workspace ws;
+    specv::Workspace ws_dev;
+    unsigned epoch = 0;             // the host's call number (eager calls)
     // profiling: a ring of event triples, drained by specv_get_profile or
     // when the ring wraps
     bool prof = false;
@@ -29,7 +38,6 @@ struct specv_ctx {
     int prof_calls = 0;
     double ms_kernel = 0.0;
     std::vector<float> samples;     // per-call kernel milliseconds since the last reset
-    unsigned epoch = 0;             // call number; the kernel tags published decisions with it
 };
 
 namespace {
@@ -70,18 +78,58 @@ hipError_t alloc(T** p, size_t count) {
     return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T) + 256);
 }
 
-void free_ws(specv::Workspace& ws) {
+// The records of one workspace form (not the shared truncation storage).
+void free_records(specv::Workspace& ws) {
     if (ws.stats) (void)hipFree(ws.stats);
     if (ws.pair) (void)hipFree(ws.pair);
     if (ws.rowrec) (void)hipFree(ws.rowrec);
     if (ws.status) (void)hipFree(ws.status);
     if (ws.wsum) (void)hipFree(ws.wsum);
     if (ws.ctr) (void)hipFree(ws.ctr);
+    if (ws.calls) (void)hipFree(ws.calls);
+    if (ws.seen) (void)hipFree(ws.seen);
+    if (ws.dims) (void)hipFree(ws.dims);
+}
+
+void free_ws(specv_ctx* h) {
+    free_records(h->ws);
+    free_records(h->ws_dev);
+    specv::Workspace& ws = h->ws;
     if (ws.cand) (void)hipFree(ws.cand);
     if (ws.cand_meta) (void)hipFree(ws.cand_meta);
     if (ws.trow) (void)hipFree(ws.trow);
     if (ws.kept) (void)hipFree(ws.kept);
-    ws = specv::Workspace{};
+    h->ws = specv::Workspace{};
+    h->ws_dev = specv::Workspace{};
+}
+
+// Allocates the records of one workspace form: ``sets`` sets of the tagged
+// records (1: host-numbered, 2: device-numbered), two sets of counters and
+// status words, and (device-numbered) the call number's words.
+bool alloc_records(specv::Workspace& ws, const specv_config* cfg, int max_chunks, int sets) {
+    const size_t groups = (size_t)cfg->max_batch * (cfg->max_gamma + 1);
+    ws.n_groups = (int)groups;
+    ws.n_rows = cfg->max_batch;
+    const long long n_stats = (long long)groups * 2 * max_chunks * 2;
+    const long long n_pair = (long long)groups;
+    const long long n_rowrec = (long long)cfg->max_batch * specv::kRowWords;
+    const long long n_wsum = (long long)cfg->max_batch * max_chunks * 2;
+    // the kernels address set p at base + p * set size: one set means size 0
+    ws.set_stats = sets == 2 ? n_stats : 0;
+    ws.set_pair = sets == 2 ? n_pair : 0;
+    ws.set_rowrec = sets == 2 ? n_rowrec : 0;
+    ws.set_wsum = sets == 2 ? n_wsum : 0;
+    bool ok = alloc(&ws.stats, sets * (size_t)n_stats) == hipSuccess &&
+              alloc(&ws.pair, sets * (size_t)n_pair) == hipSuccess &&
+              alloc(&ws.rowrec, sets * (size_t)n_rowrec) == hipSuccess &&
+              alloc(&ws.wsum, sets * (size_t)n_wsum) == hipSuccess &&
+              alloc(&ws.ctr, 2 * groups * specv::kSlot) == hipSuccess &&
+              alloc(&ws.status, (size_t)2 * cfg->max_batch * (specv::kSlot / 2)) == hipSuccess;
+    if (ok && sets == 2)
+        ok = alloc(&ws.calls, (size_t)specv::kSlot) == hipSuccess &&
+             alloc(&ws.seen, (size_t)2 * cfg->max_batch * specv::kSlot) == hipSuccess &&
+             alloc(&ws.dims, (size_t)specv::kSlot) == hipSuccess;
+    return ok;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -135,53 +183,66 @@ specv::Args base_args(const specv::Limits& lim, int B, int gamma, int V) {
     return a;
 }
 
-// Zero the epoch-tagged records and the arrival counters (handle creation,
-// and the rare epoch wrap).  Fresh allocations may
-// hold another handle's words with the same epoch numbers, so every tagged
-// array is cleared.
-hipError_t clear_ws(specv_ctx* h, hipStream_t stream) {
-    const specv::Workspace& ws = h->ws;
-    const size_t groups = (size_t)h->cfg.max_batch * (h->cfg.max_gamma + 1);
-    hipError_t e = hipMemsetAsync(ws.stats, 0, groups * 2 * h->max_chunks * 2 * sizeof(unsigned long long),
-                                  stream);
-    const size_t rows = (size_t)h->cfg.max_batch;
-    if (e == hipSuccess) e = hipMemsetAsync(ws.pair, 0, groups * sizeof(specv::PairRec), stream);
+// Zero the records of one workspace form.  Fresh allocations may hold
+// anything, another handle's tagged words included.
+hipError_t clear_records(const specv::Workspace& ws, const specv_config& cfg, int max_chunks, hipStream_t stream) {
+    const size_t groups = (size_t)cfg.max_batch * (cfg.max_gamma + 1);
+    const size_t rows = (size_t)cfg.max_batch;
+    const int sets = ws.set_stats ? 2 : 1;
+    hipError_t e = hipMemsetAsync(ws.stats, 0, sets * groups * 2 * max_chunks * 2 * sizeof(unsigned long long), stream);
+    if (e == hipSuccess) e = hipMemsetAsync(ws.pair, 0, sets * groups * sizeof(specv::PairRec), stream);
     if (e == hipSuccess)
-        e = hipMemsetAsync(ws.rowrec, 0, rows * specv::kRowWords * sizeof(unsigned long long), stream);
+        e = hipMemsetAsync(ws.rowrec, 0, sets * rows * specv::kRowWords * sizeof(unsigned long long), stream);
     if (e == hipSuccess)
-        e = hipMemsetAsync(ws.wsum, 0, rows * h->max_chunks * 2 * sizeof(unsigned long long), stream);
+        e = hipMemsetAsync(ws.wsum, 0, sets * rows * max_chunks * 2 * sizeof(unsigned long long), stream);
     if (e == hipSuccess) e = hipMemsetAsync(ws.ctr, 0, 2 * groups * specv::kSlot * sizeof(unsigned), stream);
     if (e == hipSuccess)
         e = hipMemsetAsync(ws.status, 0, 2 * rows * specv::kSlot * sizeof(unsigned), stream);
+    if (e == hipSuccess && ws.calls) e = hipMemsetAsync(ws.calls, 0, specv::kSlot * sizeof(unsigned), stream);
+    if (e == hipSuccess && ws.seen) e = hipMemsetAsync(ws.seen, 0, 2 * rows * specv::kSlot * sizeof(unsigned), stream);
+    if (e == hipSuccess && ws.dims) e = hipMemsetAsync(ws.dims, 0, 2 * specv::kSlot * sizeof(unsigned), stream);
     return e;
 }
 
-// The epoch tag of the next call, clearing every tagged record first when
-// the tags would repeat.  Verify calls advance the epoch by 1: a verify call
-// clears the counters and status words of the other parity for the next
-// one, so consecutive verify calls must alternate parity.  Sampler calls
-// touch no counters or status words and advance it by 2, keeping the parity
-// the next verify call expects; they share the tagged chunk statistics with
-// verify calls, so every call's tag is distinct.
+// The host's number of the next eager call, clearing the eager records
+// first when the tags would repeat.  Verify calls advance it by 1: a verify
+// call clears the counters and status words of the other parity for the
+// next one, so consecutive verify calls must alternate parity.  Sampler
+// calls touch no counters or status words and advance it by 2, keeping the
+// parity the next verify call expects; they share the tagged chunk
+// statistics with verify calls, so every call's tag is distinct.
 bool next_epoch(specv_handle h, hipStream_t s, unsigned step, unsigned* out) {
     unsigned next = h->epoch + step;
     if (next >= 0x7fffffffu) {
-        if (clear_ws(h, s) != hipSuccess) return false;
+        if (clear_records(h->ws, h->cfg, h->max_chunks, s) != hipSuccess) return false;
         next = step;
     }
     *out = next;
     return true;
 }
 
-// One launch of the verify kernel with the next epoch tag.  The epoch
-// advances only when the launch succeeded.
+// True while ``s`` is being captured into a graph: such a call takes its
+// number on the device, so that each replay of it gets a new one.
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
+// One launch of the verify kernel: numbered by the host (eager; the number
+// advances only when the launch succeeded) or, under capture, on the device.
 specv_status launch(specv_handle h, specv::Args& a, bool bf16, bool vec, void* stream) {
     if (hipSetDevice(h->cfg.device) != hipSuccess) return SPECV_E_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (capturing(s)) {
+        a.ws = h->ws_dev;
+        a.epoch = 0;
+        return specv::launch_verify(a, bf16, vec, true, s, nullptr) == hipSuccess ? SPECV_OK : SPECV_E_HIP;
+    }
     unsigned next;
     if (!next_epoch(h, s, 1, &next)) return SPECV_E_HIP;
+    a.ws = h->ws;
     a.epoch = next;
-    if (specv::launch_verify(a, bf16, vec, s, next_events(h)) != hipSuccess) return SPECV_E_HIP;
+    if (specv::launch_verify(a, bf16, vec, false, s, next_events(h)) != hipSuccess) return SPECV_E_HIP;
     h->epoch = next;
     return SPECV_OK;
 }
@@ -227,22 +288,21 @@ specv_status specv_create(const specv_config* cfg, specv_handle* out) {
     const size_t rows = groups * 2;                                         // logits rows
     const size_t rc = rows * h->max_chunks;
     specv::Workspace& ws = h->ws;
-    ws.n_groups = (int)groups;
-    ws.n_rows = cfg->max_batch;
-    bool ok = alloc(&ws.stats, rc * 2) == hipSuccess && alloc(&ws.pair, groups) == hipSuccess &&
-              alloc(&ws.rowrec, (size_t)cfg->max_batch * specv::kRowWords) == hipSuccess &&
-              alloc(&ws.wsum, (size_t)cfg->max_batch * h->max_chunks * 2) == hipSuccess &&
-              alloc(&ws.ctr, 2 * groups * specv::kSlot) == hipSuccess &&
-              alloc(&ws.status, (size_t)2 * cfg->max_batch * (specv::kSlot / 2)) == hipSuccess;
+    bool ok = alloc_records(h->ws, cfg, h->max_chunks, 1) && alloc_records(h->ws_dev, cfg, h->max_chunks, 2);
     // candidate storage for truncated rows, reserved only when asked for
     if (ok && h->cand_cap > 0)
         ok = alloc(&ws.cand, rc * h->cand_cap) == hipSuccess &&
              alloc(&ws.cand_meta, rc) == hipSuccess && alloc(&ws.trow, rows) == hipSuccess &&
              alloc(&ws.kept, rows * h->kept_cap) == hipSuccess;
-    if (ok) ok = clear_ws(h, nullptr) == hipSuccess;
+    h->ws_dev.cand = ws.cand;
+    h->ws_dev.cand_meta = ws.cand_meta;
+    h->ws_dev.trow = ws.trow;
+    h->ws_dev.kept = ws.kept;
+    if (ok) ok = clear_records(h->ws, *cfg, h->max_chunks, nullptr) == hipSuccess &&
+                 clear_records(h->ws_dev, *cfg, h->max_chunks, nullptr) == hipSuccess;
     if (ok) ok = hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
-        free_ws(ws);
+        free_ws(h);
         delete h;
         (void)hipGetLastError();
         return SPECV_E_NOMEM;
@@ -305,7 +365,7 @@ specv_status specv_destroy(specv_handle h) {
     (void)hipDeviceSynchronize();
     for (auto& e : h->ev)
         if (e) (void)hipEventDestroy(e);
-    free_ws(h->ws);
+    free_ws(h);
     delete h;
     return SPECV_OK;
 }
@@ -489,11 +549,18 @@ specv_status specv_sample_draft(specv_handle h, void* stream, const void* draft_
     a.cand_cap = h->cand_cap;
     a.kept_cap = h->kept_cap;
     a.max_top_k = h->cfg.max_top_k;
+    const bool vec = rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es);
+    if (capturing(s)) {
+        a.ws = h->ws_dev;
+        a.epoch = 0;
+        return specv::launch_sample_draft(a, dtype == SPECV_BF16, vec, true, s, nullptr) == hipSuccess
+                   ? SPECV_OK
+                   : SPECV_E_HIP;
+    }
     unsigned next;
     if (!next_epoch(h, s, 2, &next)) return SPECV_E_HIP;
     a.epoch = next;
-    const bool vec = rows_vec_aligned(draft_logits, d_stride_b, d_stride_pos, es);
-    if (specv::launch_sample_draft(a, dtype == SPECV_BF16, vec, s, next_events(h)) != hipSuccess)
+    if (specv::launch_sample_draft(a, dtype == SPECV_BF16, vec, false, s, next_events(h)) != hipSuccess)
         return SPECV_E_HIP;
     h->epoch = next;
     return SPECV_OK;

@@ -12,7 +12,7 @@
 // (b, i):
 //   1. reads its chunk once (16-byte loads) and reduces it to (max, sum of
 //      exp2((z - max) * log2(e) / T)), or (max, lowest argmax) for greedy
-//      rows, published as two epoch-tagged words; truncated rows also keep
+//      rows, published as two tagged words; truncated rows also keep
 //      their top-k candidates (published before the words);
 //   2. untruncated rows: wave 0 reads every chunk's words of the row (lane
 //      c: chunk c), merges them into the row's (m, s), and turns them into
@@ -134,14 +134,31 @@ __device__ __forceinline__ void draw_truncated(const DraftArgs& a, const Args& v
     }
 }
 
-template <bool BF16, bool VEC, bool TRUNC>
-__device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScratch* sc) {
+template <bool BF16, bool VEC, bool TRUNC, bool DEVCALL>
+__device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int per = a.B * a.C;
+    const int per = a0.B * a0.C;
+    const int work = a0.n * per;
+    if constexpr (DEVCALL) {
+        if ((int)blockIdx.x == work) {
+            // the closing workgroup (as in the verify kernel)
+            close_call(a0.ws, a0.B, (unsigned)(a0.n * a0.C), pack_dims(a0.B, a0.n, a0.C));
+            return;
+        }
+    }
     const int i = blockIdx.x / per;
     const int rem = blockIdx.x - i * per;
-    const int b = rem / a.C;
-    const int c = rem - b * a.C;
+    const int b = rem / a0.C;
+    const int c = rem - b * a0.C;
+    // the call number (tag and record set, as in the verify kernel); with
+    // the device's, every workgroup clears its share of the other parity's
+    // set and counts itself once nothing it waits for comes after the count
+    // (vector memory operations retire in order)
+    const unsigned e = DEVCALL ? read_call(a0.ws) : a0.epoch;
+    DraftArgs a = a0;
+    a.epoch = DEVCALL ? call_tag(e) : e;
+    a.ws = parity_set(a0.ws, e & 1u);
+    const Args va = verify_view(a);
     const float nan = __builtin_nanf("");
     const specv_row_params rp = a.params[b];
     const bool greedy = !(rp.temperature > 0.f);
@@ -152,10 +169,13 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScra
     if (trunc && (!TRUNC || a.cand_cap == 0)) {
         // the handle reserved no room for candidates
         if (c == 0 && tid == 0) write_draft(a, o, -1, nan, nan, nan, SPECV_FLAG_UNSUPPORTED);
+        if constexpr (DEVCALL) {
+            clear_other_set(a0.ws, e, blockIdx.x, work);
+            if (tid == 0) count_call(a0.ws, e, b);
+        }
         return;
     }
     const float scale = greedy ? 0.f : kLog2e / rp.temperature;
-    const Args va = verify_view(a);
     const void* row = row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i);
     const int v0 = c * kChunk;
     const int len = min(kChunk, a.V - v0);
@@ -209,6 +229,11 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScra
             for (int w = 1; w < kWaves; ++w) merge_ms(m, s, sm[w], ss[w], scale);
             publish_stats(stats_words(va, b, i, 1, c), m, __float_as_uint(s), a.epoch);
         }
+    }
+    if constexpr (DEVCALL) {
+        // behind the statistics: this workgroup's share of the clearing, and its count
+        clear_other_set(a0.ws, e, blockIdx.x, work);
+        if (tid == 0) count_call(a0.ws, e, b);
     }
     if constexpr (TRUNC) {
         if (trunc) {
@@ -395,33 +420,39 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a, TruncScra
     }
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool DEVCALL>
 __global__ __launch_bounds__(kBlock) void k_sample_draft(DraftArgs a) {
-    sample_draft_block<BF16, VEC, false>(a, nullptr);
+    sample_draft_block<BF16, VEC, false, DEVCALL>(a, nullptr);
 }
 
 // With the truncation path (handles created with max_top_k > 0) and its LDS.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool DEVCALL>
 __global__ __launch_bounds__(kBlock) void k_sample_draft_trunc(DraftArgs a) {
     __shared__ TruncScratch sc;
-    sample_draft_block<BF16, VEC, true>(a, &sc);
+    sample_draft_block<BF16, VEC, true, DEVCALL>(a, &sc);
+}
+
+template <bool DEVCALL>
+void (*pick_draft(bool bf16, bool vec, bool trunc))(DraftArgs) {
+    if (trunc)
+        return bf16 ? (vec ? k_sample_draft_trunc<true, true, DEVCALL> : k_sample_draft_trunc<true, false, DEVCALL>)
+                    : (vec ? k_sample_draft_trunc<false, true, DEVCALL> : k_sample_draft_trunc<false, false, DEVCALL>);
+    return bf16 ? (vec ? k_sample_draft<true, true, DEVCALL> : k_sample_draft<true, false, DEVCALL>)
+                : (vec ? k_sample_draft<false, true, DEVCALL> : k_sample_draft<false, false, DEVCALL>);
 }
 
 }  // namespace
 
-hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStream_t stream,
+hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, bool devcall, hipStream_t stream,
                                hipEvent_t* ev) {
-    const long long blocks = (long long)a.n * a.B * a.C;
+    const long long blocks = (long long)a.n * a.B * a.C + (devcall ? 1 : 0);   // + the closing workgroup
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    void (*fn)(DraftArgs);
-    if (a.cand_cap > 0)
-        fn = bf16 ? (vec ? k_sample_draft_trunc<true, true> : k_sample_draft_trunc<true, false>)
-                  : (vec ? k_sample_draft_trunc<false, true> : k_sample_draft_trunc<false, false>);
+    void (*fn)(DraftArgs) = devcall ? pick_draft<true>(bf16, vec, a.cand_cap > 0)
+                                    : pick_draft<false>(bf16, vec, a.cand_cap > 0);
+    if (ev)
+        hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev[0], ev[1], 0, a);
     else
-        fn = bf16 ? (vec ? k_sample_draft<true, true> : k_sample_draft<true, false>)
-                  : (vec ? k_sample_draft<false, true> : k_sample_draft<false, false>);
-    hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev ? ev[0] : nullptr,
-                          ev ? ev[1] : nullptr, 0, a);
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);   // also under capture
     return hipGetLastError();
 }
 

@@ -52,8 +52,8 @@ struct alignas(16) TruncScratch {   // 8-byte LDS atomics on v and w
 
 // Outcome of one position of one batch row (its "pair": target row k and,
 // below gamma, draft row k), published by the workgroup that decided it.
-// Every word holds (epoch << 32) | value, so a reader knows a word is this
-// call's when its epoch matches.
+// Every word holds (tag << 32) | value with the launch's tag (never 0), so a
+// reader knows a word is this launch's when its tag matches.
 enum PairWord {
     PW_STATE = 0,         // outcome | (SPECV_FLAG_* bits << 8)
     PW_P, PW_Q,           // p_k(d_k), q_k(d_k) (float bits)
@@ -68,7 +68,7 @@ struct PairRec {
 
 // How a sampling row's round ended, for its sampling workgroups: which
 // position draws the correction / bonus token, the row's flags so far, and
-// that position's normalisers.  Epoch-tagged words like PairRec.
+// that position's normalisers.  Tagged words like PairRec.
 enum RowWord {
     RW_REC = 0,           // kind | (position << 3)
     RW_MT, RW_INVT, RW_MQ, RW_INVQ,
@@ -77,16 +77,31 @@ enum RowWord {
     kRowWords = 8
 };
 
+// The records the workgroups of one launch exchange come in two sets, one
+// per parity of the call number.  A launch uses its parity's set and clears
+// the other set over the extent of the launch that used it last, which the
+// next launch then finds zeroed: every word a launch reads is either zero or
+// written by that launch.  The call number itself lives on the device, in
+// ``calls``, so that launches replayed from a captured graph still advance
+// it (the kernels' protocol: specv_rows.hpp, "call number").
 struct Workspace {
-    unsigned long long* stats;  // [max_batch * max_pos * 2 * max_chunks][2]: per (row, chunk)
-                                // epoch-tagged (max, sum) or (max, argmax)
-    PairRec* pair;              // [max_batch * max_pos]
-    unsigned long long* rowrec; // [max_batch * kRowWords]
-    unsigned long long* wsum;   // [max_batch * max_chunks * 2]: chunk sampling weight, p mass
-    unsigned* ctr;              // [2][max_batch * max_pos][kSlot]: arrivals per pair, one set
-                                // per call parity; a call clears the other parity's set
-    unsigned long long* status; // [2][max_batch][kSlot / 2]: per-row accept / stop bits, one
-                                // set per call parity
+    unsigned long long* stats;  // [2][max_batch * max_pos * 2 * max_chunks][2]: per (row,
+                                // chunk) tagged (max, sum) or (max, argmax)
+    PairRec* pair;              // [2][max_batch * max_pos]
+    unsigned long long* rowrec; // [2][max_batch * kRowWords]
+    unsigned long long* wsum;   // [2][max_batch * max_chunks * 2]: chunk sampling weight, p mass
+    unsigned* ctr;              // [2][max_batch * max_pos][kSlot]: arrivals per pair
+    unsigned long long* status; // [2][max_batch][kSlot / 2]: per-row accept / stop bits
+    long long set_stats;        // words in one set of stats
+    long long set_pair;         // records in one set of pair
+    long long set_rowrec;       // words in one set of rowrec
+    long long set_wsum;         // words in one set of wsum
+    unsigned* calls;            // [kSlot]: word 0 is the call number of the next launch
+    unsigned* seen;             // [2][max_batch][kSlot]: per parity and batch row, workgroups
+                                // of the running launch that have read the call number
+    unsigned long long* dims;   // [2] (16-byte aligned, in a slot of its own): per parity,
+                                // the extent (B, positions, chunks) of the last launch of
+                                // that parity
     int n_groups;               // max_batch * max_pos
     int n_rows;                 // max_batch
     Cand* cand;                 // [max_batch * max_pos * 2 * max_chunks * cand_cap]
@@ -120,7 +135,8 @@ struct Args {
     unsigned long long seed;
     unsigned step;
     int eos;
-    unsigned epoch;               // per-handle call number (never 0)
+    unsigned epoch;               // the launch's tag, set on the device from the call number
+                                  // (the host leaves it 0)
     int* out_acc;
     int* out_tok;
     int* out_emit;
@@ -143,7 +159,7 @@ struct DraftArgs {
     const specv_row_params* params;
     unsigned long long seed;
     unsigned step;
-    unsigned epoch;               // the handle's call number (shared with verify calls)
+    unsigned epoch;               // the launch's tag, set on the device (as Args::epoch)
     int* out_tok;                 // [B][out_stride]
     specv_draft_stats* out_stats; // [B][out_stride] or nullptr
     Workspace ws;                 // the handle's: chunk statistics and, for truncated rows,
@@ -152,7 +168,7 @@ struct DraftArgs {
     int cand_cap, kept_cap, max_top_k;
 };
 
-hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStream_t stream,
+hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, bool devcall, hipStream_t stream,
                                hipEvent_t* ev);
 
 // Launch the whole verify step on ``stream`` as one kernel: one streaming
@@ -162,7 +178,7 @@ hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, hipStrea
 // the truncation-capable variant is used when a.cand_cap > 0.  ``ev``
 // (nullable) holds two events that the launch records at the kernel's start
 // and end.
-hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev);
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, bool devcall, hipStream_t stream, hipEvent_t* ev);
 
 // The sizes a workspace is laid out for, and its truncation capacity.
 struct Limits {

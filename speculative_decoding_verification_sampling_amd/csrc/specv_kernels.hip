@@ -11,7 +11,7 @@
 //            truncated rows below gamma, of draft row k, with 16-byte loads;
 //            reduces it to chunk statistics (max / sum of exp2 for sampling
 //            rows, max / lowest argmax for greedy rows, top-k candidates for
-//            truncated rows), published as epoch-tagged words; bumps the
+//            truncated rows), published as tagged words; bumps the
 //            pair's arrival counter.  The last of the C units to arrive
 //            merges the statistics and takes position k's accept test,
 //            publishes the pair record and sets the position's bit in the
@@ -32,8 +32,10 @@
 //            and the workgroup whose chunk holds u * W finds the token with a
 //            block prefix sum.
 //
-// Hand-offs use agent-scope atomics on epoch-tagged words, polled with a
-// bound (the expiry flags the row, it never hangs the launch).  Workgroups
+// Hand-offs use agent-scope atomics on words tagged with the launch's call
+// number, polled with a bound (the expiry flags the row, it never hangs the
+// launch).  The call number is taken on the device (a ticket per workgroup,
+// specv_rows.hpp), so a launch replayed from a captured graph gets its own.  Workgroups
 // are dispatched in increasing ID order within each XCD, and every wait is
 // for words that a workgroup with a lower ID writes (the stream's decisions,
 // for the sampling workgroups) or that were stored before the status bit the
@@ -95,11 +97,12 @@ __device__ inline bool stopped_before(unsigned long long st, int k) {
     return (stop & ((1u << k) - 1u)) != 0;      // k <= 31
 }
 
-__device__ inline unsigned* pair_counter(const Args& a, unsigned par, int b, int k) {
-    return a.ws.ctr + ((long long)par * a.ws.n_groups + pair_id(a, b, k)) * kSlot;
+// (a.ws is the launch's record set: parity_set of the call number's parity)
+__device__ inline unsigned* pair_counter(const Args& a, int b, int k) {
+    return a.ws.ctr + pair_id(a, b, k) * kSlot;
 }
-__device__ inline unsigned long long* status_word(const Args& a, unsigned par, int b) {
-    return a.ws.status + ((long long)par * a.ws.n_rows + b) * (kSlot / 2);
+__device__ inline unsigned long long* status_word(const Args& a, int b) {
+    return a.ws.status + (long long)b * (kSlot / 2);
 }
 
 // ---------------------------------------------------------------- row finish
@@ -431,7 +434,7 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
         else bit = outcome == OUT_BONUS ? kBonusOk : kBonusBad;
         if (trunc) wait_stores();
         const unsigned long long old = __hip_atomic_fetch_or(
-            status_word(a, a.epoch & 1u, b), bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            status_word(a, b), bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned long long now = old | bit;
         dNew = now;
         dFinish = resolve(old, pl, a.gamma).how == H_OPEN && resolve(now, pl, a.gamma).how != H_OPEN;
@@ -621,38 +624,60 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
 // Unit (k, b, c): chunk c of target row k and (sampling and truncated rows,
 // k < gamma) of draft row k, reduced to chunk statistics that are published
 // for the pair's decision; the last unit of the pair to arrive decides it.
-// A unit at position k >= kSkipFrom first reads its row's status and skips
-// its chunk when the round is known to have stopped before k; otherwise it
-// reads (speculatively when earlier positions are undecided), so the stream
-// never waits for a decision.
+// A unit at position k >= kSkipFrom skips its chunk when its row's status
+// (st, read with the ticket) shows that the round stopped before k;
+// otherwise it reads (speculatively when earlier positions are undecided),
+// so the stream never waits for a decision.
 #ifndef SPECV_SKIP_FROM
 #define SPECV_SKIP_FROM 2
 #endif
 constexpr int kSkipFrom = SPECV_SKIP_FROM;
 
-template <bool BF16, bool VEC, bool TRUNC, int PROP>
-__device__ __forceinline__ void stream_unit(const Args& a, int k, int b, int c, TruncScratch* sc) {
+template <bool BF16, bool VEC, bool TRUNC, int PROP, bool DEVCALL>
+__device__ __forceinline__ void stream_unit(const Args& a0, int k, int b, int c, TruncScratch* sc) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const unsigned par = a.epoch & 1u;
+    // the call number (the host's, or a plain load of the device's, with the
+    // plan's loads) and, for units that may skip, the row's status word (of
+    // both parities when the number comes from the device), in one round
+    // trip.  A device-numbered workgroup counts itself only where nothing it
+    // still waits for was issued after the count (vector memory operations
+    // retire in order): on its way out, or right before the arrival, whose
+    // own round trip covers it.
     const bool check = k >= kSkipFrom;
-    // the row's status is fetched by one thread in the same memory round
-    // trip as the plan, and the skip decision shared through LDS
+    const unsigned e = DEVCALL ? read_call(a0.ws) : a0.epoch;
+    unsigned long long st0 = 0, st1 = 0;
+    if (check && tid == 0) {
+        if constexpr (DEVCALL) {
+            st0 = published(a0.ws.status + (long long)b * (kSlot / 2));
+            st1 = published(a0.ws.status + ((long long)a0.ws.n_rows + b) * (kSlot / 2));
+        } else {
+            st0 = published(a0.ws.status + ((long long)(e & 1u) * a0.ws.n_rows + b) * (kSlot / 2));
+        }
+    }
+    const Plan pl = make_plan(a0, b);
+    Args a = a0;
+    a.epoch = DEVCALL ? call_tag(e) : e;
+    a.ws = parity_set(a0.ws, e & 1u);
     __shared__ int sSkip;
-    unsigned long long st = 0;
-    if (check && tid == 0) st = published(status_word(a, par, b));
-    const Plan pl = make_plan(a, b);
     if (pl.mode == MODE_SKIP) {
         if (k == 0 && c == 0 && wave == 0) {
             write_outputs_wave(a, b, 0, 0, pl.flags, true, -1, 0.f, pl.tok);
             write_diag_wave(a, b, 0, 0.f, 0.f);
         }
+        if (DEVCALL && tid == 0) count_call(a0.ws, e, b);
         return;
     }
-    if (k >= pl.nt) return;                         // a position the round cannot consult
+    if (k >= pl.nt) {                               // a position the round cannot consult
+        if (DEVCALL && tid == 0) count_call(a0.ws, e, b);
+        return;
+    }
     if (check) {
-        if (tid == 0) sSkip = stopped_before(st, k);
+        if (tid == 0) sSkip = stopped_before((DEVCALL && (e & 1u)) ? st1 : st0, k);
         __syncthreads();
-        if (sSkip) return;
+        if (sSkip) {
+            if (DEVCALL && tid == 0) count_call(a0.ws, e, b);
+            return;
+        }
     }
     const bool greedy = pl.mode == MODE_GREEDY;
     const bool trunc = TRUNC && pl.mode == MODE_TRUNC;
@@ -719,7 +744,10 @@ __device__ __forceinline__ void stream_unit(const Args& a, int k, int b, int c, 
             }
         }
     }
-    if (tid == 0) sLast = arrive(pair_counter(a, par, b, k), trunc) == (unsigned)(a.C - 1);
+    if (tid == 0) {
+        if (DEVCALL) count_call(a0.ws, e, b);
+        sLast = arrive(pair_counter(a, b, k), trunc) == (unsigned)(a.C - 1);
+    }
     __syncthreads();
     if (sLast) decide_pair<BF16, TRUNC, PROP>(a, b, k, pl, sc);
 }
@@ -728,11 +756,22 @@ __device__ __forceinline__ void stream_unit(const Args& a, int k, int b, int c, 
 // then reads chunk c of the target (and draft) row of the position the round
 // stopped at, or of the bonus row, and takes part in the sample.  Rows of
 // other modes never need one.
-template <bool BF16, bool VEC, int PROP>
-__device__ __forceinline__ void sample_item(const Args& a, int b, int c) {
+template <bool BF16, bool VEC, int PROP, bool DEVCALL>
+__device__ __forceinline__ void sample_item(const Args& a0, int b, int c) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const Plan pl = make_plan(a, b);
+    const unsigned e = DEVCALL ? read_call(a0.ws) : a0.epoch;
+    const Plan pl = make_plan(a0, b);
+    if constexpr (DEVCALL) {
+        // the sampling workgroups clear the other parity's record set between
+        // them (they have time: most wait for their row's record), then count
+        // themselves before their first poll
+        clear_other_set(a0.ws, e, (long long)b * a0.C + c, (long long)a0.B * a0.C);
+        if (tid == 0) count_call(a0.ws, e, b);
+    }
     if (pl.mode != MODE_SAMPLE) return;
+    Args a = a0;
+    a.epoch = DEVCALL ? call_tag(e) : e;
+    a.ws = parity_set(a0.ws, e & 1u);
     __shared__ unsigned sRec[kRowWords];
     __shared__ int sGo;
     if (wave == 0) {
@@ -782,12 +821,19 @@ __device__ __forceinline__ void sample_item(const Args& a, int b, int c) {
 // ---------------------------------------------------------------- k_verify
 // One launch per call:
 //   blocks [0, P * B * C):        streaming unit (k, b, c), position-major;
-//   blocks [P * B * C, + B * C):  sampling workgroup (b, c).
-// Every workgroup also clears its share of the other call parity's arrival
-// counters and status words, which the next call starts from.
-// k_verify_trunc carries the truncation path (handles created with
-// max_top_k > 0) and its LDS scratch; without it truncated rows are flagged
-// unsupported and the kernel stays lean.
+//   blocks [P * B * C, + B * C):  sampling workgroup (b, c);
+// and, when the call number comes from the device (DEVCALL: launches that
+// may be replayed from a captured graph), one more:
+//   block P * B * C + B * C:      the closing workgroup, which advances the
+//                                 call number once every other one read it.
+// The call number gives the tag of the words a launch publishes and the
+// parity of its counters, status words and (DEVCALL) record set.  With the
+// host's number every workgroup clears its share of the other parity's
+// counters and status words; with the device's the sampling workgroups
+// clear the other parity's whole record set.  The next launch starts from
+// what was cleared.  k_verify_trunc carries the truncation path (handles
+// created with max_top_k > 0) and its LDS scratch; without it truncated rows
+// are flagged unsupported and the kernel stays lean.
 __device__ inline void clear_other_parity(const Args& a) {
     const unsigned other = (a.epoch & 1u) ^ 1u;
     const long long stride = (long long)gridDim.x * kBlock;
@@ -797,60 +843,70 @@ __device__ inline void clear_other_parity(const Args& a) {
         publish(a.ws.status + ((long long)other * a.ws.n_rows + i) * (kSlot / 2), 0ull);
 }
 
-template <bool BF16, bool VEC, bool TRUNC, int PROP>
+template <bool BF16, bool VEC, bool TRUNC, int PROP, bool DEVCALL>
 __device__ inline void verify_block(const Args& a, TruncScratch* sc) {
-    clear_other_parity(a);
     const int per_pos = a.B * a.C;
     const int t = blockIdx.x;
+    if constexpr (DEVCALL) {
+        if (t == (a.P + 1) * per_pos) {
+            close_call(a.ws, a.B, (unsigned)((a.P + 1) * a.C), pack_dims(a.B, a.P, a.C));
+            return;
+        }
+    } else {
+        clear_other_parity(a);
+    }
     const int k = t / per_pos;
     const int rem = t - k * per_pos;
     const int b = rem / a.C;
     const int c = rem - b * a.C;
-    if (k < a.P) stream_unit<BF16, VEC, TRUNC, PROP>(a, k, b, c, sc);
-    else sample_item<BF16, VEC, PROP>(a, b, c);
+    if (k < a.P) stream_unit<BF16, VEC, TRUNC, PROP, DEVCALL>(a, k, b, c, sc);
+    else sample_item<BF16, VEC, PROP, DEVCALL>(a, b, c);
 }
 
-template <bool BF16, bool VEC, int PROP>
+template <bool BF16, bool VEC, int PROP, bool DEVCALL>
 __global__ __launch_bounds__(kBlock) void k_verify(Args a) {
-    verify_block<BF16, VEC, false, PROP>(a, nullptr);
+    verify_block<BF16, VEC, false, PROP, DEVCALL>(a, nullptr);
 }
 
-template <bool BF16, bool VEC, int PROP>
+template <bool BF16, bool VEC, int PROP, bool DEVCALL>
 __global__ __launch_bounds__(kBlock) void k_verify_trunc(Args a) {
     __shared__ TruncScratch sc;
-    verify_block<BF16, VEC, true, PROP>(a, &sc);
+    verify_block<BF16, VEC, true, PROP, DEVCALL>(a, &sc);
 }
 
 using KernelFn = void (*)(Args);
 
-// Each proposal kind is a separate instantiation, so that the two-model
-// kernels carry none of the other kinds' code.
-template <int PROP>
+// Each proposal kind (and call-number source) is a separate instantiation,
+// so that the two-model kernels carry none of the other kinds' code.
+template <int PROP, bool DEVCALL>
 KernelFn pick_prop(bool bf16, bool vec, bool trunc) {
     if (trunc) {
-        if (bf16) return vec ? k_verify_trunc<true, true, PROP> : k_verify_trunc<true, false, PROP>;
-        return vec ? k_verify_trunc<false, true, PROP> : k_verify_trunc<false, false, PROP>;
+        if (bf16) return vec ? k_verify_trunc<true, true, PROP, DEVCALL> : k_verify_trunc<true, false, PROP, DEVCALL>;
+        return vec ? k_verify_trunc<false, true, PROP, DEVCALL> : k_verify_trunc<false, false, PROP, DEVCALL>;
     }
-    if (bf16) return vec ? k_verify<true, true, PROP> : k_verify<true, false, PROP>;
-    return vec ? k_verify<false, true, PROP> : k_verify<false, false, PROP>;
+    if (bf16) return vec ? k_verify<true, true, PROP, DEVCALL> : k_verify<true, false, PROP, DEVCALL>;
+    return vec ? k_verify<false, true, PROP, DEVCALL> : k_verify<false, false, PROP, DEVCALL>;
 }
 
+template <bool DEVCALL>
 KernelFn pick(bool bf16, bool vec, bool trunc, int prop) {
-    if (prop == kPropPoint) return pick_prop<kPropPoint>(bf16, vec, trunc);
-    if (prop == kPropStats) return pick_prop<kPropStats>(bf16, vec, trunc);
-    return pick_prop<kPropLogits>(bf16, vec, trunc);
+    if (prop == kPropPoint) return pick_prop<kPropPoint, DEVCALL>(bf16, vec, trunc);
+    if (prop == kPropStats) return pick_prop<kPropStats, DEVCALL>(bf16, vec, trunc);
+    return pick_prop<kPropLogits, DEVCALL>(bf16, vec, trunc);
 }
 
 }  // namespace
 
-hipError_t launch_verify(const Args& a, bool bf16, bool vec, hipStream_t stream, hipEvent_t* ev) {
-    const long long blocks = (long long)(a.P + 1) * a.B * a.C;
+hipError_t launch_verify(const Args& a, bool bf16, bool vec, bool devcall, hipStream_t stream, hipEvent_t* ev) {
+    const long long blocks = (long long)(a.P + 1) * a.B * a.C + (devcall ? 1 : 0);   // + the closing workgroup
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    KernelFn fn = pick(bf16, vec, a.cand_cap > 0, a.prop);
+    KernelFn fn = devcall ? pick<true>(bf16, vec, a.cand_cap > 0, a.prop) : pick<false>(bf16, vec, a.cand_cap > 0, a.prop);
     // the events (when profiling) are attached to the dispatch itself, so
     // that they time the kernel and not the packets around it
-    hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev ? ev[0] : nullptr,
-                          ev ? ev[1] : nullptr, 0, a);
+    if (ev)
+        hipExtLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, ev[0], ev[1], 0, a);
+    else
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);   // also under capture
     return hipGetLastError();
 }
 

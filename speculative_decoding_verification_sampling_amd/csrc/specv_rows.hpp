@@ -131,6 +131,94 @@ __device__ inline unsigned long long* stats_words(const Args& a, int b, int k, i
     return a.ws.stats + part_index(a, b, k, side, c) * 2;
 }
 
+// ---------------------------------------------------------------- call number
+// Every launch needs a tag of its own for the words it publishes, and a
+// parity that alternates from launch to launch (the record set it uses).
+// Both come from a call number kept on the device, so that a launch replayed
+// from a captured graph (whose arguments are frozen) still gets a new one:
+//   - every workgroup reads the number with a plain load (it changes only
+//     between launches, so a cached copy is this launch's), then counts
+//     itself in seen[parity][its batch row] with an atomic add whose address
+//     depends on what it read, so the count lands after the read;
+//   - the launch has one workgroup more than its work needs, the last one,
+//     which waits until every row's count is complete, resets the counts,
+//     records the launch's extent in dims[parity] and stores number + 1.
+// Nothing on a workgroup's own path waits for these atomics.  The closing
+// workgroup is dispatched after every other workgroup of its XCD and no
+// workgroup waits for it, so its wait ends.
+__device__ inline unsigned read_call(const Workspace& ws) { return ws.calls[0]; }
+
+// One thread per workgroup: count this workgroup (batch row b) as having
+// read call number e.
+__device__ inline void count_call(const Workspace& ws, unsigned e, int b) {
+    (void)__hip_atomic_fetch_add(ws.seen + ((long long)(e & 1u) * ws.n_rows + b) * kSlot, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A launch's extent: batch rows, positions per row and chunks per row (the
+// region of each record array its indexing can reach).
+__device__ inline unsigned long long pack_dims(int B, int P, int C) {
+    return (unsigned long long)(unsigned)B | ((unsigned long long)(unsigned)P << 32) |
+           ((unsigned long long)(unsigned)C << 40);
+}
+
+// The closing workgroup of a launch with B rows of per_row workgroups each
+// (whole workgroup): waits (bounded) for every row's count, resets the
+// counts, records the extent ``dims`` for the launch that clears this
+// parity's record set, and advances the call number.
+__device__ inline void close_call(const Workspace& ws, int B, unsigned per_row, unsigned long long dims) {
+    const unsigned e = read_call(ws);
+    unsigned* seen = ws.seen + (long long)(e & 1u) * ws.n_rows * kSlot;
+    for (int r = threadIdx.x; r < B; r += kBlock) {
+#pragma unroll 1
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+            if (published(seen + (long long)r * kSlot) >= per_row) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < B; r += kBlock) publish(seen + (long long)r * kSlot, 0u);
+    if (threadIdx.x == 0) {
+        publish(ws.dims + (e & 1u), dims);
+        publish(ws.calls, e + 1u);
+    }
+}
+
+// The tag of call number e: odd, so never the zero of a cleared word.
+__device__ inline unsigned call_tag(unsigned e) { return 2u * e + 1u; }
+
+// The record set of parity par.
+__device__ inline Workspace parity_set(const Workspace& ws, unsigned par) {
+    Workspace w = ws;
+    w.stats += par * ws.set_stats;
+    w.pair += par * ws.set_pair;
+    w.rowrec += par * ws.set_rowrec;
+    w.wsum += par * ws.set_wsum;
+    w.ctr += (long long)par * ws.n_groups * kSlot;
+    w.status += (long long)par * ws.n_rows * (kSlot / 2);
+    return w;
+}
+
+// Share ``wg`` of ``nwg`` workgroups (whole workgroup): zero the record set
+// of the parity other than call number e's, over the extent of the last
+// launch that used it (its B rows, P positions and C chunks).
+__device__ inline void clear_other_set(const Workspace& ws0, unsigned e, long long wg, long long nwg) {
+    const unsigned long long d = ws0.dims[(e & 1u) ^ 1u];   // written by an earlier launch
+    const long long B = (long long)(unsigned)d, P = (long long)((d >> 32) & 0xffu), C = (long long)((d >> 40) & 0xffu);
+    if (B == 0) return;
+    const Workspace ws = parity_set(ws0, (e & 1u) ^ 1u);
+    const long long stride = nwg * kBlock;
+    const long long i0 = wg * kBlock + threadIdx.x;
+    const long long n_stats = B * P * 2 * C * 2, n_pair = B * P * kPairWords, n_row = B * kRowWords,
+                    n_wsum = B * C * 2, n_ctr = B * P;
+    for (long long i = i0; i < n_stats; i += stride) publish(ws.stats + i, 0ull);
+    for (long long i = i0; i < n_pair; i += stride) publish(&ws.pair[i / kPairWords].w[i % kPairWords], 0ull);
+    for (long long i = i0; i < n_row; i += stride) publish(ws.rowrec + i, 0ull);
+    for (long long i = i0; i < n_wsum; i += stride) publish(ws.wsum + i, 0ull);
+    for (long long i = i0; i < n_ctr; i += stride) publish(ws.ctr + i * kSlot, 0u);
+    for (long long i = i0; i < B; i += stride) publish(ws.status + i * (kSlot / 2), 0ull);
+}
+
 // Diagnostics of one row by one wave: lane i holds p_i(d_i), q_i(d_i).
 __device__ inline void write_diag_wave(const Args& a, int b, int tested, float p, float q) {
     const int i = threadIdx.x % kWave;

@@ -11,9 +11,11 @@
 // array's name on the host is a stand-in, not a device address).  Every
 // call on a device shares the device's array, so calls that overlap on one
 // device (other streams, other host threads without ordering) race and
-// their outputs are undefined.  The array keeps the last call's contents;
-// what a call needs cleared (the tags' first use, the wrap of the tag
-// counter) is cleared by a fill kernel on the caller's stream.
+// their outputs are undefined.  The array keeps the last call's contents:
+// the first call on a device zeroes it with a fill kernel on the caller's
+// stream, and every launch after that clears on the device what the next
+// one needs (the record set of the other parity), and takes its call number
+// from the array itself, as a handle's launches do.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -35,20 +37,30 @@ constexpr int kNaChunks = (kNaVocab + kChunk - 1) / kChunk;
 constexpr size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // The workspace's parts, at 256-byte aligned offsets (the same parts a
-// handle allocates; no truncation candidates).
+// handle allocates, two record sets included; no truncation candidates).
+constexpr long long kSetStats = (long long)kNaBatch * kNaPos * 2 * kNaChunks * 2;
+constexpr long long kSetPair = (long long)kNaBatch * kNaPos;
+constexpr long long kSetRowrec = (long long)kNaBatch * kRowWords;
+constexpr long long kSetWsum = (long long)kNaBatch * kNaChunks * 2;
 constexpr size_t kStatsOff = 0;
-constexpr size_t kStatsBytes = (size_t)kNaBatch * kNaPos * 2 * kNaChunks * 2 * sizeof(unsigned long long);
+constexpr size_t kStatsBytes = 2 * (size_t)kSetStats * sizeof(unsigned long long);
 constexpr size_t kPairOff = round256(kStatsOff + kStatsBytes);
-constexpr size_t kPairBytes = (size_t)kNaBatch * kNaPos * sizeof(PairRec);
+constexpr size_t kPairBytes = 2 * (size_t)kSetPair * sizeof(PairRec);
 constexpr size_t kRowrecOff = round256(kPairOff + kPairBytes);
-constexpr size_t kRowrecBytes = (size_t)kNaBatch * kRowWords * sizeof(unsigned long long);
+constexpr size_t kRowrecBytes = 2 * (size_t)kSetRowrec * sizeof(unsigned long long);
 constexpr size_t kWsumOff = round256(kRowrecOff + kRowrecBytes);
-constexpr size_t kWsumBytes = (size_t)kNaBatch * kNaChunks * 2 * sizeof(unsigned long long);
+constexpr size_t kWsumBytes = 2 * (size_t)kSetWsum * sizeof(unsigned long long);
 constexpr size_t kCtrOff = round256(kWsumOff + kWsumBytes);
 constexpr size_t kCtrBytes = (size_t)2 * kNaBatch * kNaPos * kSlot * sizeof(unsigned);
 constexpr size_t kStatusOff = round256(kCtrOff + kCtrBytes);
 constexpr size_t kStatusBytes = (size_t)2 * kNaBatch * (kSlot / 2) * sizeof(unsigned long long);
-constexpr size_t kScratchBytes = round256(kStatusOff + kStatusBytes);
+constexpr size_t kCallsOff = round256(kStatusOff + kStatusBytes);
+constexpr size_t kCallsBytes = (size_t)kSlot * sizeof(unsigned);
+constexpr size_t kSeenOff = round256(kCallsOff + kCallsBytes);
+constexpr size_t kSeenBytes = (size_t)2 * kNaBatch * kSlot * sizeof(unsigned);
+constexpr size_t kDimsOff = round256(kSeenOff + kSeenBytes);
+constexpr size_t kDimsBytes = (size_t)kSlot * sizeof(unsigned long long);
+constexpr size_t kScratchBytes = round256(kDimsOff + kDimsBytes);
 static_assert(kScratchBytes == SPECV_NOALLOC_SCRATCH_BYTES, "scratch size differs from the header's");
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
@@ -71,7 +83,6 @@ hipError_t zero_scratch(void* ptr, hipStream_t s) {
 constexpr int kMaxDevices = 64;
 struct DeviceScratch {
     void* ptr = nullptr;     // the device's copy of ``scratch``, from hipGetSymbolAddress
-    unsigned epoch = 0;      // tag of the device's last call (0: none yet)
 };
 std::mutex g_mutex;
 DeviceScratch g_dev[kMaxDevices];
@@ -85,6 +96,13 @@ Workspace carve(void* ptr) {
     ws.wsum = reinterpret_cast<unsigned long long*>(base + kWsumOff);
     ws.ctr = reinterpret_cast<unsigned*>(base + kCtrOff);
     ws.status = reinterpret_cast<unsigned long long*>(base + kStatusOff);
+    ws.calls = reinterpret_cast<unsigned*>(base + kCallsOff);
+    ws.seen = reinterpret_cast<unsigned*>(base + kSeenOff);
+    ws.dims = reinterpret_cast<unsigned long long*>(base + kDimsOff);
+    ws.set_stats = kSetStats;
+    ws.set_pair = kSetPair;
+    ws.set_rowrec = kSetRowrec;
+    ws.set_wsum = kSetWsum;
     ws.n_groups = kNaBatch * kNaPos;
     ws.n_rows = kNaBatch;
     return ws;
@@ -141,18 +159,9 @@ extern "C" SPECV_API specv_status specv_verify_sample_noalloc(
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPECV_E_HIP;
         if (zero_scratch(p, s) != hipSuccess) return SPECV_E_HIP;
         d.ptr = p;
-        d.epoch = 0;
-    }
-    // tags as a handle's: a new one per call; at the wrap every tagged word
-    // (the whole array) is cleared first
-    unsigned next = d.epoch + 1;
-    if (next >= 0x7fffffffu) {
-        if (zero_scratch(d.ptr, s) != hipSuccess) return SPECV_E_HIP;
-        next = 1;
     }
     a.ws = carve(d.ptr);
-    a.epoch = next;
-    if (launch_verify(a, dtype == SPECV_BF16, vec, s, nullptr) != hipSuccess) return SPECV_E_HIP;
-    d.epoch = next;
+    // numbered on the device, captured or not: the array keeps no host state
+    if (launch_verify(a, dtype == SPECV_BF16, vec, true, s, nullptr) != hipSuccess) return SPECV_E_HIP;
     return SPECV_OK;
 }
