@@ -157,7 +157,7 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
     const unsigned e = DEVCALL ? read_call(a0.ws) : a0.epoch;
     DraftArgs a = a0;
     a.epoch = DEVCALL ? call_tag(e) : e;
-    a.ws = parity_set(a0.ws, e & 1u);
+    a.ws = parity_set<DEVCALL>(a0.ws, e & 1u);
     const Args va = verify_view(a);
     const float nan = __builtin_nanf("");
     const specv_row_params rp = a.params[b];

@@ -657,7 +657,7 @@ __device__ __forceinline__ void stream_unit(const Args& a0, int k, int b, int c,
     const Plan pl = make_plan(a0, b);
     Args a = a0;
     a.epoch = DEVCALL ? call_tag(e) : e;
-    a.ws = parity_set(a0.ws, e & 1u);
+    a.ws = parity_set<DEVCALL>(a0.ws, e & 1u);
     __shared__ int sSkip;
     if (pl.mode == MODE_SKIP) {
         if (k == 0 && c == 0 && wave == 0) {
@@ -771,7 +771,7 @@ __device__ __forceinline__ void sample_item(const Args& a0, int b, int c) {
     if (pl.mode != MODE_SAMPLE) return;
     Args a = a0;
     a.epoch = DEVCALL ? call_tag(e) : e;
-    a.ws = parity_set(a0.ws, e & 1u);
+    a.ws = parity_set<DEVCALL>(a0.ws, e & 1u);
     __shared__ unsigned sRec[kRowWords];
     __shared__ int sGo;
     if (wave == 0) {

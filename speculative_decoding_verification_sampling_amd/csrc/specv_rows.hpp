@@ -187,13 +187,18 @@ __device__ inline void close_call(const Workspace& ws, int B, unsigned per_row, 
 // The tag of call number e: odd, so never the zero of a cleared word.
 __device__ inline unsigned call_tag(unsigned e) { return 2u * e + 1u; }
 
-// The record set of parity par.
+// The record set of parity par.  Host-numbered workspaces hold one set of
+// the tagged records (set sizes 0): only their counters and status words
+// come in two sets, and SETS = false leaves the other pointers as they are.
+template <bool SETS = true>
 __device__ inline Workspace parity_set(const Workspace& ws, unsigned par) {
     Workspace w = ws;
-    w.stats += par * ws.set_stats;
-    w.pair += par * ws.set_pair;
-    w.rowrec += par * ws.set_rowrec;
-    w.wsum += par * ws.set_wsum;
+    if constexpr (SETS) {
+        w.stats += par * ws.set_stats;
+        w.pair += par * ws.set_pair;
+        w.rowrec += par * ws.set_rowrec;
+        w.wsum += par * ws.set_wsum;
+    }
     w.ctr += (long long)par * ws.n_groups * kSlot;
     w.status += (long long)par * ws.n_rows * (kSlot / 2);
     return w;
