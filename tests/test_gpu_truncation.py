@@ -94,6 +94,28 @@ def test_truncation_ties_at_threshold(gpu):
     check(out, orc, toks, tf, df, prm, max_tol=0.2)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_signed_zeros_at_threshold(gpu, dtype):
+    """-0.0 and +0.0 are the same logit: when the top-k threshold is 0, the
+    kept set holds the zeros of both signs (ties kept)."""
+    rng = np.random.default_rng(13)
+    B, gamma, V = 8, 3, 9000
+    t = np.full((B, gamma + 1, V), -6.0, np.float32)
+    d = np.full((B, gamma, V), -6.0, np.float32)
+    for arr in (t, d):
+        for idx in np.ndindex(arr.shape[:2]):
+            pos = rng.choice(V, 12, replace=False)
+            arr[idx][pos] = rng.uniform(0.5, 3.0, 12)
+            zeros = rng.choice(np.setdiff1d(np.arange(V), pos), 40, replace=False)
+            arr[idx][zeros] = np.where(rng.random(40) < 0.5, -0.0, 0.0)
+    tt, dd = torch.from_numpy(t).to(dtype), torch.from_numpy(d).to(dtype)
+    assert (torch.signbit(tt) & (tt == 0)).any()
+    for k, p in ((20, 1.0), (30, 0.97)):
+        prm = _prm(B, 1.0, k, p)
+        out, orc, toks, tf, df = run_trunc(tt, dd, prm, 21 + k)
+        check(out, orc, toks, tf, df, prm, max_tol=0.2)
+
+
 @pytest.mark.parametrize("V", [7, 300, 8193, 20001])
 def test_truncation_ragged_f32(gpu, V):
     rng = np.random.default_rng(V)
