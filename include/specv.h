@@ -260,10 +260,12 @@ SPECV_API specv_status specv_verify_point_mass(specv_handle h, void* stream,
  *                   (b, pos0 + i) gets the row's statistics and flags:
  *                   SPECV_FLAG_NONFINITE_ROW (NaN / +inf or no finite logit),
  *                   SPECV_FLAG_UNSUPPORTED (top-k / top-p on a handle without
- *                   truncation workspace), SPECV_FLAG_INTERNAL (a bounded
- *                   wait expired):
- *                   these rows get token -1; SPECV_FLAG_TOPP_NEAR (the top-p
- *                   decision was within 1e-5 of top_p) is informational
+ *                   truncation workspace): these rows get token -1;
+ *                   SPECV_FLAG_INTERNAL (a bounded wait expired): the entry's
+ *                   token and statistics are not valid (without out_stats
+ *                   such a draw may leave its token unwritten);
+ *                   SPECV_FLAG_TOPP_NEAR (the top-p decision was within 1e-5
+ *                   of top_p) is informational
  * Rows with temperature 0 take the draft argmax (lowest index on ties).
  * Other entries of the outputs are left as they are.  0 <= pos0,
  * pos0 + n_pos <= out_stride, n_pos <= max(max_gamma, 1), B <= max_batch,
@@ -343,6 +345,16 @@ SPECV_API specv_status specv_get_profile_samples(specv_handle h, int max_samples
  * SPECV_E_ALIGN, SPECV_E_HIP. */
 SPECV_API specv_status specv_read_ceiling(void* stream, const void* buf, int64_t bytes, int grid,
                                           uint32_t* sink);
+
+/* For tests of failure handling only: sets how many polls every bounded wait
+ * of the verify and draft-sampler kernels makes on ``device`` before it gives
+ * up and flags its row SPECV_FLAG_INTERNAL (the outputs of such a row are not
+ * valid; every other row's are).  polls = 0 restores the default (262144).
+ * Process-wide for the device, for every handle; waits for the device first,
+ * so no call is in flight when it changes.  The closing workgroup of a
+ * graph-replayable launch keeps the default.  Errors: SPECV_E_PARAM
+ * (polls < 0), SPECV_E_HIP. */
+SPECV_API specv_status specv_debug_set_wait_limit(int device, int32_t polls);
 
 /* Free the workspace and the handle.  Waits for the device first.  NULL is
  * accepted. */

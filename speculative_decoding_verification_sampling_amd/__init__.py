@@ -36,6 +36,7 @@ __all__ = [
     "EXPORTED_SYMBOLS",
     "read_ceiling",
     "verify_sample_noalloc",
+    "debug_set_wait_limit",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,7 +57,7 @@ EXPORTED_SYMBOLS = ("specv_create", "specv_verify_sample", "specv_verify_point_m
                     "specv_verify_sample_qstats", "specv_sample_draft", "specv_verify_greedy",
                     "specv_destroy", "specv_status_string", "specv_set_profiling",
                     "specv_get_profile", "specv_get_profile_samples", "specv_read_ceiling",
-                    "specv_verify_sample_noalloc")
+                    "specv_verify_sample_noalloc", "specv_debug_set_wait_limit")
 
 
 class SpecvError(RuntimeError):
@@ -257,6 +258,17 @@ def read_ceiling(buf, grid, sink):
     st = load_library().specv_read_ceiling(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
                                            _ptr(buf), nbytes, int(grid), _ptr(sink))
     _check(st, "specv_read_ceiling")
+
+
+def debug_set_wait_limit(polls, device=None):
+    """Failure-path tests only: the polls every bounded wait of the kernels
+    makes before it gives up and flags its row INTERNAL (0 restores the
+    default).  Process-wide for the device."""
+    dev = torch.cuda.current_device() if device is None else int(device)
+    fn = load_library().specv_debug_set_wait_limit
+    fn.argtypes = [ctypes.c_int, ctypes.c_int32]
+    fn.restype = ctypes.c_int
+    _check(fn(dev, int(polls)), "specv_debug_set_wait_limit")
 
 
 class Verifier:

@@ -359,6 +359,16 @@ specv_status specv_read_ceiling(void* stream, const void* buf, int64_t bytes, in
     return SPECV_OK;
 }
 
+specv_status specv_debug_set_wait_limit(int device, int32_t polls) {
+    if (polls < 0) return SPECV_E_PARAM;
+    const int n = polls == 0 ? specv::kDefaultWaitLimit : polls;
+    if (hipSetDevice(device) != hipSuccess) return SPECV_E_HIP;
+    if (hipDeviceSynchronize() != hipSuccess) return SPECV_E_HIP;
+    if (specv::set_wait_limit_verify(n) != hipSuccess || specv::set_wait_limit_draft(n) != hipSuccess)
+        return SPECV_E_HIP;
+    return SPECV_OK;
+}
+
 specv_status specv_destroy(specv_handle h) {
     if (!h) return SPECV_OK;
     (void)hipSetDevice(h->cfg.device);

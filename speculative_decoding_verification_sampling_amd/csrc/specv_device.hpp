@@ -17,7 +17,16 @@ enum Purpose { PURPOSE_DRAFT = 0, PURPOSE_ACCEPT = 1, PURPOSE_RESIDUAL = 2, PURP
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInf = __builtin_huge_valf();
-constexpr int kSpinLimit = 1 << 18;
+constexpr int kSpinLimit = kDefaultWaitLimit;
+
+// Polls a bounded wait makes before it gives up (the row is flagged
+// INTERNAL).  kSpinLimit, unless a failure-path test lowers it through
+// specv_debug_set_wait_limit; each translation unit holds its own copy.
+__device__ int g_wait_limit = kSpinLimit;
+
+__host__ inline hipError_t set_wait_limit_here(int n) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_wait_limit), &n, sizeof(int));
+}
 
 // ---------------------------------------------------------------- Philox
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
@@ -417,7 +426,7 @@ __device__ inline bool published_stats(const unsigned long long* w, unsigned epo
                                        unsigned& second) {
     unsigned long long w0 = 0, w1 = 0;
     bool ok = false;
-    for (int spin = 0; spin < kSpinLimit; ++spin) {
+    for (int spin = 0; spin < g_wait_limit; ++spin) {
         w0 = published(w);
         w1 = published(w + 1);
         if (tag_is(w0, epoch) && tag_is(w1, epoch)) {

@@ -368,9 +368,11 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
             }
         }
         if (late) {
-            flags = SPECV_FLAG_INTERNAL;
+            // this workgroup gave up on the row: it flags the draw and writes
+            // nothing else (another workgroup of the row may have seen every
+            // chunk and own the draw; its token is then valid)
+            if (lane == 0 && a.out_stats) atomicOr(&a.out_stats[o].flags, (int)SPECV_FLAG_INTERNAL);
             chosen = -1;
-            tok = -1;
         }
         if (lane == 0) {
             sChosen = chosen;
@@ -378,9 +380,9 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
             sLocal = local;
             sM = M;
             sS = S;
-            // rows with nothing left to draw (greedy, bad, late) are written by
-            // chunk 0's workgroup
-            if (chosen < 0 && c == 0) write_draft(a, o, tok, nan, nan, nan, flags);
+            // rows with nothing left to draw (greedy, bad) are written by chunk
+            // 0's workgroup
+            if (chosen < 0 && c == 0 && !late) write_draft(a, o, tok, nan, nan, nan, flags);
         }
     }
     __syncthreads();
@@ -442,6 +444,8 @@ void (*pick_draft(bool bf16, bool vec, bool trunc))(DraftArgs) {
 }
 
 }  // namespace
+
+hipError_t set_wait_limit_draft(int n) { return set_wait_limit_here(n); }
 
 hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, bool devcall, hipStream_t stream,
                                hipEvent_t* ev) {

@@ -179,6 +179,10 @@ hipError_t launch_sample_draft(const DraftArgs& a, bool bf16, bool vec, bool dev
 // (nullable) holds two events that the launch records at the kernel's start
 // and end.
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, bool devcall, hipStream_t stream, hipEvent_t* ev);
+// The bounded waits' poll limit in the verify and draft kernels (failure-path tests).
+constexpr int kDefaultWaitLimit = 1 << 18;
+hipError_t set_wait_limit_verify(int n);
+hipError_t set_wait_limit_draft(int n);
 
 // The sizes a workspace is laid out for, and its truncation capacity.
 struct Limits {

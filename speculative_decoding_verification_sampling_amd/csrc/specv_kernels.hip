@@ -165,7 +165,7 @@ __device__ __forceinline__ void finish_row(const Args& a, int b, int k, const Pa
                 const PairRec* pr = &a.ws.pair[pair_id(a, b, lane)];
                 ok = false;
 #pragma unroll 1
-                for (int spin = 0; spin < kSpinLimit; ++spin) {
+                for (int spin = 0; spin < g_wait_limit; ++spin) {
                     bool all = true;
 #pragma unroll
                     for (int i = 0; i < kPairWords; ++i) {
@@ -542,7 +542,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
         bool done = false;
         unsigned long long w0 = 0, w1 = 0, wf = 0;
 #pragma unroll 1
-        for (int spin = 0; spin < kSpinLimit; ++spin) {
+        for (int spin = 0; spin < g_wait_limit; ++spin) {
             if (lane < a.C) {
                 w0 = published(base + lane * 2);
                 w1 = published(base + lane * 2 + 1);
@@ -585,7 +585,7 @@ __device__ void sample_from_regs(const Args& a, int b, int k, int c, const Plan&
             sRes = res;
             sWres = wres;
             sFlags = flags;
-            if (!done && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
+            if (!done && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
         }
     }
     __syncthreads();
@@ -779,7 +779,7 @@ __device__ __forceinline__ void sample_item(const Args& a0, int b, int c) {
         int go = 0;
         unsigned long long v = 0;
 #pragma unroll 1
-        for (int spin = 0; spin < kSpinLimit; ++spin) {
+        for (int spin = 0; spin < g_wait_limit; ++spin) {
             v = lane <= RW_INVQ ? published(rr + lane) : 0ull;
             if ((__ballot(lane <= RW_INVQ && tag_is(v, a.epoch)) & 0x1full) == 0x1full) {
                 go = 1;
@@ -789,7 +789,7 @@ __device__ __forceinline__ void sample_item(const Args& a0, int b, int c) {
         }
         if (lane < kRowWords) sRec[lane] = (unsigned)v;
         if (lane == 0) sGo = go;
-        if (!go && lane == 0 && c == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
+        if (!go && lane == 0 && a.out_flags) atomicOr(&a.out_flags[b], (int)SPECV_FLAG_INTERNAL);
     }
     __syncthreads();
     if (!sGo) return;
@@ -896,6 +896,8 @@ KernelFn pick(bool bf16, bool vec, bool trunc, int prop) {
 }
 
 }  // namespace
+
+hipError_t set_wait_limit_verify(int n) { return set_wait_limit_here(n); }
 
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, bool devcall, hipStream_t stream, hipEvent_t* ev) {
     const long long blocks = (long long)(a.P + 1) * a.B * a.C + (devcall ? 1 : 0);   // + the closing workgroup

@@ -171,7 +171,7 @@ __device__ inline void close_call(const Workspace& ws, int B, unsigned per_row, 
     unsigned* seen = ws.seen + (long long)(e & 1u) * ws.n_rows * kSlot;
     for (int r = threadIdx.x; r < B; r += kBlock) {
 #pragma unroll 1
-        for (int spin = 0; spin < kSpinLimit; ++spin) {
+        for (int spin = 0; spin < kSpinLimit; ++spin) {    // (fixed: bookkeeping, no row waits on it)
             if (published(seen + (long long)r * kSlot) >= per_row) break;
             __builtin_amdgcn_s_sleep(4);
         }
