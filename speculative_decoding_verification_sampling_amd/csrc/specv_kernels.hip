@@ -277,6 +277,14 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
     const int d = test ? draft_token(a, b, k) : 0;
     if (trunc) {
         if constexpr (TRUNC) {
+            // z at d_k, requested before the merge by lane k (which holds
+            // d_k from the plan) and kept in its registers until the
+            // decision
+            float zt = 0.f, zq = 0.f;
+            if (zneed && tid == k) {
+                zt = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), pl.tok);
+                if (qside) zq = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), pl.tok);
+            }
             // both rows in lockstep when they take the usual path, else one
             // after the other
             __shared__ TruncRow dPair[2];
@@ -302,11 +310,11 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
                 dT[0] = t0;
                 dT[1] = qs && qside ? stats_trow(a.qstats[(long long)b * a.qs_sb + k]) : t1;
                 dLate[0] = dLate[1] = 0;
-                if (zneed) {
-                    dZ[0] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), d);
-                    if (qside) dZ[1] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
-                    dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
-                }
+                if (zneed) dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
+            }
+            if (zneed && tid == k) {
+                dZ[0] = zt;
+                dZ[1] = zq;
             }
         }
     } else {
@@ -342,12 +350,13 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
                 if (side == 0) dA = arg;
             }
         } else if (wave == 2 && zneed) {
-            // one load instruction for both rows' z at d_k (lane 0: target,
-            // lane 1: draft) and the drafter's statistics (lanes 3, 4), so
-            // that they share a round trip
-            if (lane == 0 || (lane == 1 && qside))
-                dZ[lane] = load_elem<BF16>(lane == 0 ? row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k)
-                                                     : row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), d);
+            // both rows' z at d_k from lane k, which holds d_k from the
+            // plan (its own register: no wait for the token's load), and the
+            // drafter's statistics (lanes 3, 4), in one round trip
+            if (lane == k) {
+                dZ[0] = load_elem<BF16>(row_ptr<BF16>(a.tgt, a.t_sb, a.t_sp, b, k), pl.tok);
+                if (qside) dZ[1] = load_elem<BF16>(row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, k), pl.tok);
+            }
             if (lane == 2) dU = uniform24(a.seed, b, k, PURPOSE_ACCEPT, a.step);
             if (qs && (lane == 3 || lane == 4)) {
                 const specv_draft_stats* st = &a.qstats[(long long)b * a.qs_sb + k];
