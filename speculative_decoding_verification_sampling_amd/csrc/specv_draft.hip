@@ -160,6 +160,13 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
     a.ws = parity_set<DEVCALL>(a0.ws, e & 1u);
     const Args va = verify_view(a);
     const float nan = __builtin_nanf("");
+    // the chunk's loads go out first: the row's parameters, read next, share
+    // their round trip
+    const void* row = row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i);
+    const int v0 = c * kChunk;
+    const int len = min(kChunk, a.V - v0);
+    ChunkRegs<BF16, VEC> r;
+    r.issue(row, v0, len);
     const specv_row_params rp = a.params[b];
     const bool greedy = !(rp.temperature > 0.f);
     const bool topk_on = rp.top_k > 0 && rp.top_k < a.V;
@@ -176,11 +183,6 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
         return;
     }
     const float scale = greedy ? 0.f : kLog2e / rp.temperature;
-    const void* row = row_ptr<BF16>(a.drf, a.d_sb, a.d_sp, b, i);
-    const int v0 = c * kChunk;
-    const int len = min(kChunk, a.V - v0);
-    ChunkRegs<BF16, VEC> r;
-    r.issue(row, v0, len);
     r.finish(row, v0, len);
 
     // 1. chunk statistics, merged across the four waves as the verify's
