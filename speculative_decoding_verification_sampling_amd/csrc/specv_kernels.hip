@@ -769,6 +769,12 @@ template <bool BF16, bool VEC, int PROP, bool DEVCALL>
 __device__ __forceinline__ void sample_item(const Args& a0, int b, int c) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const unsigned e = DEVCALL ? read_call(a0.ws) : a0.epoch;
+    // with the host's call number the record set is known at once: the
+    // record's first poll goes out with the plan's loads
+    unsigned long long first = 0;
+    if constexpr (!DEVCALL) {
+        if (wave == 0 && lane <= RW_INVQ) first = published(a0.ws.rowrec + (long long)b * kRowWords + lane);
+    }
     const Plan pl = make_plan(a0, b);
     if constexpr (DEVCALL) {
         // the sampling workgroups clear the other parity's record set between
@@ -789,7 +795,7 @@ __device__ __forceinline__ void sample_item(const Args& a0, int b, int c) {
         unsigned long long v = 0;
 #pragma unroll 1
         for (int spin = 0; spin < g_wait_limit; ++spin) {
-            v = lane <= RW_INVQ ? published(rr + lane) : 0ull;
+            v = !DEVCALL && spin == 0 ? first : lane <= RW_INVQ ? published(rr + lane) : 0ull;
             if ((__ballot(lane <= RW_INVQ && tag_is(v, a.epoch)) & 0x1full) == 0x1full) {
                 go = 1;
                 break;
