@@ -463,6 +463,35 @@ __device__ __forceinline__ void wave_chunk_ms(const Regs& r, float scale, float&
     wave_merge_ms(m, s, scale);
 }
 
+// wave_chunk_ms's statistics, bit for bit (the same sums in the same
+// order), that also leave this thread's maximum and the sums of its NG
+// groups of entries (entries i = j * (kPerThread / NG) + e, e ascending), in
+// the thread's own units exp2((z - thread max) * scale).
+template <int NG, typename Regs>
+__device__ __forceinline__ void wave_chunk_ms_groups(const Regs& r, float scale, float& m, float& s,
+                                                     float (&gsum)[NG], float& thread_max) {
+    constexpr int G = kPerThread / NG;
+    float cm = -kInf;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) cm = fmaxf(cm, r.elem(i));
+    thread_max = cm;
+    const float nms = cm == -kInf ? 0.f : -cm * scale;
+    s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        float g = 0.f;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const float x = fast_exp2(fmaf(r.elem(j * G + e), scale, nms));
+            s += x;
+            g += x;
+        }
+        gsum[j] = g;
+    }
+    m = cm;
+    wave_merge_ms(m, s, scale);
+}
+
 template <bool BF16, typename Regs>
 __device__ __forceinline__ void wave_chunk_argmax(const Regs& r, int v0, float& best, int& bi,
                                                   unsigned& bad) {

@@ -186,7 +186,12 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
     r.finish(row, v0, len);
 
     // 1. chunk statistics, merged across the four waves as the verify's
-    //    streaming units merge them (side 1 of pair (b, i) of the workspace)
+    //    streaming units merge them (side 1 of pair (b, i) of the workspace);
+    //    sampled rows also keep each thread's group sums (G-entry groups) in
+    //    the thread's own units, for the running sums of step 2
+    constexpr int G = BF16 ? 8 : 4;
+    constexpr int NG = kPerThread / G;
+    float gwt[NG], tmax = -kInf;            // (sampled rows without truncation)
     __shared__ float sm[kWaves], ss[kWaves];
     __shared__ int si[kWaves];
     __shared__ unsigned sb[kWaves];
@@ -210,7 +215,8 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
         }
     } else {
         float m, s;
-        wave_chunk_ms(r, scale, m, s);
+        if (TRUNC && trunc) wave_chunk_ms(r, scale, m, s);       // (no step 2)
+        else wave_chunk_ms_groups(r, scale, m, s, gwt, tmax);
         if (lane == 0) {
             sm[wave] = m;
             ss[wave] = s;
@@ -269,37 +275,25 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
     }
 
     // 2. (sampled rows) while the other chunks' statistics are on their way:
-    //    this chunk's weights exp2((z - m_c) * scale) in token order, as
-    //    group sums gw[j] with their starting running sums gstart[j] (group
-    //    (j, tid) follows every (j', *) with j' < j and every (j, tid') with
-    //    tid' < tid), and the last entry with weight
-    constexpr int G = BF16 ? 8 : 4;
-    constexpr int NG = kPerThread / G;
+    //    this chunk's weights in its own units exp2((z - m_c) * scale), as
+    //    group sums gw[j] (the thread's group sums of step 1, rescaled from
+    //    its maximum to the chunk's) with their starting running sums
+    //    gstart[j] (group (j, tid) follows every (j', *) with j' < j and
+    //    every (j, tid') with tid' < tid)
     __shared__ float gtot[NG][kWaves];
     __shared__ int lastW[kWaves], sTok;
     float gw[NG], gstart[NG], nms = 0.f;
     if (!greedy) {
         const float mc = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
         nms = mc == -kInf ? 0.f : -mc * scale;
-        int lastpos = -1;
+        const float f = tmax == -kInf ? 0.f : fast_exp2((tmax - mc) * scale);
         float incl[NG];
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            float sj = 0.f;
-            int lastin = -1;
-#pragma unroll
-            for (int e = 0; e < G; ++e) {
-                const float x = fast_exp2(fmaf(r.elem(j * G + e), scale, nms));
-                sj += x;
-                if (x > 0.f) lastin = e;
-            }
-            gw[j] = sj;
-            if (lastin >= 0) lastpos = (j * kBlock + tid) * G + lastin;
-            incl[j] = wave_scan_incl(sj);
+            gw[j] = gwt[j] * f;
+            incl[j] = wave_scan_incl(gw[j]);
             if (lane == kWave - 1) gtot[j][wave] = incl[j];
         }
-        lastpos = wave_max_int(lastpos);
-        if (lane == 0) lastW[wave] = lastpos;
         if (tid == 0) sTok = 0x7fffffff;
         __syncthreads();
         float gbase = 0.f;
@@ -391,10 +385,10 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
     if (sDone || sChosen != c) return;
 
     // 4. the owner of the chunk: the group whose running-sum range holds the
-    //    target claims it and scans its entries (the first whose running sum
-    //    exceeds the target, else, rounding, the group's last entry with
-    //    weight); the lowest claimed token wins; with no claim (rounding),
-    //    the chunk's last entry with weight
+    //    target claims it and scans its entries, recomputing their weights
+    //    (the first whose running sum exceeds the target, else, rounding, the
+    //    group's last entry with weight); the lowest claimed token wins; with
+    //    no claim (rounding), the chunk's last entry with weight
     const float tloc = sLocal;
     int claim = 0x7fffffff;
 #pragma unroll
@@ -411,11 +405,25 @@ __device__ __forceinline__ void sample_draft_block(const DraftArgs& a0, TruncScr
                     if (first < 0 && run > tloc) first = e;
                 }
             }
-            claim = (j * kBlock + tid) * G + (first >= 0 ? first : lastin);
+            if (first >= 0 || lastin >= 0) claim = (j * kBlock + tid) * G + (first >= 0 ? first : lastin);
         }
     }
     if (claim != 0x7fffffff) atomicMin(&sTok, claim);
     __syncthreads();
+    if (sTok == 0x7fffffff) {
+        // no claim: the chunk's last entry with weight
+        int lastpos = -1;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+#pragma unroll
+            for (int e = 0; e < G; ++e) {
+                if (fast_exp2(fmaf(r.elem(j * G + e), scale, nms)) > 0.f) lastpos = (j * kBlock + tid) * G + e;
+            }
+        }
+        lastpos = wave_max_int(lastpos);
+        if (lane == 0) lastW[wave] = lastpos;
+        __syncthreads();
+    }
     if (tid == 0) {
         int t = sTok;
         if (t == 0x7fffffff) t = max(max(lastW[0], lastW[1]), max(lastW[2], lastW[3]));
