@@ -645,10 +645,13 @@ __device__ __forceinline__ void emit_candidates(const Regs& r, float L, Cand* ds
 // finite entry >= L, where L is a lower bound of the chunk's keff-th largest
 // entry: each thread keeps its top jj = ceil(2 keff / 256) <= 8 finite
 // entries, so at least keff chunk entries are >= the keff-th largest of those
-// 256 jj values; that value is found by a radix select (two 8-bit digits,
-// each from an LDS histogram whose bin one wave finds) over the top 16 bits
-// of the values' order keys, which for float32 rounds it down to the start of
-// its key range (still a lower bound).  Row 1 (r1) is used only when two.
+// 256 jj values; that value is found over the top 16 bits of the values'
+// order keys, which for float32 rounds it down to the start of its key range
+// (still a lower bound): with one value per thread (jj = 1, keff <= 128) by
+// one wave per row, bit by bit from the top (ballot counts of the keys at or
+// above each trial prefix: three barriers in all), else by a radix select
+// (two 8-bit digits, each from an LDS histogram whose bin one wave finds).
+// Both give the same key.  Row 1 (r1) is used only when two.
 // max0 / max1: the threads' maxima from the statistics pass when given
 // (have_max), used as the tops when jj = 1 (a non-finite maximum means no
 // finite top, or a row the merge rejects as bad).
@@ -672,6 +675,57 @@ __device__ __forceinline__ void chunk_candidates_pair(const Args& a, long long r
 #pragma unroll
             for (int j = 0; j < 8; ++j) kb[j] = 0u;
         }
+    }
+    if (jj == 1) {
+        // one key per thread: the keys to LDS (row 0 in sc.hist, row 1 in
+        // sc.idx2), then one wave per row finds the keff-th largest bit by
+        // bit from the top (ballot counts of keys >= each trial prefix)
+        unsigned* ka_s = sc.hist;
+        unsigned* kb_s = reinterpret_cast<unsigned*>(sc.idx2);
+        __shared__ float sLsel[2];
+        __shared__ int sCnt1[2];
+        __syncthreads();                                    // sc may still be read
+        ka_s[tid] = ka[0];
+        kb_s[tid] = kb[0];
+        if (tid < 2) sCnt1[tid] = 0;
+        __syncthreads();
+        if (wave < (two ? 2 : 1)) {
+            const uint4 q = *reinterpret_cast<const uint4*>((wave ? kb_s : ka_s) + 4 * lane);
+            const unsigned k4[4] = {q.x, q.y, q.z, q.w};
+            int nz = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nz += __popcll(__ballot(k4[e] != 0u));
+            float L = -kInf;                                // fewer finite tops than keff
+            if (nz >= keff) {
+                unsigned T = 0;
+#pragma unroll
+                for (int bit = 15; bit >= 0; --bit) {
+                    const unsigned trial = T | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cnt += __popcll(__ballot(k4[e] >= trial));
+                    if (cnt >= keff) T = trial;
+                }
+                L = key_value(T << 16);
+            }
+            if (lane == 0) sLsel[wave] = L;
+        }
+        __syncthreads();
+        const float La = sLsel[0];
+        const float Lb = two ? sLsel[1] : -kInf;
+        const int v0 = c * kChunk;
+        emit_candidates<BF16>(r0, La, a.ws.cand + cand_base(a, row0, c), a.cand_cap, v0, &sCnt1[0]);
+        if (two) emit_candidates<BF16>(r1, Lb, a.ws.cand + cand_base(a, row1, c), a.cand_cap, v0, &sCnt1[1]);
+        wait_stores();
+        __syncthreads();
+        if (tid == 0) {
+            const int total = sCnt1[0];
+            publish_cand(a.ws.cand_meta + row0 * a.C + c, La, total <= a.cand_cap ? total : -1);
+        } else if (two && tid == kWave) {
+            const int total = sCnt1[1];
+            publish_cand(a.ws.cand_meta + row1 * a.C + c, Lb, total <= a.cand_cap ? total : -1);
+        }
+        return;
     }
     // first digit: histograms h0a / h0b; second digit: h1a / h1b
     unsigned* h0a = sc.hist;                                // kBlock == 256 bins each
