@@ -1349,8 +1349,13 @@ __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, cons
     }
     __syncthreads();
     if (pBad || pMaxCnt[0] > S || pMaxCnt[1] > S) return false;
-    // gather both rows' candidates >= their max L into the halves of (v, idx)
+    // gather both rows' candidates >= their max L into the halves of (v, idx):
+    // the round's kept slots are marked first, then each wave reserves its
+    // share of each half with one LDS atomic (the order within a half is
+    // immaterial: every later step orders by value, then index)
+    const float Lr[2] = {pL[0], pL[1]};
     for (int p0 = 0;;) {
+        unsigned km[2] = {0u, 0u};
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int p = p0 + q * kBlock + tid;
@@ -1358,14 +1363,29 @@ __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, cons
             const int ps = p - side * nspec;
             const int c = min(slot_chunk(ps), a.C - 1);
             const bool listed = p < 2 * nspec && ps - c * S < (int)(pOff[side][c + 1] - pOff[side][c]);
-            const bool keep = listed && cv[q].v >= pL[side] && finite_logit(cv[q].v);
-            // one reservation per side, so that every lane takes part in both
-            const int pos0 = wave_reserve(keep && side == 0, &pN[0]);
-            const int pos1 = wave_reserve(keep && side == 1, &pN[1]);
-            const int pos = side ? pos1 : pos0;
-            if (pos >= 0 && pos < kHalf) {
-                sc.v[side * kHalf + pos] = cv[q].v;
-                sc.idx[side * kHalf + pos] = cv[q].idx;
+            const bool keep = listed && cv[q].v >= Lr[side] && finite_logit(cv[q].v);
+            if (keep) km[side] |= 1u << q;
+        }
+        int o[2];
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            const int cnt = __popc(km[side]);
+            const int incl = wave_scan_incl(cnt);
+            int base = 0;
+            if (lane == kWave - 1 && incl > 0) base = atomicAdd(&pN[side], incl);
+            o[side] = __shfl(base, kWave - 1, kWave) + incl - cnt;
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+            for (int side = 0; side < 2; ++side) {
+                if ((km[side] >> q) & 1u) {
+                    if (o[side] < kHalf) {
+                        sc.v[side * kHalf + o[side]] = cv[q].v;
+                        sc.idx[side * kHalf + o[side]] = cv[q].idx;
+                    }
+                    ++o[side];
+                }
             }
         }
         p0 += NQ * kBlock;
