@@ -1303,6 +1303,13 @@ __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, cons
         pBad = 0;
         pN[0] = pN[1] = 0;
     }
+    // the top-k select's histograms (in idx2: row r, digit d at (r * NP + d)
+    // * 256), cleared here: the first digit is counted by the gather
+    constexpr int NP = BF16 ? 2 : 4;
+    constexpr int KB = 8 * NP;
+    unsigned* h = reinterpret_cast<unsigned*>(sc.idx2);
+#pragma unroll
+    for (int d = 0; d < 2 * NP; ++d) h[d * 256 + tid] = 0;
     __syncthreads();
     // lengths and bounds (waves 0, 2) and row statistics (waves 1, 3)
     {
@@ -1384,6 +1391,7 @@ __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, cons
                         sc.v[side * kHalf + o[side]] = cv[q].v;
                         sc.idx[side * kHalf + o[side]] = cv[q].idx;
                     }
+                    atomicAdd(&h[side * NP * 256 + ((order_key<BF16>(cv[q].v) >> (KB - 8)) & 255u)], 1u);
                     ++o[side];
                 }
             }
@@ -1397,29 +1405,25 @@ __device__ __forceinline__ bool row_merge_pair(const Args& a, int b, int k, cons
     const int n[2] = {pN[0], pN[1]};
     if (n[0] == 0 || n[1] == 0 || n[0] > kHalf || n[1] > kHalf) return false;
     // the top-k threshold of each row: radix select over 8-bit digits, both
-    // rows per pass (histograms in idx2: row r, digit d at (r * NP + d) * 256)
-    constexpr int NP = BF16 ? 2 : 4;
-    constexpr int KB = 8 * NP;
-    unsigned* h = reinterpret_cast<unsigned*>(sc.idx2);
+    // rows per pass (the first digit's counts come from the gather)
     __shared__ unsigned pSel[2];
     __shared__ int pRest[2], pFound[2];
-#pragma unroll
-    for (int d = 0; d < 2 * NP; ++d) h[d * 256 + tid] = 0;
-    __syncthreads();
     unsigned prefix[2] = {0u, 0u};
     int need[2] = {min(pl.keff, n[0]), min(pl.keff, n[1])};
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int shift = KB - 8 * (pass + 1);
+        if (pass > 0) {
 #pragma unroll
-        for (int side = 0; side < 2; ++side) {
-            unsigned* hp = h + (side * NP + pass) * 256;
-            for (int i = tid; i < n[side]; i += kBlock) {
-                const unsigned key = order_key<BF16>(sc.v[side * kHalf + i]);
-                if (pass == 0 || (key >> (shift + 8)) == prefix[side]) atomicAdd(&hp[(key >> shift) & 255u], 1u);
+            for (int side = 0; side < 2; ++side) {
+                unsigned* hp = h + (side * NP + pass) * 256;
+                for (int i = tid; i < n[side]; i += kBlock) {
+                    const unsigned key = order_key<BF16>(sc.v[side * kHalf + i]);
+                    if ((key >> (shift + 8)) == prefix[side]) atomicAdd(&hp[(key >> shift) & 255u], 1u);
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
         if (wave < 2)
             wave_find_bin(h + (wave * NP + pass) * 256, wave ? need[1] : need[0], &pSel[wave], &pRest[wave],
                           &pFound[wave]);
