@@ -371,6 +371,10 @@ __device__ __forceinline__ void decide_pair(const Args& a, int b, int k, const P
             }
         }
     }
+    // the truncation steps' untagged words (kept lists, row records) are
+    // trusted once the status bit is seen: every wave's stores complete
+    // before the barrier that precedes the status update
+    if (trunc) wait_stores();
     __syncthreads();
     if (tid == 0) {
         PairVals v{};

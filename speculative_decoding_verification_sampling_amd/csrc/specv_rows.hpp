@@ -1238,7 +1238,6 @@ __device__ __forceinline__ void short_merge_wave(const Args& a, long long rowid,
         kv[lane] = v;
         kx[lane] = x;
     }
-    wait_stores();                                  // out before the decision is published
     if (lane == 0) {
         TruncRow o{};
         o.zmax = zmax;
